@@ -1,0 +1,25 @@
+"""fp64 CPU oracle for MLA latent-cache decode (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package; the HIP library and its binding never do.
+"""
+from . import mla_ref, brute  # noqa: F401
+from .mla_ref import (  # noqa: F401
+    latent_bytes_per_token,
+    per_head_kv_bytes_per_token,
+    rope_freqs,
+    rope,
+    expand_kv,
+    query_positions,
+    attend_scores,
+    attend_sequence,
+    mla_decode_ref,
+    absorbed_query,
+    absorbed_attend_sequence,
+    split_bounds,
+    attend_partials,
+    lse_combine,
+    cache_slot,
+    cache_append_image,
+)
+from .brute import brute_sequence  # noqa: F401

@@ -1,0 +1,75 @@
+"""Pure-Python scalar MLA decode for tiny inputs.
+
+TEST INFRASTRUCTURE ONLY (same import rule as ``oracle.mla_ref``). A second,
+loop-by-loop statement of the same attention, written without NumPy, used to
+pin ``oracle.mla_ref.attend_sequence`` on inputs small enough for scalar loops.
+
+Per query j of Q (position p = L - Q + j) and head h, for every cached token
+t <= p: the content key is W_UK[h] c_t, the positional key is the RoPE key of
+token t rotated by t, the positional query is q_rope rotated by p; the score is
+scale times the sum of both dot products ("Beyond the Attention Bottleneck",
+"Down-Projection and Up-Projection Mechanics" and "The RoPE Compatibility
+Problem"). Softmax over t, then the weighted sum of V_t = W_UV[h] c_t.
+"""
+import math
+
+
+def _rotate(vec, pos, base):
+    d = len(vec)
+    out = [0.0] * d
+    for i in range(d // 2):
+        ang = pos * base ** (-2.0 * i / d)
+        c, s = math.cos(ang), math.sin(ang)
+        a, b = vec[2 * i], vec[2 * i + 1]
+        out[2 * i] = a * c - b * s
+        out[2 * i + 1] = a * s + b * c
+    return out
+
+
+def _dot(a, b):
+    acc = 0.0
+    for x, y in zip(a, b):
+        acc += x * y
+    return acc
+
+
+def _matvec(m, v):
+    return [_dot(row, v) for row in m]
+
+
+def brute_sequence(c, k_rope, q_nope, q_rope, w_uk, w_uv, scale, base=10000.0):
+    """Nested lists in, nested lists out: (o [Q][H][d_v], o_lat [Q][H][d_c], lse [Q][H])."""
+    L = len(c)
+    Q = len(q_nope)
+    H = len(w_uk)
+    o, o_lat, lse = [], [], []
+    for j in range(Q):
+        p = L - Q + j
+        oj, olj, lj = [], [], []
+        for h in range(H):
+            q_pe = _rotate(q_rope[j][h], p, base)
+            scores = []
+            for t in range(p + 1):
+                k_c = _matvec(w_uk[h], c[t])
+                k_r = _rotate(k_rope[t], t, base)
+                scores.append(scale * (_dot(q_nope[j][h], k_c) + _dot(q_pe, k_r)))
+            m = max(scores)
+            ex = [math.exp(s - m) for s in scores]
+            z = sum(ex)
+            dv = len(w_uv[h])
+            acc = [0.0] * dv
+            acc_lat = [0.0] * len(c[0])
+            for t in range(p + 1):
+                w = ex[t] / z
+                v_t = _matvec(w_uv[h], c[t])
+                for i in range(dv):
+                    acc[i] += w * v_t[i]
+                for i in range(len(c[0])):
+                    acc_lat[i] += w * c[t][i]
+            oj.append(acc)
+            olj.append(acc_lat)
+            lj.append(m + math.log(z))
+        o.append(oj)
+        o_lat.append(olj)
+        lse.append(lj)
+    return o, o_lat, lse

@@ -1,0 +1,375 @@
+"""fp64 CPU oracle for MLA decode over a latent KV cache.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The product path
+(the HIP library and its binding) never imports, links or calls it, and this
+module imports nothing from the product path.
+
+What it computes, and where the pages define it:
+
+* Latent cache entry of one token and layer: a d_c-wide latent c_t plus a
+  d_r-wide decoupled RoPE key, 576 numbers for the DeepSeek MLA shapes
+  ("DeepSeek's Config Says 16 KV Heads, Its Cache Holds a Ninth of That",
+  section 5 "Multi-head latent attention (MLA)"; "The Architecture of Memory",
+  "Decoupled Rotary Positional Encoding (RoPE)").
+* Up-projection K_t = W_UK c_t, V_t = W_UV c_t ("Beyond the Attention
+  Bottleneck", "Down-Projection and Up-Projection Mechanics"), taken per head.
+* The score of a query against a key is the sum of a content part (against
+  the expanded key) and a positional part (against the RoPE key, shared by all
+  heads) ("Beyond the Attention Bottleneck", "The RoPE Compatibility Problem";
+  "The Architecture of Memory", "Decoupled Rotary Positional Encoding (RoPE)").
+* Decode: the new token is appended, then its query attends over the whole
+  cache ("The Architecture of Memory", "The Decode Phase: The Memory Bandwidth
+  Wall"); several drafted tokens are verified in one pass and must agree with
+  token-by-token decoding ("The Architecture of Memory", "Speculative
+  Decoding: Amortizing the Memory Fetch").
+* Split-KV partials merged by a log-sum-exp reduction ("The Architecture of
+  Memory", "Flash-Decoding and FlashInfer").
+* Paged cache: fixed-size pages mapped logical -> physical through a page
+  table ("The Architecture of Memory", "PagedAttention: Virtual Memory for
+  LLMs"; "KV Cache Optimization: Scaling to Million-Token Contexts",
+  technique 7 "Paged Attention (vLLM)").
+
+This oracle NEVER absorbs weights in ``attend_sequence``: it rebuilds every
+head's K_t and V_t from the latent and runs textbook softmax attention. The
+absorbed form exists only in ``absorbed_query`` / ``absorbed_attend_sequence``,
+which the tests use to pin the associativity identity and to check the
+query-absorption kernel.
+
+Readings taken where the pages are silent (each is listed in the design notes):
+RoPE rotates interleaved pairs (x_2i, x_2i+1) by pos * base^(-2i/d_r); the
+cached RoPE key is stored rotated; query j of Q sits at position L - Q + j and
+sees keys t <= L - Q + j; the softmax scale is 1/sqrt(d_n + d_r); only the d_c
+latent columns enter the value side; logs are natural.
+
+Pins (tests/test_oracle_pins.py): brute force in pure Python on tiny inputs,
+absorbed == unabsorbed, L = 1 gives V_0, a zero query gives the mean value,
+RoPE closed forms and relative-position invariance, any split merged by LSE
+equals the unsplit result, Q-token verify equals sequential decode, cache
+accounting against the figures the pages print, append round-trip through the
+page table. No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------
+# cache accounting
+# --------------------------------------------------------------------------
+def latent_bytes_per_token(kv_rank: int, rope_dim: int, elem_bytes: int,
+                           layers: int = 1) -> int:
+    """Bytes one token adds to an MLA cache: one (d_c + d_r) row per layer.
+
+    "DeepSeek's Config Says 16 KV Heads", introduction and section 5: 576
+    numbers x 2 bytes x 27 layers for V2-Lite.
+    """
+    return (kv_rank + rope_dim) * elem_bytes * layers
+
+
+def per_head_kv_bytes_per_token(heads: int, key_dim: int, value_dim: int,
+                                elem_bytes: int, layers: int = 1) -> int:
+    """Bytes one token would add if every head kept its own key and value.
+
+    "DeepSeek's Config Says 16 KV Heads", introduction ((192 + 128) x 16 heads x
+    2 bytes x 27 layers for V2-Lite); "The Architecture of Memory", "DeepSeek's
+    Multi-Head Latent Attention (MLA)" (MHA-equivalent footprint for V3).
+    """
+    return (key_dim + value_dim) * heads * elem_bytes * layers
+
+
+# --------------------------------------------------------------------------
+# RoPE
+# --------------------------------------------------------------------------
+def rope_freqs(rope_dim: int, base: float = 10000.0) -> np.ndarray:
+    """theta_i = base^(-2i/d_r), i = 0 .. d_r/2 - 1 (fp64)."""
+    i = np.arange(rope_dim // 2, dtype=F64)
+    return np.power(F64(base), -2.0 * i / rope_dim)
+
+
+def rope(x, pos, base: float = 10000.0) -> np.ndarray:
+    """Rotate interleaved pairs of the last axis of ``x`` by pos * theta_i.
+
+    ``pos`` broadcasts against ``x.shape[:-1]``. Angles are formed in fp64.
+    The rotation is the position-dependent one the pages require to be applied
+    to the positional query/key parts only ("The Architecture of Memory",
+    "Decoupled Rotary Positional Encoding (RoPE)").
+    """
+    x = np.asarray(x, dtype=F64)
+    pos = np.asarray(pos, dtype=F64)
+    ang = pos[..., None] * rope_freqs(x.shape[-1], base)
+    cs, sn = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (x.shape[-1],)), F64)
+    out[..., 0::2] = x0 * cs - x1 * sn
+    out[..., 1::2] = x0 * sn + x1 * cs
+    return out
+
+
+# --------------------------------------------------------------------------
+# unabsorbed attention (the oracle proper)
+# --------------------------------------------------------------------------
+def expand_kv(c, k_rope_raw, positions, w_uk, w_uv=None, base: float = 10000.0):
+    """Per-head keys and values rebuilt from cached latents.
+
+    K_t,h = [W_UK[h] c_t ; RoPE(k^R_t, t)] (the RoPE key shared by all heads),
+    V_t,h = W_UV[h] c_t ("Beyond the Attention Bottleneck", "Down-Projection
+    and Up-Projection Mechanics" and "The RoPE Compatibility Problem").
+    Returns K [T][H][d_n + d_r] (None when ``w_uk`` is None) and V [T][H][d_v]
+    (None when ``w_uv`` is None).
+    """
+    c = np.asarray(c, F64)
+    T = c.shape[0]
+    k = None
+    if w_uk is not None:
+        w_uk = np.asarray(w_uk, F64)
+        H, dn, dc = w_uk.shape
+        kc = (c @ w_uk.reshape(H * dn, dc).T).reshape(T, H, dn)
+        kr = rope(k_rope_raw, positions, base)
+        k = np.concatenate([kc, np.broadcast_to(kr[:, None, :], (T, H, kr.shape[-1]))], axis=-1)
+    v = None
+    if w_uv is not None:
+        w_uv = np.asarray(w_uv, F64)
+        Hv, dv, dcv = w_uv.shape
+        v = (c @ w_uv.reshape(Hv * dv, dcv).T).reshape(T, Hv, dv)
+    return k, v
+
+
+def query_positions(seq_len: int, q_len: int) -> np.ndarray:
+    """Drafted/current query j sits at L - Q + j (appended before attending)."""
+    return seq_len - q_len + np.arange(q_len)
+
+
+def causal_mask(seq_len: int, pq) -> np.ndarray:
+    """[Q][L] True where key t lies after query position p_j (excluded).
+
+    Drafted tokens form a chain: query j sees the cache up to and including its
+    own position, never a later draft ("The Architecture of Memory", "Tree
+    Attention Verification", the chain being the one-branch tree).
+    """
+    return np.arange(seq_len)[None, :] > np.asarray(pq)[:, None]
+
+
+def attend_scores(c, k_rope_raw, q_nope, q_rope, w_uk, scale, base=10000.0,
+                  chunk: int = 1024) -> np.ndarray:
+    """Masked scores s[j][h][t] = scale * (q_j,h . K_t,h); -inf where t > p_j."""
+    c = np.asarray(c, F64)
+    L = c.shape[0]
+    q_nope = np.asarray(q_nope, F64)
+    Q, H, _ = q_nope.shape
+    pq = query_positions(L, Q)
+    q = np.concatenate([q_nope, rope(q_rope, pq[:, None], base)], axis=-1)  # [Q][H][dk]
+    qh = np.ascontiguousarray(q.transpose(1, 0, 2))                      # [H][Q][dk]
+    s = np.empty((H, Q, L), F64)
+    for t0 in range(0, L, chunk):
+        t1 = min(L, t0 + chunk)
+        k, _ = expand_kv(c[t0:t1], k_rope_raw[t0:t1], np.arange(t0, t1), w_uk, None, base)
+        s[:, :, t0:t1] = np.matmul(qh, np.ascontiguousarray(k.transpose(1, 2, 0)))
+    s *= scale
+    s = s.transpose(1, 0, 2).copy()                                      # [Q][H][L]
+    masked = causal_mask(L, pq)                                          # [Q][L]
+    s[np.broadcast_to(masked[:, None, :], s.shape)] = -np.inf
+    return s
+
+
+def attend_sequence(c, k_rope_raw, q_nope, q_rope, w_uk, w_uv, scale,
+                    base: float = 10000.0, chunk: int = 1024):
+    """Decode attention of one sequence, without absorption.
+
+    c [L][d_c], k_rope_raw [L][d_r] (unrotated, positions 0..L-1),
+    q_nope [Q][H][d_n], q_rope [Q][H][d_r] (unrotated), w_uk [H][d_n][d_c],
+    w_uv [H][d_v][d_c]. Textbook softmax: m = max s, p = e^(s-m) / sum e^(s-m).
+    Returns o [Q][H][d_v] = sum_t p_t V_t,h, o_lat [Q][H][d_c] = sum_t p_t c_t
+    (the same weights applied to the latents) and lse [Q][H] = m + ln sum e^(s-m).
+    """
+    c = np.asarray(c, F64)
+    L = c.shape[0]
+    s = attend_scores(c, k_rope_raw, q_nope, q_rope, w_uk, scale, base, chunk)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    den = e.sum(axis=-1, keepdims=True)
+    p = e / den
+    lse = m[..., 0] + np.log(den[..., 0])
+    Q, H = p.shape[:2]
+    w_uv = np.asarray(w_uv, F64)
+    dv = w_uv.shape[1]
+    o = np.zeros((Q, H, dv), F64)
+    o_lat = np.zeros((Q, H, c.shape[1]), F64)
+    ph = p.transpose(1, 0, 2)                                            # [H][Q][L]
+    for t0 in range(0, L, chunk):
+        t1 = min(L, t0 + chunk)
+        cc = c[t0:t1]
+        _, v = expand_kv(cc, None, None, None, w_uv, base)
+        o += np.matmul(ph[:, :, t0:t1], np.ascontiguousarray(v.transpose(1, 0, 2))).transpose(1, 0, 2)
+        o_lat += np.einsum("qht,tc->qhc", p[:, :, t0:t1], cc, optimize=True)
+    return o, o_lat, lse
+
+
+def mla_decode_ref(inputs, heads: Optional[Sequence[int]] = None,
+                   seqs: Optional[Sequence[int]] = None, chunk: int = 1024):
+    """Oracle over a whole batch drawn by ``workload.make``.
+
+    Returns dict(o [B][Q][H'][d_v], o_lat [B][Q][H'][d_c], lse [B][Q][H']) for
+    the selected heads (all by default) and sequences (all by default; rows of
+    unselected sequences are NaN).
+    """
+    wl = inputs.wl
+    hs = list(range(wl.heads)) if heads is None else list(heads)
+    bs = list(range(wl.batch)) if seqs is None else list(seqs)
+    B, Q = wl.batch, wl.q_len
+    o = np.full((B, Q, len(hs), wl.v_dim), np.nan)
+    o_lat = np.full((B, Q, len(hs), wl.kv_rank), np.nan)
+    lse = np.full((B, Q, len(hs)), np.nan)
+    w_uk = np.asarray(inputs.w_uk, F64)[hs]
+    w_uv = np.asarray(inputs.w_uv, F64)[hs]
+    for b in bs:
+        c, kr = inputs.seq(b)
+        ob, olb, lb = attend_sequence(c, kr, inputs.q_nope[b][:, hs], inputs.q_rope[b][:, hs],
+                                      w_uk, w_uv, wl.softmax_scale, wl.rope_base, chunk)
+        o[b], o_lat[b], lse[b] = ob, olb, lb
+    return {"o": o, "o_lat": o_lat, "lse": lse}
+
+
+# --------------------------------------------------------------------------
+# absorbed algebra (test-only: pins associativity, checks query absorption)
+# --------------------------------------------------------------------------
+def absorbed_query(q_nope, q_rope, w_uk, pos, base: float = 10000.0) -> np.ndarray:
+    """q_full = [W_UK[h]^T q_nope ; RoPE(q_rope, pos)] per (token, head).
+
+    The weight-absorption rearrangement: the content score against the
+    expanded key equals the absorbed query against the latent ("The
+    Architecture of Memory", "The Weight Absorption Trick"; "DeepSeek's Config
+    Says 16 KV Heads", section 5). q_nope [..][H][d_n], q_rope [..][H][d_r],
+    w_uk [H][d_n][d_c], pos broadcasting against q_nope.shape[:-2].
+    Returns [..][H][d_c + d_r].
+    """
+    q_nope = np.asarray(q_nope, F64)
+    w_uk = np.asarray(w_uk, F64)
+    q_lat = np.einsum("...hn,hnc->...hc", q_nope, w_uk)
+    pos = np.asarray(pos, F64)[..., None]
+    q_pe = rope(q_rope, pos, base)
+    return np.concatenate([q_lat, q_pe], axis=-1)
+
+
+def absorbed_attend_sequence(c, k_rope_raw, q_nope, q_rope, w_uk, w_uv, scale,
+                             base: float = 10000.0):
+    """The same attention scored in latent space and up-projected at the end.
+
+    s = scale * (q_lat . c_t + q_pe . RoPE(k^R_t, t)), o = W_UV (sum_t p_t c_t).
+    Used only to pin ``attend_sequence`` (associativity of the products).
+    """
+    c = np.asarray(c, F64)
+    L = c.shape[0]
+    Q = np.asarray(q_nope).shape[0]
+    pq = query_positions(L, Q)
+    qf = absorbed_query(q_nope, q_rope, w_uk, pq, base)                     # [Q][H][D]
+    kf = np.concatenate([c, rope(k_rope_raw, np.arange(L), base)], axis=-1)  # [L][D]
+    s = scale * np.einsum("qhd,td->qht", qf, kf)
+    s[np.broadcast_to(causal_mask(L, pq)[:, None, :], s.shape)] = -np.inf
+    m = s.max(-1, keepdims=True)
+    e = np.exp(s - m)
+    den = e.sum(-1, keepdims=True)
+    p = e / den
+    o_lat = np.einsum("qht,tc->qhc", p, c)
+    o = np.einsum("hvc,qhc->qhv", np.asarray(w_uv, F64), o_lat)
+    return o, o_lat, m[..., 0] + np.log(den[..., 0])
+
+
+# --------------------------------------------------------------------------
+# split-KV partials and the log-sum-exp merge
+# --------------------------------------------------------------------------
+def split_bounds(seq_len: int, num_splits: int, page: int = 64) -> List[Tuple[int, int]]:
+    """Token ranges of the split-KV units of one sequence.
+
+    Reading of "splits the cache into chunks" ("The Architecture of Memory",
+    "Flash-Decoding and FlashInfer"): chunk = page * ceil(ceil(L / S) / page)
+    tokens, unit s covers [s*chunk, min(L, (s+1)*chunk)); units past the end
+    are empty. Chunks are whole pages so a unit never splits a page.
+    """
+    per = -(-seq_len // num_splits)
+    chunk = page * (-(-per // page))
+    return [(min(seq_len, s * chunk), min(seq_len, (s + 1) * chunk)) for s in range(num_splits)]
+
+
+def attend_partials(c, k_rope_raw, q_nope, q_rope, w_uk, scale, num_splits,
+                    base: float = 10000.0, page: int = 64):
+    """Per-split normalised partials of the latent output.
+
+    For unit s over tokens [a, e): o_s = sum_t e^(s_t - m_s) c_t / sum_t e^(s_t - m_s)
+    and lse_s = m_s + ln sum_t e^(s_t - m_s), with the same causal mask as the
+    full decode. An empty (or fully masked) unit gives o_s = 0, lse_s = -inf.
+    Returns o_part [Q][H][S][d_c], lse_part [Q][H][S].
+    """
+    c = np.asarray(c, F64)
+    L = c.shape[0]
+    s = attend_scores(c, k_rope_raw, q_nope, q_rope, w_uk, scale, base)  # [Q][H][L]
+    Q, H = s.shape[:2]
+    o_part = np.zeros((Q, H, num_splits, c.shape[1]), F64)
+    lse_part = np.full((Q, H, num_splits), -np.inf, F64)
+    for si, (a, e) in enumerate(split_bounds(L, num_splits, page)):
+        if e <= a:
+            continue
+        ss = s[:, :, a:e]
+        m = ss.max(-1, keepdims=True)
+        ok = np.isfinite(m[..., 0])
+        msafe = np.where(np.isfinite(m), m, 0.0)
+        w = np.exp(ss - msafe)
+        den = w.sum(-1, keepdims=True)
+        o = np.einsum("qht,tc->qhc", w, c[a:e]) / np.where(den > 0, den, 1.0)
+        o_part[:, :, si] = np.where(ok[..., None], o, 0.0)
+        lse_part[:, :, si] = np.where(ok, msafe[..., 0] + np.log(np.where(den[..., 0] > 0, den[..., 0], 1.0)), -np.inf)
+    return o_part, lse_part
+
+
+def lse_combine(o_part, lse_part):
+    """Merge split partials: LSE = ln sum_s e^(lse_s), o = sum_s e^(lse_s - LSE) o_s.
+
+    The log-sum-exp reduction across splits ("The Architecture of Memory",
+    "Flash-Decoding and FlashInfer"). o_part [..][S][d], lse_part [..][S].
+    Splits with lse = -inf contribute nothing.
+    """
+    o_part = np.asarray(o_part, F64)
+    lse_part = np.asarray(lse_part, F64)
+    m = lse_part.max(axis=-1, keepdims=True)
+    w = np.exp(lse_part - m)
+    tot = w.sum(axis=-1, keepdims=True)
+    lse = (m + np.log(tot))[..., 0]
+    o = np.einsum("...s,...sd->...d", w / tot, o_part)
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# paged cache append (expected pool image)
+# --------------------------------------------------------------------------
+def cache_slot(page_table, seq: int, pos: int, page: int = 64) -> int:
+    """Physical row of logical token ``pos`` of sequence ``seq``:
+    page_table[seq][pos // page] * page + pos % page."""
+    return int(page_table[seq][pos // page]) * page + pos % page
+
+
+def cache_append_image(pool, c, k_rope, seq_idx, pos, page_table, kv_rank: int,
+                       page: int = 64, rotate: bool = False, base: float = 10000.0):
+    """The pool after appending rows [c_n ; k^R_n] at (seq_idx[n], pos[n]).
+
+    ``pool`` is [P][page][D] in any dtype and is copied, never modified. Raw
+    mode copies the values as given (so a bit pattern array gives a byte-exact
+    image); rotate mode stores RoPE(k^R_n, pos[n]) in fp64 instead, the rotated
+    positional key the cache carries ("Beyond the Attention Bottleneck", "The
+    RoPE Compatibility Problem").
+    """
+    out = np.array(pool, copy=True)
+    P, pg, D = out.shape
+    assert pg == page
+    flat = out.reshape(P * page, D)
+    if rotate:
+        flat = flat.astype(F64)
+    for n in range(len(pos)):
+        slot = cache_slot(page_table, int(seq_idx[n]), int(pos[n]), page)
+        flat[slot, :kv_rank] = c[n]
+        flat[slot, kv_rank:] = rope(k_rope[n], pos[n], base) if rotate else k_rope[n]
+    return flat.reshape(P, page, D)

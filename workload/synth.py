@@ -1,0 +1,214 @@
+"""Seeded synthetic MLA decode workloads.
+
+Shapes follow the model facts the pages give for the MLA family: a 512-wide
+latent plus a 64-wide decoupled-RoPE key per token and layer, 16 heads for
+DeepSeek-V2-Lite and 128 for DeepSeek-V2/V3 ("DeepSeek's Config Says 16 KV
+Heads, Its Cache Holds a Ninth of That", section 5 "Multi-head latent attention
+(MLA)"), 64-token pages mapped through a page table ("The Architecture of
+Memory", "PagedAttention: Virtual Memory for LLMs"), and a 32,768-token
+conversation as the reference context length (same page, introduction).
+
+Value recipe (the pages print no data): latents, RoPE keys and queries are
+N(0, 1); W_UK and W_UV are N(0, 1/d_c). Draws are made in float32 and, for bf16
+workloads, rounded to the nearest bf16 (ties to even); the returned float32
+arrays then hold exactly the values the GPU reads, so the oracle can upcast
+them to float64 without a second rounding.
+
+Every tensor has its own counter-free stream, ``default_rng(SeedSequence([seed,
+tag, index]))``, so one sequence's latents can be regenerated without drawing
+any other tensor. Nothing here computes attention, RoPE or any projection.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+PAGE = 64
+
+# stream tags: one independent generator per tensor (and per sequence)
+_T_LENS, _T_WUK, _T_WUV, _T_QN, _T_QR, _T_C, _T_KR, _T_PERM = range(8)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    q_len: int
+    heads: int
+    kv_rank: int          # d_c, latent width
+    rope_dim: int         # d_r, decoupled RoPE key width
+    nope_dim: int         # d_n, per-head content query/key width
+    v_dim: int            # d_v, per-head value width
+    dtype: str            # "f32" or "bf16"
+    seq_len: Optional[int] = None            # fixed length for every sequence
+    len_range: Optional[tuple] = None        # inclusive (lo, hi) uniform lengths
+    paged: bool = False   # True: one seeded permutation of the page pool
+    num_splits: int = 1   # split-KV partitions per sequence used by the bench
+    page_size: int = PAGE
+    rope_base: float = 10000.0
+    description: str = ""
+
+    @property
+    def dim(self) -> int:
+        """Cached row width D = d_c + d_r."""
+        return self.kv_rank + self.rope_dim
+
+    @property
+    def softmax_scale(self) -> float:
+        """1/sqrt(d_n + d_r): the width of one head's full query/key."""
+        return 1.0 / math.sqrt(self.nope_dim + self.rope_dim)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def max_seq_len(self) -> int:
+        return self.seq_len if self.seq_len is not None else int(self.len_range[1])
+
+    @property
+    def max_pages(self) -> int:
+        return -(-self.max_seq_len // self.page_size)
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("tiny_f32", batch=1, q_len=1, heads=4, kv_rank=64, rope_dim=16,
+                 nope_dim=32, v_dim=32, dtype="f32", seq_len=256, num_splits=4,
+                 description="tiny fp32 MLA decode, H=4, d_c=64, d_r=16, L=256"),
+        Workload("v2lite_32k", batch=8, q_len=1, heads=16, kv_rank=512, rope_dim=64,
+                 nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=32,
+                 description="DeepSeek-V2-Lite layer shape, B=8, L=32768, contiguous"),
+        Workload("v2lite_paged_varlen", batch=32, q_len=1, heads=16, kv_rank=512,
+                 rope_dim=64, nope_dim=128, v_dim=128, dtype="bf16",
+                 len_range=(1024, 32768), paged=True, num_splits=16,
+                 description="V2-Lite shape, B=32, L~U[1024,32768], permuted 64-token pages"),
+        Workload("v2_h128_8k", batch=64, q_len=1, heads=128, kv_rank=512, rope_dim=64,
+                 nope_dim=128, v_dim=128, dtype="bf16", seq_len=8192, paged=True,
+                 num_splits=4,
+                 description="DeepSeek-V2 head count, B=64, L=8192, permuted pages"),
+        Workload("v2_h128_1m_q4", batch=1, q_len=4, heads=128, kv_rank=512, rope_dim=64,
+                 nope_dim=128, v_dim=128, dtype="bf16", seq_len=1048576, num_splits=256,
+                 description="1M-token context, Q=4 chain verify, H=128, contiguous"),
+    ]
+}
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bf16 (ties to even), returned as float32 values."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).reshape(x.shape)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of float32 values that are already bf16-representable."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _rng(seed: int, tag: int, idx: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(seed), tag, idx]))
+
+
+def _normal(rng, shape, std, dtype):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return round_bf16(x) if dtype == "bf16" else x
+
+
+def seq_lengths(wl: Workload, seed: int = 0) -> np.ndarray:
+    if wl.seq_len is not None:
+        return np.full(wl.batch, wl.seq_len, dtype=np.int32)
+    lo, hi = wl.len_range
+    return _rng(seed, _T_LENS).integers(lo, hi, endpoint=True, size=wl.batch).astype(np.int32)
+
+
+def seq_latents(wl: Workload, seed: int, b: int, length: int):
+    """(c [length][d_c], k_rope [length][d_r]) of sequence b, unrotated keys."""
+    c = _normal(_rng(seed, _T_C, b), (length, wl.kv_rank), 1.0, wl.dtype)
+    kr = _normal(_rng(seed, _T_KR, b), (length, wl.rope_dim), 1.0, wl.dtype)
+    return c, kr
+
+
+def page_table_for(wl: Workload, seq_lens: np.ndarray, seed: int = 0):
+    """Logical->physical page map [B][max_pages] (-1 = unused) and pool size.
+
+    The pool holds exactly sum(ceil(L_b / page)) pages. Pages are handed out in
+    sequence order; with ``paged`` they come from one seeded permutation of the
+    pool, otherwise each sequence owns a contiguous run (identity layout).
+    """
+    npg = [-(-int(L) // wl.page_size) for L in seq_lens]
+    total = int(sum(npg))
+    order = (_rng(seed, _T_PERM).permutation(total) if wl.paged
+             else np.arange(total))
+    pt = np.full((wl.batch, wl.max_pages), -1, dtype=np.int32)
+    k = 0
+    for b, n in enumerate(npg):
+        pt[b, :n] = order[k:k + n]
+        k += n
+    return pt, total
+
+
+@dataclasses.dataclass
+class Inputs:
+    wl: Workload
+    seed: int
+    seq_lens: np.ndarray          # int32 [B]
+    offsets: np.ndarray           # int64 [B+1], token offsets into c / k_rope
+    w_uk: np.ndarray              # [H][d_n][d_c]
+    w_uv: np.ndarray              # [H][d_v][d_c]
+    q_nope: np.ndarray            # [B][Q][H][d_n]
+    q_rope: np.ndarray            # [B][Q][H][d_r], unrotated
+    page_table: np.ndarray        # int32 [B][max_pages]
+    num_pages: int
+    c: Optional[np.ndarray] = None        # [sum L_b][d_c]
+    k_rope: Optional[np.ndarray] = None   # [sum L_b][d_r], unrotated
+
+    def seq(self, b: int):
+        """Latents and unrotated RoPE keys of sequence b (views or fresh draws)."""
+        if self.c is not None:
+            s, e = int(self.offsets[b]), int(self.offsets[b + 1])
+            return self.c[s:e], self.k_rope[s:e]
+        return seq_latents(self.wl, self.seed, b, int(self.seq_lens[b]))
+
+
+def make(wl: Workload, seed: int = 0, with_latents: bool = True,
+         seq_lens: Optional[Sequence[int]] = None) -> Inputs:
+    """Draw every input of one decode step of ``wl``.
+
+    ``seq_lens`` overrides the drawn lengths (used for edge cases); latents are
+    still drawn per sequence from the same streams.
+    """
+    lens = (np.asarray(seq_lens, dtype=np.int32) if seq_lens is not None
+            else seq_lengths(wl, seed))
+    assert lens.shape == (wl.batch,)
+    H, dn, dv, dc, dr = wl.heads, wl.nope_dim, wl.v_dim, wl.kv_rank, wl.rope_dim
+    wstd = 1.0 / math.sqrt(dc)
+    w_uk = _normal(_rng(seed, _T_WUK), (H, dn, dc), wstd, wl.dtype)
+    w_uv = _normal(_rng(seed, _T_WUV), (H, dv, dc), wstd, wl.dtype)
+    q_nope = _normal(_rng(seed, _T_QN), (wl.batch, wl.q_len, H, dn), 1.0, wl.dtype)
+    q_rope = _normal(_rng(seed, _T_QR), (wl.batch, wl.q_len, H, dr), 1.0, wl.dtype)
+    offsets = np.zeros(wl.batch + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(lens.astype(np.int64))
+    pt, total = page_table_for(wl, lens, seed)
+    inp = Inputs(wl, seed, lens, offsets, w_uk, w_uv, q_nope, q_rope, pt, total)
+    if with_latents:
+        T = int(offsets[-1])
+        fdt = np.float32
+        inp.c = np.empty((T, dc), dtype=fdt)
+        inp.k_rope = np.empty((T, dr), dtype=fdt)
+        for b in range(wl.batch):
+            c, kr = seq_latents(wl, seed, b, int(lens[b]))
+            inp.c[offsets[b]:offsets[b + 1]] = c
+            inp.k_rope[offsets[b]:offsets[b + 1]] = kr
+    return inp
