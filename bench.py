@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA decode step on one MI355X.
+
+A step is the whole hot path over one batch: query absorption, append of the
+B*Q new cache rows, split-KV decode, log-sum-exp combine, value
+up-projection. The default workload is the DeepSeek-V2-Lite layer shape at
+32K context (B = 8 sequences of 32,768 tokens, 16 heads, 512 + 64 latent
+row). Inputs are seeded synthetic tensors already resident in HBM when the
+timed region starts. One cache per layer is rotated (27 layers, as V2-Lite
+has) so every step reads its latent cache from HBM rather than from the
+256 MB Infinity Cache.
+
+Prints one JSON line. value = latent-cache bytes read per step / step time
+(GB/s); the decode kernel's own rate against the 8 TB/s HBM peak is in
+"roofline"; the fp64 oracle timed on the host cores is in "cpu_baseline".
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode latent-cache GB/s (% of HBM peak) + decode tokens/s, V2-Lite 32K"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+LAYERS = {"v2lite_32k": 27, "v2lite_paged_varlen": 27, "v2_h128_8k": 4, "v2_h128_1m_q4": 2,
+          "tiny_f32": 4}
+DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc", "mla_decode_mfma.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="v2lite_32k")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0)
+    ap.add_argument("--graph", action="store_true", help="replay each layer's step as a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=0)
+    return ap.parse_args()
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(wl_name, kernel_src_hash):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current decode kernel source."""
+    p = os.path.join(ROOT, "profiles", f"decode_{wl_name}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("decode_src_sha256_16") != kernel_src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, nseq):
+    """Time the fp64 oracle on the host cores over the first ``nseq`` sequences."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    seqs = list(range(nseq))
+    t = time.perf_counter()
+    oracle.mla_decode_ref(inp, seqs=seqs)
+    dt = time.perf_counter() - t
+    nbytes = sum(int(inp.seq_lens[b]) for b in seqs) * wl.dim * wl.elem_bytes
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{nseq} of {wl.batch} sequences ({nbytes / 2**20:.0f} MiB of latent cache), "
+                      f"all {wl.heads} heads, {dt:.1f} s; fp64 unabsorbed NumPy oracle",
+            "seconds": dt, "tokens_per_s": nseq * wl.q_len / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design note, not an implementation)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import workload
+    import mla_latent_kv_03_amd as mla
+    from mla_latent_kv_03_amd.pipeline import DecodeStep, fill_cache, upload
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mla.lib()
+    wl = workload.WORKLOADS[args.workload]
+    if args.num_splits:
+        wl = wl.replace(num_splits=args.num_splits)
+    n_layers = args.layers or LAYERS.get(wl.name, 2)
+    cfg = mla.Config.from_workload(wl)
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    t_setup = time.perf_counter()
+    inp = workload.make(wl, 0)
+    B, Q, H = wl.batch, wl.q_len, wl.heads
+
+    # ---- device state: one cache pool per layer (same bytes, distinct addresses)
+    pt = upload(inp.page_table, torch.int32)
+    seq_lens = upload(inp.seq_lens, torch.int32)
+    pool0 = torch.full((inp.num_pages, wl.page_size, wl.dim), float("nan"), dtype=dt, device="cuda")
+    si = np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(inp.seq_lens)])
+    pos = np.concatenate([np.arange(int(L), dtype=np.int32) for L in inp.seq_lens])
+    fill_cache(cfg, pool0, pt, upload(inp.c, dt), upload(inp.k_rope, dt), upload(si, torch.int32),
+               upload(pos, torch.int32))
+    pools = [pool0] + [pool0.clone() for _ in range(n_layers - 1)]
+    q_nope, q_rope = upload(inp.q_nope, dt), upload(inp.q_rope, dt)
+    w_uk, w_uv = upload(inp.w_uk, dt), upload(inp.w_uv, dt)
+    rows = np.concatenate([inp.offsets[b] + np.arange(int(L) - Q, int(L))
+                           for b, L in enumerate(inp.seq_lens)])
+    c_new, k_new = upload(inp.c[rows], dt), upload(inp.k_rope[rows], dt)
+    steps = [DecodeStep(cfg, B, Q, wl.num_splits, inp.seq_lens) for _ in range(1)]
+    st = steps[0]
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    stream = torch.cuda.current_stream()
+
+    def one_step(layer):
+        pool = pools[layer % n_layers]
+        st.absorb(q_nope, q_rope, w_uk)
+        st.append(c_new, k_new, pt, pool)
+        st.decode(pool, pt, seq_lens)
+        st.combine()
+        st.up_project(w_uv)
+
+    graphs = None
+    if args.graph:
+        for layer in range(n_layers):
+            one_step(layer)
+        torch.cuda.synchronize()
+        graphs = []
+        for layer in range(n_layers):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                one_step(layer)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(layer):
+        if graphs is not None:
+            graphs[layer % n_layers].replay()
+        else:
+            one_step(layer)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        run(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- per-launch durations of the decode kernel (and decode + combine),
+    # HIP events on the launch stream around each call of a second timed pass
+    kd = max(20, min(args.steps, 200))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(kd)]
+    torch.cuda.synchronize()
+    for i in range(kd):
+        pool = pools[i % n_layers]
+        st.absorb(q_nope, q_rope, w_uk)
+        st.append(c_new, k_new, pt, pool)
+        evs[i][0].record(stream)
+        st.decode(pool, pt, seq_lens)
+        evs[i][1].record(stream)
+        st.combine()
+        evs[i][2].record(stream)
+        st.up_project(w_uv)
+    torch.cuda.synchronize()
+    d_ms = sorted(a.elapsed_time(b) for a, b, _ in evs)
+    dc_ms = sorted(a.elapsed_time(c) for a, _, c in evs)
+    decode_ms = sum(d_ms) / len(d_ms)
+    decode_med = d_ms[len(d_ms) // 2]
+    dc_med = dc_ms[len(dc_ms) // 2]
+
+    # ---- algorithmic work
+    total_tokens = int(inp.seq_lens.astype(np.int64).sum())
+    cache_bytes = total_tokens * wl.dim * wl.elem_bytes            # read once per step
+    flops = total_tokens * Q * H * (2 * wl.dim + 2 * wl.kv_rank)
+    gbs_step = cache_bytes / (ms_step * 1e-3) / 1e9
+    gbs_decode = cache_bytes / (decode_ms * 1e-3) / 1e9
+    tflops_decode = flops / (decode_ms * 1e-3) / 1e12
+    ai = flops / cache_bytes
+    bound = "hbm" if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    kernel = mla.decode_kernel_kind(cfg, Q)
+    khash = src_hash(DECODE_SRC)
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs_decode, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs_decode / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops_decode, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops_decode / BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = traffic_from_profile(wl.name, khash)
+    roof["kernel"] = "decode_mfma_kernel" if kernel == "mfma_bf16" else "decode_generic_kernel"
+    roof["algorithmic_bytes_per_launch"] = cache_bytes
+    roof["algorithmic_flops_per_launch"] = flops
+    roof["avg_launch_us"] = round(decode_ms * 1e3, 2)
+    roof["median_launch_us"] = round(decode_med * 1e3, 2)
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs_step, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded N(0,1) latents/keys/queries, N(0,1/d_c) weights",
+        "config": {"workload": wl.name, "batch": B, "q_len": Q, "heads": H,
+                   "seq_len": wl.seq_len if wl.seq_len else list(wl.len_range),
+                   "total_cached_tokens": total_tokens, "kv_rank": wl.kv_rank,
+                   "rope_dim": wl.rope_dim, "page_size": wl.page_size,
+                   "paged": wl.paged, "num_splits": wl.num_splits,
+                   "layer_caches_rotated": n_layers, "hip_graph": bool(args.graph),
+                   "decode_kernel": kernel},
+        "pct_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(B * Q / (ms_step * 1e-3), 1),
+        "decode_gbs": round(gbs_decode, 1),
+        "decode_combine_gbs": round(cache_bytes / (dc_med * 1e-3) / 1e9, 1),
+        "decode_tflops": round(tflops_decode, 2),
+        "mfma_pct": round(100 * tflops_decode / BF16_PEAK_TFLOPS, 2),
+        "roofline": roof,
+        "setup_s": round(t_setup, 1),
+        "decode_src_sha256_16": khash,
+    }
+    if wl.name.startswith("v2lite"):
+        out["v2lite_attention_tokens_per_s_27_layers"] = round(B / (27 * ms_step * 1e-3), 1)
+    if not args.no_cpu_baseline:
+        nseq = args.cpu_sample_seqs or max(1, min(B, 2))
+        out["cpu_baseline"] = cpu_baseline(wl, inp, nseq)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

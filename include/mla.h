@@ -1,0 +1,191 @@
+/*
+ * mla.h - C ABI of the MLA latent-cache decode library (libmla.so, gfx950).
+ *
+ * Multi-Head Latent Attention caches one row per token and layer: a d_c-wide
+ * latent c_t followed by a d_r-wide RoPE key k^R_t (rotated by the token's
+ * position), D = d_c + d_r numbers ("DeepSeek's Config Says 16 KV Heads, Its
+ * Cache Holds a Ninth of That", section 5 "Multi-head latent attention (MLA)";
+ * "The Architecture of Memory", "Decoupled Rotary Positional Encoding (RoPE)").
+ * One decode step runs five calls, in this order:
+ *
+ *   mla_absorb_q        query -> latent space through W_UK, RoPE on the query
+ *   mla_cache_append    write the new token rows through the page table
+ *   mla_decode_paged    split-KV attention of the absorbed queries over the cache
+ *   mla_splitkv_combine log-sum-exp merge of the split partials
+ *   mla_up_project_v    latent output -> per-head value space through W_UV
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument except `cfg` is a DEVICE pointer; `cfg` is a host
+ *     pointer read during the call only. The caller owns all memory; the
+ *     library never allocates, frees or keeps a pointer after returning.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and returns once the work is enqueued. The
+ *     library keeps no state and may be called from several threads.
+ *   - Layouts are dense, row-major, in the order written in brackets; element
+ *     type "T" is cfg->dtype (fp32 or bf16) for queries, weights, cache and
+ *     outputs; partials are always fp32.
+ *   - Device buffers must be 16-byte aligned (MLA_ERR_ALIGN otherwise).
+ *   - Host-side checks run before any launch; on error nothing is enqueued
+ *     and the call returns the status. MLA_ERR_HIP means a launch failed.
+ *   - Device-side data that the host cannot see (page-table entries, lengths,
+ *     positions) is bounds-checked in the kernels: an invalid entry is never
+ *     followed out of bounds. Appends of invalid rows are dropped; a sequence
+ *     whose length or pages are invalid gets NaN outputs.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  MLA_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent    */
+  MLA_ERR_DTYPE = 3,       /* cfg->dtype is not an mla_dtype_t                    */
+  MLA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned             */
+  MLA_ERR_CAPACITY = 5,    /* pages or lengths cannot hold what was asked         */
+  MLA_ERR_UNSUPPORTED = 6, /* a valid shape this build has no kernel for          */
+  MLA_ERR_HIP = 7          /* the HIP runtime reported an error                   */
+} mla_status_t;
+
+/* Shape of one MLA attention layer.
+ *   num_heads  H    query heads (all share the one latent row per token)
+ *   kv_rank    d_c  latent width (512 for DeepSeek-V2/V3, V2-Lite, Kimi K2)
+ *   rope_dim   d_r  decoupled RoPE key width, even (64 for the same models)
+ *   nope_dim   d_n  per-head content query/key width before absorption (128)
+ *   v_dim      d_v  per-head value width (128)
+ *   page_size       tokens per cache page; a power of two in [16, 256]
+ *   dtype           mla_dtype_t of every T-typed buffer
+ *   softmax_scale   multiplies q.k before the softmax (1/sqrt(d_n + d_r))
+ *   rope_base       RoPE base; pair i of a d_r-wide vector at position p is
+ *                   rotated by p * rope_base^(-2i/d_r) (interleaved pairs)
+ * Limits of this build: 1 <= H <= 1024, 16 <= d_c <= 1024, 2 <= d_r <= 256,
+ * 1 <= d_n, d_v <= 256, d_c and d_r multiples of 8 (bf16) or 4 (fp32). */
+typedef struct {
+  int32_t num_heads;
+  int32_t kv_rank;
+  int32_t rope_dim;
+  int32_t nope_dim;
+  int32_t v_dim;
+  int32_t page_size;
+  int32_t dtype;
+  float softmax_scale;
+  float rope_base;
+} mla_config_t;
+
+/* Append modes. */
+enum { MLA_APPEND_RAW = 0, MLA_APPEND_ROTATE = 1 };
+
+/* Library version and target, e.g. "libmla 0.1 gfx950". Static string. */
+const char* mla_build_info(void);
+
+/* Human-readable name of a status code. Static string, never NULL. */
+const char* mla_status_str(mla_status_t status);
+
+/* MLA_OK if the config is within this build's limits, else the error code. */
+mla_status_t mla_config_validate(const mla_config_t* cfg);
+
+/* Bytes of one cached row: (d_c + d_r) * sizeof(T); 0 for an invalid config.
+ * 1,152 B for d_c = 512, d_r = 64 in bf16 ("DeepSeek's Config Says 16 KV
+ * Heads", introduction; "The Architecture of Memory", "DeepSeek's Multi-Head
+ * Latent Attention (MLA)"). */
+size_t mla_cache_bytes_per_token(const mla_config_t* cfg);
+
+/* Split-KV plan: partition s of a sequence of length L covers tokens
+ * [s*chunk, min(L, (s+1)*chunk)) with chunk = page_size * ceil(ceil(L/S) /
+ * page_size); partitions past the end are empty (o = 0, lse = -inf). Writes
+ * the chunk length to *chunk_tokens. Host helper mirroring the kernels. */
+mla_status_t mla_split_chunk(const mla_config_t* cfg, int32_t seq_len, int32_t num_splits,
+                             int32_t* chunk_tokens);
+
+/* A split count that fills the GPU for this batch (a heuristic; any value in
+ * [1, 4096] is valid). num_cus = compute units of the device (256 on MI355X). */
+int32_t mla_default_num_splits(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                               int32_t max_seq_len, int32_t num_cus);
+
+/* Name of the decode kernel mla_decode_paged takes for this shape: "mfma_bf16"
+ * (bf16, d_c = 512, d_r = 64, page_size a multiple of 16, q_len*H a multiple
+ * of 16) or "generic". Static string; "invalid" for an invalid config. */
+const char* mla_decode_kernel_name(const mla_config_t* cfg, int32_t q_len);
+
+/* Bytes of o_part plus lse_part for mla_decode_paged:
+ * batch*q_len*H*num_splits*(d_c + 1)*4. 0 for invalid arguments. */
+size_t mla_decode_partials_bytes(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                 int32_t num_splits);
+
+/* a1. Query absorption and query RoPE ("The Architecture of Memory", "The
+ * Weight Absorption Trick" and "Decoupled Rotary Positional Encoding (RoPE)";
+ * "DeepSeek's Config Says 16 KV Heads", section 5):
+ *   q_full[n][h][0:d_c]   = W_UK[h]^T q_nope[n][h]          (fp32 accumulate)
+ *   q_full[n][h][d_c:D]   = RoPE(q_rope[n][h], pos[n])      (angles in fp64)
+ * q_nope [n_tok][H][d_n] T, q_rope [n_tok][H][d_r] T, pos [n_tok] int32,
+ * w_uk [H][d_n][d_c] T, q_full [n_tok][H][D] T (out). n_tok = 0 is a no-op. */
+mla_status_t mla_absorb_q(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                          const void* q_rope, const int32_t* pos, const void* w_uk,
+                          void* q_full, void* stream);
+
+/* a2. Paged cache append ("The Architecture of Memory", "PagedAttention:
+ * Virtual Memory for LLMs"; "KV Cache Optimization: Scaling to Million-Token
+ * Contexts", technique 7): row n goes to physical row
+ *   page_table[seq_idx[n]][pos[n] / page_size] * page_size + pos[n] % page_size
+ * of cache [num_pages][page_size][D] T as [c_kv[n] ; k], where k = k_rope[n]
+ * rotated by pos[n] (MLA_APPEND_ROTATE) or copied unchanged (MLA_APPEND_RAW).
+ * c_kv [n_tok][d_c] T, k_rope [n_tok][d_r] T, seq_idx, pos [n_tok] int32,
+ * page_table [batch][max_pages] int32. Rows whose seq_idx, pos or page entry
+ * is out of range are skipped. Rows that target the same slot race. */
+mla_status_t mla_cache_append(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                              const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                              const int32_t* page_table, int32_t batch, int32_t max_pages,
+                              void* cache, int64_t num_pages, int32_t flags, void* stream);
+
+/* a4. Split-KV paged decode ("The Architecture of Memory", "Flash-Decoding
+ * and FlashInfer" and "The Decode Phase: The Memory Bandwidth Wall";
+ * "Speculative Decoding: Amortizing the Memory Fetch" for q_len > 1).
+ * For sequence b (length L_b = seq_lens[b], which includes the q_len newest
+ * tokens), query j at position p = L_b - q_len + j, head h, partition s:
+ *   score_t = softmax_scale * (q_full[b][j][h] . cache_row(b, t)),  t <= p
+ *   o_part[b][j][h][s]   = sum_t e^(score_t - m) c_t / sum_t e^(score_t - m)
+ *   lse_part[b][j][h][s] = m + ln sum_t e^(score_t - m)   (natural log)
+ * over the tokens t of partition s (plan: mla_split_chunk). c_t = the first
+ * d_c entries of the row. Empty partitions: o = 0, lse = -inf.
+ * q_full [batch][q_len][H][D] T, cache [num_pages][page_size][D] T,
+ * page_table [batch][max_pages] int32, seq_lens [batch] int32,
+ * o_part [batch][q_len][H][num_splits][d_c] f32, lse_part [batch][q_len][H][num_splits] f32.
+ * Host checks: 1 <= q_len <= max_seq_len <= max_pages * page_size,
+ * 1 <= num_splits <= 4096. Device: q_len <= L_b <= max_seq_len and page
+ * entries in [0, num_pages), else that sequence's outputs are NaN. */
+mla_status_t mla_decode_paged(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                              int32_t num_splits, int32_t max_seq_len, const void* q_full,
+                              const void* cache, int64_t num_pages, const int32_t* page_table,
+                              int32_t max_pages, const int32_t* seq_lens, float* o_part,
+                              float* lse_part, void* stream);
+
+/* a5. Log-sum-exp merge of the partitions ("The Architecture of Memory",
+ * "Flash-Decoding and FlashInfer"), per row r = (b, j, h):
+ *   LSE = ln sum_s e^(lse_s),  o_lat[r] = sum_s e^(lse_s - LSE) o_part[r][s]
+ * o_part, lse_part as written by mla_decode_paged; o_lat [batch][q_len][H][d_c] T
+ * (out); lse [batch][q_len][H] f32 (out, may be NULL). */
+mla_status_t mla_splitkv_combine(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                 int32_t num_splits, const float* o_part, const float* lse_part,
+                                 void* o_lat, float* lse, void* stream);
+
+/* a6. Value up-projection ("Beyond the Attention Bottleneck", "Down-Projection
+ * and Up-Projection Mechanics"; "DeepSeek's Config Says 16 KV Heads", section
+ * 5, where the expansion is folded into the output side):
+ *   out[n][h][0:d_v] = W_UV[h] o_lat[n][h]   (fp32 accumulate)
+ * o_lat [n_tok][H][d_c] T, w_uv [H][d_v][d_c] T, out [n_tok][H][d_v] T. */
+mla_status_t mla_up_project_v(const mla_config_t* cfg, int32_t n_tok, const void* o_lat,
+                              const void* w_uv, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

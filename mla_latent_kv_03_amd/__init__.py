@@ -1,0 +1,38 @@
+"""MLA latent-cache decode on MI355X (gfx950): Python binding of libmla.so.
+
+The binding only marshals arguments: it checks tensor dtypes, devices and
+sizes on the host (the C ABI sees raw pointers and cannot), then calls the
+entry point of the same name in libmla.so on the current torch stream. Every
+step of the decode path runs in the library's HIP kernels; there is no
+fallback. If the library is missing, every call raises.
+
+    cfg = Config(num_heads=16, kv_rank=512, rope_dim=64, nope_dim=128, v_dim=128)
+    absorb_q(cfg, q_nope, q_rope, pos, w_uk, q_full)
+    cache_append(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache)
+    decode_paged(cfg, q_full, cache, page_table, seq_lens, o_part, lse_part, max_seq_len)
+    splitkv_combine(cfg, o_part, lse_part, o_lat, lse)
+    up_project_v(cfg, o_lat, w_uv, out)
+"""
+from ._binding import (  # noqa: F401
+    F32,
+    BF16,
+    APPEND_RAW,
+    APPEND_ROTATE,
+    Config,
+    MLAError,
+    lib,
+    lib_path,
+    build_info,
+    status_str,
+    config_validate,
+    cache_bytes_per_token,
+    split_chunk,
+    default_num_splits,
+    decode_partials_bytes,
+    decode_kernel_kind,
+    absorb_q,
+    cache_append,
+    decode_paged,
+    splitkv_combine,
+    up_project_v,
+)

@@ -1,0 +1,277 @@
+"""ctypes binding of include/mla.h (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla.so")
+
+F32, BF16 = 0, 1
+APPEND_RAW, APPEND_ROTATE = 0, 1
+_STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE",
+           4: "MLA_ERR_ALIGN", 5: "MLA_ERR_CAPACITY", 6: "MLA_ERR_UNSUPPORTED", 7: "MLA_ERR_HIP"}
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}")
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("kv_rank", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32), ("nope_dim", ctypes.c_int32),
+                ("v_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("rope_base", ctypes.c_float)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """Mirror of mla_config_t. ``softmax_scale`` defaults to 1/sqrt(d_n + d_r)."""
+    num_heads: int
+    kv_rank: int = 512
+    rope_dim: int = 64
+    nope_dim: int = 128
+    v_dim: int = 128
+    page_size: int = 64
+    dtype: int = BF16
+    softmax_scale: Optional[float] = None
+    rope_base: float = 10000.0
+
+    @property
+    def dim(self) -> int:
+        return self.kv_rank + self.rope_dim
+
+    @property
+    def scale(self) -> float:
+        return (self.softmax_scale if self.softmax_scale is not None
+                else 1.0 / math.sqrt(self.nope_dim + self.rope_dim))
+
+    def c(self) -> _Cfg:
+        return _Cfg(self.num_heads, self.kv_rank, self.rope_dim, self.nope_dim, self.v_dim,
+                    self.page_size, self.dtype, self.scale, self.rope_base)
+
+    @staticmethod
+    def from_workload(wl) -> "Config":
+        return Config(num_heads=wl.heads, kv_rank=wl.kv_rank, rope_dim=wl.rope_dim,
+                      nope_dim=wl.nope_dim, v_dim=wl.v_dim, page_size=wl.page_size,
+                      dtype=F32 if wl.dtype == "f32" else BF16,
+                      softmax_scale=wl.softmax_scale, rope_base=wl.rope_base)
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmla.so not found at {LIB_PATH}: build it first "
+                           "(python -m mla_latent_kv_03_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, VP, FP = (ctypes.POINTER(_Cfg), ctypes.c_int32, ctypes.c_int64,
+                           ctypes.c_void_p, ctypes.c_void_p)
+    sig = {
+        "mla_build_info": (ctypes.c_char_p, []),
+        "mla_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "mla_config_validate": (ctypes.c_int, [P]),
+        "mla_cache_bytes_per_token": (ctypes.c_size_t, [P]),
+        "mla_split_chunk": (ctypes.c_int, [P, I32, I32, ctypes.POINTER(ctypes.c_int32)]),
+        "mla_default_num_splits": (ctypes.c_int32, [P, I32, I32, I32, I32]),
+        "mla_decode_partials_bytes": (ctypes.c_size_t, [P, I32, I32, I32]),
+        "mla_decode_kernel_name": (ctypes.c_char_p, [P, I32]),
+        "mla_absorb_q": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, VP]),
+        "mla_cache_append": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, I32, I32, VP, I64, I32, VP]),
+        "mla_decode_paged": (ctypes.c_int, [P, I32, I32, I32, I32, VP, VP, I64, VP, I32, VP, FP, FP, VP]),
+        "mla_splitkv_combine": (ctypes.c_int, [P, I32, I32, I32, FP, FP, VP, FP, VP]),
+        "mla_up_project_v": (ctypes.c_int, [P, I32, VP, VP, VP, VP]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    try:
+        return lib().mla_status_str(int(status)).decode()
+    except RuntimeError:
+        return _STATUS.get(int(status), f"status {status}")
+
+
+def build_info() -> str:
+    return lib().mla_build_info().decode()
+
+
+def _ck(status: int, where: str):
+    if status != 0:
+        raise MLAError(status, where)
+
+
+def config_validate(cfg: Config) -> int:
+    return lib().mla_config_validate(ctypes.byref(cfg.c()))
+
+
+def cache_bytes_per_token(cfg: Config) -> int:
+    return lib().mla_cache_bytes_per_token(ctypes.byref(cfg.c()))
+
+
+def split_chunk(cfg: Config, seq_len: int, num_splits: int) -> int:
+    out = ctypes.c_int32(0)
+    _ck(lib().mla_split_chunk(ctypes.byref(cfg.c()), seq_len, num_splits, ctypes.byref(out)),
+        "mla_split_chunk")
+    return out.value
+
+
+def default_num_splits(cfg: Config, batch: int, q_len: int, max_seq_len: int,
+                       num_cus: int = 256) -> int:
+    return lib().mla_default_num_splits(ctypes.byref(cfg.c()), batch, q_len, max_seq_len, num_cus)
+
+
+def decode_partials_bytes(cfg: Config, batch: int, q_len: int, num_splits: int) -> int:
+    return lib().mla_decode_partials_bytes(ctypes.byref(cfg.c()), batch, q_len, num_splits)
+
+
+def decode_kernel_kind(cfg: Config, q_len: int) -> str:
+    """Which decode kernel libmla takes for this shape: "mfma_bf16" or "generic"."""
+    return lib().mla_decode_kernel_name(ctypes.byref(cfg.c()), q_len).decode()
+
+
+# --------------------------------------------------------------------------
+# tensor marshalling
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _elem_dtype(cfg: Config):
+    t = _torch()
+    return t.float32 if cfg.dtype == F32 else t.bfloat16
+
+
+def _need(x, name: str, dtype, numel: int):
+    t = _torch()
+    if not isinstance(x, t.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not x.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if x.dtype != dtype:
+        raise TypeError(f"{name}: dtype {x.dtype}, expected {dtype}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if x.numel() != numel:
+        raise ValueError(f"{name}: {x.numel()} elements, expected {numel}")
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    t = _torch()
+    if stream is None:
+        stream = t.cuda.current_stream()
+    h = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(h)
+
+
+def absorb_q(cfg: Config, q_nope, q_rope, pos, w_uk, q_full, stream=None):
+    """a1: q_full[n][h] = [W_UK[h]^T q_nope[n][h] ; RoPE(q_rope[n][h], pos[n])]."""
+    t = _torch()
+    n = int(pos.numel())
+    H, dt = cfg.num_heads, _elem_dtype(cfg)
+    args = (_need(q_nope, "q_nope", dt, n * H * cfg.nope_dim),
+            _need(q_rope, "q_rope", dt, n * H * cfg.rope_dim),
+            _need(pos, "pos", t.int32, n),
+            _need(w_uk, "w_uk", dt, H * cfg.nope_dim * cfg.kv_rank),
+            _need(q_full, "q_full", dt, n * H * cfg.dim))
+    _ck(lib().mla_absorb_q(ctypes.byref(cfg.c()), n, *args, _stream(stream)), "mla_absorb_q")
+
+
+def cache_append(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache,
+                 mode: int = APPEND_ROTATE, stream=None):
+    """a2: write rows [c_kv[n] ; k] at page_table[seq_idx[n]][pos[n] // page] ..."""
+    t = _torch()
+    n = int(pos.numel())
+    dt = _elem_dtype(cfg)
+    if page_table.dim() != 2:
+        raise ValueError("page_table: expected [batch][max_pages]")
+    batch, max_pages = page_table.shape
+    if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != cfg.dim:
+        raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{cfg.dim}]")
+    num_pages = int(cache.shape[0])
+    args = (_need(c_kv, "c_kv", dt, n * cfg.kv_rank),
+            _need(k_rope, "k_rope", dt, n * cfg.rope_dim),
+            _need(seq_idx, "seq_idx", t.int32, n),
+            _need(pos, "pos", t.int32, n),
+            _need(page_table, "page_table", t.int32, batch * max_pages))
+    cp = _need(cache, "cache", dt, cache.numel())
+    _ck(lib().mla_cache_append(ctypes.byref(cfg.c()), n, *args, batch, max_pages, cp, num_pages,
+                               mode, _stream(stream)), "mla_cache_append")
+
+
+def decode_paged(cfg: Config, q_full, cache, page_table, seq_lens, o_part, lse_part,
+                 max_seq_len: int, stream=None):
+    """a4: split-KV partials. q_full [B][Q][H][D]; o_part [B][Q][H][S][d_c] f32;
+    lse_part [B][Q][H][S] f32 (S = num_splits from lse_part's last axis)."""
+    t = _torch()
+    if q_full.dim() != 4:
+        raise ValueError("q_full: expected [batch][q_len][H][D]")
+    B, Q = int(q_full.shape[0]), int(q_full.shape[1])
+    if lse_part.dim() != 4:
+        raise ValueError("lse_part: expected [batch][q_len][H][num_splits]")
+    S = int(lse_part.shape[3])
+    H, dt = cfg.num_heads, _elem_dtype(cfg)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table: expected [batch][max_pages]")
+    max_pages = int(page_table.shape[1])
+    if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != cfg.dim:
+        raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{cfg.dim}]")
+    num_pages = int(cache.shape[0])
+    args = (_need(q_full, "q_full", dt, B * Q * H * cfg.dim),
+            _need(cache, "cache", dt, cache.numel()))
+    pt = _need(page_table, "page_table", t.int32, B * max_pages)
+    sl = _need(seq_lens, "seq_lens", t.int32, B)
+    op = _need(o_part, "o_part", t.float32, B * Q * H * S * cfg.kv_rank)
+    lp = _need(lse_part, "lse_part", t.float32, B * Q * H * S)
+    _ck(lib().mla_decode_paged(ctypes.byref(cfg.c()), B, Q, S, int(max_seq_len), args[0], args[1],
+                               num_pages, pt, max_pages, sl, op, lp, _stream(stream)),
+        "mla_decode_paged")
+
+
+def splitkv_combine(cfg: Config, o_part, lse_part, o_lat, lse=None, stream=None):
+    """a5: LSE merge. o_lat [B][Q][H][d_c] (cfg dtype); lse [B][Q][H] f32 or None."""
+    t = _torch()
+    if lse_part.dim() != 4:
+        raise ValueError("lse_part: expected [batch][q_len][H][num_splits]")
+    B, Q, H, S = (int(x) for x in lse_part.shape)
+    if H != cfg.num_heads:
+        raise ValueError("lse_part: head axis does not match cfg.num_heads")
+    dt = _elem_dtype(cfg)
+    op = _need(o_part, "o_part", t.float32, B * Q * H * S * cfg.kv_rank)
+    lp = _need(lse_part, "lse_part", t.float32, B * Q * H * S)
+    ol = _need(o_lat, "o_lat", dt, B * Q * H * cfg.kv_rank)
+    ls = ctypes.c_void_p(None) if lse is None else _need(lse, "lse", t.float32, B * Q * H)
+    _ck(lib().mla_splitkv_combine(ctypes.byref(cfg.c()), B, Q, S, op, lp, ol, ls, _stream(stream)),
+        "mla_splitkv_combine")
+
+
+def up_project_v(cfg: Config, o_lat, w_uv, out, stream=None):
+    """a6: out[n][h] = W_UV[h] o_lat[n][h]; o_lat [N][H][d_c] -> out [N][H][d_v]."""
+    H, dt = cfg.num_heads, _elem_dtype(cfg)
+    n = int(o_lat.numel()) // (H * cfg.kv_rank)
+    args = (_need(o_lat, "o_lat", dt, n * H * cfg.kv_rank),
+            _need(w_uv, "w_uv", dt, H * cfg.v_dim * cfg.kv_rank),
+            _need(out, "out", dt, n * H * cfg.v_dim))
+    _ck(lib().mla_up_project_v(ctypes.byref(cfg.c()), n, *args, _stream(stream)), "mla_up_project_v")

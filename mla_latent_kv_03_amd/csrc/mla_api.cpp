@@ -1,0 +1,225 @@
+// Host entry points of libmla: argument checks, sizing and the split plan.
+// Plain C++ (no HIP headers): every check here runs before any launch, so the
+// error paths are testable on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mla.h"
+#include "mla_launch.h"
+
+namespace {
+
+constexpr int kMaxSplits = 4096;
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(const mla_config_t* c) { return c->dtype == MLA_F32 ? 4 : 2; }
+
+mla_status_t check_config(const mla_config_t* c) {
+  if (!c) return MLA_ERR_NULL;
+  if (c->dtype != MLA_F32 && c->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  const int vec = c->dtype == MLA_F32 ? 4 : 8;  // elements per 16-byte chunk
+  if (c->num_heads < 1 || c->num_heads > 1024) return MLA_ERR_SHAPE;
+  if (c->kv_rank < 16 || c->kv_rank > 1024 || c->kv_rank % vec) return MLA_ERR_SHAPE;
+  if (c->rope_dim < 2 || c->rope_dim > 256 || c->rope_dim % 2) return MLA_ERR_SHAPE;
+  if ((c->kv_rank + c->rope_dim) % vec) return MLA_ERR_SHAPE;
+  if (c->nope_dim < 1 || c->nope_dim > 256) return MLA_ERR_SHAPE;
+  if (c->v_dim < 1 || c->v_dim > 256) return MLA_ERR_SHAPE;
+  if (!pow2(c->page_size) || c->page_size < 16 || c->page_size > 256) return MLA_ERR_SHAPE;
+  if (!(c->softmax_scale > 0.0f) || !isfinite(c->softmax_scale)) return MLA_ERR_SHAPE;
+  if (!(c->rope_base > 1.0f) || !isfinite(c->rope_base)) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+mla::Shape shape_of(const mla_config_t* c) {
+  mla::Shape s;
+  s.H = c->num_heads;
+  s.dc = c->kv_rank;
+  s.dr = c->rope_dim;
+  s.dn = c->nope_dim;
+  s.dv = c->v_dim;
+  s.page = c->page_size;
+  s.dtype = c->dtype;
+  s.scale = c->softmax_scale;
+  s.log2_base = log2((double)c->rope_base);
+  return s;
+}
+
+mla_status_t hip_status(int rc) { return rc == 0 ? MLA_OK : MLA_ERR_HIP; }
+
+#define MLA_REQUIRE(cond, code) \
+  do {                          \
+    if (!(cond)) return (code); \
+  } while (0)
+
+#define MLA_CHECK_PTR(p)                  \
+  do {                                    \
+    if (!(p)) return MLA_ERR_NULL;        \
+    if (!aligned16(p)) return MLA_ERR_ALIGN; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_build_info(void) { return "libmla 0.1 gfx950 (HIP, MFMA bf16 decode)"; }
+
+const char* mla_status_str(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: size out of range or inconsistent";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unknown element type";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: device pointer not 16-byte aligned";
+    case MLA_ERR_CAPACITY: return "MLA_ERR_CAPACITY: pages or lengths too small";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: no kernel for this shape";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime error";
+  }
+  return "MLA_ERR_?: unknown status";
+}
+
+mla_status_t mla_config_validate(const mla_config_t* cfg) { return check_config(cfg); }
+
+size_t mla_cache_bytes_per_token(const mla_config_t* cfg) {
+  if (check_config(cfg) != MLA_OK) return 0;
+  return (size_t)(cfg->kv_rank + cfg->rope_dim) * (size_t)elem_bytes(cfg);
+}
+
+mla_status_t mla_split_chunk(const mla_config_t* cfg, int32_t seq_len, int32_t num_splits,
+                             int32_t* chunk_tokens) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(chunk_tokens, MLA_ERR_NULL);
+  MLA_REQUIRE(seq_len >= 0 && num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
+  const int64_t per = ((int64_t)seq_len + num_splits - 1) / num_splits;
+  const int64_t pg = cfg->page_size;
+  *chunk_tokens = (int32_t)(pg * ((per + pg - 1) / pg));
+  return MLA_OK;
+}
+
+int32_t mla_default_num_splits(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                               int32_t max_seq_len, int32_t num_cus) {
+  if (check_config(cfg) != MLA_OK || batch < 1 || q_len < 1 || max_seq_len < 1) return 1;
+  if (num_cus < 1) num_cus = 256;
+  // Work units are (sequence, split, 128-row group); aim for about one unit
+  // per compute unit with at least 16 pages (1,024 tokens) in each.
+  const int64_t rows = (int64_t)q_len * cfg->num_heads;
+  const int64_t groups = (rows + 127) / 128;
+  const int64_t pages = ((int64_t)max_seq_len + cfg->page_size - 1) / cfg->page_size;
+  int64_t want = ((int64_t)num_cus + batch * groups - 1) / (batch * groups);
+  const int64_t cap = pages / 16 > 0 ? pages / 16 : 1;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  if (want > kMaxSplits) want = kMaxSplits;
+  return (int32_t)want;
+}
+
+const char* mla_decode_kernel_name(const mla_config_t* cfg, int32_t q_len) {
+  if (check_config(cfg) != MLA_OK || q_len < 1) return "invalid";
+  return mla::decode_kernel_kind(shape_of(cfg), q_len) == 1 ? "mfma_bf16" : "generic";
+}
+
+size_t mla_decode_partials_bytes(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                 int32_t num_splits) {
+  if (check_config(cfg) != MLA_OK || batch < 0 || q_len < 0 || num_splits < 1 ||
+      num_splits > kMaxSplits)
+    return 0;
+  return (size_t)batch * (size_t)q_len * (size_t)cfg->num_heads * (size_t)num_splits *
+         (size_t)(cfg->kv_rank + 1) * sizeof(float);
+}
+
+mla_status_t mla_absorb_q(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                          const void* q_rope, const int32_t* pos, const void* w_uk,
+                          void* q_full, void* stream) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(n_tok >= 0, MLA_ERR_SHAPE);
+  if (n_tok == 0) return MLA_OK;
+  MLA_CHECK_PTR(q_nope);
+  MLA_CHECK_PTR(q_rope);
+  MLA_CHECK_PTR(pos);
+  MLA_CHECK_PTR(w_uk);
+  MLA_CHECK_PTR(q_full);
+  return hip_status(
+      mla::launch_absorb_q(shape_of(cfg), n_tok, q_nope, q_rope, pos, w_uk, q_full, stream));
+}
+
+mla_status_t mla_cache_append(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                              const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                              const int32_t* page_table, int32_t batch, int32_t max_pages,
+                              void* cache, int64_t num_pages, int32_t flags, void* stream) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(n_tok >= 0 && batch >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(flags == MLA_APPEND_RAW || flags == MLA_APPEND_ROTATE, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size <= INT32_MAX, MLA_ERR_CAPACITY);
+  if (n_tok == 0) return MLA_OK;
+  MLA_CHECK_PTR(c_kv);
+  MLA_CHECK_PTR(k_rope);
+  MLA_CHECK_PTR(seq_idx);
+  MLA_CHECK_PTR(pos);
+  MLA_CHECK_PTR(page_table);
+  MLA_CHECK_PTR(cache);
+  return hip_status(mla::launch_cache_append(shape_of(cfg), n_tok, c_kv, k_rope, seq_idx, pos,
+                                             page_table, batch, max_pages, cache, num_pages,
+                                             flags == MLA_APPEND_ROTATE, stream));
+}
+
+mla_status_t mla_decode_paged(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                              int32_t num_splits, int32_t max_seq_len, const void* q_full,
+                              const void* cache, int64_t num_pages, const int32_t* page_table,
+                              int32_t max_pages, const int32_t* seq_lens, float* o_part,
+                              float* lse_part, void* stream) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(batch >= 0 && q_len >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)q_len * cfg->num_heads <= 65536, MLA_ERR_SHAPE);
+  MLA_REQUIRE(max_seq_len >= q_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
+  if (batch == 0) return MLA_OK;
+  MLA_CHECK_PTR(q_full);
+  MLA_CHECK_PTR(cache);
+  MLA_CHECK_PTR(page_table);
+  MLA_CHECK_PTR(seq_lens);
+  MLA_CHECK_PTR(o_part);
+  MLA_CHECK_PTR(lse_part);
+  return hip_status(mla::launch_decode(shape_of(cfg), batch, q_len, num_splits, max_seq_len,
+                                       q_full, cache, num_pages, page_table, max_pages,
+                                       seq_lens, o_part, lse_part, stream));
+}
+
+mla_status_t mla_splitkv_combine(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                 int32_t num_splits, const float* o_part, const float* lse_part,
+                                 void* o_lat, float* lse, void* stream) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(batch >= 0 && q_len >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)batch * q_len * cfg->num_heads <= INT32_MAX, MLA_ERR_SHAPE);
+  if (batch == 0) return MLA_OK;
+  MLA_CHECK_PTR(o_part);
+  MLA_CHECK_PTR(lse_part);
+  MLA_CHECK_PTR(o_lat);
+  if (lse && !aligned16(lse)) return MLA_ERR_ALIGN;
+  const int rows = batch * q_len * cfg->num_heads;
+  return hip_status(
+      mla::launch_combine(shape_of(cfg), rows, num_splits, o_part, lse_part, o_lat, lse, stream));
+}
+
+mla_status_t mla_up_project_v(const mla_config_t* cfg, int32_t n_tok, const void* o_lat,
+                              const void* w_uv, void* out, void* stream) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(n_tok >= 0, MLA_ERR_SHAPE);
+  if (n_tok == 0) return MLA_OK;
+  MLA_CHECK_PTR(o_lat);
+  MLA_CHECK_PTR(w_uv);
+  MLA_CHECK_PTR(out);
+  return hip_status(mla::launch_up_project_v(shape_of(cfg), n_tok, o_lat, w_uv, out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Device helpers shared by the HIP kernels of libmla (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef uint16_t bf16_t;  // raw bf16 bits
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T>
+struct Elt;
+
+template <>
+struct Elt<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+
+template <>
+struct Elt<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+};
+
+// Rotate the pair (x0, x1) of a d_r-wide RoPE vector, pair index i, by
+// pos * base^(-2i/d_r). Angle and rotation in fp64: at positions near 2^20
+// an fp32 angle would be off by up to 0.06 rad.
+__device__ __forceinline__ void rope_pair(double x0, double x1, int64_t pos, int i, int dr,
+                                          double log2_base, double* y0, double* y1) {
+  const double theta = exp2(-(2.0 * (double)i / (double)dr) * log2_base);
+  const double ang = (double)pos * theta;
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  *y0 = x0 * cs - x1 * sn;
+  *y1 = x0 * sn + x1 * cs;
+}
+
+// Split plan: tokens of partition s of a length-L sequence (page-aligned chunk).
+__device__ __forceinline__ void split_range(int L, int S, int page, int s, int* t0, int* t1) {
+  const int64_t per = ((int64_t)L + S - 1) / S;
+  const int64_t chunk = (int64_t)page * ((per + page - 1) / page);
+  int64_t a = (int64_t)s * chunk, e = a + chunk;
+  if (a > L) a = L;
+  if (e > L) e = L;
+  *t0 = (int)a;
+  *t1 = (int)e;
+}
+
+}  // namespace mla

@@ -1,0 +1,416 @@
+// Small kernels of the decode step (query absorption, cache append, split
+// combine, value up-projection) and the generic (any-shape, fp32 or bf16)
+// split-KV decode kernel. The bf16 MFMA decode kernel for the DeepSeek MLA
+// shape (d_c = 512, d_r = 64) lives in mla_decode_mfma.hip.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "mla_common.h"
+#include "mla_launch.h"
+
+namespace mla {
+
+#define HIPCHK(expr)                          \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return (int)e_;     \
+  } while (0)
+
+static inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------------------
+// a1: query absorption + query RoPE
+// ("The Architecture of Memory", "The Weight Absorption Trick" and "Decoupled
+// Rotary Positional Encoding (RoPE)")
+// grid (H, ceil(n_tok / 8)), 256 threads. Each block streams W_UK[h] once and
+// applies it to up to 8 tokens; thread c owns output columns c, c + 256, ...
+// ---------------------------------------------------------------------------
+constexpr int kAbsorbTok = 8;
+
+template <typename T>
+__global__ __launch_bounds__(256) void absorb_q_kernel(int n_tok, int H, int dn, int dc, int dr,
+                                                       double log2_base, const T* __restrict__ q_nope,
+                                                       const T* __restrict__ q_rope,
+                                                       const int32_t* __restrict__ pos,
+                                                       const T* __restrict__ w_uk,
+                                                       T* __restrict__ q_full) {
+  __shared__ float qs[kAbsorbTok][256];
+  const int h = blockIdx.x;
+  const int n0 = blockIdx.y * kAbsorbTok;
+  const int nt = min(kAbsorbTok, n_tok - n0);
+  const int D = dc + dr;
+  for (int i = threadIdx.x; i < kAbsorbTok * dn; i += blockDim.x) {
+    const int n = i / dn, k = i % dn;
+    qs[n][k] = n < nt ? Elt<T>::ld(q_nope + ((size_t)(n0 + n) * H + h) * dn + k) : 0.0f;
+  }
+  __syncthreads();
+  const T* W = w_uk + (size_t)h * dn * dc;
+  for (int c = threadIdx.x; c < dc; c += blockDim.x) {
+    float acc[kAbsorbTok];
+#pragma unroll
+    for (int n = 0; n < kAbsorbTok; ++n) acc[n] = 0.0f;
+    for (int k = 0; k < dn; ++k) {
+      const float w = Elt<T>::ld(W + (size_t)k * dc + c);
+#pragma unroll
+      for (int n = 0; n < kAbsorbTok; ++n) acc[n] = fmaf(qs[n][k], w, acc[n]);
+    }
+    for (int n = 0; n < nt; ++n) Elt<T>::st(q_full + ((size_t)(n0 + n) * H + h) * D + c, acc[n]);
+  }
+  const int half = dr / 2;
+  for (int i = threadIdx.x; i < nt * half; i += blockDim.x) {
+    const int n = i / half, p = i % half;
+    const T* src = q_rope + ((size_t)(n0 + n) * H + h) * dr + 2 * p;
+    double y0, y1;
+    rope_pair(Elt<T>::ld(src), Elt<T>::ld(src + 1), pos[n0 + n], p, dr, log2_base, &y0, &y1);
+    T* dst = q_full + ((size_t)(n0 + n) * H + h) * D + dc + 2 * p;
+    Elt<T>::st(dst, (float)y0);
+    Elt<T>::st(dst + 1, (float)y1);
+  }
+}
+
+template <typename T>
+static int absorb_impl(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
+                       const int32_t* pos, const void* w_uk, void* q_full, void* stream) {
+  dim3 grid(s.H, (n_tok + kAbsorbTok - 1) / kAbsorbTok);
+  hipLaunchKernelGGL(absorb_q_kernel<T>, grid, dim3(256), 0, as_stream(stream), n_tok, s.H, s.dn,
+                     s.dc, s.dr, s.log2_base, (const T*)q_nope, (const T*)q_rope, pos,
+                     (const T*)w_uk, (T*)q_full);
+  return (int)hipGetLastError();
+}
+
+int launch_absorb_q(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
+                    const int32_t* pos, const void* w_uk, void* q_full, void* stream) {
+  return s.dtype == 0 ? absorb_impl<float>(s, n_tok, q_nope, q_rope, pos, w_uk, q_full, stream)
+                      : absorb_impl<bf16_t>(s, n_tok, q_nope, q_rope, pos, w_uk, q_full, stream);
+}
+
+// ---------------------------------------------------------------------------
+// a2: paged cache append ("The Architecture of Memory", "PagedAttention:
+// Virtual Memory for LLMs"). One block per appended row.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(128) void append_kernel(int dc, int dr, int page,
+                                                     const T* __restrict__ c_kv,
+                                                     const T* __restrict__ k_rope,
+                                                     const int32_t* __restrict__ seq_idx,
+                                                     const int32_t* __restrict__ pos,
+                                                     const int32_t* __restrict__ page_table,
+                                                     int batch, int max_pages, T* __restrict__ cache,
+                                                     int64_t num_pages, int rotate, double log2_base) {
+  const int n = blockIdx.x;
+  const int b = seq_idx[n];
+  const int p = pos[n];
+  if (b < 0 || b >= batch || p < 0 || p >= max_pages * page) return;
+  const int pg = page_table[(size_t)b * max_pages + p / page];
+  if (pg < 0 || (int64_t)pg >= num_pages) return;
+  const int D = dc + dr;
+  T* row = cache + ((size_t)pg * page + p % page) * D;
+  for (int i = threadIdx.x; i < dc; i += blockDim.x) row[i] = c_kv[(size_t)n * dc + i];
+  const T* kr = k_rope + (size_t)n * dr;
+  for (int i = threadIdx.x; i < dr / 2; i += blockDim.x) {
+    if (rotate) {
+      double y0, y1;
+      rope_pair(Elt<T>::ld(kr + 2 * i), Elt<T>::ld(kr + 2 * i + 1), p, i, dr, log2_base, &y0, &y1);
+      Elt<T>::st(row + dc + 2 * i, (float)y0);
+      Elt<T>::st(row + dc + 2 * i + 1, (float)y1);
+    } else {
+      row[dc + 2 * i] = kr[2 * i];
+      row[dc + 2 * i + 1] = kr[2 * i + 1];
+    }
+  }
+}
+
+int launch_cache_append(const Shape& s, int n_tok, const void* c_kv, const void* k_rope,
+                        const int32_t* seq_idx, const int32_t* pos, const int32_t* page_table,
+                        int batch, int max_pages, void* cache, int64_t num_pages, int rotate,
+                        void* stream) {
+  if (s.dtype == 0)
+    hipLaunchKernelGGL(append_kernel<float>, dim3(n_tok), dim3(128), 0, as_stream(stream), s.dc,
+                       s.dr, s.page, (const float*)c_kv, (const float*)k_rope, seq_idx, pos,
+                       page_table, batch, max_pages, (float*)cache, num_pages, rotate, s.log2_base);
+  else
+    hipLaunchKernelGGL(append_kernel<bf16_t>, dim3(n_tok), dim3(128), 0, as_stream(stream), s.dc,
+                       s.dr, s.page, (const bf16_t*)c_kv, (const bf16_t*)k_rope, seq_idx, pos,
+                       page_table, batch, max_pages, (bf16_t*)cache, num_pages, rotate,
+                       s.log2_base);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// a4 (generic): split-KV decode for any supported shape, fp32 or bf16, on the
+// vector ALUs. Block = (partition s, sequence b, group of 8 query rows).
+// Tokens are staged 16 at a time in LDS (as fp32, rows padded to an odd
+// stride); scores use one thread per (row, token); the online softmax keeps a
+// running max m and sum l per row; thread f accumulates output columns
+// f, f + 256, ... of all rows.
+// ---------------------------------------------------------------------------
+constexpr int kGenRows = 8;
+constexpr int kGenTok = 16;
+constexpr int kGenMaxF = 4;  // d_c <= 1024
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_generic_kernel(
+    int Q, int H, int dc, int dr, int page, int S, int max_seq_len, float scale,
+    const T* __restrict__ q_full, const T* __restrict__ cache, int64_t num_pages,
+    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
+  extern __shared__ float smem[];
+  const int s = blockIdx.x, b = blockIdx.y;
+  const int R = Q * H;
+  const int r0 = blockIdx.z * kGenRows;
+  const int nr = min(kGenRows, R - r0);
+  const int D = dc + dr, Dp = D + 1;
+  float* qs = smem;                    // [kGenRows][D]
+  float* cs = qs + kGenRows * D;       // [kGenTok][Dp]
+  float* ps = cs + kGenTok * Dp;       // [kGenRows][kGenTok]
+  float* al = ps + kGenRows * kGenTok; // [kGenRows] rescale factors
+  const int tid = threadIdx.x;
+
+  const int L = seq_lens[b];
+  bool bad = (L < Q) || (L > max_seq_len);
+  int t0 = 0, t1 = 0;
+  if (!bad) split_range(L, S, page, s, &t0, &t1);
+
+  for (int i = tid; i < nr * D; i += blockDim.x)
+    qs[i] = Elt<T>::ld(q_full + ((size_t)b * R + r0) * D + i);
+
+  float acc[kGenRows][kGenMaxF];
+#pragma unroll
+  for (int r = 0; r < kGenRows; ++r)
+#pragma unroll
+    for (int k = 0; k < kGenMaxF; ++k) acc[r][k] = 0.0f;
+  // per-row softmax state, replicated in the 16 threads of the row
+  const int my_r = tid / kGenTok, my_k = tid % kGenTok;
+  float m_run = -INFINITY, l_run = 0.0f;
+  const int my_j = (r0 + my_r) / H;   // query index of this thread's row
+  const int my_p = L - Q + my_j;      // its position
+
+  for (int t = t0; t < t1 && !bad; t += kGenTok) {
+    const int nt = min(kGenTok, t1 - t);
+    const int pg = page_table[(size_t)b * max_pages + t / page];
+    if (pg < 0 || (int64_t)pg >= num_pages) {
+      bad = true;  // uniform across the block: every thread read the same entry
+      break;
+    }
+    __syncthreads();  // previous step done with cs / ps / al
+    const T* src = cache + ((size_t)pg * page + (t % page)) * D;
+    for (int i = tid; i < nt * D; i += blockDim.x) cs[(i / D) * Dp + (i % D)] = Elt<T>::ld(src + i);
+    __syncthreads();
+    float sc = -INFINITY;
+    if (my_r < nr && my_k < nt && t + my_k <= my_p) {
+      const float* qr = qs + my_r * D;
+      const float* cr = cs + my_k * Dp;
+      float dot = 0.0f;
+      for (int f = 0; f < D; ++f) dot = fmaf(qr[f], cr[f], dot);
+      sc = dot * scale;
+    }
+    float mx = sc;
+    for (int off = kGenTok / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kGenTok));
+    const float m_new = fmaxf(m_run, mx);
+    const float p = (sc == -INFINITY) ? 0.0f : expf(sc - m_new);
+    float ps_sum = p;
+    for (int off = kGenTok / 2; off > 0; off >>= 1) ps_sum += __shfl_xor(ps_sum, off, kGenTok);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : expf(m_run - m_new);
+    l_run = l_run * alpha + ps_sum;
+    m_run = m_new;
+    if (my_r < kGenRows) {
+      ps[my_r * kGenTok + my_k] = p;
+      if (my_k == 0) al[my_r] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kGenRows; ++r) {
+      if (r < nr) {
+        const float a = al[r];
+#pragma unroll
+        for (int k = 0; k < kGenMaxF; ++k) {
+          const int f = tid + 256 * k;
+          if (f < dc) {
+            float v = acc[r][k] * a;
+            for (int u = 0; u < nt; ++u) v = fmaf(ps[r * kGenTok + u], cs[u * Dp + f], v);
+            acc[r][k] = v;
+          }
+        }
+      }
+    }
+  }
+  // final: broadcast each row's (m, l) through LDS, then write the partials
+  __syncthreads();
+  if (my_k == 0 && my_r < kGenRows) {
+    ps[my_r * 2] = m_run;
+    ps[my_r * 2 + 1] = l_run;
+  }
+  __syncthreads();
+  const float nanv = __int_as_float(0x7fc00000);
+  for (int r = 0; r < nr; ++r) {
+    const float m = ps[r * 2], l = ps[r * 2 + 1];
+    const size_t row = (size_t)b * R + r0 + r;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+    for (int k = 0; k < kGenMaxF; ++k) {
+      const int f = tid + 256 * k;
+      if (f < dc) o_part[(row * S + s) * dc + f] = bad ? nanv : acc[r][k] * inv;
+    }
+    if (tid == 0) lse_part[row * S + s] = bad ? nanv : (l > 0.0f ? m + logf(l) : -INFINITY);
+  }
+}
+
+template <typename T>
+static int decode_generic_impl(const Shape& s, int batch, int q_len, int num_splits,
+                               int max_seq_len, const void* q_full, const void* cache,
+                               int64_t num_pages, const int32_t* page_table, int max_pages,
+                               const int32_t* seq_lens, float* o_part, float* lse_part,
+                               void* stream) {
+  const int D = s.D();
+  const size_t lds = sizeof(float) * ((size_t)kGenRows * D + (size_t)kGenTok * (D + 1) +
+                                      kGenRows * kGenTok + kGenRows);
+  static bool attr_set = false;
+  if (!attr_set) {
+    HIPCHK(hipFuncSetAttribute((const void*)decode_generic_kernel<T>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024));
+    attr_set = true;
+  }
+  const int R = q_len * s.H;
+  dim3 grid(num_splits, batch, (R + kGenRows - 1) / kGenRows);
+  hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(256), lds, as_stream(stream), q_len, s.H,
+                     s.dc, s.dr, s.page, num_splits, max_seq_len, s.scale, (const T*)q_full,
+                     (const T*)cache, num_pages, page_table, max_pages, seq_lens, o_part, lse_part);
+  return (int)hipGetLastError();
+}
+
+int launch_decode_generic(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
+                          const void* q_full, const void* cache, int64_t num_pages,
+                          const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                          float* o_part, float* lse_part, void* stream) {
+  return s.dtype == 0
+             ? decode_generic_impl<float>(s, batch, q_len, num_splits, max_seq_len, q_full, cache,
+                                          num_pages, page_table, max_pages, seq_lens, o_part,
+                                          lse_part, stream)
+             : decode_generic_impl<bf16_t>(s, batch, q_len, num_splits, max_seq_len, q_full, cache,
+                                           num_pages, page_table, max_pages, seq_lens, o_part,
+                                           lse_part, stream);
+}
+
+// ---------------------------------------------------------------------------
+// a5: log-sum-exp merge of the partitions ("The Architecture of Memory",
+// "Flash-Decoding and FlashInfer"). One block per output row.
+// ---------------------------------------------------------------------------
+constexpr int kMaxSplits = 4096;
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(int S, int dc, const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part,
+                                                      T* __restrict__ o_lat, float* __restrict__ lse) {
+  __shared__ float w[kMaxSplits];
+  __shared__ float red[256];
+  __shared__ int any_nan;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* lp = lse_part + (size_t)r * S;
+  if (tid == 0) any_nan = 0;
+  float mx = -INFINITY;
+  int nan_seen = 0;
+  for (int s = tid; s < S; s += blockDim.x) {
+    const float v = lp[s];
+    w[s] = v;
+    nan_seen |= (v != v);
+    mx = fmaxf(mx, v);
+  }
+  red[tid] = mx;
+  __syncthreads();
+  if (nan_seen) any_nan = 1;
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+  float sum = 0.0f;
+  for (int s = tid; s < S; s += blockDim.x) {
+    const float e = (w[s] == -INFINITY) ? 0.0f : expf(w[s] - mx);
+    w[s] = e;
+    sum += e;
+  }
+  red[tid] = sum;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  sum = red[0];
+  const bool bad = any_nan != 0;
+  const float nanv = __int_as_float(0x7fc00000);
+  const float inv = 1.0f / sum;
+  const float* op = o_part + (size_t)r * S * dc;
+  for (int f = tid; f < dc; f += blockDim.x) {
+    float acc = 0.0f;
+    for (int s = 0; s < S; ++s) acc = fmaf(w[s], op[(size_t)s * dc + f], acc);
+    Elt<T>::st(o_lat + (size_t)r * dc + f, bad ? nanv : acc * inv);
+  }
+  if (lse && tid == 0) lse[r] = bad ? nanv : mx + logf(sum);
+}
+
+int launch_combine(const Shape& s, int rows, int num_splits, const float* o_part,
+                   const float* lse_part, void* o_lat, float* lse, void* stream) {
+  if (s.dtype == 0)
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(rows), dim3(256), 0, as_stream(stream),
+                       num_splits, s.dc, o_part, lse_part, (float*)o_lat, lse);
+  else
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(rows), dim3(256), 0, as_stream(stream),
+                       num_splits, s.dc, o_part, lse_part, (bf16_t*)o_lat, lse);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// a6: value up-projection through W_UV ("Beyond the Attention Bottleneck",
+// "Down-Projection and Up-Projection Mechanics").
+// grid (H, ceil(n_tok / 8)), 4 waves; wave w computes output rows v = w,
+// w + 4, ... for up to 8 tokens: lanes stride the d_c axis, then a wave
+// reduction.
+// ---------------------------------------------------------------------------
+constexpr int kUpTok = 8;
+
+template <typename T>
+__global__ __launch_bounds__(256) void up_v_kernel(int n_tok, int H, int dc, int dv,
+                                                   const T* __restrict__ o_lat,
+                                                   const T* __restrict__ w_uv, T* __restrict__ out) {
+  __shared__ float os[kUpTok][1024];
+  const int h = blockIdx.x;
+  const int n0 = blockIdx.y * kUpTok;
+  const int nt = min(kUpTok, n_tok - n0);
+  for (int i = threadIdx.x; i < kUpTok * dc; i += blockDim.x) {
+    const int n = i / dc, c = i % dc;
+    os[n][c] = n < nt ? Elt<T>::ld(o_lat + ((size_t)(n0 + n) * H + h) * dc + c) : 0.0f;
+  }
+  __syncthreads();
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const T* W = w_uv + (size_t)h * dv * dc;
+  for (int v = wave; v < dv; v += 4) {
+    float acc[kUpTok];
+#pragma unroll
+    for (int n = 0; n < kUpTok; ++n) acc[n] = 0.0f;
+    for (int c = lane; c < dc; c += 64) {
+      const float w = Elt<T>::ld(W + (size_t)v * dc + c);
+#pragma unroll
+      for (int n = 0; n < kUpTok; ++n) acc[n] = fmaf(w, os[n][c], acc[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < kUpTok; ++n)
+      for (int off = 32; off > 0; off >>= 1) acc[n] += __shfl_xor(acc[n], off, 64);
+    if (lane == 0)
+      for (int n = 0; n < nt; ++n) Elt<T>::st(out + ((size_t)(n0 + n) * H + h) * dv + v, acc[n]);
+  }
+}
+
+int launch_up_project_v(const Shape& s, int n_tok, const void* o_lat, const void* w_uv,
+                        void* out, void* stream) {
+  dim3 grid(s.H, (n_tok + kUpTok - 1) / kUpTok);
+  if (s.dtype == 0)
+    hipLaunchKernelGGL(up_v_kernel<float>, grid, dim3(256), 0, as_stream(stream), n_tok, s.H, s.dc,
+                       s.dv, (const float*)o_lat, (const float*)w_uv, (float*)out);
+  else
+    hipLaunchKernelGGL(up_v_kernel<bf16_t>, grid, dim3(256), 0, as_stream(stream), n_tok, s.H,
+                       s.dc, s.dv, (const bf16_t*)o_lat, (const bf16_t*)w_uv, (bf16_t*)out);
+  return (int)hipGetLastError();
+}
+
+}  // namespace mla

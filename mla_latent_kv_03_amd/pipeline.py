@@ -1,0 +1,92 @@
+"""One MLA decode step on the device: buffers plus the five library calls.
+
+Plumbing only: torch allocates the device buffers and supplies the stream;
+every step of the computation runs in libmla's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+from . import _binding as B
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_of(cfg: B.Config):
+    t = _torch()
+    return t.float32 if cfg.dtype == B.F32 else t.bfloat16
+
+
+def upload(x, dtype, device="cuda"):
+    """numpy -> contiguous device tensor (exact for bf16-representable values)."""
+    t = _torch()
+    return t.from_numpy(x).to(device=device).to(dtype).contiguous()
+
+
+class DecodeStep:
+    """Device state of one decode step for ``batch`` sequences of ``q_len`` tokens.
+
+    The cache pool, page table and lengths are the caller's (shared across
+    steps or rotated per layer); this object owns only the per-step buffers:
+    absorbed queries, split partials, merged latent output and final output.
+    """
+
+    def __init__(self, cfg: B.Config, batch: int, q_len: int, num_splits: int,
+                 seq_lens_host, device="cuda"):
+        t = _torch()
+        self.cfg, self.batch, self.q_len, self.num_splits = cfg, batch, q_len, num_splits
+        H, D, dc, dv = cfg.num_heads, cfg.dim, cfg.kv_rank, cfg.v_dim
+        dt = dtype_of(cfg)
+        lens = [int(x) for x in seq_lens_host]
+        self.max_seq_len = max(lens)
+        # query j of sequence b sits at position L_b - Q + j
+        pos = [L - q_len + j for L in lens for j in range(q_len)]
+        self.qpos = t.tensor(pos, dtype=t.int32, device=device)
+        self.seq_idx = t.tensor([b for b in range(batch) for _ in range(q_len)], dtype=t.int32,
+                                device=device)
+        self.q_full = t.empty((batch, q_len, H, D), dtype=dt, device=device)
+        self.o_part = t.empty((batch, q_len, H, num_splits, dc), dtype=t.float32, device=device)
+        self.lse_part = t.empty((batch, q_len, H, num_splits), dtype=t.float32, device=device)
+        self.o_lat = t.empty((batch, q_len, H, dc), dtype=dt, device=device)
+        self.lse = t.empty((batch, q_len, H), dtype=t.float32, device=device)
+        self.out = t.empty((batch, q_len, H, dv), dtype=dt, device=device)
+
+    def absorb(self, q_nope, q_rope, w_uk, stream=None):
+        B.absorb_q(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, stream)
+
+    def append(self, c_new, k_new, page_table, cache, stream=None):
+        B.cache_append(self.cfg, c_new, k_new, self.seq_idx, self.qpos, page_table, cache,
+                       B.APPEND_ROTATE, stream)
+
+    def decode(self, cache, page_table, seq_lens, stream=None, max_seq_len: Optional[int] = None):
+        B.decode_paged(self.cfg, self.q_full, cache, page_table, seq_lens, self.o_part,
+                       self.lse_part, max_seq_len or self.max_seq_len, stream)
+
+    def combine(self, stream=None):
+        B.splitkv_combine(self.cfg, self.o_part, self.lse_part, self.o_lat, self.lse, stream)
+
+    def up_project(self, w_uv, stream=None):
+        B.up_project_v(self.cfg, self.o_lat, w_uv, self.out, stream)
+
+    def run(self, q_nope, q_rope, w_uk, w_uv, c_new, k_new, cache, page_table, seq_lens,
+            stream=None, max_seq_len: Optional[int] = None):
+        """absorb -> append (B*Q new rows) -> decode -> combine -> up-project."""
+        self.absorb(q_nope, q_rope, w_uk, stream)
+        self.append(c_new, k_new, page_table, cache, stream)
+        self.decode(cache, page_table, seq_lens, stream, max_seq_len)
+        self.combine(stream)
+        self.up_project(w_uv, stream)
+        return self.out
+
+
+def fill_cache(cfg: B.Config, cache, page_table, c_all, k_all, seq_idx, pos, stream=None,
+               rows_per_call: int = 1 << 20):
+    """Write every cached row (setup): rows n go to (seq_idx[n], pos[n]), keys rotated."""
+    n = int(pos.numel())
+    for a in range(0, n, rows_per_call):
+        e = min(n, a + rows_per_call)
+        B.cache_append(cfg, c_all[a:e], k_all[a:e], seq_idx[a:e], pos[a:e], page_table, cache,
+                       B.APPEND_ROTATE, stream)

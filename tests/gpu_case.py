@@ -1,0 +1,113 @@
+"""Device-side setup shared by the GPU parity tests.
+
+Builds one decode step of a workload on the GPU through the library's own
+entry points (the cache is filled with mla_cache_append), and runs the fp64
+oracle on the same seeded inputs. Nothing here computes the method itself.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import workload
+import mla_latent_kv_03_amd as mla
+from mla_latent_kv_03_amd.pipeline import DecodeStep, dtype_of, fill_cache, upload
+
+NAN_BF16 = 0x7FC1      # quiet NaN with a payload: poison for unused cache slots
+NAN_F32 = 0x7FC00001
+
+
+def tau(wl):
+    """Global tolerance: max|err| <= tau * max|ref| (1e-4 fp32, 1e-2 bf16)."""
+    return 1e-4 if wl.dtype == "f32" else 1e-2
+
+
+def lse_atol(wl):
+    return 1e-5 if wl.dtype == "f32" else 1e-2
+
+
+def poisoned_pool(cfg, num_pages, device="cuda"):
+    if cfg.dtype == mla.F32:
+        t = torch.full((num_pages, cfg.page_size, cfg.dim), NAN_F32, dtype=torch.int32, device=device)
+        return t.view(torch.float32)
+    t = torch.full((num_pages, cfg.page_size, cfg.dim), NAN_BF16, dtype=torch.int16, device=device)
+    return t.view(torch.bfloat16)
+
+
+def tok_index(inp):
+    """(seq_idx, pos) of every cached token, in the order of inp.c rows."""
+    seq_idx = np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(inp.seq_lens)])
+    pos = np.concatenate([np.arange(int(L), dtype=np.int32) for L in inp.seq_lens])
+    return seq_idx, pos
+
+
+class Case:
+    """One decode step of ``wl`` on the device, with its oracle reference."""
+
+    def __init__(self, wl, seed=0, seq_lens=None, num_splits=None, inputs=None):
+        self.wl = wl
+        self.inp = inputs if inputs is not None else workload.make(wl, seed, seq_lens=seq_lens)
+        inp = self.inp
+        self.cfg = cfg = mla.Config.from_workload(wl)
+        self.S = num_splits or wl.num_splits
+        dt = dtype_of(cfg)
+        self.dt = dt
+        B, Q, H = wl.batch, wl.q_len, wl.heads
+        self.pool = poisoned_pool(cfg, inp.num_pages)
+        self.pt = upload(inp.page_table, torch.int32)
+        self.seq_lens = upload(inp.seq_lens, torch.int32)
+        si, pos = tok_index(inp)
+        fill_cache(cfg, self.pool, self.pt, upload(inp.c, dt), upload(inp.k_rope, dt),
+                   upload(si, torch.int32), upload(pos, torch.int32))
+        self.q_nope = upload(np.ascontiguousarray(inp.q_nope), dt)
+        self.q_rope = upload(np.ascontiguousarray(inp.q_rope), dt)
+        self.w_uk = upload(inp.w_uk, dt)
+        self.w_uv = upload(inp.w_uv, dt)
+        # the B*Q newest rows (re-appended by every step, same values)
+        rows = np.concatenate([inp.offsets[b] + np.arange(int(L) - Q, int(L))
+                               for b, L in enumerate(inp.seq_lens)])
+        self.c_new = upload(inp.c[rows], dt)
+        self.k_new = upload(inp.k_rope[rows], dt)
+        self.step = DecodeStep(cfg, B, Q, self.S, inp.seq_lens)
+        torch.cuda.synchronize()
+
+    def run(self, max_seq_len=None):
+        out = self.step.run(self.q_nope, self.q_rope, self.w_uk, self.w_uv, self.c_new, self.k_new,
+                            self.pool, self.pt, self.seq_lens, max_seq_len=max_seq_len)
+        torch.cuda.synchronize()
+        return out
+
+    def results(self):
+        s = self.step
+        return {"o": to64(s.out), "o_lat": to64(s.o_lat), "lse": to64(s.lse)}
+
+    def oracle(self, heads=None, seqs=None):
+        return oracle.mla_decode_ref(self.inp, heads=heads, seqs=seqs)
+
+
+def to64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def assert_close(got, ref, tol, what, lse=False):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    bound = tol if lse else tol * float(np.max(np.abs(ref)))
+    assert err <= bound, f"{what}: max|err| = {err:.3e} > bound {bound:.3e}"
+    return err, bound
+
+
+def check_against_oracle(case, got, ref, heads=None, seqs=None):
+    """Compare o, o_lat, lse on the selected heads/sequences."""
+    wl = case.wl
+    hs = slice(None) if heads is None else list(heads)
+    bs = list(range(wl.batch)) if seqs is None else list(seqs)
+    for key in ["o", "o_lat"]:
+        g = got[key][bs][:, :, hs]
+        r = ref[key][bs]
+        assert_close(g, r, tau(wl), key)
+    assert_close(got["lse"][bs][:, :, hs], ref["lse"][bs], lse_atol(wl), "lse", lse=True)

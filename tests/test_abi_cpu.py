@@ -1,0 +1,150 @@
+"""C ABI of libmla on the CPU: the library loads, exports every declared entry
+point, and its host-side checks and sizing behave as documented. No call here
+reaches a kernel launch (every call either fails validation or is a no-op)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+mla = pytest.importorskip("mla_latent_kv_03_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    try:
+        return mla.lib()
+    except RuntimeError as e:
+        pytest.fail(f"libmla.so must be built before the tests: {e}")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ["mla_absorb_q", "mla_cache_append", "mla_decode_paged", "mla_splitkv_combine",
+              "mla_up_project_v"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert "gfx950" in mla.build_info()
+
+
+V2 = mla.Config(num_heads=16)
+TINY = mla.Config(num_heads=4, kv_rank=64, rope_dim=16, nope_dim=32, v_dim=32, dtype=mla.F32)
+
+
+def test_config_validation_codes(L):
+    assert mla.config_validate(V2) == 0
+    assert mla.config_validate(TINY) == 0
+    bad = {
+        2: [V2.__class__(num_heads=0), V2.__class__(num_heads=16, rope_dim=3),
+            V2.__class__(num_heads=16, page_size=48), V2.__class__(num_heads=16, kv_rank=500),
+            V2.__class__(num_heads=16, softmax_scale=-1.0)],
+        3: [V2.__class__(num_heads=16, dtype=7)],
+    }
+    for code, cfgs in bad.items():
+        for c in cfgs:
+            assert mla.config_validate(c) == code, c
+    assert L.mla_config_validate(None) == 1
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert mla.status_str(s).startswith("MLA_")
+    assert "unknown" in mla.status_str(99)
+
+
+def test_cache_bytes_per_token_matches_pages(L):
+    assert mla.cache_bytes_per_token(V2) == 1152
+    assert mla.cache_bytes_per_token(V2) * 27 == oracle.latent_bytes_per_token(512, 64, 2, 27) == 31104
+    assert mla.cache_bytes_per_token(TINY) == 320
+    assert mla.cache_bytes_per_token(V2.__class__(num_heads=0)) == 0
+
+
+@pytest.mark.parametrize("page", [16, 64, 128])
+def test_split_plan_matches_oracle(L, page):
+    cfg = mla.Config(num_heads=16, page_size=page)
+    for Lq in [1, 15, 16, 63, 64, 65, 1000, 32768, 1048576]:
+        for S in [1, 3, 7, 32, 256, 4096]:
+            chunk = mla.split_chunk(cfg, Lq, S)
+            want = oracle.split_bounds(Lq, S, page)
+            got = [(min(Lq, s * chunk), min(Lq, (s + 1) * chunk)) for s in range(S)]
+            assert got == want, (Lq, S)
+
+
+def test_partials_bytes_and_default_splits(L):
+    assert mla.decode_partials_bytes(V2, 8, 1, 32) == 8 * 16 * 32 * 513 * 4
+    assert mla.decode_partials_bytes(V2, 8, 1, 0) == 0
+    for wl in workload.WORKLOADS.values():
+        cfg = mla.Config.from_workload(wl)
+        s = mla.default_num_splits(cfg, wl.batch, wl.q_len, wl.max_seq_len, 256)
+        assert 1 <= s <= 4096
+
+
+def test_decode_kernel_selection(L):
+    assert mla.decode_kernel_kind(V2, 1) == "mfma_bf16"
+    assert mla.decode_kernel_kind(mla.Config(num_heads=128), 4) == "mfma_bf16"
+    assert mla.decode_kernel_kind(TINY, 1) == "generic"
+    assert mla.decode_kernel_kind(mla.Config(num_heads=4), 1) == "generic"  # 4 rows < 16
+
+
+P = ctypes.c_void_p
+A16 = P(0x10000)      # aligned, never dereferenced: every call below fails first
+MIS = P(0x10008)
+
+
+def _c(cfg):
+    return ctypes.byref(cfg.c())
+
+
+def test_absorb_errors(L):
+    assert L.mla_absorb_q(_c(V2), 4, None, A16, A16, A16, A16, None) == 1
+    assert L.mla_absorb_q(_c(V2), 4, MIS, A16, A16, A16, A16, None) == 4
+    assert L.mla_absorb_q(_c(V2), -1, A16, A16, A16, A16, A16, None) == 2
+    assert L.mla_absorb_q(_c(V2), 0, None, None, None, None, None, None) == 0   # no-op
+    assert L.mla_absorb_q(None, 4, A16, A16, A16, A16, A16, None) == 1
+
+
+def test_append_errors(L):
+    args = [A16, A16, A16, A16, A16]
+    assert L.mla_cache_append(_c(V2), 8, *args, 2, 4, None, 16, 1, None) == 1
+    assert L.mla_cache_append(_c(V2), 8, *args, 2, 4, A16, 16, 5, None) == 2     # bad mode
+    assert L.mla_cache_append(_c(V2), 8, *args, 0, 4, A16, 16, 1, None) == 2     # batch 0
+    assert L.mla_cache_append(_c(V2), 8, MIS, *args[1:], 2, 4, A16, 16, 1, None) == 4
+    assert L.mla_cache_append(_c(V2), 0, *args, 2, 4, A16, 16, 1, None) == 0     # no-op
+
+
+def test_decode_errors(L):
+    def call(cfg=V2, batch=2, q_len=1, S=4, max_seq=256, npages=8, max_pages=4, o=A16, q=A16):
+        return L.mla_decode_paged(_c(cfg), batch, q_len, S, max_seq, q, A16, npages, A16,
+                                  max_pages, A16, o, A16, None)
+    assert call(o=None) == 1
+    assert call(q=MIS) == 4
+    assert call(S=0) == 2 and call(S=4097) == 2
+    assert call(max_seq=257) == 5            # 4 pages x 64 < 257
+    assert call(q_len=5, max_seq=4) == 5     # q_len > max_seq_len
+    assert call(q_len=0) == 2
+    assert call(cfg=V2.__class__(num_heads=16, dtype=9)) == 3
+    assert call(batch=0) == 0                # nothing to do
+
+
+def test_combine_and_up_errors(L):
+    assert L.mla_splitkv_combine(_c(V2), 2, 1, 4, None, A16, A16, None, None) == 1
+    assert L.mla_splitkv_combine(_c(V2), 2, 1, 4, A16, A16, A16, MIS, None) == 4
+    assert L.mla_splitkv_combine(_c(V2), 2, 1, 0, A16, A16, A16, None, None) == 2
+    assert L.mla_up_project_v(_c(V2), 3, A16, None, A16, None) == 1
+    assert L.mla_up_project_v(_c(V2), 0, None, None, None, None) == 0

@@ -1,0 +1,330 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Bounds (from the required tolerance): attention outputs max|err| <= 1e-4 *
+max|ref| for the fp32 workload and <= 1e-2 * max|ref| for bf16 workloads;
+lse within 1e-5 (fp32) / 1e-2 (bf16) absolute; page-table and append
+indexing bit-exact. Every cache pool starts NaN-poisoned, so an unwritten or
+out-of-range slot that reached an output would show up as a non-finite value.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+import mla_latent_kv_03_amd as mla
+from mla_latent_kv_03_amd.pipeline import upload
+
+from gpu_case import (Case, assert_close, check_against_oracle, lse_atol, poisoned_pool, tau,
+                      to64, NAN_BF16)
+
+pytestmark = pytest.mark.gpu
+
+W = workload.WORKLOADS
+
+
+def small(name, **kw):
+    return W[name].replace(**kw)
+
+
+# small versions of the five workloads: several tiles, ragged tails
+SMALL = {
+    "tiny_f32": W["tiny_f32"],
+    "v2lite_small": small("v2lite_32k", batch=2, seq_len=2048 + 37, num_splits=5),
+    "v2lite_paged_small": small("v2lite_paged_varlen", batch=5, len_range=(1, 700), num_splits=3),
+    "v2_h128_small": small("v2_h128_8k", batch=2, seq_len=1000, num_splits=3),
+    "q4_h128_small": small("v2_h128_1m_q4", seq_len=3001, num_splits=16),
+    "f32_ragged": small("tiny_f32", batch=3, seq_len=None, len_range=(1, 300), paged=True,
+                        num_splits=3),
+    "bf16_generic_h8": small("v2lite_32k", batch=2, heads=8, seq_len=333, num_splits=2),
+}
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu] {request.node.name}", flush=True)
+    yield
+
+
+# ---------------------------------------------------------------- a2 append
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_append_raw_bitexact(dtype):
+    wl = small("v2lite_paged_varlen", batch=3, len_range=(1, 200), dtype=dtype)
+    if dtype == "f32":
+        wl = wl.replace(kv_rank=64, rope_dim=16)
+    inp = workload.make(wl, 2)
+    cfg = mla.Config.from_workload(wl)
+    pool = poisoned_pool(cfg, inp.num_pages)
+    si = np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(inp.seq_lens)])
+    pos = np.concatenate([np.arange(int(L), dtype=np.int32) for L in inp.seq_lens])
+    # shuffle the append order: the image must not depend on it
+    perm = np.random.default_rng(0).permutation(len(pos))
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    mla.cache_append(cfg, upload(inp.c[perm], dt), upload(inp.k_rope[perm], dt),
+                     upload(si[perm], torch.int32), upload(pos[perm], torch.int32),
+                     upload(inp.page_table, torch.int32), pool, mla.APPEND_RAW)
+    torch.cuda.synchronize()
+    if dtype == "f32":
+        bits = pool.view(torch.int32).cpu().numpy().view(np.uint32)
+        cb, kb = inp.c.view(np.uint32), inp.k_rope.view(np.uint32)
+        before = np.full(bits.shape, 0x7FC00001, np.uint32)
+    else:
+        bits = pool.view(torch.int16).cpu().numpy().view(np.uint16)
+        cb, kb = workload.bf16_bits(inp.c), workload.bf16_bits(inp.k_rope)
+        before = np.full(bits.shape, NAN_BF16, np.uint16)
+    want = oracle.cache_append_image(before, cb, kb, si, pos, inp.page_table, wl.kv_rank)
+    assert np.array_equal(bits, want)
+
+
+def test_append_rotate_matches_rope_at_far_positions():
+    wl = small("v2lite_32k", batch=1, seq_len=64)
+    cfg = mla.Config.from_workload(wl)
+    positions = np.array([0, 1, 63, 64, 4097, 32767, 524287, 1048575], np.int32)
+    n = len(positions)
+    max_pages = 16384
+    pt = np.full((1, max_pages), -1, np.int32)
+    pages = sorted(set(int(p) // 64 for p in positions))
+    for i, lp in enumerate(pages):
+        pt[0, lp] = i
+    rng = np.random.default_rng(5)
+    c = workload.round_bf16(rng.standard_normal((n, 512)).astype(np.float32))
+    k = workload.round_bf16(rng.standard_normal((n, 64)).astype(np.float32))
+    pool = poisoned_pool(cfg, len(pages))
+    mla.cache_append(cfg, upload(c, torch.bfloat16), upload(k, torch.bfloat16),
+                     upload(np.zeros(n, np.int32), torch.int32), upload(positions, torch.int32),
+                     upload(pt, torch.int32), pool, mla.APPEND_ROTATE)
+    torch.cuda.synchronize()
+    got = to64(pool).reshape(-1, 576)
+    for i, p in enumerate(positions):
+        row = got[pt[0, p // 64] * 64 + p % 64]
+        assert np.array_equal(row[:512], c[i].astype(np.float64))
+        ref = oracle.rope(k[i], int(p))
+        # one bf16 rounding of an fp64 rotation: within half an ulp (2^-9 relative)
+        assert np.all(np.abs(row[512:] - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30), p
+
+
+def test_append_skips_invalid_rows():
+    wl = small("v2lite_32k", batch=2, seq_len=128)
+    cfg = mla.Config.from_workload(wl)
+    pt = np.array([[0, 1], [2, -1]], np.int32)
+    pool = poisoned_pool(cfg, 3)
+    n = 5
+    c = np.ones((n, 512), np.float32)
+    k = np.ones((n, 64), np.float32)
+    si = np.array([0, 1, 2, -1, 1], np.int32)          # seq 2 and -1 out of range
+    pos = np.array([5, 70, 3, 3, 200], np.int32)       # (1, 70): page entry -1; (1, 200) > max
+    mla.cache_append(cfg, upload(c, torch.bfloat16), upload(k, torch.bfloat16),
+                     upload(si, torch.int32), upload(pos, torch.int32), upload(pt, torch.int32),
+                     pool, mla.APPEND_RAW)
+    torch.cuda.synchronize()
+    bits = pool.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, 576)
+    written = np.where(np.any(bits != NAN_BF16, axis=1))[0]
+    assert list(written) == [5]
+
+
+# ---------------------------------------------------------------- a1 absorb
+@pytest.mark.parametrize("name", ["tiny_f32", "v2lite_small", "v2_h128_small"])
+def test_absorb_q(name):
+    wl = SMALL[name].replace(batch=3, q_len=2)
+    inp = workload.make(wl, 1, with_latents=False)
+    cfg = mla.Config.from_workload(wl)
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    N = wl.batch * wl.q_len
+    pos = np.array([1000 * i + 7 for i in range(N)], np.int32)
+    q_full = torch.empty((N, wl.heads, wl.dim), dtype=dt, device="cuda")
+    mla.absorb_q(cfg, upload(inp.q_nope.reshape(N, wl.heads, -1), dt),
+                 upload(inp.q_rope.reshape(N, wl.heads, -1), dt), upload(pos, torch.int32),
+                 upload(inp.w_uk, dt), q_full)
+    torch.cuda.synchronize()
+    got = to64(q_full)
+    ref = oracle.absorbed_query(inp.q_nope.reshape(N, wl.heads, -1),
+                                inp.q_rope.reshape(N, wl.heads, -1), inp.w_uk, pos, wl.rope_base)
+    rel = 1e-6 if wl.dtype == "f32" else 2.0 ** -8
+    assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-5 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------- a4 decode alone
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_partials(name):
+    wl = SMALL[name]
+    case = Case(wl, seed=3)
+    inp = case.inp
+    B, Q, H = wl.batch, wl.q_len, wl.heads
+    # absorbed queries from the oracle's helper, rounded to the cache dtype
+    qf = np.empty((B, Q, H, wl.dim))
+    for b in range(B):
+        pq = oracle.query_positions(int(inp.seq_lens[b]), Q)
+        qf[b] = oracle.absorbed_query(inp.q_nope[b], inp.q_rope[b], inp.w_uk, pq, wl.rope_base)
+    qf32 = qf.astype(np.float32)
+    if wl.dtype == "bf16":
+        qf32 = workload.round_bf16(qf32)
+    case.step.q_full.copy_(upload(qf32, case.dt))
+    case.step.decode(case.pool, case.pt, case.seq_lens)
+    torch.cuda.synchronize()
+    op, lp = to64(case.step.o_part), to64(case.step.lse_part)
+    ref_o = np.zeros_like(op)
+    ref_l = np.zeros_like(lp)
+    for b in range(B):
+        c, kr = inp.seq(b)
+        ref_o[b], ref_l[b] = oracle.attend_partials(c, kr, inp.q_nope[b], inp.q_rope[b], inp.w_uk,
+                                                    wl.softmax_scale, case.S, wl.rope_base)
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(lp), empty)
+    assert np.all(op[empty] == 0.0)
+    assert_close(op, ref_o, tau(wl), "o_part")
+    assert_close(lp[~empty], ref_l[~empty], lse_atol(wl), "lse_part", lse=True)
+
+
+# ---------------------------------------------------------------- a5 combine alone
+@pytest.mark.parametrize("S", [1, 3, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_combine(S, dtype):
+    rng = np.random.default_rng(S)
+    B, Q, H, dc = 2, 2, 16, 512
+    op = rng.standard_normal((B, Q, H, S, dc)).astype(np.float32)
+    lp = (rng.standard_normal((B, Q, H, S)) * 3).astype(np.float32)
+    if S > 1:
+        lp[:, :, :, -1] = -np.inf                     # an empty partition
+        op[:, :, :, -1] = 0.0
+    cfg = mla.Config(num_heads=H, dtype=mla.F32 if dtype == "f32" else mla.BF16)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    o_lat = torch.empty((B, Q, H, dc), dtype=dt, device="cuda")
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device="cuda")
+    mla.splitkv_combine(cfg, upload(op, torch.float32), upload(lp, torch.float32), o_lat, lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.lse_combine(op.astype(np.float64), lp.astype(np.float64))
+    if S == 1 and dtype == "f32":
+        assert np.array_equal(to64(o_lat), op[:, :, :, 0].astype(np.float64))   # identity
+    assert_close(to64(o_lat), ro, 1e-6 if dtype == "f32" else 2.0 ** -8, "o_lat")
+    assert_close(to64(lse), rl, 1e-5, "lse", lse=True)
+
+
+# ---------------------------------------------------------------- a6 up-projection alone
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_up_project(dtype):
+    wl = (SMALL["tiny_f32"] if dtype == "f32" else SMALL["v2_h128_small"]).replace(batch=5)
+    inp = workload.make(wl, 4, with_latents=False)
+    rng = np.random.default_rng(4)
+    N = 13
+    ol = (rng.standard_normal((N, wl.heads, wl.kv_rank)) * 0.05).astype(np.float32)
+    if dtype == "bf16":
+        ol = workload.round_bf16(ol)
+    cfg = mla.Config.from_workload(wl)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    out = torch.empty((N, wl.heads, wl.v_dim), dtype=dt, device="cuda")
+    mla.up_project_v(cfg, upload(ol, dt), upload(inp.w_uv, dt), out)
+    torch.cuda.synchronize()
+    ref = np.einsum("hvc,nhc->nhv", inp.w_uv.astype(np.float64), ol.astype(np.float64))
+    assert_close(to64(out), ref, 1e-6 if dtype == "f32" else 2.0 ** -8, "out")
+
+
+# ---------------------------------------------------------------- whole step
+@pytest.mark.parametrize("name", list(SMALL))
+def test_end_to_end_small(name):
+    case = Case(SMALL[name], seed=0)
+    case.run()
+    check_against_oracle(case, case.results(), case.oracle())
+
+
+# full sizes, in the launch configuration the benchmark uses; sampled rows
+FULL = [
+    ("v2lite_32k", None, [0, 7]),
+    ("v2lite_paged_varlen", None, "extremes"),
+    ("v2_h128_8k", [0, 37, 127], [0, 63]),
+    ("v2_h128_1m_q4", [0, 77], [0]),
+]
+
+
+@pytest.mark.parametrize("name,heads,seqs", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(name, heads, seqs):
+    wl = W[name]
+    case = Case(wl, seed=0)
+    if seqs == "extremes":
+        seqs = [int(np.argmax(case.inp.seq_lens)), int(np.argmin(case.inp.seq_lens))]
+    case.run()
+    got = case.results()
+    ref = case.oracle(heads=heads, seqs=seqs)
+    check_against_oracle(case, got, ref, heads=heads, seqs=seqs)
+    for k in got:                                   # every row is finite, sampled or not
+        assert np.all(np.isfinite(got[k]))
+
+
+# ---------------------------------------------------------------- invariants
+def test_paged_equals_identity_bit_exact():
+    wl = SMALL["v2lite_paged_small"]
+    inp = workload.make(wl, 6)
+    a = Case(wl, inputs=inp)
+    ident = workload.make(wl.replace(paged=False), 6)
+    assert np.array_equal(ident.seq_lens, inp.seq_lens)
+    b = Case(wl.replace(paged=False), inputs=ident)
+    a.run()
+    b.run()
+    ra, rb = a.results(), b.results()
+    for k in ra:
+        assert np.array_equal(ra[k], rb[k]), k
+    assert np.array_equal(to64(a.step.o_part), to64(b.step.o_part))
+
+
+def test_repeat_runs_bit_exact():
+    case = Case(SMALL["v2_h128_small"], seed=1)
+    case.run()
+    r1 = {k: v.copy() for k, v in case.results().items()}
+    case.run()
+    for k, v in case.results().items():
+        assert np.array_equal(v, r1[k]), k
+
+
+@pytest.mark.parametrize("S", [1, 7, 64, 256])
+def test_split_counts(S):
+    wl = small("v2lite_32k", batch=2, seq_len=4000)
+    case = Case(wl, seed=2, num_splits=S)
+    case.run()
+    check_against_oracle(case, case.results(), case.oracle())
+    if S == 256:  # more partitions than pages: the empty ones carry lse = -inf
+        lp = to64(case.step.lse_part)
+        assert np.isneginf(lp).any()
+
+
+@pytest.mark.parametrize("lens,Q", [((1,), 1), ((4,), 4), ((5, 17, 64, 65), 1), ((16, 63), 4)])
+def test_edge_lengths(lens, Q):
+    for heads in (16, 128):
+        wl = small("v2lite_32k", batch=len(lens), q_len=Q, heads=heads, seq_len=None,
+                   len_range=(1, 128), num_splits=2)
+        case = Case(wl, seed=9, seq_lens=list(lens))
+        case.run()
+        check_against_oracle(case, case.results(), case.oracle())
+
+
+def test_single_token_output_is_v0():
+    wl = small("v2lite_32k", batch=2, seq_len=1, num_splits=1)
+    case = Case(wl, seed=4)
+    case.run()
+    got = case.results()
+    for b in range(2):
+        c0 = case.inp.seq(b)[0][0].astype(np.float64)
+        v0 = np.einsum("hvc,c->hv", case.inp.w_uv.astype(np.float64), c0)
+        assert_close(got["o"][b, 0], v0, tau(wl), "o vs V_0")
+        assert_close(got["o_lat"][b, 0], np.broadcast_to(c0, (16, 512)), tau(wl), "o_lat vs c_0")
+
+
+@pytest.mark.parametrize("fault", ["length", "page"])
+def test_invalid_sequence_gives_nan_only_there(fault):
+    wl = small("v2lite_paged_varlen", batch=3, len_range=(100, 300), num_splits=2)
+    case = Case(wl, seed=7)
+    if fault == "length":
+        bad_lens = case.inp.seq_lens.copy()
+        bad_lens[1] = 5000                       # above max_seq_len
+        case.seq_lens = upload(bad_lens, torch.int32)
+    else:
+        pt = case.inp.page_table.copy()
+        pt[1, 0] = case.inp.num_pages + 3        # out of the pool
+        case.pt = upload(pt, torch.int32)
+    case.step.absorb(case.q_nope, case.q_rope, case.w_uk)
+    case.step.decode(case.pool, case.pt, case.seq_lens, max_seq_len=300)
+    case.step.combine()
+    torch.cuda.synchronize()
+    ol = to64(case.step.o_lat)
+    assert np.all(np.isnan(ol[1]))
+    assert np.all(np.isfinite(ol[[0, 2]]))
