@@ -40,14 +40,15 @@ DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc", "mla_decode_mfma
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="v2lite_32k")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--graph", action="store_true", help="replay each layer's step as a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -70,24 +71,44 @@ def traffic_from_profile(wl_name, kernel_src_hash):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, nseq):
-    """Time the fp64 oracle on the host cores over the first ``nseq`` sequences."""
-    import numpy as np
+def cpu_baseline(wl, inp, budget_flops=6e11):
+    """Time the fp64 oracle on the host cores over a bounded sample of the workload.
+
+    The sample is the first sequences (and, when one sequence with every head
+    is over budget, the first heads) such that the oracle's work is about
+    ``budget_flops`` (roughly 10-20 s). The rate is scaled to the metric's
+    unit: latent-cache bytes processed per second, counting a sequence's bytes
+    in proportion to the heads sampled.
+    """
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = 1
-    seqs = list(range(nseq))
+    per_tok_head = 2 * wl.kv_rank * (wl.nope_dim + wl.v_dim) + 4 * (wl.nope_dim + wl.rope_dim)
+    heads = wl.heads
+    seq_cost = lambda b, h: int(inp.seq_lens[b]) * h * wl.q_len * per_tok_head  # noqa: E731
+    if seq_cost(0, heads) > budget_flops:
+        heads = max(1, min(heads, int(budget_flops // seq_cost(0, 1))))
+    seqs, spent = [], 0
+    for b in range(wl.batch):
+        if seqs and spent + seq_cost(b, heads) > budget_flops:
+            break
+        seqs.append(b)
+        spent += seq_cost(b, heads)
     t = time.perf_counter()
-    oracle.mla_decode_ref(inp, seqs=seqs)
+    oracle.mla_decode_ref(inp, heads=list(range(heads)), seqs=seqs)
     dt = time.perf_counter() - t
-    nbytes = sum(int(inp.seq_lens[b]) for b in seqs) * wl.dim * wl.elem_bytes
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{nseq} of {wl.batch} sequences ({nbytes / 2**20:.0f} MiB of latent cache), "
-                      f"all {wl.heads} heads, {dt:.1f} s; fp64 unabsorbed NumPy oracle",
-            "seconds": dt, "tokens_per_s": nseq * wl.q_len / dt}
+    tokens = sum(int(inp.seq_lens[b]) for b in seqs)
+    nbytes = tokens * wl.dim * wl.elem_bytes * heads / wl.heads
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(seqs)} of {wl.batch} sequences ({tokens} cached tokens), "
+                      f"{heads} of {wl.heads} heads, {dt:.1f} s; fp64 unabsorbed NumPy oracle; "
+                      f"bytes counted x {heads}/{wl.heads}",
+            "seconds": round(dt, 2),
+            "decode_tokens_per_s": round(len(seqs) * wl.q_len * heads / wl.heads / dt, 4)}
 
 
 def main():
@@ -258,9 +279,19 @@ def main():
     }
     if wl.name.startswith("v2lite"):
         out["v2lite_attention_tokens_per_s_27_layers"] = round(B / (27 * ms_step * 1e-3), 1)
+    props = torch.cuda.get_device_properties(0)
+    out["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
+                     "gcn_arch": getattr(props, "gcnArchName", "")}
+    if args.calibrate_copy:
+        # a plain copy of known size, for scaling the HBM byte counters
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
-        nseq = args.cpu_sample_seqs or max(1, min(B, 2))
-        out["cpu_baseline"] = cpu_baseline(wl, inp, nseq)
+        out["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(out), flush=True)
 
 

@@ -102,11 +102,18 @@ WORKLOADS: Dict[str, Workload] = {
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """float32 -> nearest bf16 (ties to even), returned as float32 values."""
+    """float32 -> nearest bf16 (ties to even), returned as float32 values.
+
+    Finite inputs only (the draws are finite): their bit patterns are at most
+    0xFF7FFFFF, so adding 0x8000 cannot wrap a uint32.
+    """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).reshape(x.shape)
+    u = x.view(np.uint32).copy()
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32).reshape(x.shape)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
