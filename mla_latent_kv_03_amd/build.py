@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["mla_api.cpp", "mla_kernels.hip", "mla_decode_mfma.hip"]
+SOURCES = ["mla_api.cpp", "mla_kernels.hip", "mla_decode_mfma.hip", "mla_proj_mfma.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -110,6 +110,14 @@ void decode_mfma_kernel(int Q, int H, int S, int page, int max_seq_len, float sc
   if (!bad) split_range(L, S, page, s, &t0, &t1);
   const int nslices = (t1 - t0 + kSlice - 1) / kSlice;
 
+  // Page-table window: lane i holds the physical page of the unit's page
+  // pt_base + i, so a slice's page is a register read instead of a dependent
+  // global load in front of its cache loads.
+  const int upages = (t1 - t0 + page - 1) / page;
+  const size_t pt_row = (size_t)b * max_pages + t0 / page;
+  int pt_base = 0;
+  int pt_reg = lane < upages ? page_table[pt_row + lane] : 0;
+
   // absorbed queries of the 16 rows as the B operand of S^T = C . Q^T
   bf16x8_t qreg[kKSteps];
   {
@@ -133,7 +141,12 @@ void decode_mfma_kernel(int Q, int H, int S, int page, int max_seq_len, float sc
 
   auto issue = [&](int si) {
     const int t = t0 + si * kSlice;
-    int pg = page_table[(size_t)b * max_pages + t / page];
+    const int u = (t - t0) / page;  // unit page of this slice (wave-uniform)
+    if (u - pt_base >= 64) {        // next window of 64 pages
+      pt_base = u & ~63;
+      pt_reg = pt_base + lane < upages ? page_table[pt_row + pt_base + lane] : 0;
+    }
+    int pg = __builtin_amdgcn_readlane(pt_reg, u - pt_base);
     if (pg < 0 || (int64_t)pg >= num_pages) {
       bad = true;
       pg = 0;

@@ -78,8 +78,17 @@ static int absorb_impl(const Shape& s, int n_tok, const void* q_nope, const void
   return (int)hipGetLastError();
 }
 
+bool absorb_mfma_ok(const Shape& s);
+int launch_absorb_q_mfma(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
+                         const int32_t* pos, const void* w_uk, void* q_full, void* stream);
+bool up_v_mfma_ok(const Shape& s);
+int launch_up_project_v_mfma(const Shape& s, int n_tok, const void* o_lat, const void* w_uv,
+                             void* out, void* stream);
+
 int launch_absorb_q(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
                     const int32_t* pos, const void* w_uk, void* q_full, void* stream) {
+  if (absorb_mfma_ok(s))
+    return launch_absorb_q_mfma(s, n_tok, q_nope, q_rope, pos, w_uk, q_full, stream);
   return s.dtype == 0 ? absorb_impl<float>(s, n_tok, q_nope, q_rope, pos, w_uk, q_full, stream)
                       : absorb_impl<bf16_t>(s, n_tok, q_nope, q_rope, pos, w_uk, q_full, stream);
 }
@@ -296,20 +305,37 @@ int launch_decode_generic(const Shape& s, int batch, int q_len, int num_splits, 
 // "Flash-Decoding and FlashInfer"). One block per output row.
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplits = 4096;
+constexpr int kCombThreads = 128;
 
 template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(int S, int dc, const float* __restrict__ o_part,
-                                                      const float* __restrict__ lse_part,
-                                                      T* __restrict__ o_lat, float* __restrict__ lse) {
+__device__ __forceinline__ void store4(T* p, float4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float4 v) {
+  *reinterpret_cast<float4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
+  uint2 u;
+  u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+  u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+
+// One block per output row; weights e^(lse_s - max) in LDS, then each thread
+// accumulates 4 adjacent columns with 16-byte loads of every partition.
+template <typename T>
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(
+    int S, int dc, const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    T* __restrict__ o_lat, float* __restrict__ lse) {
   __shared__ float w[kMaxSplits];
-  __shared__ float red[256];
+  __shared__ float red[kCombThreads];
   __shared__ int any_nan;
   const int r = blockIdx.x, tid = threadIdx.x;
   const float* lp = lse_part + (size_t)r * S;
   if (tid == 0) any_nan = 0;
   float mx = -INFINITY;
   int nan_seen = 0;
-  for (int s = tid; s < S; s += blockDim.x) {
+  for (int s = tid; s < S; s += kCombThreads) {
     const float v = lp[s];
     w[s] = v;
     nan_seen |= (v != v);
@@ -318,21 +344,21 @@ __global__ __launch_bounds__(256) void combine_kernel(int S, int dc, const float
   red[tid] = mx;
   __syncthreads();
   if (nan_seen) any_nan = 1;
-  for (int off = 128; off > 0; off >>= 1) {
+  for (int off = kCombThreads / 2; off > 0; off >>= 1) {
     if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
     __syncthreads();
   }
   mx = red[0];
   __syncthreads();
   float sum = 0.0f;
-  for (int s = tid; s < S; s += blockDim.x) {
+  for (int s = tid; s < S; s += kCombThreads) {
     const float e = (w[s] == -INFINITY) ? 0.0f : expf(w[s] - mx);
     w[s] = e;
     sum += e;
   }
   red[tid] = sum;
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
+  for (int off = kCombThreads / 2; off > 0; off >>= 1) {
     if (tid < off) red[tid] += red[tid + off];
     __syncthreads();
   }
@@ -340,11 +366,28 @@ __global__ __launch_bounds__(256) void combine_kernel(int S, int dc, const float
   const bool bad = any_nan != 0;
   const float nanv = __int_as_float(0x7fc00000);
   const float inv = 1.0f / sum;
-  const float* op = o_part + (size_t)r * S * dc;
-  for (int f = tid; f < dc; f += blockDim.x) {
-    float acc = 0.0f;
-    for (int s = 0; s < S; ++s) acc = fmaf(w[s], op[(size_t)s * dc + f], acc);
-    Elt<T>::st(o_lat + (size_t)r * dc + f, bad ? nanv : acc * inv);
+  const float4* op = reinterpret_cast<const float4*>(o_part + (size_t)r * S * dc);
+  const int d4 = dc / 4;
+  for (int f = tid; f < d4; f += kCombThreads) {
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    int s = 0;
+    for (; s + 4 <= S; s += 4) {
+      const float4 x0 = op[(size_t)s * d4 + f], x1 = op[(size_t)(s + 1) * d4 + f];
+      const float4 x2 = op[(size_t)(s + 2) * d4 + f], x3 = op[(size_t)(s + 3) * d4 + f];
+      const float w0 = w[s], w1 = w[s + 1], w2 = w[s + 2], w3 = w[s + 3];
+      a.x = fmaf(w0, x0.x, a.x); a.y = fmaf(w0, x0.y, a.y); a.z = fmaf(w0, x0.z, a.z); a.w = fmaf(w0, x0.w, a.w);
+      a.x = fmaf(w1, x1.x, a.x); a.y = fmaf(w1, x1.y, a.y); a.z = fmaf(w1, x1.z, a.z); a.w = fmaf(w1, x1.w, a.w);
+      a.x = fmaf(w2, x2.x, a.x); a.y = fmaf(w2, x2.y, a.y); a.z = fmaf(w2, x2.z, a.z); a.w = fmaf(w2, x2.w, a.w);
+      a.x = fmaf(w3, x3.x, a.x); a.y = fmaf(w3, x3.y, a.y); a.z = fmaf(w3, x3.z, a.z); a.w = fmaf(w3, x3.w, a.w);
+    }
+    for (; s < S; ++s) {
+      const float4 x = op[(size_t)s * d4 + f];
+      const float ws = w[s];
+      a.x = fmaf(ws, x.x, a.x); a.y = fmaf(ws, x.y, a.y); a.z = fmaf(ws, x.z, a.z); a.w = fmaf(ws, x.w, a.w);
+    }
+    float4 v = bad ? make_float4(nanv, nanv, nanv, nanv)
+                   : make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    store4<T>(o_lat + (size_t)r * dc + 4 * f, v);
   }
   if (lse && tid == 0) lse[r] = bad ? nanv : mx + logf(sum);
 }
@@ -352,11 +395,11 @@ __global__ __launch_bounds__(256) void combine_kernel(int S, int dc, const float
 int launch_combine(const Shape& s, int rows, int num_splits, const float* o_part,
                    const float* lse_part, void* o_lat, float* lse, void* stream) {
   if (s.dtype == 0)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(rows), dim3(256), 0, as_stream(stream),
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(rows), dim3(kCombThreads), 0, as_stream(stream),
                        num_splits, s.dc, o_part, lse_part, (float*)o_lat, lse);
   else
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(rows), dim3(256), 0, as_stream(stream),
-                       num_splits, s.dc, o_part, lse_part, (bf16_t*)o_lat, lse);
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(rows), dim3(kCombThreads), 0,
+                       as_stream(stream), num_splits, s.dc, o_part, lse_part, (bf16_t*)o_lat, lse);
   return (int)hipGetLastError();
 }
 
@@ -403,6 +446,7 @@ __global__ __launch_bounds__(256) void up_v_kernel(int n_tok, int H, int dc, int
 
 int launch_up_project_v(const Shape& s, int n_tok, const void* o_lat, const void* w_uv,
                         void* out, void* stream) {
+  if (up_v_mfma_ok(s)) return launch_up_project_v_mfma(s, n_tok, o_lat, w_uv, out, stream);
   dim3 grid(s.H, (n_tok + kUpTok - 1) / kUpTok);
   if (s.dtype == 0)
     hipLaunchKernelGGL(up_v_kernel<float>, grid, dim3(256), 0, as_stream(stream), n_tok, s.H, s.dc,
