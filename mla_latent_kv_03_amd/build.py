@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # keep MFMA accumulators in ordinary VGPRs: the online softmax rescales
+    # them with vector ALU ops, which cannot address the accumulation registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -305,7 +305,7 @@ int launch_decode_generic(const Shape& s, int batch, int q_len, int num_splits, 
 // "Flash-Decoding and FlashInfer"). One block per output row.
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplits = 4096;
-constexpr int kCombThreads = 128;
+constexpr int kCombCols = 256;  // latent columns per block: 64 lanes x 4
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float4 v);
@@ -321,85 +321,89 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 
-// One block per output row; weights e^(lse_s - max) in LDS, then each thread
-// accumulates 4 adjacent columns with 16-byte loads of every partition.
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One wave per (output row, 256 latent columns). The wave turns the row's S
+// partition LSEs into weights e^(lse_s - max) in LDS, then each lane
+// accumulates 4 adjacent columns over all partitions with 16-byte loads, 8
+// partitions in flight at a time.
 template <typename T>
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(
-    int S, int dc, const float* __restrict__ o_part, const float* __restrict__ lse_part,
-    T* __restrict__ o_lat, float* __restrict__ lse) {
+__global__ __launch_bounds__(64) void combine_kernel(int S, int dc, const float* __restrict__ o_part,
+                                                     const float* __restrict__ lse_part,
+                                                     T* __restrict__ o_lat, float* __restrict__ lse) {
   __shared__ float w[kMaxSplits];
-  __shared__ float red[kCombThreads];
-  __shared__ int any_nan;
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const int col = blockIdx.y * kCombCols + 4 * lane;
   const float* lp = lse_part + (size_t)r * S;
-  if (tid == 0) any_nan = 0;
   float mx = -INFINITY;
-  int nan_seen = 0;
-  for (int s = tid; s < S; s += kCombThreads) {
+  bool nan_seen = false;
+  for (int s = lane; s < S; s += 64) {
     const float v = lp[s];
     w[s] = v;
     nan_seen |= (v != v);
     mx = fmaxf(mx, v);
   }
-  red[tid] = mx;
-  __syncthreads();
-  if (nan_seen) any_nan = 1;
-  for (int off = kCombThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  mx = red[0];
-  __syncthreads();
+  mx = wave_max(mx);
+  const bool bad = __any(nan_seen);
   float sum = 0.0f;
-  for (int s = tid; s < S; s += kCombThreads) {
+  for (int s = lane; s < S; s += 64) {
     const float e = (w[s] == -INFINITY) ? 0.0f : expf(w[s] - mx);
     w[s] = e;
     sum += e;
   }
-  red[tid] = sum;
+  sum = wave_sum(sum);
   __syncthreads();
-  for (int off = kCombThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  sum = red[0];
-  const bool bad = any_nan != 0;
   const float nanv = __int_as_float(0x7fc00000);
-  const float inv = 1.0f / sum;
-  const float4* op = reinterpret_cast<const float4*>(o_part + (size_t)r * S * dc);
-  const int d4 = dc / 4;
-  for (int f = tid; f < d4; f += kCombThreads) {
+  if (col < dc) {
+    const float4* op = reinterpret_cast<const float4*>(o_part + (size_t)r * S * dc + col);
+    const size_t st = dc / 4;  // float4 stride between partitions
     float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     int s = 0;
-    for (; s + 4 <= S; s += 4) {
-      const float4 x0 = op[(size_t)s * d4 + f], x1 = op[(size_t)(s + 1) * d4 + f];
-      const float4 x2 = op[(size_t)(s + 2) * d4 + f], x3 = op[(size_t)(s + 3) * d4 + f];
-      const float w0 = w[s], w1 = w[s + 1], w2 = w[s + 2], w3 = w[s + 3];
-      a.x = fmaf(w0, x0.x, a.x); a.y = fmaf(w0, x0.y, a.y); a.z = fmaf(w0, x0.z, a.z); a.w = fmaf(w0, x0.w, a.w);
-      a.x = fmaf(w1, x1.x, a.x); a.y = fmaf(w1, x1.y, a.y); a.z = fmaf(w1, x1.z, a.z); a.w = fmaf(w1, x1.w, a.w);
-      a.x = fmaf(w2, x2.x, a.x); a.y = fmaf(w2, x2.y, a.y); a.z = fmaf(w2, x2.z, a.z); a.w = fmaf(w2, x2.w, a.w);
-      a.x = fmaf(w3, x3.x, a.x); a.y = fmaf(w3, x3.y, a.y); a.z = fmaf(w3, x3.z, a.z); a.w = fmaf(w3, x3.w, a.w);
+    for (; s + 8 <= S; s += 8) {
+      float4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = op[(size_t)(s + u) * st];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float ws = w[s + u];
+        a.x = fmaf(ws, x[u].x, a.x);
+        a.y = fmaf(ws, x[u].y, a.y);
+        a.z = fmaf(ws, x[u].z, a.z);
+        a.w = fmaf(ws, x[u].w, a.w);
+      }
     }
     for (; s < S; ++s) {
-      const float4 x = op[(size_t)s * d4 + f];
+      const float4 x = op[(size_t)s * st];
       const float ws = w[s];
-      a.x = fmaf(ws, x.x, a.x); a.y = fmaf(ws, x.y, a.y); a.z = fmaf(ws, x.z, a.z); a.w = fmaf(ws, x.w, a.w);
+      a.x = fmaf(ws, x.x, a.x);
+      a.y = fmaf(ws, x.y, a.y);
+      a.z = fmaf(ws, x.z, a.z);
+      a.w = fmaf(ws, x.w, a.w);
     }
-    float4 v = bad ? make_float4(nanv, nanv, nanv, nanv)
-                   : make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
-    store4<T>(o_lat + (size_t)r * dc + 4 * f, v);
+    const float inv = 1.0f / sum;
+    const float4 v = bad ? make_float4(nanv, nanv, nanv, nanv)
+                         : make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    store4<T>(o_lat + (size_t)r * dc + col, v);
   }
-  if (lse && tid == 0) lse[r] = bad ? nanv : mx + logf(sum);
+  if (lse && blockIdx.y == 0 && lane == 0) lse[r] = bad ? nanv : mx + logf(sum);
 }
 
 int launch_combine(const Shape& s, int rows, int num_splits, const float* o_part,
                    const float* lse_part, void* o_lat, float* lse, void* stream) {
+  dim3 grid(rows, (s.dc + kCombCols - 1) / kCombCols);
   if (s.dtype == 0)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(rows), dim3(kCombThreads), 0, as_stream(stream),
-                       num_splits, s.dc, o_part, lse_part, (float*)o_lat, lse);
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(64), 0, as_stream(stream), num_splits,
+                       s.dc, o_part, lse_part, (float*)o_lat, lse);
   else
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(rows), dim3(kCombThreads), 0,
-                       as_stream(stream), num_splits, s.dc, o_part, lse_part, (bf16_t*)o_lat, lse);
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(64), 0, as_stream(stream), num_splits,
+                       s.dc, o_part, lse_part, (bf16_t*)o_lat, lse);
   return (int)hipGetLastError();
 }
 
