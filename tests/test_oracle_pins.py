@@ -43,12 +43,12 @@ def test_cache_accounting_matches_printed_figures():
     per_tok = oracle.latent_bytes_per_token(dc, dr, 2, g["v2lite_layers"])
     assert per_tok == g["v2lite_latent_bytes_per_token_all_layers"]
     assert per_tok * 32768 == g["v2lite_latent_mib_at_32768"] * MiB
-    # vLLM's reservation is "within 0.01%" of the calculation
+    # the page puts vLLM's reservation within 0.01% of the calculation
     assert abs(per_tok - g["vllm_reserved_bytes_per_token"]) / per_tok < 1e-4
     plain = oracle.per_head_kv_bytes_per_token(g["v2lite_heads"], g["v2lite_key_width"],
                                                g["v2lite_value_width"], 2, g["v2lite_layers"])
     assert plain * 32768 == g["v2lite_plain_mib_at_32768"] * MiB
-    assert round(plain / per_tok) == 9          # "a ninth"
+    assert round(plain / per_tok) == 9          # one ninth
     v3 = oracle.latent_bytes_per_token(512, 64, 2)
     assert v3 == g["v3_latent_bytes_per_token_per_layer"]
     v3_mha = oracle.per_head_kv_bytes_per_token(128, 128, 128, 2)
