@@ -238,6 +238,22 @@ __device__ __forceinline__ void slice_pv(const char* bufb, const int* pv, const 
   }
 }
 
+// Max / sum over the 4 lanes {l, l^16, l^32, l^48} (one query row of an MFMA
+// accumulator), with the gfx950 lane-swap instructions instead of LDS
+// permutes: permlane16_swap pairs lane l with l^16, permlane32_swap with l^32.
+__device__ __forceinline__ float row_max4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float row_sum4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Online softmax step for one 16-row tile on one 16-token slice. sacc[r] is
 // the score of row n (= lane % 16) against token 4*kg + r; tok0 is the slice's
 // first token. Returns the A operand (P in bf16) and updates m, l, acc.
@@ -250,9 +266,7 @@ __device__ __forceinline__ s16x4_t slice_softmax(f32x4_t sacc, int tok0, int kg,
     const int t = tok0 + 4 * kg + r;
     sv[r] = (t <= p_lim) ? sacc[r] * scale_log2 : -INFINITY;
   }
-  float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+  const float mloc = row_max4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
   // raise the reference max only when a score exceeds it by more than kLazy
   const bool raise = mloc > m_run + kLazy;
   if (__any(raise)) {
@@ -395,8 +409,7 @@ void decode_slices_kernel(int Q, int H, int S, int page, int max_seq_len, float 
   }
 
   // ---- merge the four waves ------------------------------------------------
-  float l_row = l_run + __shfl_xor(l_run, 16, 64);
-  l_row += __shfl_xor(l_row, 32, 64);
+  const float l_row = row_sum4(l_run);
   __syncthreads();  // every wave is done with its slice buffers
   float* fl = reinterpret_cast<float*>(lds);
   float* sm = fl + kWaves * kRowsA * kDC;  // m[4][16], l[4][16], bad[4]
@@ -456,16 +469,26 @@ void decode_slices_kernel(int Q, int H, int S, int page, int max_seq_len, float 
 }
 
 // ---------------------------------------------------------------------------
-// 64*RT query rows per block, row-split waves over shared 64-token tiles
+// 64 query rows per block (16 per wave) over shared 64-token tiles
+//
+// Per tile each wave runs three phases with no branch between the MFMAs of a
+// phase, so the 4 independent QK chains and the 32 independent PV products
+// overlap their LDS reads:
+//   QK   S^T for the 4 16-token subtiles (4 x 18 v_mfma_f32_16x16x32_bf16)
+//   max  row max over the 64 tokens (2 permlane swaps), rare rescale, P = 2^(s-m)
+//   PV   two 32-token halves with v_mfma_f32_16x16x32_bf16 (K = 32 tokens):
+//        the A operand takes the 8 tokens {4kg..4kg+3, 16+4kg..16+4kg+3} of
+//        the half straight from two QK accumulators; the B operand gathers the
+//        same 8 token rows (ds_read_b64, 4 features each) and transposes 8x4
+//        in registers (v_perm_b32).
 // ---------------------------------------------------------------------------
-template <int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_rows_kernel(int Q, int H, int S, int page, int max_seq_len, float scale_log2,
-                        int units, int groups, const bf16_t* __restrict__ q_full,
-                        const bf16_t* __restrict__ cache, int64_t num_pages,
-                        const int32_t* __restrict__ page_table, int max_pages,
-                        const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
-                        float* __restrict__ lse_part) {
+void decode_tiles_kernel(int Q, int H, int S, int page, int max_seq_len, float scale_log2,
+                         int units, int groups, const bf16_t* __restrict__ q_full,
+                         const bf16_t* __restrict__ cache, int64_t num_pages,
+                         const int32_t* __restrict__ page_table, int max_pages,
+                         const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
+                         float* __restrict__ lse_part) {
   extern __shared__ u32x4_t lds[];
   int unit, grp;
   if (!map_block(units, groups, &unit, &grp)) return;
@@ -474,7 +497,7 @@ void decode_rows_kernel(int Q, int H, int S, int page, int max_seq_len, float sc
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 15, kg = lane >> 4;
-  const int row0 = grp * (64 * RT) + wave * (16 * RT);
+  const int row0 = grp * 64 + wave * 16;
 
   const int L = seq_lens[b];
   const bool bad_len = (L < Q) || (L > max_seq_len);
@@ -495,42 +518,37 @@ void decode_rows_kernel(int Q, int H, int S, int page, int max_seq_len, float sc
       bad = true;
       pg = 0;
     }
-    // this wave copies LDS chunks [wave*1152, wave*1152 + 1152) of the tile
+    // this wave copies tile rows [16*wave, 16*wave + 16)
     const bf16_t* src = cache + ((size_t)pg * page + (t % page)) * kD;
     dma.issue(src, __builtin_amdgcn_readfirstlane(lds_addr(dst + wave * kSliceChunks)));
   };
   if (ntiles > 0) issue(0, lds);  // the first tile loads while the queries are fetched
 
-  bf16x8_t qreg[RT][kKSteps];
-  int p_lim[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = row0 + 16 * rt + n;
+  bf16x8_t qreg[kKSteps];
+  const int row = row0 + n;
+  {
     const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(q_full + ((size_t)b * R + row) * kD);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      qreg[rt][ks] = __builtin_bit_cast(bf16x8_t, qsrc[ks * 4 + kg]);
-    p_lim[rt] = L - Q + row / H;
+    for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8_t, qsrc[ks * 4 + kg]);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) settle(qreg[rt][ks]);
+    for (int ks = 0; ks < kKSteps; ++ks) settle(qreg[ks]);
   }
+  const int p_lim = L - Q + row / H;
 
-  float m_run[RT], l_run[RT];
-  f32x4_t acc[RT][kFB][4];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.0f;
-    zero_acc(acc[rt]);
-  }
+  // LDS addressing inside a tile: QK reads row 16u + n, chunk 4 ks + kg;
+  // PV reads rows 32 v + sigma(kg, j), sigma = {4kg..4kg+3, 16+4kg..16+4kg+3}
   const int qk0 = n * kChunks + (kg ^ (n & 7));
   const int qk1 = n * kChunks + ((4 + kg) ^ (n & 7));
-  int pv[4];
+  int pv[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = 4 * kg + j;
+  for (int j = 0; j < 8; ++j) {
+    const int t = (j < 4) ? 4 * kg + j : 16 + 4 * kg + (j - 4);
     pv[j] = 16 * (t * kChunks + ((n >> 1) ^ (t & 7))) + 8 * (n & 1);
   }
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4_t acc[kFB][4];
+  zero_acc(acc);
 
   for (int ti = 0; ti < ntiles; ++ti) {
     u32x4_t* cur = lds + (ti & 1) * kTileChunks;
@@ -540,53 +558,154 @@ void decode_rows_kernel(int Q, int H, int S, int page, int max_seq_len, float sc
       zero_rows(cur + wave * kSliceChunks, wave * kSliceChunks, lane, t1 - ts);
     __syncthreads();  // tile ti landed for every wave; tile ti-1 fully consumed
     if (ti + 1 < ntiles) issue(ti + 1, lds + ((ti + 1) & 1) * kTileChunks);
-#pragma unroll 1
-    for (int st = 0; st < kTile / kSlice; ++st) {
-      const int tok0 = ts + st * kSlice;
-      if (tok0 >= t1) break;
-      const u32x4_t* sb = cur + st * kSliceChunks;
-      f32x4_t sacc[RT];
-      slice_qk<RT>(sb, qk0, qk1, qreg, sacc);
-      s16x4_t pa[RT];
+
+    // ---- QK: 4 independent 18-step chains
+    f32x4_t s4[4];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        pa[rt] = slice_softmax(sacc[rt], tok0, kg, p_lim[rt], scale_log2, m_run[rt], l_run[rt],
-                               acc[rt]);
-      slice_pv<RT>(reinterpret_cast<const char*>(sb), pv, pa, acc);
+    for (int u = 0; u < 4; ++u) s4[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // software pipeline: the 4 operands of k-step ks+1 are read while the 4
+    // MFMAs of k-step ks issue (the scheduling barriers keep that order)
+    u32x4_t a_cur[4], a_nxt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a_cur[u] = cur[qk0 + u * kSliceChunks];
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if (ks + 1 < kKSteps) {
+        const int kn = ks + 1;
+        const int base = ((kn & 1) ? qk1 : qk0) + 8 * (kn >> 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a_nxt[u] = cur[base + u * kSliceChunks];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        s4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a_cur[u]),
+                                                        qreg[ks], s4[u], 0, 0, 0);
+      if (ks + 1 < kKSteps) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then 4 MFMA
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a_cur[u] = a_nxt[u];
+    }
+    // ---- softmax over the tile's 64 tokens (lane: row n, tokens 16u + 4kg + r)
+    float sv[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = ts + 16 * u + 4 * kg + r;
+        sv[4 * u + r] = (t <= p_lim) ? s4[u][r] * scale_log2 : -INFINITY;
+      }
+    float mloc = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, sv[i]);
+    mloc = row_max4(mloc);
+    const bool raise = mloc > m_run + kLazy;
+    if (__any(raise)) {
+      const float m_new = raise ? mloc : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      if (__any(raise && m_run != -INFINITY)) {
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * kg + r, 64);
+#pragma unroll
+        for (int fb = 0; fb < kFB; ++fb)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[fb][m][r] *= ar[r];
+      }
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    float lsum = 0.0f;
+    uint32_t pk[8];  // P as bf16 pairs: half v, tokens sigma(kg, 0..7)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int u = 2 * v + h;
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(sv[4 * u + r] - m_use);
+          lsum += p[r];
+        }
+        bf16x2_t p01 = {(__bf16)p[0], (__bf16)p[1]};
+        bf16x2_t p23 = {(__bf16)p[2], (__bf16)p[3]};
+        pk[4 * v + 2 * h] = __builtin_bit_cast(uint32_t, p01);
+        pk[4 * v + 2 * h + 1] = __builtin_bit_cast(uint32_t, p23);
+      }
+    l_run += lsum;
+    // ---- PV: two 32-token halves, K = 32; the 8 rows of step it+1 are read
+    // while step it is transposed and multiplied
+    const char* tb = reinterpret_cast<const char*>(cur);
+    bf16x8_t pa[2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      u32x4_t pav = {pk[4 * v], pk[4 * v + 1], pk[4 * v + 2], pk[4 * v + 3]};
+      pa[v] = __builtin_bit_cast(bf16x8_t, pav);
+    }
+    u32x2_t xa[8], xb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xa[j] = *reinterpret_cast<const u32x2_t*>(tb + pv[j]);
+#pragma unroll
+    for (int it = 0; it < 2 * kFB; ++it) {
+      const int v = it / kFB, fb = it % kFB;
+      if (it + 1 < 2 * kFB) {
+        const int vn = (it + 1) / kFB, fn = (it + 1) % kFB;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          xb[j] = *reinterpret_cast<const u32x2_t*>(tb + pv[j] + vn * (32 * kChunks * 16) + fn * 128);
+      }
+      u32x4_t bm[4];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        bm[0][q2] = pack_lo(xa[2 * q2].x, xa[2 * q2 + 1].x);
+        bm[1][q2] = pack_hi(xa[2 * q2].x, xa[2 * q2 + 1].x);
+        bm[2][q2] = pack_lo(xa[2 * q2].y, xa[2 * q2 + 1].y);
+        bm[3][q2] = pack_hi(xa[2 * q2].y, xa[2 * q2 + 1].y);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        acc[fb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            pa[v], __builtin_bit_cast(bf16x8_t, bm[m]), acc[fb][m], 0, 0, 0);
+      if (it + 1 < 2 * kFB) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);   // next step's LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 1);  // this step's transposes
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);   // this step's MFMAs
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xa[j] = xb[j];
     }
   }
   wait_vmcnt<0>();
 
-  // ---- write this wave's rows ----------------------------------------------
+  // ---- write this wave's 16 rows ------------------------------------------
   const float nanv = __int_as_float(0x7fc00000);
+  const float l_row = row_sum4(l_run);
+  float inv[4];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    float l_row = l_run[rt] + __shfl_xor(l_run[rt], 16, 64);
-    l_row += __shfl_xor(l_row, 32, 64);
-    // lane holds rows 4*kg + r of the tile; their sums live in lanes 4*kg + r
-    float inv[4];
+  for (int r = 0; r < 4; ++r) {
+    const float lr = __shfl(l_row, 4 * kg + r, 64);
+    inv[r] = lr > 0.0f ? 1.0f / lr : 0.0f;
+  }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float lr = __shfl(l_row, 4 * kg + r, 64);
-      inv[r] = lr > 0.0f ? 1.0f / lr : 0.0f;
+  for (int r = 0; r < 4; ++r) {
+    const int orow = row0 + 4 * kg + r;
+    float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + 4 * n;
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb) {
+      float4 v = make_float4(acc[fb][0][r] * inv[r], acc[fb][1][r] * inv[r],
+                             acc[fb][2][r] * inv[r], acc[fb][3][r] * inv[r]);
+      if (bad) v = make_float4(nanv, nanv, nanv, nanv);
+      *reinterpret_cast<float4*>(dst + fb * 64) = v;
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 16 * rt + 4 * kg + r;
-      float* dst = o_part + (((size_t)b * R + row) * S + s) * kDC + 4 * n;
-#pragma unroll
-      for (int fb = 0; fb < kFB; ++fb) {
-        float4 v = make_float4(acc[rt][fb][0][r] * inv[r], acc[rt][fb][1][r] * inv[r],
-                               acc[rt][fb][2][r] * inv[r], acc[rt][fb][3][r] * inv[r]);
-        if (bad) v = make_float4(nanv, nanv, nanv, nanv);
-        *reinterpret_cast<float4*>(dst + fb * 64) = v;
-      }
-    }
-    if (kg == 0) {
-      const int row = row0 + 16 * rt + n;
-      const float lse = l_row > 0.0f ? (m_run[rt] + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
-      lse_part[((size_t)b * R + row) * S + s] = bad ? nanv : lse;
-    }
+  }
+  if (kg == 0) {
+    const float lse = l_row > 0.0f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
+    lse_part[((size_t)b * R + row) * S + s] = bad ? nanv : lse;
   }
 }
 
@@ -638,13 +757,13 @@ int launch_decode(const Shape& s, int batch, int q_len, int num_splits, int max_
     hipLaunchKernelGGL(decode_slices_kernel, dim3(blocks), dim3(256), kLdsBytesA, st, q_len, s.H,
                        num_splits, s.page, max_seq_len, scale_log2, units, groups, q, c, num_pages,
                        page_table, max_pages, seq_lens, o_part, lse_part);
-  } else if (kind == 2) {
+  } else {
     static bool attr = false;
-    int rc = set_lds(decode_rows_kernel<1>, kLdsBytesB, &attr);
+    int rc = set_lds(decode_tiles_kernel, kLdsBytesB, &attr);
     if (rc) return rc;
     const int groups = R / 64;
     const int blocks = ((units + 7) / 8) * 8 * groups;
-    hipLaunchKernelGGL(decode_rows_kernel<1>, dim3(blocks), dim3(256), kLdsBytesB, st, q_len, s.H,
+    hipLaunchKernelGGL(decode_tiles_kernel, dim3(blocks), dim3(256), kLdsBytesB, st, q_len, s.H,
                        num_splits, s.page, max_seq_len, scale_log2, units, groups, q, c, num_pages,
                        page_table, max_pages, seq_lens, o_part, lse_part);
   }
