@@ -3,7 +3,8 @@
 
 A step is the whole hot path over one batch: query absorption, append of the
 B*Q new cache rows, split-KV decode, log-sum-exp combine, value
-up-projection. The default workload is the DeepSeek-V2-Lite layer shape at
+up-projection (three library calls: absorption + append and combine +
+up-projection each run as one fused call; --unfused runs five). The default workload is the DeepSeek-V2-Lite layer shape at
 32K context (B = 8 sequences of 32,768 tokens, 16 heads, 512 + 64 latent
 row). Inputs are seeded synthetic tensors already resident in HBM when the
 timed region starts. One cache per layer is rotated (27 layers, as V2-Lite
@@ -34,7 +35,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LAYERS = {"v2lite_32k": 27, "v2lite_paged_varlen": 27, "v2_h128_8k": 4, "v2_h128_1m_q4": 2,
           "tiny_f32": 4}
-DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc", "mla_decode_mfma.hip")
+CSRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc")
+# decode kernel name (mla_decode_kernel_name) -> (kernel symbol, the sources that define it)
+DECODE_KERNELS = {
+    "mfma_rows16": ("decode_rows16_kernel", ["mla_decode_common.h", "mla_decode_rows16.hip"]),
+    "mfma_tiles": ("decode_tiles_kernel", ["mla_decode_common.h", "mla_decode_tiles.hip"]),
+    "generic": ("decode_generic_kernel", ["mla_kernels.hip"]),
+}
 
 
 def parse():
@@ -47,13 +54,20 @@ def parse():
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--graph", action="store_true", help="replay each layer's step as a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step as five library calls instead of three")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
-def src_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def src_hash(names):
+    """sha256[:16] over the given sources (concatenated, in order)."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(wl_name, kernel_src_hash):
@@ -161,11 +175,17 @@ def main():
 
     def one_step(layer):
         pool = pools[layer % n_layers]
-        st.absorb(q_nope, q_rope, w_uk)
-        st.append(c_new, k_new, pt, pool)
+        if args.unfused:
+            st.absorb(q_nope, q_rope, w_uk)
+            st.append(c_new, k_new, pt, pool)
+        else:
+            st.absorb_append(q_nope, q_rope, w_uk, c_new, k_new, pt, pool)
         st.decode(pool, pt, seq_lens)
-        st.combine()
-        st.up_project(w_uv)
+        if args.unfused:
+            st.combine()
+            st.up_project(w_uv)
+        else:
+            st.combine_up_project(w_uv)
 
     graphs = None
     if args.graph:
@@ -202,14 +222,14 @@ def main():
 
     # ---- per-launch durations of the decode kernel (and decode + combine),
     # HIP events on the launch stream around each call of a second timed pass
+    # (there the merge and the up-projection run as separate calls)
     kd = max(20, min(args.steps, 200))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
             torch.cuda.Event(enable_timing=True)) for _ in range(kd)]
     torch.cuda.synchronize()
     for i in range(kd):
         pool = pools[i % n_layers]
-        st.absorb(q_nope, q_rope, w_uk)
-        st.append(c_new, k_new, pt, pool)
+        st.absorb_append(q_nope, q_rope, w_uk, c_new, k_new, pt, pool)
         evs[i][0].record(stream)
         st.decode(pool, pt, seq_lens)
         evs[i][1].record(stream)
@@ -233,7 +253,8 @@ def main():
     ai = flops / cache_bytes
     bound = "hbm" if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
     kernel = mla.decode_kernel_kind(cfg, Q)
-    khash = src_hash(DECODE_SRC)
+    ksym, ksrc = DECODE_KERNELS[kernel]
+    khash = src_hash(ksrc)
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(gbs_decode, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs_decode / HBM_PEAK_GBS, 4)}
@@ -241,7 +262,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(tflops_decode, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops_decode / BF16_PEAK_TFLOPS, 4)}
     roof["traffic"] = traffic_from_profile(wl.name, khash)
-    roof["kernel"] = "decode_mfma_kernel" if kernel == "mfma_bf16" else "decode_generic_kernel"
+    roof["kernel"] = ksym
     roof["algorithmic_bytes_per_launch"] = cache_bytes
     roof["algorithmic_flops_per_launch"] = flops
     roof["avg_launch_us"] = round(decode_ms * 1e3, 2)
@@ -266,6 +287,7 @@ def main():
                    "rope_dim": wl.rope_dim, "page_size": wl.page_size,
                    "paged": wl.paged, "num_splits": wl.num_splits,
                    "layer_caches_rotated": n_layers, "hip_graph": bool(args.graph),
+                   "library_calls_per_step": 5 if args.unfused else 3,
                    "decode_kernel": kernel},
         "pct_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B * Q / (ms_step * 1e-3), 1),

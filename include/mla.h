@@ -13,6 +13,8 @@
  *   mla_decode_paged    split-KV attention of the absorbed queries over the cache
  *   mla_splitkv_combine log-sum-exp merge of the split partials
  *   mla_up_project_v    latent output -> per-head value space through W_UV
+ *   mla_absorb_append, mla_combine_up_project
+ *                       two pairs of the above, each in one launch
  *
  * Conventions shared by every call
  *   - Every pointer argument except `cfg` is a DEVICE pointer; `cfg` is a host
@@ -110,9 +112,11 @@ mla_status_t mla_split_chunk(const mla_config_t* cfg, int32_t seq_len, int32_t n
 int32_t mla_default_num_splits(const mla_config_t* cfg, int32_t batch, int32_t q_len,
                                int32_t max_seq_len, int32_t num_cus);
 
-/* Name of the decode kernel mla_decode_paged takes for this shape: "mfma_bf16"
- * (bf16, d_c = 512, d_r = 64, page_size a multiple of 16, q_len*H a multiple
- * of 16) or "generic". Static string; "invalid" for an invalid config. */
+/* Name of the decode kernel mla_decode_paged takes for this shape. With bf16,
+ * d_c = 512 and d_r = 64: "mfma_tiles" (64 query rows per block) when
+ * page_size and q_len*H are multiples of 64, else "mfma_rows16" (16 rows per
+ * block) when q_len*H is a multiple of 16; otherwise "generic". Static
+ * string; "invalid" for an invalid config. */
 const char* mla_decode_kernel_name(const mla_config_t* cfg, int32_t q_len);
 
 /* Bytes of o_part plus lse_part for mla_decode_paged:
@@ -144,6 +148,21 @@ mla_status_t mla_cache_append(const mla_config_t* cfg, int32_t n_tok, const void
                               const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
                               const int32_t* page_table, int32_t batch, int32_t max_pages,
                               void* cache, int64_t num_pages, int32_t flags, void* stream);
+
+/* a1 + a2 in one launch, for callers that run both every step: the same
+ * arguments, work and results (bit for bit) as
+ *   mla_absorb_q(cfg, n_tok, q_nope, q_rope, pos_q, w_uk, q_full, stream);
+ *   mla_cache_append(cfg, n_app, c_kv, k_rope, seq_idx, pos, page_table,
+ *                    batch, max_pages, cache, num_pages, flags, stream);
+ * whose outputs are disjoint. One launch when the absorption runs on bf16
+ * MFMA (bf16, d_n and d_c multiples of 64), the two launches otherwise.
+ * Errors as for the two calls (the absorb arguments are checked first). */
+mla_status_t mla_absorb_append(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                               const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                               void* q_full, int32_t n_app, const void* c_kv, const void* k_rope,
+                               const int32_t* seq_idx, const int32_t* pos,
+                               const int32_t* page_table, int32_t batch, int32_t max_pages,
+                               void* cache, int64_t num_pages, int32_t flags, void* stream);
 
 /* a4. Split-KV paged decode ("The Architecture of Memory", "Flash-Decoding
  * and FlashInfer" and "The Decode Phase: The Memory Bandwidth Wall";
@@ -183,6 +202,18 @@ mla_status_t mla_splitkv_combine(const mla_config_t* cfg, int32_t batch, int32_t
  * o_lat [n_tok][H][d_c] T, w_uv [H][d_v][d_c] T, out [n_tok][H][d_v] T. */
 mla_status_t mla_up_project_v(const mla_config_t* cfg, int32_t n_tok, const void* o_lat,
                               const void* w_uv, void* out, void* stream);
+
+/* a5 + a6 in one launch: the same arguments and results (bit for bit) as
+ *   mla_splitkv_combine(cfg, batch, q_len, num_splits, o_part, lse_part,
+ *                       o_lat, lse, stream);
+ *   mla_up_project_v(cfg, batch * q_len, o_lat, w_uv, out, stream);
+ * (o_lat is written as well). One launch for bf16 with d_c = 512, d_v = 128,
+ * batch*q_len*H <= 4096 and num_splits <= 32 (the decode-step shapes where
+ * launch latency dominates), the two launches otherwise. */
+mla_status_t mla_combine_up_project(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                    int32_t num_splits, const float* o_part,
+                                    const float* lse_part, void* o_lat, float* lse,
+                                    const void* w_uv, void* out, void* stream);
 
 #ifdef __cplusplus
 }

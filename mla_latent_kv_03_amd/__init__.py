@@ -12,6 +12,9 @@ fallback. If the library is missing, every call raises.
     decode_paged(cfg, q_full, cache, page_table, seq_lens, o_part, lse_part, max_seq_len)
     splitkv_combine(cfg, o_part, lse_part, o_lat, lse)
     up_project_v(cfg, o_lat, w_uv, out)
+
+absorb_append and combine_up_project run the first two and the last two of
+these calls in one launch each, with the same results.
 """
 from ._binding import (  # noqa: F401
     F32,
@@ -35,4 +38,6 @@ from ._binding import (  # noqa: F401
     decode_paged,
     splitkv_combine,
     up_project_v,
+    absorb_append,
+    combine_up_project,
 )

@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
         "mla_decode_paged": (ctypes.c_int, [P, I32, I32, I32, I32, VP, VP, I64, VP, I32, VP, FP, FP, VP]),
         "mla_splitkv_combine": (ctypes.c_int, [P, I32, I32, I32, FP, FP, VP, FP, VP]),
         "mla_up_project_v": (ctypes.c_int, [P, I32, VP, VP, VP, VP]),
+        "mla_absorb_append": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, I32, VP, VP, VP, VP, VP,
+                                             I32, I32, VP, I64, I32, VP]),
+        "mla_combine_up_project": (ctypes.c_int, [P, I32, I32, I32, FP, FP, VP, FP, VP, VP, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -146,7 +149,8 @@ def decode_partials_bytes(cfg: Config, batch: int, q_len: int, num_splits: int) 
 
 
 def decode_kernel_kind(cfg: Config, q_len: int) -> str:
-    """Which decode kernel libmla takes for this shape: "mfma_bf16" or "generic"."""
+    """Which decode kernel libmla takes for this shape: "mfma_tiles", "mfma_rows16"
+    or "generic"."""
     return lib().mla_decode_kernel_name(ctypes.byref(cfg.c()), q_len).decode()
 
 
@@ -186,22 +190,18 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(h)
 
 
-def absorb_q(cfg: Config, q_nope, q_rope, pos, w_uk, q_full, stream=None):
-    """a1: q_full[n][h] = [W_UK[h]^T q_nope[n][h] ; RoPE(q_rope[n][h], pos[n])]."""
+def _absorb_args(cfg: Config, q_nope, q_rope, pos, w_uk, q_full):
     t = _torch()
     n = int(pos.numel())
     H, dt = cfg.num_heads, _elem_dtype(cfg)
-    args = (_need(q_nope, "q_nope", dt, n * H * cfg.nope_dim),
+    return (n, _need(q_nope, "q_nope", dt, n * H * cfg.nope_dim),
             _need(q_rope, "q_rope", dt, n * H * cfg.rope_dim),
             _need(pos, "pos", t.int32, n),
             _need(w_uk, "w_uk", dt, H * cfg.nope_dim * cfg.kv_rank),
             _need(q_full, "q_full", dt, n * H * cfg.dim))
-    _ck(lib().mla_absorb_q(ctypes.byref(cfg.c()), n, *args, _stream(stream)), "mla_absorb_q")
 
 
-def cache_append(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache,
-                 mode: int = APPEND_ROTATE, stream=None):
-    """a2: write rows [c_kv[n] ; k] at page_table[seq_idx[n]][pos[n] // page] ..."""
+def _append_args(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache, mode):
     t = _torch()
     n = int(pos.numel())
     dt = _elem_dtype(cfg)
@@ -211,14 +211,36 @@ def cache_append(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache,
     if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != cfg.dim:
         raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{cfg.dim}]")
     num_pages = int(cache.shape[0])
-    args = (_need(c_kv, "c_kv", dt, n * cfg.kv_rank),
+    return (n, _need(c_kv, "c_kv", dt, n * cfg.kv_rank),
             _need(k_rope, "k_rope", dt, n * cfg.rope_dim),
             _need(seq_idx, "seq_idx", t.int32, n),
             _need(pos, "pos", t.int32, n),
-            _need(page_table, "page_table", t.int32, batch * max_pages))
-    cp = _need(cache, "cache", dt, cache.numel())
-    _ck(lib().mla_cache_append(ctypes.byref(cfg.c()), n, *args, batch, max_pages, cp, num_pages,
-                               mode, _stream(stream)), "mla_cache_append")
+            _need(page_table, "page_table", t.int32, batch * max_pages),
+            int(batch), int(max_pages), _need(cache, "cache", dt, cache.numel()), num_pages,
+            int(mode))
+
+
+def absorb_q(cfg: Config, q_nope, q_rope, pos, w_uk, q_full, stream=None):
+    """a1: q_full[n][h] = [W_UK[h]^T q_nope[n][h] ; RoPE(q_rope[n][h], pos[n])]."""
+    args = _absorb_args(cfg, q_nope, q_rope, pos, w_uk, q_full)
+    _ck(lib().mla_absorb_q(ctypes.byref(cfg.c()), *args, _stream(stream)), "mla_absorb_q")
+
+
+def cache_append(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache,
+                 mode: int = APPEND_ROTATE, stream=None):
+    """a2: write rows [c_kv[n] ; k] at page_table[seq_idx[n]][pos[n] // page] ..."""
+    args = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode)
+    _ck(lib().mla_cache_append(ctypes.byref(cfg.c()), *args, _stream(stream)), "mla_cache_append")
+
+
+def absorb_append(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_rope, seq_idx, pos,
+                  page_table, cache, mode: int = APPEND_ROTATE, stream=None):
+    """a1 + a2 in one launch: absorb_q(q_nope, q_rope, pos_q, w_uk, q_full) and
+    cache_append(c_kv, k_rope, seq_idx, pos, page_table, cache, mode)."""
+    a = _absorb_args(cfg, q_nope, q_rope, pos_q, w_uk, q_full)
+    b = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode)
+    _ck(lib().mla_absorb_append(ctypes.byref(cfg.c()), *a, *b, _stream(stream)),
+        "mla_absorb_append")
 
 
 def decode_paged(cfg: Config, q_full, cache, page_table, seq_lens, o_part, lse_part,
@@ -250,8 +272,7 @@ def decode_paged(cfg: Config, q_full, cache, page_table, seq_lens, o_part, lse_p
         "mla_decode_paged")
 
 
-def splitkv_combine(cfg: Config, o_part, lse_part, o_lat, lse=None, stream=None):
-    """a5: LSE merge. o_lat [B][Q][H][d_c] (cfg dtype); lse [B][Q][H] f32 or None."""
+def _combine_args(cfg: Config, o_part, lse_part, o_lat, lse):
     t = _torch()
     if lse_part.dim() != 4:
         raise ValueError("lse_part: expected [batch][q_len][H][num_splits]")
@@ -263,8 +284,25 @@ def splitkv_combine(cfg: Config, o_part, lse_part, o_lat, lse=None, stream=None)
     lp = _need(lse_part, "lse_part", t.float32, B * Q * H * S)
     ol = _need(o_lat, "o_lat", dt, B * Q * H * cfg.kv_rank)
     ls = ctypes.c_void_p(None) if lse is None else _need(lse, "lse", t.float32, B * Q * H)
-    _ck(lib().mla_splitkv_combine(ctypes.byref(cfg.c()), B, Q, S, op, lp, ol, ls, _stream(stream)),
+    return (B, Q, S, op, lp, ol, ls)
+
+
+def splitkv_combine(cfg: Config, o_part, lse_part, o_lat, lse=None, stream=None):
+    """a5: LSE merge. o_lat [B][Q][H][d_c] (cfg dtype); lse [B][Q][H] f32 or None."""
+    args = _combine_args(cfg, o_part, lse_part, o_lat, lse)
+    _ck(lib().mla_splitkv_combine(ctypes.byref(cfg.c()), *args, _stream(stream)),
         "mla_splitkv_combine")
+
+
+def combine_up_project(cfg: Config, o_part, lse_part, o_lat, w_uv, out, lse=None, stream=None):
+    """a5 + a6 in one launch: splitkv_combine(o_part, lse_part, o_lat, lse), then
+    up_project_v(o_lat, w_uv, out); out [B][Q][H][d_v]."""
+    B, Q, S, op, lp, ol, ls = _combine_args(cfg, o_part, lse_part, o_lat, lse)
+    H, dt = cfg.num_heads, _elem_dtype(cfg)
+    wv = _need(w_uv, "w_uv", dt, H * cfg.v_dim * cfg.kv_rank)
+    ot = _need(out, "out", dt, B * Q * H * cfg.v_dim)
+    _ck(lib().mla_combine_up_project(ctypes.byref(cfg.c()), B, Q, S, op, lp, ol, ls, wv, ot,
+                                     _stream(stream)), "mla_combine_up_project")
 
 
 def up_project_v(cfg: Config, o_lat, w_uv, out, stream=None):

@@ -20,12 +20,13 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["mla_api.cpp", "mla_kernels.hip", "mla_decode_mfma.hip", "mla_proj_mfma.hip"]
+SOURCES = ["mla_api.cpp", "mla_kernels.hip", "mla_decode_rows16.hip", "mla_decode_tiles.hip",
+           "mla_proj_mfma.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-fvisibility=hidden",
     # keep MFMA accumulators in ordinary VGPRs: the online softmax rescales
     # them with vector ALU ops, which cannot address the accumulation registers
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
@@ -50,7 +51,8 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(objdir, src + ".o")
         cmd = [cc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
         if src.endswith(".cpp"):
-            cmd = [cc, "-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"),
+            cmd = [cc, "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
+                   "-I", os.path.join(ROOT, "include"),
                    "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

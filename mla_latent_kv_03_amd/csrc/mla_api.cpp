@@ -5,7 +5,10 @@
 #include <stdint.h>
 #include <string.h>
 
+// the C ABI keeps default visibility; everything else in the library is hidden
+#pragma GCC visibility push(default)
 #include "../../include/mla.h"
+#pragma GCC visibility pop
 #include "mla_launch.h"
 
 namespace {
@@ -60,6 +63,68 @@ mla_status_t hip_status(int rc) { return rc == 0 ? MLA_OK : MLA_ERR_HIP; }
     if (!(p)) return MLA_ERR_NULL;        \
     if (!aligned16(p)) return MLA_ERR_ALIGN; \
   } while (0)
+
+mla_status_t check_absorb(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                          const void* q_rope, const int32_t* pos, const void* w_uk,
+                          const void* q_full) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(n_tok >= 0, MLA_ERR_SHAPE);
+  if (n_tok == 0) return MLA_OK;
+  MLA_CHECK_PTR(q_nope);
+  MLA_CHECK_PTR(q_rope);
+  MLA_CHECK_PTR(pos);
+  MLA_CHECK_PTR(w_uk);
+  MLA_CHECK_PTR(q_full);
+  return MLA_OK;
+}
+
+mla_status_t check_append(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                          const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                          const int32_t* page_table, int32_t batch, int32_t max_pages,
+                          const void* cache, int64_t num_pages, int32_t flags) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(n_tok >= 0 && batch >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(flags == MLA_APPEND_RAW || flags == MLA_APPEND_ROTATE, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size <= INT32_MAX, MLA_ERR_CAPACITY);
+  if (n_tok == 0) return MLA_OK;
+  MLA_CHECK_PTR(c_kv);
+  MLA_CHECK_PTR(k_rope);
+  MLA_CHECK_PTR(seq_idx);
+  MLA_CHECK_PTR(pos);
+  MLA_CHECK_PTR(page_table);
+  MLA_CHECK_PTR(cache);
+  return MLA_OK;
+}
+
+mla_status_t check_combine(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                           int32_t num_splits, const float* o_part, const float* lse_part,
+                           const void* o_lat, const float* lse) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(batch >= 0 && q_len >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)batch * q_len * cfg->num_heads <= INT32_MAX, MLA_ERR_SHAPE);
+  if (batch == 0) return MLA_OK;
+  MLA_CHECK_PTR(o_part);
+  MLA_CHECK_PTR(lse_part);
+  MLA_CHECK_PTR(o_lat);
+  if (lse && !aligned16(lse)) return MLA_ERR_ALIGN;
+  return MLA_OK;
+}
+
+mla_status_t check_up_project(const mla_config_t* cfg, int32_t n_tok, const void* o_lat,
+                              const void* w_uv, const void* out) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(n_tok >= 0, MLA_ERR_SHAPE);
+  if (n_tok == 0) return MLA_OK;
+  MLA_CHECK_PTR(o_lat);
+  MLA_CHECK_PTR(w_uv);
+  MLA_CHECK_PTR(out);
+  return MLA_OK;
+}
 
 }  // namespace
 
@@ -119,7 +184,14 @@ int32_t mla_default_num_splits(const mla_config_t* cfg, int32_t batch, int32_t q
 
 const char* mla_decode_kernel_name(const mla_config_t* cfg, int32_t q_len) {
   if (check_config(cfg) != MLA_OK || q_len < 1) return "invalid";
-  return mla::decode_kernel_kind(shape_of(cfg), q_len) == 1 ? "mfma_bf16" : "generic";
+  switch (mla::decode_kernel_kind(shape_of(cfg), q_len)) {
+    case 2:
+      return "mfma_tiles";
+    case 1:
+      return "mfma_rows16";
+    default:
+      return "generic";
+  }
 }
 
 size_t mla_decode_partials_bytes(const mla_config_t* cfg, int32_t batch, int32_t q_len,
@@ -134,15 +206,8 @@ size_t mla_decode_partials_bytes(const mla_config_t* cfg, int32_t batch, int32_t
 mla_status_t mla_absorb_q(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
                           const void* q_rope, const int32_t* pos, const void* w_uk,
                           void* q_full, void* stream) {
-  mla_status_t st = check_config(cfg);
-  if (st != MLA_OK) return st;
-  MLA_REQUIRE(n_tok >= 0, MLA_ERR_SHAPE);
-  if (n_tok == 0) return MLA_OK;
-  MLA_CHECK_PTR(q_nope);
-  MLA_CHECK_PTR(q_rope);
-  MLA_CHECK_PTR(pos);
-  MLA_CHECK_PTR(w_uk);
-  MLA_CHECK_PTR(q_full);
+  mla_status_t st = check_absorb(cfg, n_tok, q_nope, q_rope, pos, w_uk, q_full);
+  if (st != MLA_OK || n_tok == 0) return st;
   return hip_status(
       mla::launch_absorb_q(shape_of(cfg), n_tok, q_nope, q_rope, pos, w_uk, q_full, stream));
 }
@@ -151,21 +216,28 @@ mla_status_t mla_cache_append(const mla_config_t* cfg, int32_t n_tok, const void
                               const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
                               const int32_t* page_table, int32_t batch, int32_t max_pages,
                               void* cache, int64_t num_pages, int32_t flags, void* stream) {
-  mla_status_t st = check_config(cfg);
-  if (st != MLA_OK) return st;
-  MLA_REQUIRE(n_tok >= 0 && batch >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
-  MLA_REQUIRE(flags == MLA_APPEND_RAW || flags == MLA_APPEND_ROTATE, MLA_ERR_SHAPE);
-  MLA_REQUIRE((int64_t)max_pages * cfg->page_size <= INT32_MAX, MLA_ERR_CAPACITY);
-  if (n_tok == 0) return MLA_OK;
-  MLA_CHECK_PTR(c_kv);
-  MLA_CHECK_PTR(k_rope);
-  MLA_CHECK_PTR(seq_idx);
-  MLA_CHECK_PTR(pos);
-  MLA_CHECK_PTR(page_table);
-  MLA_CHECK_PTR(cache);
+  mla_status_t st = check_append(cfg, n_tok, c_kv, k_rope, seq_idx, pos, page_table, batch,
+                                 max_pages, cache, num_pages, flags);
+  if (st != MLA_OK || n_tok == 0) return st;
   return hip_status(mla::launch_cache_append(shape_of(cfg), n_tok, c_kv, k_rope, seq_idx, pos,
                                              page_table, batch, max_pages, cache, num_pages,
                                              flags == MLA_APPEND_ROTATE, stream));
+}
+
+mla_status_t mla_absorb_append(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                               const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                               void* q_full, int32_t n_app, const void* c_kv, const void* k_rope,
+                               const int32_t* seq_idx, const int32_t* pos,
+                               const int32_t* page_table, int32_t batch, int32_t max_pages,
+                               void* cache, int64_t num_pages, int32_t flags, void* stream) {
+  mla_status_t st = check_absorb(cfg, n_tok, q_nope, q_rope, pos_q, w_uk, q_full);
+  if (st != MLA_OK) return st;
+  st = check_append(cfg, n_app, c_kv, k_rope, seq_idx, pos, page_table, batch, max_pages, cache,
+                    num_pages, flags);
+  if (st != MLA_OK || (n_tok == 0 && n_app == 0)) return st;
+  return hip_status(mla::launch_absorb_append(
+      shape_of(cfg), n_tok, q_nope, q_rope, pos_q, w_uk, q_full, n_app, c_kv, k_rope, seq_idx, pos,
+      page_table, batch, max_pages, cache, num_pages, flags == MLA_APPEND_ROTATE, stream));
 }
 
 mla_status_t mla_decode_paged(const mla_config_t* cfg, int32_t batch, int32_t q_len,
@@ -195,16 +267,8 @@ mla_status_t mla_decode_paged(const mla_config_t* cfg, int32_t batch, int32_t q_
 mla_status_t mla_splitkv_combine(const mla_config_t* cfg, int32_t batch, int32_t q_len,
                                  int32_t num_splits, const float* o_part, const float* lse_part,
                                  void* o_lat, float* lse, void* stream) {
-  mla_status_t st = check_config(cfg);
-  if (st != MLA_OK) return st;
-  MLA_REQUIRE(batch >= 0 && q_len >= 1, MLA_ERR_SHAPE);
-  MLA_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
-  MLA_REQUIRE((int64_t)batch * q_len * cfg->num_heads <= INT32_MAX, MLA_ERR_SHAPE);
-  if (batch == 0) return MLA_OK;
-  MLA_CHECK_PTR(o_part);
-  MLA_CHECK_PTR(lse_part);
-  MLA_CHECK_PTR(o_lat);
-  if (lse && !aligned16(lse)) return MLA_ERR_ALIGN;
+  mla_status_t st = check_combine(cfg, batch, q_len, num_splits, o_part, lse_part, o_lat, lse);
+  if (st != MLA_OK || batch == 0) return st;
   const int rows = batch * q_len * cfg->num_heads;
   return hip_status(
       mla::launch_combine(shape_of(cfg), rows, num_splits, o_part, lse_part, o_lat, lse, stream));
@@ -212,14 +276,22 @@ mla_status_t mla_splitkv_combine(const mla_config_t* cfg, int32_t batch, int32_t
 
 mla_status_t mla_up_project_v(const mla_config_t* cfg, int32_t n_tok, const void* o_lat,
                               const void* w_uv, void* out, void* stream) {
-  mla_status_t st = check_config(cfg);
-  if (st != MLA_OK) return st;
-  MLA_REQUIRE(n_tok >= 0, MLA_ERR_SHAPE);
-  if (n_tok == 0) return MLA_OK;
-  MLA_CHECK_PTR(o_lat);
-  MLA_CHECK_PTR(w_uv);
-  MLA_CHECK_PTR(out);
+  mla_status_t st = check_up_project(cfg, n_tok, o_lat, w_uv, out);
+  if (st != MLA_OK || n_tok == 0) return st;
   return hip_status(mla::launch_up_project_v(shape_of(cfg), n_tok, o_lat, w_uv, out, stream));
+}
+
+mla_status_t mla_combine_up_project(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                    int32_t num_splits, const float* o_part,
+                                    const float* lse_part, void* o_lat, float* lse,
+                                    const void* w_uv, void* out, void* stream) {
+  mla_status_t st = check_combine(cfg, batch, q_len, num_splits, o_part, lse_part, o_lat, lse);
+  if (st != MLA_OK || batch == 0) return st;
+  const int n_tok = batch * q_len;
+  st = check_up_project(cfg, n_tok, o_lat, w_uv, out);
+  if (st != MLA_OK) return st;
+  return hip_status(mla::launch_combine_up_project(shape_of(cfg), n_tok, num_splits, o_part,
+                                                   lse_part, o_lat, lse, w_uv, out, stream));
 }
 
 }  // extern "C"

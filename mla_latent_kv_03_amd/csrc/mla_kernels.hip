@@ -6,6 +6,8 @@
 #include <math.h>
 
 #include "mla_common.h"
+#include "mla_append.h"
+#include "mla_combine.h"
 #include "mla_launch.h"
 
 namespace mla {
@@ -94,8 +96,8 @@ int launch_absorb_q(const Shape& s, int n_tok, const void* q_nope, const void* q
 }
 
 // ---------------------------------------------------------------------------
-// a2: paged cache append ("The Architecture of Memory", "PagedAttention:
-// Virtual Memory for LLMs"). One block per appended row.
+// a2: paged cache append: one block per appended row (append_row, shared with
+// the launch that fuses it with query absorption).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(128) void append_kernel(int dc, int dr, int page,
@@ -105,43 +107,27 @@ __global__ __launch_bounds__(128) void append_kernel(int dc, int dr, int page,
                                                      const int32_t* __restrict__ pos,
                                                      const int32_t* __restrict__ page_table,
                                                      int batch, int max_pages, T* __restrict__ cache,
-                                                     int64_t num_pages, int rotate, double log2_base) {
-  const int n = blockIdx.x;
-  const int b = seq_idx[n];
-  const int p = pos[n];
-  if (b < 0 || b >= batch || p < 0 || p >= max_pages * page) return;
-  const int pg = page_table[(size_t)b * max_pages + p / page];
-  if (pg < 0 || (int64_t)pg >= num_pages) return;
-  const int D = dc + dr;
-  T* row = cache + ((size_t)pg * page + p % page) * D;
-  for (int i = threadIdx.x; i < dc; i += blockDim.x) row[i] = c_kv[(size_t)n * dc + i];
-  const T* kr = k_rope + (size_t)n * dr;
-  for (int i = threadIdx.x; i < dr / 2; i += blockDim.x) {
-    if (rotate) {
-      double y0, y1;
-      rope_pair(Elt<T>::ld(kr + 2 * i), Elt<T>::ld(kr + 2 * i + 1), p, i, dr, log2_base, &y0, &y1);
-      Elt<T>::st(row + dc + 2 * i, (float)y0);
-      Elt<T>::st(row + dc + 2 * i + 1, (float)y1);
-    } else {
-      row[dc + 2 * i] = kr[2 * i];
-      row[dc + 2 * i + 1] = kr[2 * i + 1];
-    }
-  }
+                                                     int64_t num_pages, int rotate, double log2_base,
+                                                     int vec) {
+  append_row<T>(blockIdx.x, dc, dr, page, c_kv, k_rope, seq_idx, pos, page_table, batch, max_pages,
+                cache, num_pages, rotate, log2_base, vec);
 }
 
 int launch_cache_append(const Shape& s, int n_tok, const void* c_kv, const void* k_rope,
                         const int32_t* seq_idx, const int32_t* pos, const int32_t* page_table,
                         int batch, int max_pages, void* cache, int64_t num_pages, int rotate,
                         void* stream) {
+  const int vec = append_vectorizable(s, c_kv, cache);
   if (s.dtype == 0)
     hipLaunchKernelGGL(append_kernel<float>, dim3(n_tok), dim3(128), 0, as_stream(stream), s.dc,
                        s.dr, s.page, (const float*)c_kv, (const float*)k_rope, seq_idx, pos,
-                       page_table, batch, max_pages, (float*)cache, num_pages, rotate, s.log2_base);
+                       page_table, batch, max_pages, (float*)cache, num_pages, rotate, s.log2_base,
+                       vec);
   else
     hipLaunchKernelGGL(append_kernel<bf16_t>, dim3(n_tok), dim3(128), 0, as_stream(stream), s.dc,
                        s.dr, s.page, (const bf16_t*)c_kv, (const bf16_t*)k_rope, seq_idx, pos,
                        page_table, batch, max_pages, (bf16_t*)cache, num_pages, rotate,
-                       s.log2_base);
+                       s.log2_base, vec);
   return (int)hipGetLastError();
 }
 
@@ -287,10 +273,42 @@ static int decode_generic_impl(const Shape& s, int batch, int q_len, int num_spl
   return (int)hipGetLastError();
 }
 
-int launch_decode_generic(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
-                          const void* q_full, const void* cache, int64_t num_pages,
-                          const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                          float* o_part, float* lse_part, void* stream) {
+bool decode_rows16_ok(const Shape& s, int q_len);
+int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
+                         const void* q_full, const void* cache, int64_t num_pages,
+                         const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                         float* o_part, float* lse_part, void* stream);
+bool decode_tiles_ok(const Shape& s, int q_len);
+int launch_decode_tiles(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
+                        const void* q_full, const void* cache, int64_t num_pages,
+                        const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                        float* o_part, float* lse_part, void* stream);
+
+// bf16 MFMA kernels for the 576-wide DeepSeek row: 64 query rows per block
+// when the row count and page size allow it, else 16; everything else takes
+// the generic kernel
+int decode_kernel_kind(const Shape& s, int q_len) {
+  if (decode_tiles_ok(s, q_len)) return 2;
+  if (decode_rows16_ok(s, q_len)) return 1;
+  return 0;
+}
+
+int launch_decode(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
+                  const void* q_full, const void* cache, int64_t num_pages,
+                  const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                  float* o_part, float* lse_part, void* stream) {
+  switch (decode_kernel_kind(s, q_len)) {
+    case 2:
+      return launch_decode_tiles(s, batch, q_len, num_splits, max_seq_len, q_full, cache,
+                                 num_pages, page_table, max_pages, seq_lens, o_part, lse_part,
+                                 stream);
+    case 1:
+      return launch_decode_rows16(s, batch, q_len, num_splits, max_seq_len, q_full, cache,
+                                  num_pages, page_table, max_pages, seq_lens, o_part, lse_part,
+                                  stream);
+    default:
+      break;
+  }
   return s.dtype == 0
              ? decode_generic_impl<float>(s, batch, q_len, num_splits, max_seq_len, q_full, cache,
                                           num_pages, page_table, max_pages, seq_lens, o_part,
@@ -302,38 +320,10 @@ int launch_decode_generic(const Shape& s, int batch, int q_len, int num_splits, 
 
 // ---------------------------------------------------------------------------
 // a5: log-sum-exp merge of the partitions ("The Architecture of Memory",
-// "Flash-Decoding and FlashInfer"). One block per output row.
+// "Flash-Decoding and FlashInfer"). One wave per (output row, 256 latent
+// columns); the arithmetic is in mla_combine.h, shared with the launch that
+// fuses the merge with the value up-projection.
 // ---------------------------------------------------------------------------
-constexpr int kMaxSplits = 4096;
-constexpr int kCombCols = 256;  // latent columns per block: 64 lanes x 4
-
-template <typename T>
-__device__ __forceinline__ void store4(T* p, float4 v);
-template <>
-__device__ __forceinline__ void store4<float>(float* p, float4 v) {
-  *reinterpret_cast<float4*>(p) = v;
-}
-template <>
-__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
-  uint2 u;
-  u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
-  u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
-  *reinterpret_cast<uint2*>(p) = u;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// One wave per (output row, 256 latent columns). The wave turns the row's S
-// partition LSEs into weights e^(lse_s - max) in LDS, then each lane
-// accumulates 4 adjacent columns over all partitions with 16-byte loads, 8
-// partitions in flight at a time.
 template <typename T>
 __global__ __launch_bounds__(64) void combine_kernel(int S, int dc, const float* __restrict__ o_part,
                                                      const float* __restrict__ lse_part,
@@ -341,58 +331,13 @@ __global__ __launch_bounds__(64) void combine_kernel(int S, int dc, const float*
   __shared__ float w[kMaxSplits];
   const int r = blockIdx.x, lane = threadIdx.x;
   const int col = blockIdx.y * kCombCols + 4 * lane;
-  const float* lp = lse_part + (size_t)r * S;
-  float mx = -INFINITY;
-  bool nan_seen = false;
-  for (int s = lane; s < S; s += 64) {
-    const float v = lp[s];
-    w[s] = v;
-    nan_seen |= (v != v);
-    mx = fmaxf(mx, v);
-  }
-  mx = wave_max(mx);
-  const bool bad = __any(nan_seen);
-  float sum = 0.0f;
-  for (int s = lane; s < S; s += 64) {
-    const float e = (w[s] == -INFINITY) ? 0.0f : expf(w[s] - mx);
-    w[s] = e;
-    sum += e;
-  }
-  sum = wave_sum(sum);
+  CombineCols<> cc;
+  cc.start(o_part + (size_t)r * S * dc, S, dc, col);
+  const CombineWeights cw = combine_weights(lse_part + (size_t)r * S, S, w, lane);
   __syncthreads();
-  const float nanv = __int_as_float(0x7fc00000);
-  if (col < dc) {
-    const float4* op = reinterpret_cast<const float4*>(o_part + (size_t)r * S * dc + col);
-    const size_t st = dc / 4;  // float4 stride between partitions
-    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    int s = 0;
-    for (; s + 8 <= S; s += 8) {
-      float4 x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = op[(size_t)(s + u) * st];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float ws = w[s + u];
-        a.x = fmaf(ws, x[u].x, a.x);
-        a.y = fmaf(ws, x[u].y, a.y);
-        a.z = fmaf(ws, x[u].z, a.z);
-        a.w = fmaf(ws, x[u].w, a.w);
-      }
-    }
-    for (; s < S; ++s) {
-      const float4 x = op[(size_t)s * st];
-      const float ws = w[s];
-      a.x = fmaf(ws, x.x, a.x);
-      a.y = fmaf(ws, x.y, a.y);
-      a.z = fmaf(ws, x.z, a.z);
-      a.w = fmaf(ws, x.w, a.w);
-    }
-    const float inv = 1.0f / sum;
-    const float4 v = bad ? make_float4(nanv, nanv, nanv, nanv)
-                         : make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
-    store4<T>(o_lat + (size_t)r * dc + col, v);
-  }
-  if (lse && blockIdx.y == 0 && lane == 0) lse[r] = bad ? nanv : mx + logf(sum);
+  const float4 v = cc.finish(w, cw);
+  if (col < dc) store4<T>(o_lat + (size_t)r * dc + col, v);
+  if (lse && blockIdx.y == 0 && lane == 0) lse[r] = cw.lse();
 }
 
 int launch_combine(const Shape& s, int rows, int num_splits, const float* o_part,

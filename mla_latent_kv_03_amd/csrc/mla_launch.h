@@ -15,6 +15,14 @@ struct Shape {
   int D() const { return dc + dr; }
 };
 
+// Whether the append may copy the latent part in 16-byte vectors: every
+// source and destination row 16-byte aligned.
+inline int append_vectorizable(const Shape& s, const void* c_kv, const void* cache) {
+  const size_t es = s.dtype == 0 ? 4 : 2;
+  return ((uintptr_t)c_kv % 16 == 0) && ((uintptr_t)cache % 16 == 0) && (s.dc * es) % 16 == 0 &&
+         ((size_t)s.D() * es) % 16 == 0;
+}
+
 // Each returns 0 on success or the hipError_t of the failed launch.
 int launch_absorb_q(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
                     const int32_t* pos, const void* w_uk, void* q_full, void* stream);
@@ -23,6 +31,15 @@ int launch_cache_append(const Shape& s, int n_tok, const void* c_kv, const void*
                         const int32_t* seq_idx, const int32_t* pos, const int32_t* page_table,
                         int batch, int max_pages, void* cache, int64_t num_pages, int rotate,
                         void* stream);
+
+// a1 and a2 of one decode step in one launch when the absorption takes the
+// bf16 MFMA kernel, else the two launches in order; results identical to
+// launch_absorb_q followed by launch_cache_append.
+int launch_absorb_append(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
+                         const int32_t* pos_q, const void* w_uk, void* q_full, int n_app,
+                         const void* c_kv, const void* k_rope, const int32_t* seq_idx,
+                         const int32_t* pos, const int32_t* page_table, int batch, int max_pages,
+                         void* cache, int64_t num_pages, int rotate, void* stream);
 
 int launch_decode(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
                   const void* q_full, const void* cache, int64_t num_pages,
@@ -35,8 +52,16 @@ int launch_combine(const Shape& s, int rows, int num_splits, const float* o_part
 int launch_up_project_v(const Shape& s, int n_tok, const void* o_lat, const void* w_uv,
                         void* out, void* stream);
 
+// a5 and a6 in one launch for the bf16 d_c = 512, d_v = 128 shape when the
+// row count and split count are small, else the two launches in order;
+// results identical to launch_combine followed by launch_up_project_v.
+int launch_combine_up_project(const Shape& s, int n_tok, int num_splits, const float* o_part,
+                              const float* lse_part, void* o_lat, float* lse, const void* w_uv,
+                              void* out, void* stream);
+
 // Which decode kernel a shape takes (for tests and tools): 0 = generic VALU
-// kernel, 1 = bf16 MFMA kernel.
+// kernel, 1 = bf16 MFMA kernel with 16 query rows per block, 2 = bf16 MFMA
+// kernel with 64 query rows per block.
 int decode_kernel_kind(const Shape& s, int q_len);
 
 }  // namespace mla

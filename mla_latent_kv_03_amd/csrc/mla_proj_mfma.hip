@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "mla_append.h"
+#include "mla_combine.h"
 #include "mla_common.h"
 #include "mla_launch.h"
 
@@ -41,56 +43,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // ---------------------------------------------------------------------------
 // a1: q_full[n][h][0:d_c] = W_UK[h]^T q_nope[n][h]; q_full[n][h][d_c:] = RoPE.
-// grid (H, d_c / 256, ceil(N / 16)); 4 waves, wave w owns 64 output columns.
+// grid (H, d_c / 64 + 1, ceil(N / 16)). Blocks y < d_c / 64 own 64 output
+// columns of 16 tokens; their 4 waves split the d_n contraction (wave w takes
+// rows [w d_n / 4, (w + 1) d_n / 4)) and sum through LDS. The last block row
+// (y = d_c / 64) rotates the RoPE part, in parallel with the contraction.
 // v_mfma_f32_16x16x16_bf16 with M = 16 tokens, K = 16 rows of W_UK, N = 16
 // columns. W_UK is row-major [d_n][d_c], so a lane loads 8 contiguous bytes
 // (4 columns) from each of 4 rows and transposes the 4x4 block in registers
-// into 4 B operands; MFMA m then covers columns c0 + 4*(lane%16) + m.
+// into 4 B operands; MFMA m then covers columns c0 + 4*(lane%16) + m. All
+// loads of a 32-row step are issued before its MFMAs.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void absorb_q_mfma_kernel(
-    int n_tok, int H, int dn, int dc, int dr, double log2_base, const bf16_t* __restrict__ q_nope,
-    const bf16_t* __restrict__ q_rope, const int32_t* __restrict__ pos,
-    const bf16_t* __restrict__ w_uk, bf16_t* __restrict__ q_full) {
-  const int h = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nn = lane & 15, g = lane >> 4;
-  const int c0 = blockIdx.y * 256 + wave * 64;
-  const int n0 = blockIdx.z * 16;
+__device__ __forceinline__ void absorb_block(int h, int by, int bz, int n_tok, int H, int dn, int dc,
+                                             int dr, double log2_base,
+                                             const bf16_t* __restrict__ q_nope,
+                                             const bf16_t* __restrict__ q_rope,
+                                             const int32_t* __restrict__ pos,
+                                             const bf16_t* __restrict__ w_uk,
+                                             bf16_t* __restrict__ q_full) {
+  __shared__ f32x4_t red[3][4][64];
+  const int n0 = bz * 16;
   const int D = dc + dr;
-  const int tok = n0 + nn;  // A-operand row of this lane
-  const bool tok_ok = tok < n_tok;
-  const bf16_t* qrow = q_nope + ((size_t)(tok_ok ? tok : 0) * H + h) * dn;
-  const bf16_t* W = w_uk + (size_t)h * dn * dc + c0 + 4 * nn;
-  f32x4_t acc[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) acc[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int i0 = 0; i0 < dn; i0 += 16) {
-    u32x2_t qa = *reinterpret_cast<const u32x2_t*>(qrow + i0 + 4 * g);
-    if (!tok_ok) qa = u32x2_t{0u, 0u};
-    u32x2_t x[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      x[j] = *reinterpret_cast<const u32x2_t*>(W + (size_t)(i0 + 4 * g + j) * dc);
-    const s16x4_t a = __builtin_bit_cast(s16x4_t, qa);
-    const s16x4_t b0 = as_s16x4(pack_lo(x[0].x, x[1].x), pack_lo(x[2].x, x[3].x));
-    const s16x4_t b1 = as_s16x4(pack_hi(x[0].x, x[1].x), pack_hi(x[2].x, x[3].x));
-    const s16x4_t b2 = as_s16x4(pack_lo(x[0].y, x[1].y), pack_lo(x[2].y, x[3].y));
-    const s16x4_t b3 = as_s16x4(pack_hi(x[0].y, x[1].y), pack_hi(x[2].y, x[3].y));
-    acc[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b0, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b1, acc[1], 0, 0, 0);
-    acc[2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b2, acc[2], 0, 0, 0);
-    acc[3] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b3, acc[3], 0, 0, 0);
-  }
-  // lane holds tokens n0 + 4g + r, columns c0 + 4*nn + m (m = 0..3)
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = n0 + 4 * g + r;
-    if (t < n_tok) {
-      u32x2_t v = {pack_bf16x2(acc[0][r], acc[1][r]), pack_bf16x2(acc[2][r], acc[3][r])};
-      *reinterpret_cast<u32x2_t*>(q_full + ((size_t)t * H + h) * D + c0 + 4 * nn) = v;
-    }
-  }
-  if (blockIdx.y == 0) {
+  if (by == dc / 64) {
     const int half = dr / 2;
     const int nt = min(16, n_tok - n0);
     for (int i = threadIdx.x; i < nt * half; i += blockDim.x) {
@@ -102,14 +75,110 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(
       dst[0] = f2bf((float)y0);
       dst[1] = f2bf((float)y1);
     }
+    return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nn = lane & 15, g = lane >> 4;
+  const int c0 = by * 64;
+  const int tok = n0 + nn;  // A-operand row of this lane
+  const bool tok_ok = tok < n_tok;
+  const bf16_t* qrow = q_nope + ((size_t)(tok_ok ? tok : 0) * H + h) * dn;
+  const bf16_t* W = w_uk + (size_t)h * dn * dc + c0 + 4 * nn;
+  const int kw = dn / 4;  // rows per wave, a multiple of 16
+  const int i_end = (wave + 1) * kw;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto step = [&](const u32x2_t& qa, const u32x2_t* x) {
+    const s16x4_t a = __builtin_bit_cast(s16x4_t, qa);
+    const s16x4_t b0 = as_s16x4(pack_lo(x[0].x, x[1].x), pack_lo(x[2].x, x[3].x));
+    const s16x4_t b1 = as_s16x4(pack_hi(x[0].x, x[1].x), pack_hi(x[2].x, x[3].x));
+    const s16x4_t b2 = as_s16x4(pack_lo(x[0].y, x[1].y), pack_lo(x[2].y, x[3].y));
+    const s16x4_t b3 = as_s16x4(pack_hi(x[0].y, x[1].y), pack_hi(x[2].y, x[3].y));
+    acc[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b0, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b1, acc[1], 0, 0, 0);
+    acc[2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b2, acc[2], 0, 0, 0);
+    acc[3] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b3, acc[3], 0, 0, 0);
+  };
+  int i0 = wave * kw;
+  for (; i0 + 32 <= i_end; i0 += 32) {
+    u32x2_t qa[2], x[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      qa[u] = *reinterpret_cast<const u32x2_t*>(qrow + i0 + 16 * u + 4 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        x[u][j] = *reinterpret_cast<const u32x2_t*>(W + (size_t)(i0 + 16 * u + 4 * g + j) * dc);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!tok_ok) qa[u] = u32x2_t{0u, 0u};
+      step(qa[u], x[u]);
+    }
+  }
+  if (i0 < i_end) {  // one 16-row step left
+    u32x2_t qa = *reinterpret_cast<const u32x2_t*>(qrow + i0 + 4 * g);
+    u32x2_t x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x[j] = *reinterpret_cast<const u32x2_t*>(W + (size_t)(i0 + 4 * g + j) * dc);
+    if (!tok_ok) qa = u32x2_t{0u, 0u};
+    step(qa, x);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) red[wave - 1][m][lane] = acc[m];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] += (red[0][m][lane] + red[1][m][lane]) + red[2][m][lane];
+    // lane holds tokens n0 + 4g + r, columns c0 + 4*nn + m (m = 0..3)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = n0 + 4 * g + r;
+      if (t < n_tok) {
+        u32x2_t v = {pack_bf16x2(acc[0][r], acc[1][r]), pack_bf16x2(acc[2][r], acc[3][r])};
+        *reinterpret_cast<u32x2_t*>(q_full + ((size_t)t * H + h) * D + c0 + 4 * nn) = v;
+      }
+    }
   }
 }
 
-bool absorb_mfma_ok(const Shape& s) { return s.dtype == 1 && s.dn % 16 == 0 && s.dc % 256 == 0; }
+__global__ __launch_bounds__(256) void absorb_q_mfma_kernel(
+    int n_tok, int H, int dn, int dc, int dr, double log2_base, const bf16_t* __restrict__ q_nope,
+    const bf16_t* __restrict__ q_rope, const int32_t* __restrict__ pos,
+    const bf16_t* __restrict__ w_uk, bf16_t* __restrict__ q_full) {
+  absorb_block(blockIdx.x, blockIdx.y, blockIdx.z, n_tok, H, dn, dc, dr, log2_base, q_nope, q_rope,
+               pos, w_uk, q_full);
+}
+
+// a1 + a2 in one launch: blocks [0, n_abs) are the blocks of
+// absorb_q_mfma_kernel in its own order (x fastest), the next blocks append
+// one row each.
+__global__ __launch_bounds__(256) void absorb_append_kernel(
+    int n_tok, int H, int dn, int dc, int dr, double log2_base, const bf16_t* __restrict__ q_nope,
+    const bf16_t* __restrict__ q_rope, const int32_t* __restrict__ pos_q,
+    const bf16_t* __restrict__ w_uk, bf16_t* __restrict__ q_full, int ny, int n_abs, int page,
+    const bf16_t* __restrict__ c_kv, const bf16_t* __restrict__ k_rope,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ page_table, int batch, int max_pages, bf16_t* __restrict__ cache,
+    int64_t num_pages, int rotate, int vec) {
+  const int id = blockIdx.x;
+  if (id < n_abs) {
+    absorb_block(id % H, (id / H) % ny, id / (H * ny), n_tok, H, dn, dc, dr, log2_base, q_nope,
+                 q_rope, pos_q, w_uk, q_full);
+  } else {
+    append_row<bf16_t>(id - n_abs, dc, dr, page, c_kv, k_rope, seq_idx, pos, page_table, batch,
+                       max_pages, cache, num_pages, rotate, log2_base, vec);
+  }
+}
+
+bool absorb_mfma_ok(const Shape& s) { return s.dtype == 1 && s.dn % 64 == 0 && s.dc % 64 == 0; }
 
 int launch_absorb_q_mfma(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
                          const int32_t* pos, const void* w_uk, void* q_full, void* stream) {
-  dim3 grid(s.H, s.dc / 256, (n_tok + 15) / 16);
+  dim3 grid(s.H, s.dc / 64 + 1, (n_tok + 15) / 16);
   hipLaunchKernelGGL(absorb_q_mfma_kernel, grid, dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), n_tok, s.H, s.dn, s.dc, s.dr,
                      s.log2_base, (const bf16_t*)q_nope, (const bf16_t*)q_rope, pos,
@@ -120,7 +189,8 @@ int launch_absorb_q_mfma(const Shape& s, int n_tok, const void* q_nope, const vo
 // ---------------------------------------------------------------------------
 // a6: out[n][h][v] = sum_c W_UV[h][v][c] o_lat[n][h][c].
 // grid (H, d_v / 16, ceil(N / 16)); 4 waves split the d_c contraction (wave
-// w takes 32-wide k-steps w, w+4, ...), then sum through LDS.
+// w takes 32-wide k-steps w, w+4, ..., loading 4 of them before their
+// MFMAs), then sum through LDS.
 // v_mfma_f32_16x16x32_bf16 with M = 16 tokens, N = 16 rows v of W_UV,
 // K = 32 latent columns: both operands are contiguous 16-byte loads.
 // ---------------------------------------------------------------------------
@@ -139,12 +209,20 @@ __global__ __launch_bounds__(256) void up_v_mfma_kernel(int n_tok, int H, int dc
   const bf16_t* arow = o_lat + ((size_t)(tok_ok ? tok : 0) * H + h) * dc + 8 * g;
   const bf16_t* brow = w_uv + ((size_t)h * dv + v0 + nn) * dc + 8 * g;
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k = wave * 32; k < dc; k += 128) {
-    u32x4_t av = *reinterpret_cast<const u32x4_t*>(arow + k);
-    if (!tok_ok) av = u32x4_t{0u, 0u, 0u, 0u};
-    const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(brow + k);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                  __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+  // 4 k-steps per iteration (all of d_c = 512 in one): loads first, then MFMAs
+  for (int k0 = wave * 32; k0 < dc; k0 += 4 * 128) {
+    u32x4_t av[4], bv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u * 128;
+      const bool in = k < dc;
+      av[u] = (in && tok_ok) ? *reinterpret_cast<const u32x4_t*>(arow + k) : u32x4_t{0u, 0u, 0u, 0u};
+      bv[u] = in ? *reinterpret_cast<const u32x4_t*>(brow + k) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
+                                                    __builtin_bit_cast(bf16x8_t, bv[u]), acc, 0, 0, 0);
   }
   red[wave][lane] = acc;
   __syncthreads();
@@ -160,6 +238,30 @@ __global__ __launch_bounds__(256) void up_v_mfma_kernel(int n_tok, int H, int dc
   }
 }
 
+int launch_absorb_append(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
+                         const int32_t* pos_q, const void* w_uk, void* q_full, int n_app,
+                         const void* c_kv, const void* k_rope, const int32_t* seq_idx,
+                         const int32_t* pos, const int32_t* page_table, int batch, int max_pages,
+                         void* cache, int64_t num_pages, int rotate, void* stream) {
+  if (!absorb_mfma_ok(s) || n_tok == 0 || n_app == 0) {
+    int rc = 0;
+    if (n_tok > 0) rc = launch_absorb_q(s, n_tok, q_nope, q_rope, pos_q, w_uk, q_full, stream);
+    if (rc == 0 && n_app > 0)
+      rc = launch_cache_append(s, n_app, c_kv, k_rope, seq_idx, pos, page_table, batch, max_pages,
+                               cache, num_pages, rotate, stream);
+    return rc;
+  }
+  const int ny = s.dc / 64 + 1;
+  const int n_abs = s.H * ny * ((n_tok + 15) / 16);
+  hipLaunchKernelGGL(absorb_append_kernel, dim3(n_abs + n_app), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), n_tok, s.H, s.dn, s.dc, s.dr,
+                     s.log2_base, (const bf16_t*)q_nope, (const bf16_t*)q_rope, pos_q,
+                     (const bf16_t*)w_uk, (bf16_t*)q_full, ny, n_abs, s.page, (const bf16_t*)c_kv,
+                     (const bf16_t*)k_rope, seq_idx, pos, page_table, batch, max_pages,
+                     (bf16_t*)cache, num_pages, rotate, append_vectorizable(s, c_kv, cache));
+  return (int)hipGetLastError();
+}
+
 bool up_v_mfma_ok(const Shape& s) { return s.dtype == 1 && s.dc % 32 == 0 && s.dv % 16 == 0; }
 
 int launch_up_project_v_mfma(const Shape& s, int n_tok, const void* o_lat, const void* w_uv,
@@ -168,6 +270,131 @@ int launch_up_project_v_mfma(const Shape& s, int n_tok, const void* o_lat, const
   hipLaunchKernelGGL(up_v_mfma_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      n_tok, s.H, s.dc, s.dv, (const bf16_t*)o_lat, (const bf16_t*)w_uv,
                      (bf16_t*)out);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// a5 + a6 in one launch (bf16, d_c = 512, d_v = 128): one block of 6 waves
+// per output row r = (token n, head h).
+//   waves 0, 1  merge columns [256 w, 256 w + 256) of the row exactly as the
+//               combine kernel does (wave 0 also forms the weights), with all
+//               S <= 32 partitions loaded at once; the bf16 row goes to o_lat
+//               and to LDS.
+//   waves 2..5  load their W_UV[h] operands at the start (they depend on
+//               nothing), then run the MFMA sequence of up_v_mfma_kernel's
+//               wave (w - 2) for this token, with the token in A-operand row
+//               0 and zeros in the other rows (an MFMA output row depends
+//               only on its own A row), and sum across waves in that
+//               kernel's order, so both paths give the same bits.
+// Blocks of one head share blockIdx % 8 (one XCD, one L2) when H % 8 == 0.
+// ---------------------------------------------------------------------------
+constexpr int kFusedDc = 512, kFusedDv = 128;
+constexpr int kFusedVt = kFusedDv / 16;   // 8 v-tiles of 16 rows
+constexpr int kFusedKs = kFusedDc / 128;  // 4 k-steps per up-projection wave
+constexpr int kFusedSplits = 32;          // at most this many partitions
+
+__global__ __launch_bounds__(384) void combine_up_v_kernel(
+    int n_tok, int H, int S, const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    bf16_t* __restrict__ o_lat, float* __restrict__ lse, const bf16_t* __restrict__ w_uv,
+    bf16_t* __restrict__ out) {
+  __shared__ float w[kMaxSplits];
+  __shared__ u32x4_t orow[kFusedDc / 8];             // the bf16 o_lat row, 16-byte chunks
+  __shared__ f32x4_t red[4][kFusedVt][64];
+  __shared__ float cw_s[3];
+  const int id = blockIdx.x;
+  int n, h;
+  if (H % 8 == 0) {
+    const int rest = id >> 3;
+    n = rest % n_tok;
+    h = (rest / n_tok) * 8 + (id & 7);
+  } else {
+    n = id / H;
+    h = id % H;
+  }
+  const size_t r = (size_t)n * H + h;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (a scalar branch below): the two roles each pass the same
+  // three block barriers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nn = lane & 15, g = lane >> 4;
+
+  if (wave < 2) {
+    const int col = wave * kCombCols + 4 * lane;
+    CombineCols<kFusedSplits, true> cc;  // every partition in flight at once
+    cc.start(o_part + r * S * kFusedDc, S, kFusedDc, col);
+    if (wave == 0) {
+      const CombineWeights cw = combine_weights(lse_part + r * S, S, w, lane);
+      if (lane == 0) {
+        cw_s[0] = cw.mx;
+        cw_s[1] = cw.sum;
+        cw_s[2] = cw.bad ? 1.0f : 0.0f;
+        if (lse) lse[r] = cw.lse();
+      }
+    }
+    __syncthreads();  // weights ready
+    const CombineWeights cw = {cw_s[0], cw_s[1], cw_s[2] != 0.0f};
+    const float4 v = cc.finish(w, cw);
+    store4<bf16_t>(o_lat + r * kFusedDc + col, v);
+    uint2 u;
+    u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+    u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    reinterpret_cast<uint2*>(orow)[col / 4] = u;
+    __syncthreads();  // row in LDS
+    __syncthreads();  // partial sums in LDS
+    return;
+  }
+  const int uw = wave - 2;  // the up-projection wave this one replays
+  const bf16_t* brow = w_uv + ((size_t)h * kFusedDv + nn) * kFusedDc + 8 * g + 32 * uw;
+  u32x4_t bv[kFusedVt][kFusedKs];
+#pragma unroll
+  for (int vt = 0; vt < kFusedVt; ++vt)
+#pragma unroll
+    for (int i = 0; i < kFusedKs; ++i)
+      bv[vt][i] = *reinterpret_cast<const u32x4_t*>(brow + (size_t)vt * 16 * kFusedDc + 128 * i);
+  __syncthreads();  // weights ready
+  __syncthreads();  // row in LDS
+  f32x4_t acc[kFusedVt];
+#pragma unroll
+  for (int vt = 0; vt < kFusedVt; ++vt) acc[vt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kFusedKs; ++i) {
+    const int k = 32 * uw + 128 * i;
+    const u32x4_t av = (nn == 0) ? orow[(k + 8 * g) / 8] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int vt = 0; vt < kFusedVt; ++vt)
+      acc[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                        __builtin_bit_cast(bf16x8_t, bv[vt][i]),
+                                                        acc[vt], 0, 0, 0);
+  }
+#pragma unroll
+  for (int vt = 0; vt < kFusedVt; ++vt) red[uw][vt][lane] = acc[vt];
+  __syncthreads();  // partial sums in LDS
+  // v-tiles uw and uw + 4; output row 0 (token n) sits in lanes g == 0, r = 0
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int vt = uw + 4 * j;
+    f32x4_t sum = red[0][vt][lane] + red[1][vt][lane];
+    sum += red[2][vt][lane] + red[3][vt][lane];
+    if (g == 0) out[r * kFusedDv + vt * 16 + nn] = f2bf(sum[0]);
+  }
+}
+
+bool combine_up_v_fused_ok(const Shape& s, int n_tok, int num_splits) {
+  return s.dtype == 1 && s.dc == kFusedDc && s.dv == kFusedDv && n_tok * s.H <= 4096 &&
+         num_splits <= kFusedSplits;
+}
+
+int launch_combine_up_project(const Shape& s, int n_tok, int num_splits, const float* o_part,
+                              const float* lse_part, void* o_lat, float* lse, const void* w_uv,
+                              void* out, void* stream) {
+  if (!combine_up_v_fused_ok(s, n_tok, num_splits)) {
+    int rc = launch_combine(s, n_tok * s.H, num_splits, o_part, lse_part, o_lat, lse, stream);
+    if (rc == 0) rc = launch_up_project_v(s, n_tok, o_lat, w_uv, out, stream);
+    return rc;
+  }
+  hipLaunchKernelGGL(combine_up_v_kernel, dim3(n_tok * s.H), dim3(384), 0,
+                     reinterpret_cast<hipStream_t>(stream), n_tok, s.H, num_splits, o_part,
+                     lse_part, (bf16_t*)o_lat, lse, (const bf16_t*)w_uv, (bf16_t*)out);
   return (int)hipGetLastError();
 }
 

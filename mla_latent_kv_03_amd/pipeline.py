@@ -1,4 +1,4 @@
-"""One MLA decode step on the device: buffers plus the five library calls.
+"""One MLA decode step on the device: buffers plus the library calls.
 
 Plumbing only: torch allocates the device buffers and supplies the stream;
 every step of the computation runs in libmla's kernels.
@@ -71,14 +71,31 @@ class DecodeStep:
     def up_project(self, w_uv, stream=None):
         B.up_project_v(self.cfg, self.o_lat, w_uv, self.out, stream)
 
+    def absorb_append(self, q_nope, q_rope, w_uk, c_new, k_new, page_table, cache, stream=None):
+        B.absorb_append(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, c_new, k_new,
+                        self.seq_idx, self.qpos, page_table, cache, B.APPEND_ROTATE, stream)
+
+    def combine_up_project(self, w_uv, stream=None):
+        B.combine_up_project(self.cfg, self.o_part, self.lse_part, self.o_lat, w_uv, self.out,
+                             self.lse, stream)
+
     def run(self, q_nope, q_rope, w_uk, w_uv, c_new, k_new, cache, page_table, seq_lens,
-            stream=None, max_seq_len: Optional[int] = None):
-        """absorb -> append (B*Q new rows) -> decode -> combine -> up-project."""
-        self.absorb(q_nope, q_rope, w_uk, stream)
-        self.append(c_new, k_new, page_table, cache, stream)
+            stream=None, max_seq_len: Optional[int] = None, fused: bool = True):
+        """absorb -> append (B*Q new rows) -> decode -> combine -> up-project.
+
+        fused: the first two and the last two calls each as one library call
+        (mla_absorb_append, mla_combine_up_project; same results)."""
+        if fused:
+            self.absorb_append(q_nope, q_rope, w_uk, c_new, k_new, page_table, cache, stream)
+        else:
+            self.absorb(q_nope, q_rope, w_uk, stream)
+            self.append(c_new, k_new, page_table, cache, stream)
         self.decode(cache, page_table, seq_lens, stream, max_seq_len)
-        self.combine(stream)
-        self.up_project(w_uv, stream)
+        if fused:
+            self.combine_up_project(w_uv, stream)
+        else:
+            self.combine(stream)
+            self.up_project(w_uv, stream)
         return self.out
 
 

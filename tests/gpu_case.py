@@ -72,9 +72,10 @@ class Case:
         self.step = DecodeStep(cfg, B, Q, self.S, inp.seq_lens)
         torch.cuda.synchronize()
 
-    def run(self, max_seq_len=None):
+    def run(self, max_seq_len=None, fused=True):
         out = self.step.run(self.q_nope, self.q_rope, self.w_uk, self.w_uv, self.c_new, self.k_new,
-                            self.pool, self.pt, self.seq_lens, max_seq_len=max_seq_len)
+                            self.pool, self.pt, self.seq_lens, max_seq_len=max_seq_len,
+                            fused=fused)
         torch.cuda.synchronize()
         return out
 

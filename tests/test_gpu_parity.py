@@ -267,6 +267,32 @@ def test_paged_equals_identity_bit_exact():
     assert np.array_equal(to64(a.step.o_part), to64(b.step.o_part))
 
 
+FUSED = ["tiny_f32", "v2lite_small", "v2lite_paged_small", "v2_h128_small", "q4_h128_small",
+         "bf16_generic_h8", "bf16_h12"]
+
+
+@pytest.mark.parametrize("name", FUSED)
+def test_fused_calls_bit_exact(name):
+    """mla_absorb_append and mla_combine_up_project give the bits of the calls they fuse."""
+    wl = SMALL[name] if name in SMALL else small("v2lite_32k", batch=3, heads=12, seq_len=500,
+                                                  num_splits=4)
+    case = Case(wl, seed=3)
+    case.run(fused=False)
+    s = case.step
+    ref = {k: v.copy() for k, v in case.results().items()}
+    ref["q_full"] = to64(s.q_full)
+    ref["pool"] = case.pool.view(torch.int16 if wl.dtype == "bf16" else torch.int32).cpu().numpy()
+    for k in ("q_full", "o_lat", "out", "lse"):
+        getattr(s, k).fill_(float("nan"))
+    case.run(fused=True)
+    got = case.results()
+    got["q_full"] = to64(s.q_full)
+    got["pool"] = case.pool.view(torch.int16 if wl.dtype == "bf16" else torch.int32).cpu().numpy()
+    for k in ref:
+        assert np.array_equal(got[k], ref[k], equal_nan=True), k
+    check_against_oracle(case, got, case.oracle())
+
+
 def test_repeat_runs_bit_exact():
     case = Case(SMALL["v2_h128_small"], seed=1)
     case.run()
@@ -295,6 +321,19 @@ def test_edge_lengths(lens, Q):
         case = Case(wl, seed=9, seq_lens=list(lens))
         case.run()
         check_against_oracle(case, case.results(), case.oracle())
+
+
+@pytest.mark.parametrize("page", [16, 32, 128])
+@pytest.mark.parametrize("heads,Q", [(16, 1), (16, 2), (128, 1)])
+def test_page_sizes(page, heads, Q):
+    # 5 partitions: with 16-token pages the 803-token sequence gets 176-token
+    # partitions, whose bounds fall inside 32-token tiles; with 16/32-token
+    # pages a 64-row block shape takes the 16-row kernel
+    wl = small("v2lite_paged_varlen", batch=3, q_len=Q, heads=heads, len_range=(30, 1000),
+               num_splits=5, page_size=page)
+    case = Case(wl, seed=11)
+    case.run()
+    check_against_oracle(case, case.results(), case.oracle())
 
 
 def test_single_token_output_is_v0():
