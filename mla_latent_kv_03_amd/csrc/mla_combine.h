@@ -73,6 +73,29 @@ __device__ __forceinline__ CombineWeights combine_weights(const float* __restric
   return CombineWeights{mx, sum, bad};
 }
 
+// The same weights for S <= 64 from v = lse_part[row][lane] (any value for
+// lane >= S) loaded by the caller, so that the load can be issued ahead of
+// others: the operations are those of combine_weights' single iteration.
+__device__ __forceinline__ CombineWeights combine_weights_one(float v, int S, float* w, int lane) {
+  float mx = -INFINITY;
+  bool nan_seen = false;
+  if (lane < S) {
+    w[lane] = v;
+    nan_seen |= (v != v);
+    mx = fmaxf(mx, v);
+  }
+  mx = wave_max(mx);
+  const bool bad = __any(nan_seen);
+  float sum = 0.0f;
+  if (lane < S) {
+    const float e = (w[lane] == -INFINITY) ? 0.0f : expf(w[lane] - mx);
+    w[lane] = e;
+    sum += e;
+  }
+  sum = wave_sum(sum);
+  return CombineWeights{mx, sum, bad};
+}
+
 // One lane's 4 columns of a row, summed over the partitions in order. The
 // partials do not depend on the weights, so start() issues the first
 // kCombChunk partition loads before the weights exist; finish() then adds the

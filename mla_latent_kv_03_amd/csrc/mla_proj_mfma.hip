@@ -274,34 +274,44 @@ int launch_up_project_v_mfma(const Shape& s, int n_tok, const void* o_lat, const
 }
 
 // ---------------------------------------------------------------------------
-// a5 + a6 in one launch (bf16, d_c = 512, d_v = 128): one block of 6 waves
-// per output row r = (token n, head h).
+// a5 + a6 in one launch (bf16, d_c = 512, d_v = 128): two blocks of 6 waves
+// per output row r = (token n, head h), block half j taking value columns
+// [64 j, 64 j + 64): twice as many CUs share the partial and W_UV streams
+// (both halves merge the whole row, which costs less than it saves).
 //   waves 0, 1  merge columns [256 w, 256 w + 256) of the row exactly as the
-//               combine kernel does (wave 0 also forms the weights), with all
-//               S <= 32 partitions loaded at once; the bf16 row goes to o_lat
-//               and to LDS.
-//   waves 2..5  load their W_UV[h] operands at the start (they depend on
-//               nothing), then run the MFMA sequence of up_v_mfma_kernel's
-//               wave (w - 2) for this token, with the token in A-operand row
-//               0 and zeros in the other rows (an MFMA output row depends
-//               only on its own A row), and sum across waves in that
-//               kernel's order, so both paths give the same bits.
+//               combine kernel does (wave 0 also forms the weights), with the
+//               row's LSEs and all of its S <= 32 partitions loaded at once;
+//               the bf16 row goes to LDS, and (half 0 only) to o_lat and lse.
+//   waves 2..5  load their W_UV[h] operands once the merge's loads are
+//               queued (they depend on nothing), then run the MFMA sequence
+//               of up_v_mfma_kernel's wave (w - 2) for this token and the
+//               half's 4 v-tiles, with the token in A-operand row 0 and zeros
+//               in the other rows (an MFMA output row depends only on its own
+//               A row), and sum across waves in that kernel's order, so both
+//               paths give the same bits.
 // Blocks of one head share blockIdx % 8 (one XCD, one L2) when H % 8 == 0.
+// The barriers order LDS traffic only, so they wait for LDS operations, not
+// for the loads still in flight.
 // ---------------------------------------------------------------------------
 constexpr int kFusedDc = 512, kFusedDv = 128;
-constexpr int kFusedVt = kFusedDv / 16;   // 8 v-tiles of 16 rows
-constexpr int kFusedKs = kFusedDc / 128;  // 4 k-steps per up-projection wave
-constexpr int kFusedSplits = 32;          // at most this many partitions
+constexpr int kFusedVt = kFusedDv / 16 / 2;  // 4 v-tiles of 16 rows per block
+constexpr int kFusedKs = kFusedDc / 128;     // 4 k-steps per up-projection wave
+constexpr int kFusedSplits = 32;             // at most this many partitions
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __global__ __launch_bounds__(384) void combine_up_v_kernel(
     int n_tok, int H, int S, const float* __restrict__ o_part, const float* __restrict__ lse_part,
     bf16_t* __restrict__ o_lat, float* __restrict__ lse, const bf16_t* __restrict__ w_uv,
     bf16_t* __restrict__ out) {
-  __shared__ float w[kMaxSplits];
+  __shared__ float w[kFusedSplits];
   __shared__ u32x4_t orow[kFusedDc / 8];             // the bf16 o_lat row, 16-byte chunks
   __shared__ f32x4_t red[4][kFusedVt][64];
   __shared__ float cw_s[3];
-  const int id = blockIdx.x;
+  const int half = blockIdx.x & 1;
+  const int id = blockIdx.x >> 1;
   int n, h;
   if (H % 8 == 0) {
     const int rest = id >> 3;
@@ -314,45 +324,52 @@ __global__ __launch_bounds__(384) void combine_up_v_kernel(
   const size_t r = (size_t)n * H + h;
   const int lane = threadIdx.x & 63;
   // wave-uniform (a scalar branch below): the two roles each pass the same
-  // three block barriers
+  // four block barriers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nn = lane & 15, g = lane >> 4;
 
   if (wave < 2) {
     const int col = wave * kCombCols + 4 * lane;
+    // the row's LSEs first, then all of its partitions: these loads are
+    // queued before the W_UV loads of the other waves (start barrier)
+    const float lv = (wave == 0 && lane < S) ? lse_part[r * S + lane] : 0.0f;
     CombineCols<kFusedSplits, true> cc;  // every partition in flight at once
     cc.start(o_part + r * S * kFusedDc, S, kFusedDc, col);
+    lds_barrier();  // start
     if (wave == 0) {
-      const CombineWeights cw = combine_weights(lse_part + r * S, S, w, lane);
+      const CombineWeights cw = combine_weights_one(lv, S, w, lane);
       if (lane == 0) {
         cw_s[0] = cw.mx;
         cw_s[1] = cw.sum;
         cw_s[2] = cw.bad ? 1.0f : 0.0f;
-        if (lse) lse[r] = cw.lse();
+        if (lse && half == 0) lse[r] = cw.lse();
       }
     }
-    __syncthreads();  // weights ready
+    lds_barrier();  // weights ready
     const CombineWeights cw = {cw_s[0], cw_s[1], cw_s[2] != 0.0f};
     const float4 v = cc.finish(w, cw);
-    store4<bf16_t>(o_lat + r * kFusedDc + col, v);
+    if (half == 0) store4<bf16_t>(o_lat + r * kFusedDc + col, v);
     uint2 u;
     u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
     u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
     reinterpret_cast<uint2*>(orow)[col / 4] = u;
-    __syncthreads();  // row in LDS
-    __syncthreads();  // partial sums in LDS
+    lds_barrier();  // row in LDS
+    lds_barrier();  // partial sums in LDS
     return;
   }
+  lds_barrier();  // start
   const int uw = wave - 2;  // the up-projection wave this one replays
-  const bf16_t* brow = w_uv + ((size_t)h * kFusedDv + nn) * kFusedDc + 8 * g + 32 * uw;
+  const int vt0 = half * kFusedVt;
+  const bf16_t* brow =
+      w_uv + ((size_t)h * kFusedDv + vt0 * 16 + nn) * kFusedDc + 8 * g + 32 * uw;
   u32x4_t bv[kFusedVt][kFusedKs];
 #pragma unroll
   for (int vt = 0; vt < kFusedVt; ++vt)
 #pragma unroll
     for (int i = 0; i < kFusedKs; ++i)
       bv[vt][i] = *reinterpret_cast<const u32x4_t*>(brow + (size_t)vt * 16 * kFusedDc + 128 * i);
-  __syncthreads();  // weights ready
-  __syncthreads();  // row in LDS
+  lds_barrier();  // weights ready
+  lds_barrier();  // row in LDS
   f32x4_t acc[kFusedVt];
 #pragma unroll
   for (int vt = 0; vt < kFusedVt; ++vt) acc[vt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -368,14 +385,13 @@ __global__ __launch_bounds__(384) void combine_up_v_kernel(
   }
 #pragma unroll
   for (int vt = 0; vt < kFusedVt; ++vt) red[uw][vt][lane] = acc[vt];
-  __syncthreads();  // partial sums in LDS
-  // v-tiles uw and uw + 4; output row 0 (token n) sits in lanes g == 0, r = 0
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int vt = uw + 4 * j;
+  lds_barrier();  // partial sums in LDS
+  // v-tile uw of this half; output row 0 (token n) sits in lanes g == 0, r = 0
+  {
+    const int vt = uw;
     f32x4_t sum = red[0][vt][lane] + red[1][vt][lane];
     sum += red[2][vt][lane] + red[3][vt][lane];
-    if (g == 0) out[r * kFusedDv + vt * 16 + nn] = f2bf(sum[0]);
+    if (g == 0) out[r * kFusedDv + (vt0 + vt) * 16 + nn] = f2bf(sum[0]);
   }
 }
 
@@ -392,7 +408,7 @@ int launch_combine_up_project(const Shape& s, int n_tok, int num_splits, const f
     if (rc == 0) rc = launch_up_project_v(s, n_tok, o_lat, w_uv, out, stream);
     return rc;
   }
-  hipLaunchKernelGGL(combine_up_v_kernel, dim3(n_tok * s.H), dim3(384), 0,
+  hipLaunchKernelGGL(combine_up_v_kernel, dim3(2 * n_tok * s.H), dim3(384), 0,
                      reinterpret_cast<hipStream_t>(stream), n_tok, s.H, num_splits, o_part,
                      lse_part, (bf16_t*)o_lat, lse, (const bf16_t*)w_uv, (bf16_t*)out);
   return (int)hipGetLastError();
