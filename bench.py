@@ -85,7 +85,7 @@ def traffic_from_profile(wl_name, kernel_src_hash):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, budget_flops=6e11):
+def cpu_baseline(wl, inp, budget_flops=2.4e12):
     """Time the fp64 oracle on the host cores over a bounded sample of the workload.
 
     The sample is the first sequences (and, when one sequence with every head
