@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="v2lite_32k")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--split-chunk", type=int, default=0,
+                    help="fixed partition size in tokens (-1: per-sequence plan; 0: the workload's)")
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--graph", action="store_true", help="replay each layer's step as a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -143,6 +145,11 @@ def main():
         sys.exit(1)
     mla.lib()
     wl = workload.WORKLOADS[args.workload]
+    if args.split_chunk < 0:
+        wl = wl.replace(split_chunk=0)
+    elif args.split_chunk > 0:
+        wl = wl.replace(split_chunk=args.split_chunk,
+                        num_splits=-(-wl.max_seq_len // args.split_chunk))
     if args.num_splits:
         wl = wl.replace(num_splits=args.num_splits)
     n_layers = args.layers or LAYERS.get(wl.name, 2)
@@ -166,7 +173,8 @@ def main():
     rows = np.concatenate([inp.offsets[b] + np.arange(int(L) - Q, int(L))
                            for b, L in enumerate(inp.seq_lens)])
     c_new, k_new = upload(inp.c[rows], dt), upload(inp.k_rope[rows], dt)
-    steps = [DecodeStep(cfg, B, Q, wl.num_splits, inp.seq_lens) for _ in range(1)]
+    steps = [DecodeStep(cfg, B, Q, wl.num_splits, inp.seq_lens, split_chunk=wl.split_chunk)
+             for _ in range(1)]
     st = steps[0]
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
@@ -286,6 +294,7 @@ def main():
                    "total_cached_tokens": total_tokens, "kv_rank": wl.kv_rank,
                    "rope_dim": wl.rope_dim, "page_size": wl.page_size,
                    "paged": wl.paged, "num_splits": wl.num_splits,
+                   "split_chunk": wl.split_chunk,
                    "layer_caches_rotated": n_layers, "hip_graph": bool(args.graph),
                    "library_calls_per_step": 5 if args.unfused else 3,
                    "decode_kernel": kernel},

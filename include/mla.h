@@ -11,6 +11,7 @@
  *   mla_absorb_q        query -> latent space through W_UK, RoPE on the query
  *   mla_cache_append    write the new token rows through the page table
  *   mla_decode_paged    split-KV attention of the absorbed queries over the cache
+ *                       (mla_decode_paged_chunked: fixed-size partitions)
  *   mla_splitkv_combine log-sum-exp merge of the split partials
  *   mla_up_project_v    latent output -> per-head value space through W_UV
  *   mla_absorb_append, mla_combine_up_project
@@ -102,8 +103,8 @@ size_t mla_cache_bytes_per_token(const mla_config_t* cfg);
 
 /* Split-KV plan: partition s of a sequence of length L covers tokens
  * [s*chunk, min(L, (s+1)*chunk)) with chunk = page_size * ceil(ceil(L/S) /
- * page_size); partitions past the end are empty (o = 0, lse = -inf). Writes
- * the chunk length to *chunk_tokens. Host helper mirroring the kernels. */
+ * page_size); partitions past the end are empty. Writes the chunk length to
+ * *chunk_tokens. Host helper mirroring the kernels. */
 mla_status_t mla_split_chunk(const mla_config_t* cfg, int32_t seq_len, int32_t num_splits,
                              int32_t* chunk_tokens);
 
@@ -173,7 +174,10 @@ mla_status_t mla_absorb_append(const mla_config_t* cfg, int32_t n_tok, const voi
  *   o_part[b][j][h][s]   = sum_t e^(score_t - m) c_t / sum_t e^(score_t - m)
  *   lse_part[b][j][h][s] = m + ln sum_t e^(score_t - m)   (natural log)
  * over the tokens t of partition s (plan: mla_split_chunk). c_t = the first
- * d_c entries of the row. Empty partitions: o = 0, lse = -inf.
+ * d_c entries of the row. A partition whose tokens are all masked gives
+ * o = 0, lse = -inf; an empty partition (no tokens) gives lse = -inf and
+ * leaves its o_part row unwritten (mla_splitkv_combine never reads a
+ * partition of weight 0).
  * q_full [batch][q_len][H][D] T, cache [num_pages][page_size][D] T,
  * page_table [batch][max_pages] int32, seq_lens [batch] int32,
  * o_part [batch][q_len][H][num_splits][d_c] f32, lse_part [batch][q_len][H][num_splits] f32.
@@ -185,6 +189,30 @@ mla_status_t mla_decode_paged(const mla_config_t* cfg, int32_t batch, int32_t q_
                               const void* cache, int64_t num_pages, const int32_t* page_table,
                               int32_t max_pages, const int32_t* seq_lens, float* o_part,
                               float* lse_part, void* stream);
+
+/* a4 with fixed-size partitions: partition s of sequence b covers tokens
+ * [s*chunk_tokens, min(L_b, (s+1)*chunk_tokens)), so a long sequence has more
+ * non-empty partitions than a short one and every partition is at most
+ * chunk_tokens long: with lengths that differ, the work per block stays even
+ * (the per-sequence plan of mla_decode_paged gives every sequence S partitions
+ * of L_b/S tokens). Partitions past a sequence's end are empty (lse_part =
+ * -inf, o_part unwritten). chunk_tokens must be a positive multiple of page_size and
+ * chunk_tokens*num_splits >= max_seq_len (MLA_ERR_CAPACITY otherwise). Other
+ * arguments, layouts and errors as for mla_decode_paged; the outputs of
+ * mla_splitkv_combine are the same for either plan up to rounding. */
+mla_status_t mla_decode_paged_chunked(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                      int32_t chunk_tokens, int32_t num_splits,
+                                      int32_t max_seq_len, const void* q_full, const void* cache,
+                                      int64_t num_pages, const int32_t* page_table,
+                                      int32_t max_pages, const int32_t* seq_lens, float* o_part,
+                                      float* lse_part, void* stream);
+
+/* A fixed-size partition plan for mla_decode_paged_chunked: about six
+ * partitions per compute unit over total_tokens = sum of the batch's lengths,
+ * whole pages, at most 4,096 partitions per sequence. Writes chunk_tokens and
+ * num_splits = ceil(max_seq_len / chunk_tokens). */
+mla_status_t mla_chunk_plan(const mla_config_t* cfg, int64_t total_tokens, int32_t max_seq_len,
+                            int32_t num_cus, int32_t* chunk_tokens, int32_t* num_splits);
 
 /* a5. Log-sum-exp merge of the partitions ("The Architecture of Memory",
  * "Flash-Decoding and FlashInfer"), per row r = (b, j, h):

@@ -40,4 +40,5 @@ from ._binding import (  # noqa: F401
     up_project_v,
     absorb_append,
     combine_up_project,
+    chunk_plan,
 )

@@ -99,6 +99,10 @@ def lib() -> ctypes.CDLL:
         "mla_absorb_append": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, I32, VP, VP, VP, VP, VP,
                                              I32, I32, VP, I64, I32, VP]),
         "mla_combine_up_project": (ctypes.c_int, [P, I32, I32, I32, FP, FP, VP, FP, VP, VP, VP]),
+        "mla_decode_paged_chunked": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32,
+                                                    VP, FP, FP, VP]),
+        "mla_chunk_plan": (ctypes.c_int, [P, I64, I32, I32, ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -243,10 +247,19 @@ def absorb_append(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_rope
         "mla_absorb_append")
 
 
+def chunk_plan(cfg: Config, total_tokens: int, max_seq_len: int, num_cus: int = 256):
+    """A fixed-size partition plan (chunk_tokens, num_splits) for decode_paged(chunk_tokens=...)."""
+    ck, ns = ctypes.c_int32(0), ctypes.c_int32(0)
+    _ck(lib().mla_chunk_plan(ctypes.byref(cfg.c()), int(total_tokens), int(max_seq_len),
+                             int(num_cus), ctypes.byref(ck), ctypes.byref(ns)), "mla_chunk_plan")
+    return ck.value, ns.value
+
+
 def decode_paged(cfg: Config, q_full, cache, page_table, seq_lens, o_part, lse_part,
-                 max_seq_len: int, stream=None):
+                 max_seq_len: int, stream=None, chunk_tokens: int = 0):
     """a4: split-KV partials. q_full [B][Q][H][D]; o_part [B][Q][H][S][d_c] f32;
-    lse_part [B][Q][H][S] f32 (S = num_splits from lse_part's last axis)."""
+    lse_part [B][Q][H][S] f32 (S = num_splits from lse_part's last axis).
+    chunk_tokens > 0: fixed-size partitions (mla_decode_paged_chunked)."""
     t = _torch()
     if q_full.dim() != 4:
         raise ValueError("q_full: expected [batch][q_len][H][D]")
@@ -267,6 +280,12 @@ def decode_paged(cfg: Config, q_full, cache, page_table, seq_lens, o_part, lse_p
     sl = _need(seq_lens, "seq_lens", t.int32, B)
     op = _need(o_part, "o_part", t.float32, B * Q * H * S * cfg.kv_rank)
     lp = _need(lse_part, "lse_part", t.float32, B * Q * H * S)
+    if chunk_tokens:
+        _ck(lib().mla_decode_paged_chunked(ctypes.byref(cfg.c()), B, Q, int(chunk_tokens), S,
+                                           int(max_seq_len), args[0], args[1], num_pages, pt,
+                                           max_pages, sl, op, lp, _stream(stream)),
+            "mla_decode_paged_chunked")
+        return
     _ck(lib().mla_decode_paged(ctypes.byref(cfg.c()), B, Q, S, int(max_seq_len), args[0], args[1],
                                num_pages, pt, max_pages, sl, op, lp, _stream(stream)),
         "mla_decode_paged")

@@ -14,6 +14,7 @@
 namespace {
 
 constexpr int kMaxSplits = 4096;
+constexpr int kChunksPerCu = 6;
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -96,6 +97,32 @@ mla_status_t check_append(const mla_config_t* cfg, int32_t n_tok, const void* c_
   MLA_CHECK_PTR(page_table);
   MLA_CHECK_PTR(cache);
   return MLA_OK;
+}
+
+mla_status_t decode_call(const mla_config_t* cfg, int32_t batch, int32_t q_len, int32_t fixed,
+                         int32_t num_splits, int32_t max_seq_len, const void* q_full,
+                         const void* cache, int64_t num_pages, const int32_t* page_table,
+                         int32_t max_pages, const int32_t* seq_lens, float* o_part,
+                         float* lse_part, void* stream) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(batch >= 0 && q_len >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)q_len * cfg->num_heads <= 65536, MLA_ERR_SHAPE);
+  MLA_REQUIRE(max_seq_len >= q_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
+  if (batch == 0) return MLA_OK;
+  MLA_CHECK_PTR(q_full);
+  MLA_CHECK_PTR(cache);
+  MLA_CHECK_PTR(page_table);
+  MLA_CHECK_PTR(seq_lens);
+  MLA_CHECK_PTR(o_part);
+  MLA_CHECK_PTR(lse_part);
+  mla::Shape sh = shape_of(cfg);
+  sh.split_fixed = fixed;
+  return hip_status(mla::launch_decode(sh, batch, q_len, num_splits, max_seq_len, q_full, cache,
+                                       num_pages, page_table, max_pages, seq_lens, o_part,
+                                       lse_part, stream));
 }
 
 mla_status_t check_combine(const mla_config_t* cfg, int32_t batch, int32_t q_len,
@@ -245,23 +272,47 @@ mla_status_t mla_decode_paged(const mla_config_t* cfg, int32_t batch, int32_t q_
                               const void* cache, int64_t num_pages, const int32_t* page_table,
                               int32_t max_pages, const int32_t* seq_lens, float* o_part,
                               float* lse_part, void* stream) {
+  return decode_call(cfg, batch, q_len, 0, num_splits, max_seq_len, q_full, cache, num_pages,
+                     page_table, max_pages, seq_lens, o_part, lse_part, stream);
+}
+
+mla_status_t mla_decode_paged_chunked(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                      int32_t chunk_tokens, int32_t num_splits,
+                                      int32_t max_seq_len, const void* q_full, const void* cache,
+                                      int64_t num_pages, const int32_t* page_table,
+                                      int32_t max_pages, const int32_t* seq_lens, float* o_part,
+                                      float* lse_part, void* stream) {
   mla_status_t st = check_config(cfg);
   if (st != MLA_OK) return st;
-  MLA_REQUIRE(batch >= 0 && q_len >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(chunk_tokens >= cfg->page_size && chunk_tokens % cfg->page_size == 0,
+              MLA_ERR_SHAPE);
   MLA_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
-  MLA_REQUIRE((int64_t)q_len * cfg->num_heads <= 65536, MLA_ERR_SHAPE);
-  MLA_REQUIRE(max_seq_len >= q_len, MLA_ERR_CAPACITY);
-  MLA_REQUIRE((int64_t)max_pages * cfg->page_size >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
-  if (batch == 0) return MLA_OK;
-  MLA_CHECK_PTR(q_full);
-  MLA_CHECK_PTR(cache);
-  MLA_CHECK_PTR(page_table);
-  MLA_CHECK_PTR(seq_lens);
-  MLA_CHECK_PTR(o_part);
-  MLA_CHECK_PTR(lse_part);
-  return hip_status(mla::launch_decode(shape_of(cfg), batch, q_len, num_splits, max_seq_len,
-                                       q_full, cache, num_pages, page_table, max_pages,
-                                       seq_lens, o_part, lse_part, stream));
+  MLA_REQUIRE((int64_t)chunk_tokens * num_splits >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
+  return decode_call(cfg, batch, q_len, chunk_tokens, num_splits, max_seq_len, q_full, cache,
+                     num_pages, page_table, max_pages, seq_lens, o_part, lse_part, stream);
+}
+
+mla_status_t mla_chunk_plan(const mla_config_t* cfg, int64_t total_tokens, int32_t max_seq_len,
+                            int32_t num_cus, int32_t* chunk_tokens, int32_t* num_splits) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(chunk_tokens && num_splits, MLA_ERR_NULL);
+  MLA_REQUIRE(total_tokens >= 1 && max_seq_len >= 1, MLA_ERR_SHAPE);
+  if (num_cus < 1) num_cus = 256;
+  // about kChunksPerCu partitions per compute unit: the block dispatcher then
+  // evens out the work, and the last round is short
+  const int64_t pg = cfg->page_size;
+  const int64_t want = (total_tokens + (int64_t)kChunksPerCu * num_cus - 1) /
+                       ((int64_t)kChunksPerCu * num_cus);
+  int64_t chunk = pg * ((want + pg - 1) / pg);
+  const int64_t min_chunk = pg * (((int64_t)max_seq_len + (int64_t)kMaxSplits * pg - 1) /
+                                  ((int64_t)kMaxSplits * pg));
+  if (chunk < min_chunk) chunk = min_chunk;
+  if (chunk < pg) chunk = pg;
+  if (chunk > INT32_MAX / 2) return MLA_ERR_CAPACITY;
+  *chunk_tokens = (int32_t)chunk;
+  *num_splits = (int32_t)(((int64_t)max_seq_len + chunk - 1) / chunk);
+  return MLA_OK;
 }
 
 mla_status_t mla_splitkv_combine(const mla_config_t* cfg, int32_t batch, int32_t q_len,

@@ -3,8 +3,9 @@
 // s = 0..S-1,
 //   o_lat[r] = sum_s e^(lse_s - max) o_part[r][s] / sum_s e^(lse_s - max),
 //   lse[r]   = max + ln sum_s e^(lse_s - max);
-// empty partitions (lse = -inf) weigh 0, and a NaN partition LSE (an invalid
-// sequence) makes the whole row NaN. The pieces here are executed by one wave
+// partitions of weight 0 (lse = -inf: empty or fully masked) are left out, so
+// their o_part rows are never used (the decode leaves empty ones unwritten),
+// and a NaN partition LSE (an invalid sequence) makes the whole row NaN. The pieces here are executed by one wave
 // for 256 columns (lane l: columns 4l .. 4l+3) and shared by the combine
 // kernel and the fused merge + up-projection kernel, so both produce the
 // same bits.
@@ -122,32 +123,40 @@ struct CombineCols {
   __device__ __forceinline__ void add(const float* w, int s0, float4& a) const {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const bool in = s0 + u < S;
       const float ws = w[min(s0 + u, S - 1)];
+      const bool in = s0 + u < S && ws != 0.0f;
       a.x = in ? fmaf(ws, x[u].x, a.x) : a.x;
       a.y = in ? fmaf(ws, x[u].y, a.y) : a.y;
       a.z = in ? fmaf(ws, x[u].z, a.z) : a.z;
       a.w = in ? fmaf(ws, x[u].w, a.w) : a.w;
     }
   }
-  // normalized columns (NaN for a bad row)
-  __device__ __forceinline__ float4 finish(const float* w, const CombineWeights& cw) {
+  // normalized columns (NaN for a bad row). A later group of CH partitions
+  // whose weights are all 0 is neither loaded nor added.
+  __device__ __forceinline__ float4 finish(const float* w, const CombineWeights& cw, int lane) {
     float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (kOne) {
       add(w, 0, a);
     } else {
+      bool use = true;  // the first group was loaded speculatively in start()
       for (int s0 = 0; s0 < S; s0 += CH) {
         const int s1 = s0 + CH;
         float4 y[CH];
+        bool next = false;
         if (s1 < S) {  // wave-uniform
+          const int sl = s1 + lane % CH;
+          next = __any(sl < S && w[min(sl, S - 1)] != 0.0f);
+          if (next) {
 #pragma unroll
-          for (int u = 0; u < CH; ++u) y[u] = op[(size_t)min(s1 + u, S - 1) * st];
+            for (int u = 0; u < CH; ++u) y[u] = op[(size_t)min(s1 + u, S - 1) * st];
+          }
         }
-        add(w, s0, a);
-        if (s1 < S) {
+        if (use) add(w, s0, a);
+        if (next) {
 #pragma unroll
           for (int u = 0; u < CH; ++u) x[u] = y[u];
         }
+        use = next;
       }
     }
     const float nanv = __int_as_float(0x7fc00000);

@@ -46,10 +46,14 @@ __device__ __forceinline__ void rope_pair(double x0, double x1, int64_t pos, int
   *y1 = x0 * sn + x1 * cs;
 }
 
-// Split plan: tokens of partition s of a length-L sequence (page-aligned chunk).
-__device__ __forceinline__ void split_range(int L, int S, int page, int s, int* t0, int* t1) {
+// Split plan: tokens of partition s of a length-L sequence. fixed > 0: every
+// partition holds `fixed` tokens (a multiple of the page), so a long sequence
+// has more non-empty partitions than a short one; fixed == 0: the S
+// partitions of each sequence share it evenly, page-aligned.
+__device__ __forceinline__ void split_range(int L, int S, int page, int fixed, int s, int* t0,
+                                            int* t1) {
   const int64_t per = ((int64_t)L + S - 1) / S;
-  const int64_t chunk = (int64_t)page * ((per + page - 1) / page);
+  const int64_t chunk = fixed > 0 ? (int64_t)fixed : (int64_t)page * ((per + page - 1) / page);
   int64_t a = (int64_t)s * chunk, e = a + chunk;
   if (a > L) a = L;
   if (e > L) e = L;

@@ -56,8 +56,9 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
 }  // namespace
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_rows16_kernel(int Q, int H, int S, int page, int max_seq_len, float scale_log2,
-                          int units, int groups, const bf16_t* __restrict__ q_full,
+void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
+                          float scale_log2, int units, int groups,
+                          const bf16_t* __restrict__ q_full,
                           const bf16_t* __restrict__ cache, int64_t num_pages,
                           const int32_t* __restrict__ page_table, int max_pages,
                           const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
@@ -76,7 +77,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int max_seq_len, float 
   const int L = seq_lens[b];
   const bool bad_len = (L < Q) || (L > max_seq_len);
   int t0 = 0, t1 = 0;
-  if (!bad_len) split_range(L, S, page, s, &t0, &t1);
+  if (!bad_len) split_range(L, S, page, fixed, s, &t0, &t1);
   const int ntiles = (t1 - t0 + kT - 1) / kT;
   bool bad = bad_len;
 
@@ -277,8 +278,9 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int max_seq_len, float 
     const float lr = __shfl(l_row, 4 * kg + r, 64);
     inv[r] = lr > 0.0f ? 1.0f / lr : 0.0f;
   }
+  // an empty partition (no tokens) leaves its o_part rows unwritten
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < 4 && (t1 > t0 || any_bad); ++r) {
     const int orow = row0 + 4 * kg + r;
     float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + 128 * wave + 4 * n;
 #pragma unroll
@@ -316,7 +318,7 @@ int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, i
   const int blocks = ((units + 7) / 8) * 8 * groups;
   hipLaunchKernelGGL(decode_rows16_kernel, dim3(blocks), dim3(256), kLdsBytes,
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page,
-                     max_seq_len, s.scale * 1.4426950408889634f, units, groups,
+                     s.split_fixed, max_seq_len, s.scale * 1.4426950408889634f, units, groups,
                      (const bf16_t*)q_full, (const bf16_t*)cache, num_pages, page_table, max_pages,
                      seq_lens, o_part, lse_part);
   return (int)hipGetLastError();

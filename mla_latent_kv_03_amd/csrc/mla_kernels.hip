@@ -145,7 +145,7 @@ constexpr int kGenMaxF = 4;  // d_c <= 1024
 
 template <typename T>
 __global__ __launch_bounds__(256) void decode_generic_kernel(
-    int Q, int H, int dc, int dr, int page, int S, int max_seq_len, float scale,
+    int Q, int H, int dc, int dr, int page, int S, int fixed, int max_seq_len, float scale,
     const T* __restrict__ q_full, const T* __restrict__ cache, int64_t num_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens,
     float* __restrict__ o_part, float* __restrict__ lse_part) {
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   const int L = seq_lens[b];
   bool bad = (L < Q) || (L > max_seq_len);
   int t0 = 0, t1 = 0;
-  if (!bad) split_range(L, S, page, s, &t0, &t1);
+  if (!bad) split_range(L, S, page, fixed, s, &t0, &t1);
 
   for (int i = tid; i < nr * D; i += blockDim.x)
     qs[i] = Elt<T>::ld(q_full + ((size_t)b * R + r0) * D + i);
@@ -244,7 +244,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 #pragma unroll
     for (int k = 0; k < kGenMaxF; ++k) {
       const int f = tid + 256 * k;
-      if (f < dc) o_part[(row * S + s) * dc + f] = bad ? nanv : acc[r][k] * inv;
+      // an empty partition (no tokens) leaves its o_part row unwritten
+      if (f < dc && (t1 > t0 || bad)) o_part[(row * S + s) * dc + f] = bad ? nanv : acc[r][k] * inv;
     }
     if (tid == 0) lse_part[row * S + s] = bad ? nanv : (l > 0.0f ? m + logf(l) : -INFINITY);
   }
@@ -268,7 +269,8 @@ static int decode_generic_impl(const Shape& s, int batch, int q_len, int num_spl
   const int R = q_len * s.H;
   dim3 grid(num_splits, batch, (R + kGenRows - 1) / kGenRows);
   hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(256), lds, as_stream(stream), q_len, s.H,
-                     s.dc, s.dr, s.page, num_splits, max_seq_len, s.scale, (const T*)q_full,
+                     s.dc, s.dr, s.page, num_splits, s.split_fixed, max_seq_len, s.scale,
+                     (const T*)q_full,
                      (const T*)cache, num_pages, page_table, max_pages, seq_lens, o_part, lse_part);
   return (int)hipGetLastError();
 }
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(64) void combine_kernel(int S, int dc, const float*
   cc.start(o_part + (size_t)r * S * dc, S, dc, col);
   const CombineWeights cw = combine_weights(lse_part + (size_t)r * S, S, w, lane);
   __syncthreads();
-  const float4 v = cc.finish(w, cw);
+  const float4 v = cc.finish(w, cw, lane);
   if (col < dc) store4<T>(o_lat + (size_t)r * dc + col, v);
   if (lse && blockIdx.y == 0 && lane == 0) lse[r] = cw.lse();
 }

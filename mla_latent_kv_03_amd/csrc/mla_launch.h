@@ -12,6 +12,7 @@ struct Shape {
   int H, dc, dr, dn, dv, page, dtype;  // dtype: 0 = fp32, 1 = bf16
   float scale;
   double log2_base;                    // log2(rope_base), for fp64 RoPE angles
+  int split_fixed = 0;                 // decode partitions of this many tokens (0: per sequence)
   int D() const { return dc + dr; }
 };
 

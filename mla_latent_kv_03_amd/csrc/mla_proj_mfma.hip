@@ -347,7 +347,7 @@ __global__ __launch_bounds__(384) void combine_up_v_kernel(
     }
     lds_barrier();  // weights ready
     const CombineWeights cw = {cw_s[0], cw_s[1], cw_s[2] != 0.0f};
-    const float4 v = cc.finish(w, cw);
+    const float4 v = cc.finish(w, cw, lane);
     if (half == 0) store4<bf16_t>(o_lat + r * kFusedDc + col, v);
     uint2 u;
     u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);

@@ -35,9 +35,10 @@ class DecodeStep:
     """
 
     def __init__(self, cfg: B.Config, batch: int, q_len: int, num_splits: int,
-                 seq_lens_host, device="cuda"):
+                 seq_lens_host, device="cuda", split_chunk: int = 0):
         t = _torch()
         self.cfg, self.batch, self.q_len, self.num_splits = cfg, batch, q_len, num_splits
+        self.split_chunk = split_chunk  # > 0: fixed-size partitions
         H, D, dc, dv = cfg.num_heads, cfg.dim, cfg.kv_rank, cfg.v_dim
         dt = dtype_of(cfg)
         lens = [int(x) for x in seq_lens_host]
@@ -63,7 +64,8 @@ class DecodeStep:
 
     def decode(self, cache, page_table, seq_lens, stream=None, max_seq_len: Optional[int] = None):
         B.decode_paged(self.cfg, self.q_full, cache, page_table, seq_lens, self.o_part,
-                       self.lse_part, max_seq_len or self.max_seq_len, stream)
+                       self.lse_part, max_seq_len or self.max_seq_len, stream,
+                       chunk_tokens=self.split_chunk)
 
     def combine(self, stream=None):
         B.splitkv_combine(self.cfg, self.o_part, self.lse_part, self.o_lat, self.lse, stream)

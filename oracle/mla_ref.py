@@ -283,21 +283,27 @@ def absorbed_attend_sequence(c, k_rope_raw, q_nope, q_rope, w_uk, w_uv, scale,
 # --------------------------------------------------------------------------
 # split-KV partials and the log-sum-exp merge
 # --------------------------------------------------------------------------
-def split_bounds(seq_len: int, num_splits: int, page: int = 64) -> List[Tuple[int, int]]:
+def split_bounds(seq_len: int, num_splits: int, page: int = 64,
+                 chunk_tokens: int = 0) -> List[Tuple[int, int]]:
     """Token ranges of the split-KV units of one sequence.
 
     Reading of "splits the cache into chunks" ("The Architecture of Memory",
     "Flash-Decoding and FlashInfer"): chunk = page * ceil(ceil(L / S) / page)
     tokens, unit s covers [s*chunk, min(L, (s+1)*chunk)); units past the end
-    are empty. Chunks are whole pages so a unit never splits a page.
+    are empty. Chunks are whole pages so a unit never splits a page. With
+    chunk_tokens > 0 the chunk is that fixed size for every sequence instead
+    (a long sequence then fills more of its S units than a short one).
     """
-    per = -(-seq_len // num_splits)
-    chunk = page * (-(-per // page))
+    if chunk_tokens > 0:
+        chunk = chunk_tokens
+    else:
+        per = -(-seq_len // num_splits)
+        chunk = page * (-(-per // page))
     return [(min(seq_len, s * chunk), min(seq_len, (s + 1) * chunk)) for s in range(num_splits)]
 
 
 def attend_partials(c, k_rope_raw, q_nope, q_rope, w_uk, scale, num_splits,
-                    base: float = 10000.0, page: int = 64):
+                    base: float = 10000.0, page: int = 64, chunk_tokens: int = 0):
     """Per-split normalised partials of the latent output.
 
     For unit s over tokens [a, e): o_s = sum_t e^(s_t - m_s) c_t / sum_t e^(s_t - m_s)
@@ -311,7 +317,7 @@ def attend_partials(c, k_rope_raw, q_nope, q_rope, w_uk, scale, num_splits,
     Q, H = s.shape[:2]
     o_part = np.zeros((Q, H, num_splits, c.shape[1]), F64)
     lse_part = np.full((Q, H, num_splits), -np.inf, F64)
-    for si, (a, e) in enumerate(split_bounds(L, num_splits, page)):
+    for si, (a, e) in enumerate(split_bounds(L, num_splits, page, chunk_tokens)):
         if e <= a:
             continue
         ss = s[:, :, a:e]

@@ -69,7 +69,8 @@ class Case:
                                for b, L in enumerate(inp.seq_lens)])
         self.c_new = upload(inp.c[rows], dt)
         self.k_new = upload(inp.k_rope[rows], dt)
-        self.step = DecodeStep(cfg, B, Q, self.S, inp.seq_lens)
+        self.chunk = wl.split_chunk if num_splits is None else 0
+        self.step = DecodeStep(cfg, B, Q, self.S, inp.seq_lens, split_chunk=self.chunk)
         torch.cuda.synchronize()
 
     def run(self, max_seq_len=None, fused=True):

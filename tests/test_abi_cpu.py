@@ -86,6 +86,20 @@ def test_split_plan_matches_oracle(L, page):
             assert got == want, (Lq, S)
 
 
+def test_chunk_plan(L):
+    cfg = mla.Config(num_heads=16)
+    # V2-Lite varlen batch: ~568K tokens over 256 CUs -> about 6 partitions per CU
+    ck, ns = mla.chunk_plan(cfg, 568107, 32768, 256)
+    assert ck % 64 == 0 and ck * ns >= 32768 and (ns - 1) * ck < 32768
+    assert 4 * 256 <= 568107 / ck <= 8 * 256
+    ck, ns = mla.chunk_plan(cfg, 100, 100, 256)          # tiny batch: one page
+    assert (ck, ns) == (64, 2)
+    ck, ns = mla.chunk_plan(cfg, 1 << 30, 1 << 30, 256)  # at most 4096 partitions
+    assert ns <= 4096 and ck * ns >= 1 << 30
+    with pytest.raises(mla.MLAError):
+        mla.chunk_plan(cfg, 0, 10, 256)
+
+
 def test_partials_bytes_and_default_splits(L):
     assert mla.decode_partials_bytes(V2, 8, 1, 32) == 8 * 16 * 32 * 513 * 4
     assert mla.decode_partials_bytes(V2, 8, 1, 0) == 0
@@ -149,3 +163,28 @@ def test_combine_and_up_errors(L):
     assert L.mla_splitkv_combine(_c(V2), 2, 1, 0, A16, A16, A16, None, None) == 2
     assert L.mla_up_project_v(_c(V2), 3, A16, None, A16, None) == 1
     assert L.mla_up_project_v(_c(V2), 0, None, None, None, None) == 0
+
+
+def test_chunked_decode_errors(L):
+    def call(chunk=64, S=4, max_seq=256, batch=2, o=A16):
+        return L.mla_decode_paged_chunked(_c(V2), batch, 1, chunk, S, max_seq, A16, A16, 8, A16,
+                                          4, A16, o, A16, None)
+    assert call(chunk=0) == 2 and call(chunk=100) == 2      # not a positive multiple of the page
+    assert call(chunk=64, S=2) == 5                          # 2 x 64 tokens < max_seq_len 256
+    assert call(S=0) == 2
+    assert call(o=None) == 1
+    assert call(batch=0) == 0
+
+
+def test_fused_call_errors(L):
+    a = [A16] * 5
+    # absorb arguments are checked first, then the append arguments
+    assert L.mla_absorb_append(_c(V2), 4, None, *a[:4], 4, *a, 2, 4, A16, 16, 1, None) == 1
+    assert L.mla_absorb_append(_c(V2), 4, *a, 4, *a, 2, 4, None, 16, 1, None) == 1
+    assert L.mla_absorb_append(_c(V2), 4, *a, 4, *a, 2, 4, A16, 16, 7, None) == 2
+    assert L.mla_absorb_append(_c(V2), 0, *[None] * 5, 0, *[None] * 5, 1, 1, None, 1, 1,
+                               None) == 0
+    assert L.mla_combine_up_project(_c(V2), 2, 1, 4, A16, A16, A16, None, None, A16, None) == 1
+    assert L.mla_combine_up_project(_c(V2), 2, 1, 4, A16, A16, A16, MIS, A16, A16, None) == 4
+    assert L.mla_combine_up_project(_c(V2), 0, 1, 4, None, None, None, None, None, None,
+                                    None) == 0

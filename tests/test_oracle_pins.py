@@ -246,8 +246,22 @@ def test_split_bounds_invariants():
                 assert a % 64 == 0 or a == L
 
 
-@pytest.mark.parametrize("L,S", [(256, 1), (256, 4), (200, 7), (65, 3), (64, 64), (300, 2)])
-def test_split_merge_equals_unsplit(L, S):
+def test_split_bounds_fixed_chunk():
+    # every sequence is cut at multiples of the same chunk; units past its end are empty
+    for L in [1, 63, 64, 65, 383, 384, 385, 1000, 32768]:
+        for chunk in [64, 128, 384]:
+            S = -(-32768 // chunk)
+            b = oracle.split_bounds(L, S, 64, chunk)
+            assert len(b) == S
+            assert [(a, e) for a, e in b if e > a] == [(a, min(L, a + chunk))
+                                                       for a in range(0, L, chunk)]
+            assert all(e - a <= chunk for a, e in b)
+            assert all(a == e == L for a, e in b[-(-L // chunk):])
+
+
+@pytest.mark.parametrize("L,S,chunk", [(256, 1, 0), (256, 4, 0), (200, 7, 0), (65, 3, 0),
+                                       (64, 64, 0), (300, 2, 0), (300, 8, 64), (130, 5, 64)])
+def test_split_merge_equals_unsplit(L, S, chunk):
     rng = np.random.default_rng(L * 31 + S)
     H, dn, dc, dr, Q = 3, 8, 16, 8, 2
     w_uk = rng.standard_normal((H, dn, dc)) / 4
@@ -255,7 +269,7 @@ def test_split_merge_equals_unsplit(L, S):
     c, kr = rng.standard_normal((L, dc)), rng.standard_normal((L, dr))
     qn, qr = rng.standard_normal((Q, H, dn)), rng.standard_normal((Q, H, dr))
     o, ol, lse = oracle.attend_sequence(c, kr, qn, qr, w_uk, w_uv, 0.3)
-    op, lp = oracle.attend_partials(c, kr, qn, qr, w_uk, 0.3, S)
+    op, lp = oracle.attend_partials(c, kr, qn, qr, w_uk, 0.3, S, chunk_tokens=chunk)
     mo, ml = oracle.lse_combine(op, lp)
     np.testing.assert_allclose(mo, ol, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(ml, lse, rtol=1e-13)

@@ -47,6 +47,7 @@ class Workload:
     len_range: Optional[tuple] = None        # inclusive (lo, hi) uniform lengths
     paged: bool = False   # True: one seeded permutation of the page pool
     num_splits: int = 1   # split-KV partitions per sequence used by the bench
+    split_chunk: int = 0  # > 0: every partition holds this many tokens (fixed-size plan)
     page_size: int = PAGE
     rope_base: float = 10000.0
     description: str = ""
