@@ -152,6 +152,32 @@ __device__ __forceinline__ float row_sum4(float v) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// Blocks start in id order, and the partitions of a sequence in the
+// per-sequence plan all hold about L_b / S tokens, so a batch of uneven
+// lengths finishes soonest when its longest sequences start first (the short
+// ones then fill the tail). For batch <= 64 each block ranks the lengths
+// (longest first, ties by index) with one lane per sequence and takes the
+// sequence of rank `rank`; larger batches keep their order. Writes that
+// sequence's length to *len. A partition's result does not depend on which
+// block computes it, so the order changes no output.
+__device__ __forceinline__ int seq_by_rank(const int32_t* __restrict__ seq_lens, int batch,
+                                           int rank, int lane, int* len) {
+  if (batch > 64) {
+    *len = seq_lens[rank];
+    return rank;
+  }
+  const int li = lane < batch ? seq_lens[lane] : 0;
+  int r = 0;
+  for (int j = 0; j < batch; ++j) {
+    const int lj = __builtin_amdgcn_readlane(li, j);
+    r += (lj > li) || (lj == li && j < lane);
+  }
+  const uint64_t hit = __ballot(lane < batch && r == rank);
+  const int b = hit ? __builtin_ctzll(hit) : rank;
+  *len = __builtin_amdgcn_readlane(li, b);
+  return b;
+}
+
 // block id -> (unit, row group): all groups of one unit share id % 8, i.e.
 // run on the same XCD and share its L2
 __device__ __forceinline__ bool map_block(int units, int groups, int* unit, int* grp) {

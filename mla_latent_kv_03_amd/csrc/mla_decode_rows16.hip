@@ -66,15 +66,15 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   extern __shared__ u32x4_t lds[];
   int unit, grp;
   if (!map_block(units, groups, &unit, &grp)) return;
-  const int s = unit % S, b = unit / S;
   const int R = Q * H;
   const int row0 = grp * kRows;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 15, kg = lane >> 4;
   const int sub = wave & 1, khalf = wave >> 1;  // QK share: subtile, half of the columns
-
-  const int L = seq_lens[b];
+  const int s = unit % S;
+  int L;
+  const int b = seq_by_rank(seq_lens, units / S, unit / S, lane, &L);
   const bool bad_len = (L < Q) || (L > max_seq_len);
   int t0 = 0, t1 = 0;
   if (!bad_len) split_range(L, S, page, fixed, s, &t0, &t1);

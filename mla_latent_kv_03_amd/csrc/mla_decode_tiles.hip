@@ -55,14 +55,14 @@ void decode_tiles_kernel(int Q, int H, int S, int page, int fixed, int max_seq_l
   extern __shared__ u32x4_t lds[];
   int unit, grp;
   if (!map_block(units, groups, &unit, &grp)) return;
-  const int s = unit % S, b = unit / S;
   const int R = Q * H;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 15, kg = lane >> 4;
   const int row0 = grp * 64 + wave * 16;
-
-  const int L = seq_lens[b];
+  const int s = unit % S;
+  int L;
+  const int b = seq_by_rank(seq_lens, units / S, unit / S, lane, &L);
   const bool bad_len = (L < Q) || (L > max_seq_len);
   int t0 = 0, t1 = 0;
   if (!bad_len) split_range(L, S, page, fixed, s, &t0, &t1);
