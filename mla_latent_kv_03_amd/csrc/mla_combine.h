@@ -120,15 +120,26 @@ struct CombineCols {
 #pragma unroll
     for (int u = 0; u < CH; ++u) x[u] = op[(size_t)min(u, S - 1) * st];
   }
-  __device__ __forceinline__ void add(const float* w, int s0, float4& a) const {
+  // Adds partitions s0 .. s0+CH-1. Whether a partition counts (inside S,
+  // weight not 0) is the same for every lane of the row, so it is taken from
+  // one ballot and tested as a scalar; a partition of weight 0 may be
+  // unwritten and never reaches the sum.
+  __device__ __forceinline__ void add(const float* w, int s0, float4& a, int lane) const {
+    static_assert(CH <= 64, "one ballot per group");
+    const int sl = s0 + lane % CH;
+    const uint64_t use = __ballot(lane < CH && sl < S && w[min(sl, S - 1)] != 0.0f);
+    float wv[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) wv[u] = w[min(s0 + u, S - 1)];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const float ws = w[min(s0 + u, S - 1)];
-      const bool in = s0 + u < S && ws != 0.0f;
-      a.x = in ? fmaf(ws, x[u].x, a.x) : a.x;
-      a.y = in ? fmaf(ws, x[u].y, a.y) : a.y;
-      a.z = in ? fmaf(ws, x[u].z, a.z) : a.z;
-      a.w = in ? fmaf(ws, x[u].w, a.w) : a.w;
+      if ((use >> u) & 1) {
+        const float ws = wv[u];
+        a.x = fmaf(ws, x[u].x, a.x);
+        a.y = fmaf(ws, x[u].y, a.y);
+        a.z = fmaf(ws, x[u].z, a.z);
+        a.w = fmaf(ws, x[u].w, a.w);
+      }
     }
   }
   // normalized columns (NaN for a bad row). A later group of CH partitions
@@ -136,7 +147,7 @@ struct CombineCols {
   __device__ __forceinline__ float4 finish(const float* w, const CombineWeights& cw, int lane) {
     float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (kOne) {
-      add(w, 0, a);
+      add(w, 0, a, lane);
     } else {
       bool use = true;  // the first group was loaded speculatively in start()
       for (int s0 = 0; s0 < S; s0 += CH) {
@@ -151,7 +162,7 @@ struct CombineCols {
             for (int u = 0; u < CH; ++u) y[u] = op[(size_t)min(s1 + u, S - 1) * st];
           }
         }
-        if (use) add(w, s0, a);
+        if (use) add(w, s0, a, lane);
         if (next) {
 #pragma unroll
           for (int u = 0; u < CH; ++u) x[u] = y[u];
