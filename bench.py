@@ -39,7 +39,7 @@ CSRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc")
 # decode kernel name (mla_decode_kernel_name) -> (kernel symbol, the sources that define it)
 DECODE_KERNELS = {
     "mfma_rows16": ("decode_rows16_kernel", ["mla_decode_common.h", "mla_decode_rows16.hip"]),
-    "mfma_tiles": ("decode_tiles_kernel", ["mla_decode_common.h", "mla_decode_tiles.hip"]),
+    "mfma_ws": ("decode_ws_kernel", ["mla_decode_common.h", "mla_decode_ws.hip"]),
     "generic": ("decode_generic_kernel", ["mla_kernels.hip"]),
 }
 

@@ -114,8 +114,8 @@ int32_t mla_default_num_splits(const mla_config_t* cfg, int32_t batch, int32_t q
                                int32_t max_seq_len, int32_t num_cus);
 
 /* Name of the decode kernel mla_decode_paged takes for this shape. With bf16,
- * d_c = 512 and d_r = 64: "mfma_tiles" (64 query rows per block) when
- * page_size and q_len*H are multiples of 64, else "mfma_rows16" (16 rows per
+ * d_c = 512 and d_r = 64: "mfma_ws" (64 query rows per block) when
+ * page_size is a multiple of 8 and q_len*H a multiple of 64, else "mfma_rows16" (16 rows per
  * block) when q_len*H is a multiple of 16; otherwise "generic". Static
  * string; "invalid" for an invalid config. */
 const char* mla_decode_kernel_name(const mla_config_t* cfg, int32_t q_len);

@@ -153,7 +153,7 @@ def decode_partials_bytes(cfg: Config, batch: int, q_len: int, num_splits: int) 
 
 
 def decode_kernel_kind(cfg: Config, q_len: int) -> str:
-    """Which decode kernel libmla takes for this shape: "mfma_tiles", "mfma_rows16"
+    """Which decode kernel libmla takes for this shape: "mfma_ws", "mfma_rows16"
     or "generic"."""
     return lib().mla_decode_kernel_name(ctypes.byref(cfg.c()), q_len).decode()
 

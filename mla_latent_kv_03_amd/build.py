@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["mla_api.cpp", "mla_kernels.hip", "mla_decode_rows16.hip", "mla_decode_tiles.hip",
+SOURCES = ["mla_api.cpp", "mla_kernels.hip", "mla_decode_rows16.hip", "mla_decode_ws.hip",
            "mla_proj_mfma.hip"]
 
 HIPCC_FLAGS = [

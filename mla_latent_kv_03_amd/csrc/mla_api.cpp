@@ -213,7 +213,7 @@ const char* mla_decode_kernel_name(const mla_config_t* cfg, int32_t q_len) {
   if (check_config(cfg) != MLA_OK || q_len < 1) return "invalid";
   switch (mla::decode_kernel_kind(shape_of(cfg), q_len)) {
     case 2:
-      return "mfma_tiles";
+      return "mfma_ws";
     case 1:
       return "mfma_rows16";
     default:

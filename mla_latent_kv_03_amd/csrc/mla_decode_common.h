@@ -1,5 +1,5 @@
 // Device building blocks shared by the two bf16 MFMA decode kernels
-// (decode_rows16_kernel, decode_tiles_kernel) for the DeepSeek MLA row shape:
+// (decode_rows16_kernel, decode_ws_kernel) for the DeepSeek MLA row shape:
 // d_c = 512 latent + d_r = 64 RoPE columns, 576 bf16 = 1,152 bytes per cached
 // row ("The Architecture of Memory", "Flash-Decoding and FlashInfer";
 // "DeepSeek's Config Says 16 KV Heads", section 5).

@@ -280,17 +280,17 @@ int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, i
                          const void* q_full, const void* cache, int64_t num_pages,
                          const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                          float* o_part, float* lse_part, void* stream);
-bool decode_tiles_ok(const Shape& s, int q_len);
-int launch_decode_tiles(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
-                        const void* q_full, const void* cache, int64_t num_pages,
-                        const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                        float* o_part, float* lse_part, void* stream);
+bool decode_ws_ok(const Shape& s, int q_len);
+int launch_decode_ws(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
+                     const void* q_full, const void* cache, int64_t num_pages,
+                     const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                     float* o_part, float* lse_part, void* stream);
 
 // bf16 MFMA kernels for the 576-wide DeepSeek row: 64 query rows per block
-// when the row count and page size allow it, else 16; everything else takes
-// the generic kernel
+// (specialised QK and PV waves) when the row count and page size allow it,
+// else 16; everything else takes the generic kernel
 int decode_kernel_kind(const Shape& s, int q_len) {
-  if (decode_tiles_ok(s, q_len)) return 2;
+  if (decode_ws_ok(s, q_len)) return 2;
   if (decode_rows16_ok(s, q_len)) return 1;
   return 0;
 }
@@ -301,9 +301,8 @@ int launch_decode(const Shape& s, int batch, int q_len, int num_splits, int max_
                   float* o_part, float* lse_part, void* stream) {
   switch (decode_kernel_kind(s, q_len)) {
     case 2:
-      return launch_decode_tiles(s, batch, q_len, num_splits, max_seq_len, q_full, cache,
-                                 num_pages, page_table, max_pages, seq_lens, o_part, lse_part,
-                                 stream);
+      return launch_decode_ws(s, batch, q_len, num_splits, max_seq_len, q_full, cache, num_pages,
+                              page_table, max_pages, seq_lens, o_part, lse_part, stream);
     case 1:
       return launch_decode_rows16(s, batch, q_len, num_splits, max_seq_len, q_full, cache,
                                   num_pages, page_table, max_pages, seq_lens, o_part, lse_part,

@@ -111,8 +111,9 @@ def test_partials_bytes_and_default_splits(L):
 
 def test_decode_kernel_selection(L):
     assert mla.decode_kernel_kind(V2, 1) == "mfma_rows16"
-    assert mla.decode_kernel_kind(mla.Config(num_heads=128), 4) == "mfma_tiles"
-    assert mla.decode_kernel_kind(mla.Config(num_heads=128, page_size=32), 1) == "mfma_rows16"
+    assert mla.decode_kernel_kind(mla.Config(num_heads=128), 4) == "mfma_ws"
+    assert mla.decode_kernel_kind(mla.Config(num_heads=128, page_size=16), 1) == "mfma_ws"
+    assert mla.decode_kernel_kind(mla.Config(num_heads=48), 1) == "mfma_rows16"  # 48 rows
     assert mla.decode_kernel_kind(TINY, 1) == "generic"
     assert mla.decode_kernel_kind(mla.Config(num_heads=4), 1) == "generic"  # 4 rows < 16
 

@@ -340,8 +340,8 @@ def test_edge_lengths(lens, Q):
 @pytest.mark.parametrize("heads,Q", [(16, 1), (16, 2), (128, 1)])
 def test_page_sizes(page, heads, Q):
     # 5 partitions: with 16-token pages the 803-token sequence gets 176-token
-    # partitions, whose bounds fall inside 32-token tiles; with 16/32-token
-    # pages a 64-row block shape takes the 16-row kernel
+    # partitions, whose bounds fall inside 32-token tiles (both bf16 MFMA
+    # kernels copy 8-row pieces, so a piece never crosses a page)
     wl = small("v2lite_paged_varlen", batch=3, q_len=Q, heads=heads, len_range=(30, 1000),
                num_splits=5, page_size=page)
     case = Case(wl, seed=11)
