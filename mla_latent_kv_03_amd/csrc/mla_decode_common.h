@@ -83,13 +83,24 @@ struct RowDma {
   // address of chunk part_chunk
   __device__ __forceinline__ void issue(const void* src, uint32_t lds_base) const {
 #pragma unroll
-    for (int i = 0; i < N; ++i)
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-                   :
-                   : "s"(lds_base + i * 1024), "v"(off[i]), "s"(src)
-                   : "memory");
+    for (int i = 0; i < N; ++i) issue_one(src, lds_base, i);
+  }
+  // load i alone (i a compile-time constant after unrolling)
+  __device__ __forceinline__ void issue_one(const void* src, uint32_t lds_base, int i) const {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(lds_base + i * 1024), "v"(off[i]), "s"(src)
+                 : "memory");
   }
 };
+
+// ds_read_b64_tr_b16 (gfx950): in each group of 16 lanes, lane 4 a + b
+// receives 16-bit element b of the 8 bytes addressed by lanes a, a + 4,
+// a + 8 and a + 12 of its group, in that order (layout checked on the device)
+__device__ __forceinline__ s16x4_t ds_read_tr16(uint32_t lds_byte_addr) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)lds_byte_addr);
+}
 
 // Make the compiler complete the loads behind v here (it then has no loads of
 // its own pending when the token loop starts, where its waits would also

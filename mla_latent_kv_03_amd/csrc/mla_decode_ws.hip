@@ -9,13 +9,15 @@
 // with different jobs whose LDS reads and MFMAs interleave:
 //
 //   QK wave (0..3)   rows [32 rh, 32 rh + 32), tokens [16 u, 16 u + 16) of
-//                    each 32-token tile (rh = w & 1, u = w >> 1): also copies
-//                    rows [8 w, 8 w + 8) of every tile into LDS (direct-to-LDS
-//                    loads); holds its 32 query rows in registers and scores
-//                    its 16 tokens over all 576 columns (18 k-steps x 2 row
-//                    groups of v_mfma_f32_16x16x32_bf16, one LDS read per
-//                    k-step serving both row groups); leaves the fp32 scores
-//                    in LDS
+//                    each 32-token tile (rh = w & 1, u = w >> 1): holds its 32
+//                    query rows in registers and scores its 16 tokens over all
+//                    576 columns (18 k-steps x 2 row groups of
+//                    v_mfma_f32_16x16x32_bf16, one LDS read per k-step serving
+//                    both row groups, read 6 k-steps ahead); leaves the fp32
+//                    scores in LDS. It also copies rows [8 w, 8 w + 8) of
+//                    every tile into LDS (direct-to-LDS loads), one load after
+//                    every second k-step of the scores two tiles earlier, so
+//                    the load issue overlaps the MFMAs
 //   PV wave (4..7)   rows [32 rh, 32 rh + 32), latent columns [256 fh,
 //                    256 fh + 256) (rh = w & 1, fh = w >> 1): reads the scores
 //                    of its rows, runs the online softmax (row max with two
@@ -23,8 +25,8 @@
 //                    exceeds it by more than 2^8, so the accumulator rescale
 //                    almost never runs) and adds P.C (K = 32 tokens: P goes
 //                    from the score layout straight into the A operand; the B
-//                    operand gathers 4 columns of 8 token rows with
-//                    ds_read_b64 and transposes them in registers, and serves
+//                    operand, 8 tokens of one column per lane, comes from two
+//                    transposing LDS reads, ds_read_b64_tr_b16, and serves
 //                    both row groups)
 //
 // Per tile the block reads 72 KB of cache operands for the scores, 64 KB for
@@ -132,21 +134,43 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
       for (int ks = 0; ks < kKSteps; ++ks) settle(qreg[rg][ks]);  // (also lands tiles 0..2)
     const int arow = (16 * u + n) * kChunks;  // A operand: token 16 u + n of the tile
 
-    // scores of tokens [16 u, 16 u + 16) of tile k for the wave's 32 rows
-    auto qk = [&](int k) {
+    // scores of tokens [16 u, 16 u + 16) of tile k for the wave's 32 rows;
+    // kiss >= 0: the copy of this wave's rows of tile kiss is issued between
+    // the MFMAs (load i after k-step 2 i + 1)
+    auto qk = [&](int k, int kiss) {
       const u32x4_t* buf = slot(k) + arow;
+      constexpr int kAhead = 6;  // k-steps of A operand in flight
       u32x4_t a[kKSteps];
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) a[ks] = buf[(4 * ks + kg) ^ (n & 7)];
+      for (int ks = 0; ks < kAhead; ++ks) a[ks] = buf[(4 * ks + kg) ^ (n & 7)];
+      const bf16_t* isrc = cache;
+      uint32_t ilds = 0;
+      if (kiss >= 0) {
+        const int t = t0 + kiss * kWT + w4 * kWPartRows;
+        int pg = pw.get((t - t0) / page, lane);
+        if (pg < 0 || (int64_t)pg >= num_pages) {
+          bad = true;
+          pg = 0;
+        }
+        isrc = cache + ((size_t)pg * page + (t % page)) * kD;
+        ilds = __builtin_amdgcn_readfirstlane(lds_addr(slot(kiss) + w4 * kWPartChunks));
+      }
       f32x4_t c[2][2];
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg) c[rg][0] = c[rg][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks)
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        if (ks + kAhead < kKSteps) a[ks + kAhead] = buf[(4 * (ks + kAhead) + kg) ^ (n & 7)];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg)
           c[rg][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8_t, a[ks]), qreg[rg][ks], c[rg][ks & 1], 0, 0, 0);
+        if ((ks & 1) && kiss >= 0) {  // keep each load between its MFMAs
+          __builtin_amdgcn_sched_barrier(0);
+          dma.issue_one(isrc, ilds, ks >> 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       f32x4_t* dst = sbuf + (k & 1) * kWScoreVecs + (rh * 2 + u) * 128 + lane;
       dst[0] = c[0][0] + c[0][1];
       dst[64] = c[1][0] + c[1][1];
@@ -163,7 +187,7 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
         zero_rows<kWPartLoads>(slot(0) + w4 * kWPartChunks, w4 * kWPartChunks, lane, t1 - t0);
     }
     __syncthreads();  // tile 0 landed
-    if (ntiles > 0) qk(0);
+    if (ntiles > 0) qk(0, -1);
     for (int k = 0; k < ntiles; ++k) {
       if (k + 1 < ntiles) {  // own part of tile k+1 (tile k+2 may stay in flight)
         if (k + 2 < ntiles)
@@ -178,8 +202,7 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
       // tile k+1 landed; the scores of tile k are handed over; slot k-1
       // (= k+3) and score buffer k+1 are no longer read
       __syncthreads();
-      if (k + 3 < ntiles) issue(k + 3);
-      if (k + 1 < ntiles) qk(k + 1);
+      if (k + 1 < ntiles) qk(k + 1, k + 3 < ntiles ? k + 3 : -1);
     }
     wait_vmcnt<0>();
     if (lane == 0) flags[w4] = bad ? 1 : 0;
@@ -189,12 +212,28 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
 
   // ======================== PV waves ========================
   const int fh = w4 >> 1;
-  int pv[8];  // byte offsets: token rows sigma(kg, j), columns 256 fh + 4 n .. + 3
+  // B operand of P.C for columns c0 .. c0 + 15 (lane n: column c0 + n; tokens
+  // sigma(kg, j), the order of P in the A operand): in each 16-lane group a
+  // transposing read hands lane 4a + b element b of the 8 bytes that lanes
+  // a, a + 4, a + 8, a + 12 address, so lane s = a + 4 i of group kg reads
+  // token 16 h + 4 kg + i, columns c0 + 4 a .. + 3. pvt[h][m]: byte offset for
+  // half h and c0 = 256 fh + 16 m (+ 64 fb: + 128 bytes, within the swizzle)
+  int pvt[2][4];
+  {
+    const int a = n & 3, i = n >> 2;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int t = (j < 4) ? 4 * kg + j : 16 + 4 * kg + (j - 4);
-    pv[j] = 16 * (t * kChunks + ((32 * fh + (n >> 1)) ^ (t & 7))) + 8 * (n & 1);
+    for (int h = 0; h < 2; ++h) {
+      const int t = 16 * h + 4 * kg + i;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        pvt[h][m] = 16 * (t * kChunks + 32 * fh + ((2 * m + (a >> 1)) ^ (t & 7))) + 8 * (a & 1);
+    }
   }
+  auto bop = [&](uint32_t tbase, int fb, int m) {
+    const s16x4_t lo = ds_read_tr16(tbase + pvt[0][m] + fb * 128);
+    const s16x4_t hi = ds_read_tr16(tbase + pvt[1][m] + fb * 128);
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   f32x4_t acc[2][kFB / 2][4];
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg)
@@ -210,10 +249,10 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   __syncthreads();  // tile 0 landed
   for (int k = 0; k < ntiles; ++k) {
     __syncthreads();  // scores of tile k handed over
-    const char* tb = reinterpret_cast<const char*>(slot(k));
-    u32x2_t xa[8], xn[8];
+    const uint32_t tbase = lds_addr(slot(k));
+    bf16x8_t bcur[4], bnxt[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = *reinterpret_cast<const u32x2_t*>(tb + pv[j]);
+    for (int m = 0; m < 4; ++m) bcur[m] = bop(tbase, 0, m);
 
     // ---- online softmax of both row groups (lane: row n, tokens sigma(kg, j))
     const int ts = t0 + k * kWT;
@@ -271,25 +310,16 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
     for (int fb = 0; fb < kFB / 2; ++fb) {
       if (fb + 1 < kFB / 2) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          xn[j] = *reinterpret_cast<const u32x2_t*>(tb + pv[j] + (fb + 1) * 128);
-      }
-      u32x4_t bm[4];
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        bm[0][q2] = pack_lo(xa[2 * q2].x, xa[2 * q2 + 1].x);
-        bm[1][q2] = pack_hi(xa[2 * q2].x, xa[2 * q2 + 1].x);
-        bm[2][q2] = pack_lo(xa[2 * q2].y, xa[2 * q2 + 1].y);
-        bm[3][q2] = pack_hi(xa[2 * q2].y, xa[2 * q2 + 1].y);
+        for (int m = 0; m < 4; ++m) bnxt[m] = bop(tbase, fb + 1, m);
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg)
-          acc[rg][fb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              pa[rg], __builtin_bit_cast(bf16x8_t, bm[m]), acc[rg][fb][m], 0, 0, 0);
+          acc[rg][fb][m] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[rg], bcur[m], acc[rg][fb][m], 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) xa[j] = xn[j];
+      for (int m = 0; m < 4; ++m) bcur[m] = bnxt[m];
     }
   }
   __syncthreads();  // flags handed over
@@ -309,16 +339,14 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
         inv[r] = lr > 0.0f ? 1.0f / lr : 0.0f;
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; ++r) {  // row 4 kg + r, column 256 fh + 64 fb + 16 m + n
         const int orow = row0 + 16 * rg + 4 * kg + r;
-        float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + 256 * fh + 4 * n;
+        float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + 256 * fh + n;
 #pragma unroll
-        for (int fb = 0; fb < kFB / 2; ++fb) {
-          float4 v = make_float4(acc[rg][fb][0][r] * inv[r], acc[rg][fb][1][r] * inv[r],
-                                 acc[rg][fb][2][r] * inv[r], acc[rg][fb][3][r] * inv[r]);
-          if (any_bad) v = make_float4(nanv, nanv, nanv, nanv);
-          *reinterpret_cast<float4*>(dst + fb * 64) = v;
-        }
+        for (int fb = 0; fb < kFB / 2; ++fb)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            dst[64 * fb + 16 * m] = any_bad ? nanv : acc[rg][fb][m][r] * inv[r];
       }
     }
   }

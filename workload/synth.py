@@ -93,7 +93,7 @@ WORKLOADS: Dict[str, Workload] = {
                  description="V2-Lite shape, B=32, L~U[1024,32768], permuted 64-token pages"),
         Workload("v2_h128_8k", batch=64, q_len=1, heads=128, kv_rank=512, rope_dim=64,
                  nope_dim=128, v_dim=128, dtype="bf16", seq_len=8192, paged=True,
-                 num_splits=4,
+                 num_splits=2,
                  description="DeepSeek-V2 head count, B=64, L=8192, permuted pages"),
         Workload("v2_h128_1m_q4", batch=1, q_len=4, heads=128, kv_rank=512, rope_dim=64,
                  nope_dim=128, v_dim=128, dtype="bf16", seq_len=1048576, num_splits=256,
