@@ -11,6 +11,10 @@ from .mla_ref import (  # noqa: F401
     rope,
     expand_kv,
     query_positions,
+    tree_depths,
+    tree_ancestry,
+    tree_positions,
+    tree_excluded,
     attend_scores,
     attend_sequence,
     mla_decode_ref,

@@ -10,6 +10,12 @@ token t rotated by t, the positional query is q_rope rotated by p; the score is
 scale times the sum of both dot products ("Beyond the Attention Bottleneck",
 "Down-Projection and Up-Projection Mechanics" and "The RoPE Compatibility
 Problem"). Softmax over t, then the weighted sum of V_t = W_UV[h] c_t.
+
+With a drafted tree (``parents``, "The Architecture of Memory", "Tree
+Attention Verification"), query j sees every prefix token and the drafted
+tokens met by following parent links up from j; a drafted token's position,
+for its key and its query, is L - Q plus the number of parent links from it
+to the prefix.
 """
 import math
 
@@ -37,21 +43,51 @@ def _matvec(m, v):
     return [_dot(row, v) for row in m]
 
 
-def brute_sequence(c, k_rope, q_nope, q_rope, w_uk, w_uv, scale, base=10000.0):
+def _links_to_prefix(parents, i):
+    n = 0
+    while parents[i] != -1:
+        i = parents[i]
+        n += 1
+    return n
+
+
+def _on_branch(parents, j, i):
+    k = j
+    while k != -1:
+        if k == i:
+            return True
+        k = parents[k]
+    return False
+
+
+def brute_sequence(c, k_rope, q_nope, q_rope, w_uk, w_uv, scale, base=10000.0, parents=None):
     """Nested lists in, nested lists out: (o [Q][H][d_v], o_lat [Q][H][d_c], lse [Q][H])."""
     L = len(c)
     Q = len(q_nope)
     H = len(w_uk)
+    pre = L - Q
+
+    def key_pos(t):
+        if parents is None or t < pre:
+            return t
+        return pre + _links_to_prefix(parents, t - pre)
+
+    def sees(j, t):
+        if parents is None:
+            return t <= pre + j
+        return t < pre or _on_branch(parents, j, t - pre)
+
     o, o_lat, lse = [], [], []
     for j in range(Q):
-        p = L - Q + j
+        p = pre + j if parents is None else pre + _links_to_prefix(parents, j)
+        vis = [t for t in range(L) if sees(j, t)]
         oj, olj, lj = [], [], []
         for h in range(H):
             q_pe = _rotate(q_rope[j][h], p, base)
             scores = []
-            for t in range(p + 1):
+            for t in vis:
                 k_c = _matvec(w_uk[h], c[t])
-                k_r = _rotate(k_rope[t], t, base)
+                k_r = _rotate(k_rope[t], key_pos(t), base)
                 scores.append(scale * (_dot(q_nope[j][h], k_c) + _dot(q_pe, k_r)))
             m = max(scores)
             ex = [math.exp(s - m) for s in scores]
@@ -59,8 +95,8 @@ def brute_sequence(c, k_rope, q_nope, q_rope, w_uk, w_uv, scale, base=10000.0):
             dv = len(w_uv[h])
             acc = [0.0] * dv
             acc_lat = [0.0] * len(c[0])
-            for t in range(p + 1):
-                w = ex[t] / z
+            for k, t in enumerate(vis):
+                w = ex[k] / z
                 v_t = _matvec(w_uv[h], c[t])
                 for i in range(dv):
                     acc[i] += w * v_t[i]

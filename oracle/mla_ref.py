@@ -23,6 +23,14 @@ What it computes, and where the pages define it:
   Wall"); several drafted tokens are verified in one pass and must agree with
   token-by-token decoding ("The Architecture of Memory", "Speculative
   Decoding: Amortizing the Memory Fetch").
+* Tree verification: the drafted tokens form a tree whose branches must not
+  see each other; the query of a drafted token attends to the whole prefix
+  with no mask and to the drafted tokens on its own branch under a causal
+  tree mask ("The Architecture of Memory", "Tree Attention Verification").
+  Reading: a drafted token attached to the prefix sits at position
+  L - Q, a child one position after its parent (position = L - Q + depth),
+  for its query and its cached RoPE key alike, so that every branch is scored
+  exactly as the chain of its tokens decoded one by one would be.
 * Split-KV partials merged by a log-sum-exp reduction ("The Architecture of
   Memory", "Flash-Decoding and FlashInfer").
 * Paged cache: fixed-size pages mapped logical -> physical through a page
@@ -145,6 +153,55 @@ def query_positions(seq_len: int, q_len: int) -> np.ndarray:
     return seq_len - q_len + np.arange(q_len)
 
 
+def tree_depths(parents) -> np.ndarray:
+    """Depth of each drafted token: 0 when its parent is -1 (attached to the
+    prefix), else one more than its parent's. Parents precede their children."""
+    parents = [int(p) for p in parents]
+    depth = np.zeros(len(parents), dtype=np.int64)
+    for j, p in enumerate(parents):
+        if not -1 <= p < j:
+            raise ValueError(f"drafted token {j} has parent {p}: parents must precede children")
+        depth[j] = 0 if p < 0 else depth[p] + 1
+    return depth
+
+
+def tree_ancestry(parents) -> np.ndarray:
+    """[Q][Q] bool: entry (j, i) is True when drafted token i is j itself or one
+    of its ancestors, i.e. when i lies on j's branch ("Tree Attention
+    Verification": independent branches do not attend to one another)."""
+    Q = len(parents)
+    tree_depths(parents)  # validates the order
+    anc = np.zeros((Q, Q), dtype=bool)
+    for j in range(Q):
+        i = j
+        while i >= 0:
+            anc[j, i] = True
+            i = int(parents[i])
+    return anc
+
+
+def tree_positions(seq_len: int, parents):
+    """(key positions [L], query positions [Q]) with a drafted tree: prefix
+    token t keeps position t, drafted token i (cached at slot L - Q + i) and
+    its query sit at L - Q + depth(i)."""
+    Q = len(parents)
+    pre = seq_len - Q
+    d = tree_depths(parents)
+    kp = np.arange(seq_len, dtype=np.int64)
+    kp[pre:] = pre + d
+    return kp, pre + d
+
+
+def tree_excluded(seq_len: int, parents) -> np.ndarray:
+    """[Q][L] True where key t is hidden from query j: a drafted token off j's
+    branch. The prefix is visible to every query."""
+    Q = len(parents)
+    pre = seq_len - Q
+    out = np.zeros((Q, seq_len), dtype=bool)
+    out[:, pre:] = ~tree_ancestry(parents)
+    return out
+
+
 def causal_mask(seq_len: int, pq) -> np.ndarray:
     """[Q][L] True where key t lies after query position p_j (excluded).
 
@@ -156,29 +213,38 @@ def causal_mask(seq_len: int, pq) -> np.ndarray:
 
 
 def attend_scores(c, k_rope_raw, q_nope, q_rope, w_uk, scale, base=10000.0,
-                  chunk: int = 1024) -> np.ndarray:
-    """Masked scores s[j][h][t] = scale * (q_j,h . K_t,h); -inf where t > p_j."""
+                  chunk: int = 1024, parents=None) -> np.ndarray:
+    """Masked scores s[j][h][t] = scale * (q_j,h . K_t,h); -inf where t > p_j.
+
+    With ``parents`` (the drafted tree, [Q] ints) the positions and the mask
+    are the tree's: tree_positions and tree_excluded.
+    """
     c = np.asarray(c, F64)
     L = c.shape[0]
     q_nope = np.asarray(q_nope, F64)
     Q, H, _ = q_nope.shape
-    pq = query_positions(L, Q)
+    if parents is None:
+        pq = query_positions(L, Q)
+        kpos = np.arange(L)
+        masked = causal_mask(L, pq)                                      # [Q][L]
+    else:
+        kpos, pq = tree_positions(L, parents)
+        masked = tree_excluded(L, parents)
     q = np.concatenate([q_nope, rope(q_rope, pq[:, None], base)], axis=-1)  # [Q][H][dk]
     qh = np.ascontiguousarray(q.transpose(1, 0, 2))                      # [H][Q][dk]
     s = np.empty((H, Q, L), F64)
     for t0 in range(0, L, chunk):
         t1 = min(L, t0 + chunk)
-        k, _ = expand_kv(c[t0:t1], k_rope_raw[t0:t1], np.arange(t0, t1), w_uk, None, base)
+        k, _ = expand_kv(c[t0:t1], k_rope_raw[t0:t1], kpos[t0:t1], w_uk, None, base)
         s[:, :, t0:t1] = np.matmul(qh, np.ascontiguousarray(k.transpose(1, 2, 0)))
     s *= scale
     s = s.transpose(1, 0, 2).copy()                                      # [Q][H][L]
-    masked = causal_mask(L, pq)                                          # [Q][L]
     s[np.broadcast_to(masked[:, None, :], s.shape)] = -np.inf
     return s
 
 
 def attend_sequence(c, k_rope_raw, q_nope, q_rope, w_uk, w_uv, scale,
-                    base: float = 10000.0, chunk: int = 1024):
+                    base: float = 10000.0, chunk: int = 1024, parents=None):
     """Decode attention of one sequence, without absorption.
 
     c [L][d_c], k_rope_raw [L][d_r] (unrotated, positions 0..L-1),
@@ -186,10 +252,11 @@ def attend_sequence(c, k_rope_raw, q_nope, q_rope, w_uk, w_uv, scale,
     w_uv [H][d_v][d_c]. Textbook softmax: m = max s, p = e^(s-m) / sum e^(s-m).
     Returns o [Q][H][d_v] = sum_t p_t V_t,h, o_lat [Q][H][d_c] = sum_t p_t c_t
     (the same weights applied to the latents) and lse [Q][H] = m + ln sum e^(s-m).
+    ``parents``: the drafted tokens form this tree instead of a chain.
     """
     c = np.asarray(c, F64)
     L = c.shape[0]
-    s = attend_scores(c, k_rope_raw, q_nope, q_rope, w_uk, scale, base, chunk)
+    s = attend_scores(c, k_rope_raw, q_nope, q_rope, w_uk, scale, base, chunk, parents=parents)
     m = s.max(axis=-1, keepdims=True)
     e = np.exp(s - m)
     den = e.sum(axis=-1, keepdims=True)
@@ -216,7 +283,8 @@ def mla_decode_ref(inputs, heads: Optional[Sequence[int]] = None,
 
     Returns dict(o [B][Q][H'][d_v], o_lat [B][Q][H'][d_c], lse [B][Q][H']) for
     the selected heads (all by default) and sequences (all by default; rows of
-    unselected sequences are NaN).
+    unselected sequences are NaN). A workload with a drafted tree
+    (``inputs.parents``) is verified under that tree.
     """
     wl = inputs.wl
     hs = list(range(wl.heads)) if heads is None else list(heads)
@@ -229,8 +297,10 @@ def mla_decode_ref(inputs, heads: Optional[Sequence[int]] = None,
     w_uv = np.asarray(inputs.w_uv, F64)[hs]
     for b in bs:
         c, kr = inputs.seq(b)
+        par = None if getattr(inputs, "parents", None) is None else inputs.parents[b]
         ob, olb, lb = attend_sequence(c, kr, inputs.q_nope[b][:, hs], inputs.q_rope[b][:, hs],
-                                      w_uk, w_uv, wl.softmax_scale, wl.rope_base, chunk)
+                                      w_uk, w_uv, wl.softmax_scale, wl.rope_base, chunk,
+                                      parents=par)
         o[b], o_lat[b], lse[b] = ob, olb, lb
     return {"o": o, "o_lat": o_lat, "lse": lse}
 
@@ -257,7 +327,7 @@ def absorbed_query(q_nope, q_rope, w_uk, pos, base: float = 10000.0) -> np.ndarr
 
 
 def absorbed_attend_sequence(c, k_rope_raw, q_nope, q_rope, w_uk, w_uv, scale,
-                             base: float = 10000.0):
+                             base: float = 10000.0, parents=None):
     """The same attention scored in latent space and up-projected at the end.
 
     s = scale * (q_lat . c_t + q_pe . RoPE(k^R_t, t)), o = W_UV (sum_t p_t c_t).
@@ -266,11 +336,16 @@ def absorbed_attend_sequence(c, k_rope_raw, q_nope, q_rope, w_uk, w_uv, scale,
     c = np.asarray(c, F64)
     L = c.shape[0]
     Q = np.asarray(q_nope).shape[0]
-    pq = query_positions(L, Q)
+    if parents is None:
+        pq, kpos = query_positions(L, Q), np.arange(L)
+        masked = causal_mask(L, pq)
+    else:
+        kpos, pq = tree_positions(L, parents)
+        masked = tree_excluded(L, parents)
     qf = absorbed_query(q_nope, q_rope, w_uk, pq, base)                     # [Q][H][D]
-    kf = np.concatenate([c, rope(k_rope_raw, np.arange(L), base)], axis=-1)  # [L][D]
+    kf = np.concatenate([c, rope(k_rope_raw, kpos, base)], axis=-1)         # [L][D]
     s = scale * np.einsum("qhd,td->qht", qf, kf)
-    s[np.broadcast_to(causal_mask(L, pq)[:, None, :], s.shape)] = -np.inf
+    s[np.broadcast_to(masked[:, None, :], s.shape)] = -np.inf
     m = s.max(-1, keepdims=True)
     e = np.exp(s - m)
     den = e.sum(-1, keepdims=True)
@@ -303,7 +378,8 @@ def split_bounds(seq_len: int, num_splits: int, page: int = 64,
 
 
 def attend_partials(c, k_rope_raw, q_nope, q_rope, w_uk, scale, num_splits,
-                    base: float = 10000.0, page: int = 64, chunk_tokens: int = 0):
+                    base: float = 10000.0, page: int = 64, chunk_tokens: int = 0,
+                    parents=None):
     """Per-split normalised partials of the latent output.
 
     For unit s over tokens [a, e): o_s = sum_t e^(s_t - m_s) c_t / sum_t e^(s_t - m_s)
@@ -313,7 +389,8 @@ def attend_partials(c, k_rope_raw, q_nope, q_rope, w_uk, scale, num_splits,
     """
     c = np.asarray(c, F64)
     L = c.shape[0]
-    s = attend_scores(c, k_rope_raw, q_nope, q_rope, w_uk, scale, base)  # [Q][H][L]
+    s = attend_scores(c, k_rope_raw, q_nope, q_rope, w_uk, scale, base,
+                      parents=parents)                                   # [Q][H][L]
     Q, H = s.shape[:2]
     o_part = np.zeros((Q, H, num_splits, c.shape[1]), F64)
     lse_part = np.full((Q, H, num_splits), -np.inf, F64)

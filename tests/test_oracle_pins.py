@@ -427,8 +427,8 @@ def test_planted_mistakes_are_caught(monkeypatch, target, mutant):
 def test_planted_scale_and_mask_mistakes_are_caught(monkeypatch):
     orig = mla_ref.attend_scores
 
-    def no_scale(c, kr, qn, qr, w_uk, scale, base=10000.0, chunk=1024):
-        return orig(c, kr, qn, qr, w_uk, 1.0, base, chunk)
+    def no_scale(c, kr, qn, qr, w_uk, scale, base=10000.0, chunk=1024, parents=None):
+        return orig(c, kr, qn, qr, w_uk, 1.0, base, chunk, parents=parents)
 
     monkeypatch.setattr(mla_ref, "attend_scores", no_scale)
     assert not _battery()

@@ -29,7 +29,7 @@ import numpy as np
 PAGE = 64
 
 # stream tags: one independent generator per tensor (and per sequence)
-_T_LENS, _T_WUK, _T_WUV, _T_QN, _T_QR, _T_C, _T_KR, _T_PERM = range(8)
+_T_LENS, _T_WUK, _T_WUV, _T_QN, _T_QR, _T_C, _T_KR, _T_PERM, _T_TREE = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -50,6 +50,10 @@ class Workload:
     split_chunk: int = 0  # > 0: every partition holds this many tokens (fixed-size plan)
     page_size: int = PAGE
     rope_base: float = 10000.0
+    # drafted tokens (the last q_len of each sequence): None = a chain; a
+    # tuple = that parent array for every sequence; "random" = a seeded
+    # random tree per sequence (parent of token j uniform in [-1, j-1])
+    tree: object = None
     description: str = ""
 
     @property
@@ -148,6 +152,23 @@ def seq_latents(wl: Workload, seed: int, b: int, length: int):
     return c, kr
 
 
+def tree_parents(wl: Workload, seed: int = 0) -> Optional[np.ndarray]:
+    """[B][Q] int32 parent of each drafted token (-1: attached to the prefix),
+    or None for a chain. Parents always precede their children."""
+    if wl.tree is None:
+        return None
+    Q = wl.q_len
+    if wl.tree == "random":
+        out = np.empty((wl.batch, Q), dtype=np.int32)
+        for b in range(wl.batch):
+            rng = _rng(seed, _T_TREE, b)
+            out[b] = [-1] + [int(rng.integers(-1, j, endpoint=False)) for j in range(1, Q)]
+        return out
+    par = np.asarray(wl.tree, dtype=np.int32)
+    assert par.shape == (Q,) and all(-1 <= int(p) < j for j, p in enumerate(par))
+    return np.broadcast_to(par, (wl.batch, Q)).copy()
+
+
 def page_table_for(wl: Workload, seq_lens: np.ndarray, seed: int = 0):
     """Logical->physical page map [B][max_pages] (-1 = unused) and pool size.
 
@@ -181,6 +202,7 @@ class Inputs:
     num_pages: int
     c: Optional[np.ndarray] = None        # [sum L_b][d_c]
     k_rope: Optional[np.ndarray] = None   # [sum L_b][d_r], unrotated
+    parents: Optional[np.ndarray] = None  # int32 [B][Q] drafted tree (None: chain)
 
     def seq(self, b: int):
         """Latents and unrotated RoPE keys of sequence b (views or fresh draws)."""
@@ -209,7 +231,8 @@ def make(wl: Workload, seed: int = 0, with_latents: bool = True,
     offsets = np.zeros(wl.batch + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(lens.astype(np.int64))
     pt, total = page_table_for(wl, lens, seed)
-    inp = Inputs(wl, seed, lens, offsets, w_uk, w_uv, q_nope, q_rope, pt, total)
+    inp = Inputs(wl, seed, lens, offsets, w_uk, w_uv, q_nope, q_rope, pt, total,
+                 parents=tree_parents(wl, seed))
     if with_latents:
         T = int(offsets[-1])
         fdt = np.float32
