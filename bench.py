@@ -34,7 +34,7 @@ METRIC = "MLA decode latent-cache GB/s (% of HBM peak) + decode tokens/s, V2-Lit
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LAYERS = {"v2lite_32k": 27, "v2lite_paged_varlen": 27, "v2_h128_8k": 4, "v2_h128_1m_q4": 2,
-          "tiny_f32": 4}
+          "v2lite_32k_tree8": 27, "tiny_f32": 4}
 CSRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc")
 # decode kernel name (mla_decode_kernel_name) -> (kernel symbol, the sources that define it)
 DECODE_KERNELS = {
@@ -138,7 +138,7 @@ def main():
 
     import workload
     import mla_latent_kv_03_amd as mla
-    from mla_latent_kv_03_amd.pipeline import DecodeStep, fill_cache, upload
+    from mla_latent_kv_03_amd.pipeline import DecodeStep, fill_cache, token_rope_positions, upload
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -165,16 +165,20 @@ def main():
     pool0 = torch.full((inp.num_pages, wl.page_size, wl.dim), float("nan"), dtype=dt, device="cuda")
     si = np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(inp.seq_lens)])
     pos = np.concatenate([np.arange(int(L), dtype=np.int32) for L in inp.seq_lens])
+    rope_pos = None
+    if inp.parents is not None:  # a drafted tree: its keys sit at prefix + depth
+        rope_pos = upload(np.asarray(token_rope_positions(inp.seq_lens, wl.q_len, inp.parents),
+                                     np.int32), torch.int32)
     fill_cache(cfg, pool0, pt, upload(inp.c, dt), upload(inp.k_rope, dt), upload(si, torch.int32),
-               upload(pos, torch.int32))
+               upload(pos, torch.int32), rope_pos=rope_pos)
     pools = [pool0] + [pool0.clone() for _ in range(n_layers - 1)]
     q_nope, q_rope = upload(inp.q_nope, dt), upload(inp.q_rope, dt)
     w_uk, w_uv = upload(inp.w_uk, dt), upload(inp.w_uv, dt)
     rows = np.concatenate([inp.offsets[b] + np.arange(int(L) - Q, int(L))
                            for b, L in enumerate(inp.seq_lens)])
     c_new, k_new = upload(inp.c[rows], dt), upload(inp.k_rope[rows], dt)
-    steps = [DecodeStep(cfg, B, Q, wl.num_splits, inp.seq_lens, split_chunk=wl.split_chunk)
-             for _ in range(1)]
+    steps = [DecodeStep(cfg, B, Q, wl.num_splits, inp.seq_lens, split_chunk=wl.split_chunk,
+                        tree_parents=inp.parents) for _ in range(1)]
     st = steps[0]
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
@@ -314,6 +318,7 @@ def main():
                    "split_chunk": wl.split_chunk,
                    "layer_caches_rotated": n_layers, "hip_graph": bool(args.graph),
                    "library_calls_per_step": 5 if args.unfused else 3,
+                   "drafted_tree": None if wl.tree is None else list(wl.tree),
                    "decode_kernel": kernel},
         "pct_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B * Q / (ms_step * 1e-3), 1),

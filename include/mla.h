@@ -16,6 +16,9 @@
  *   mla_up_project_v    latent output -> per-head value space through W_UV
  *   mla_absorb_append, mla_combine_up_project
  *                       two pairs of the above, each in one launch
+ * Verifying a tree of drafted tokens instead of a chain takes
+ * mla_absorb_append_at / mla_cache_append_at (a token's cache slot and its
+ * RoPE position differ) and mla_decode_paged_tree (the tree mask).
  *
  * Conventions shared by every call
  *   - Every pointer argument except `cfg` is a DEVICE pointer; `cfg` is a host
@@ -150,6 +153,18 @@ mla_status_t mla_cache_append(const mla_config_t* cfg, int32_t n_tok, const void
                               const int32_t* page_table, int32_t batch, int32_t max_pages,
                               void* cache, int64_t num_pages, int32_t flags, void* stream);
 
+/* a2 with the RoPE key rotated by rope_pos[n] instead of pos[n] (MLA_APPEND_
+ * ROTATE; pos[n] still picks the slot). A drafted token of a tree sits in the
+ * cache after its siblings but is positioned one past its parent ("The
+ * Architecture of Memory", "Tree Attention Verification"): slot L - Q + i,
+ * position L - Q + depth(i). rope_pos [n_tok] int32 (device); NULL means pos.
+ * Other arguments, layouts and errors as for mla_cache_append. */
+mla_status_t mla_cache_append_at(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                                 const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                 const int32_t* rope_pos, const int32_t* page_table,
+                                 int32_t batch, int32_t max_pages, void* cache, int64_t num_pages,
+                                 int32_t flags, void* stream);
+
 /* a1 + a2 in one launch, for callers that run both every step: the same
  * arguments, work and results (bit for bit) as
  *   mla_absorb_q(cfg, n_tok, q_nope, q_rope, pos_q, w_uk, q_full, stream);
@@ -164,6 +179,16 @@ mla_status_t mla_absorb_append(const mla_config_t* cfg, int32_t n_tok, const voi
                                const int32_t* seq_idx, const int32_t* pos,
                                const int32_t* page_table, int32_t batch, int32_t max_pages,
                                void* cache, int64_t num_pages, int32_t flags, void* stream);
+
+/* mla_absorb_append with the appended RoPE keys rotated by rope_pos (NULL:
+ * pos), i.e. mla_absorb_q followed by mla_cache_append_at, bit for bit. */
+mla_status_t mla_absorb_append_at(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                                  const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                                  void* q_full, int32_t n_app, const void* c_kv,
+                                  const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                  const int32_t* rope_pos, const int32_t* page_table,
+                                  int32_t batch, int32_t max_pages, void* cache,
+                                  int64_t num_pages, int32_t flags, void* stream);
 
 /* a4. Split-KV paged decode ("The Architecture of Memory", "Flash-Decoding
  * and FlashInfer" and "The Decode Phase: The Memory Bandwidth Wall";
@@ -206,6 +231,26 @@ mla_status_t mla_decode_paged_chunked(const mla_config_t* cfg, int32_t batch, in
                                       int64_t num_pages, const int32_t* page_table,
                                       int32_t max_pages, const int32_t* seq_lens, float* o_part,
                                       float* lse_part, void* stream);
+
+/* a4 verifying a tree of drafted tokens ("The Architecture of Memory", "Tree
+ * Attention Verification"; "Speculative Decoding: Amortizing the Memory
+ * Fetch"). The last q_len cached tokens of sequence b are drafted tokens;
+ * tree_parent[b][i] in [-1, i) names the drafted token that token i continues
+ * (-1: it continues the prefix). Query j (its query position is
+ * L_b - q_len + depth(j), as are the RoPE keys of the drafted tokens: see
+ * mla_cache_append_at) sees every prefix token t < L_b - q_len with no mask
+ * and the drafted tokens on its own branch: j and its ancestors. A chain
+ * (tree_parent[b][i] = i - 1) gives the same bits as mla_decode_paged.
+ * tree_parent [batch][q_len] int32 (device), 1 <= q_len <= 64. chunk_tokens:
+ * 0 for the per-sequence plan of mla_decode_paged, else the fixed-size plan
+ * of mla_decode_paged_chunked. A sequence whose tree entries break the rule
+ * gets NaN outputs. Other arguments, layouts and errors as mla_decode_paged. */
+mla_status_t mla_decode_paged_tree(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                   int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
+                                   const void* q_full, const void* cache, int64_t num_pages,
+                                   const int32_t* page_table, int32_t max_pages,
+                                   const int32_t* seq_lens, const int32_t* tree_parent,
+                                   float* o_part, float* lse_part, void* stream);
 
 /* A fixed-size partition plan for mla_decode_paged_chunked: about six
  * partitions per compute unit over total_tokens = sum of the batch's lengths,

@@ -14,7 +14,9 @@ fallback. If the library is missing, every call raises.
     up_project_v(cfg, o_lat, w_uv, out)
 
 absorb_append and combine_up_project run the first two and the last two of
-these calls in one launch each, with the same results.
+these calls in one launch each, with the same results. A tree of drafted
+tokens is verified with cache_append_at / absorb_append_at (slot and RoPE
+position differ) and decode_paged_tree.
 """
 from ._binding import (  # noqa: F401
     F32,
@@ -41,4 +43,7 @@ from ._binding import (  # noqa: F401
     absorb_append,
     combine_up_project,
     chunk_plan,
+    cache_append_at,
+    absorb_append_at,
+    decode_paged_tree,
 )

@@ -103,6 +103,12 @@ def lib() -> ctypes.CDLL:
                                                     VP, FP, FP, VP]),
         "mla_chunk_plan": (ctypes.c_int, [P, I64, I32, I32, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32)]),
+        "mla_cache_append_at": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, VP, I32, I32, VP, I64,
+                                               I32, VP]),
+        "mla_absorb_append_at": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, I32, VP, VP, VP, VP,
+                                                VP, VP, I32, I32, VP, I64, I32, VP]),
+        "mla_decode_paged_tree": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32,
+                                                 VP, VP, FP, FP, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -247,6 +253,32 @@ def absorb_append(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_rope
         "mla_absorb_append")
 
 
+def _rope_pos_arg(rope_pos, n: int):
+    if rope_pos is None:
+        return None
+    return _need(rope_pos, "rope_pos", _torch().int32, n)
+
+
+def cache_append_at(cfg: Config, c_kv, k_rope, seq_idx, pos, rope_pos, page_table, cache,
+                    mode: int = APPEND_ROTATE, stream=None):
+    """a2 with row n's RoPE key rotated by rope_pos[n] (None: pos[n]); pos[n]
+    still picks the slot (drafted tokens of a tree)."""
+    a = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode)
+    rp = _rope_pos_arg(rope_pos, a[0])
+    _ck(lib().mla_cache_append_at(ctypes.byref(cfg.c()), *a[:5], rp, *a[5:], _stream(stream)),
+        "mla_cache_append_at")
+
+
+def absorb_append_at(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_rope, seq_idx,
+                     pos, rope_pos, page_table, cache, mode: int = APPEND_ROTATE, stream=None):
+    """absorb_q followed by cache_append_at, in one launch where possible."""
+    a = _absorb_args(cfg, q_nope, q_rope, pos_q, w_uk, q_full)
+    b = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode)
+    rp = _rope_pos_arg(rope_pos, b[0])
+    _ck(lib().mla_absorb_append_at(ctypes.byref(cfg.c()), *a, *b[:5], rp, *b[5:],
+                                   _stream(stream)), "mla_absorb_append_at")
+
+
 def chunk_plan(cfg: Config, total_tokens: int, max_seq_len: int, num_cus: int = 256):
     """A fixed-size partition plan (chunk_tokens, num_splits) for decode_paged(chunk_tokens=...)."""
     ck, ns = ctypes.c_int32(0), ctypes.c_int32(0)
@@ -260,6 +292,21 @@ def decode_paged(cfg: Config, q_full, cache, page_table, seq_lens, o_part, lse_p
     """a4: split-KV partials. q_full [B][Q][H][D]; o_part [B][Q][H][S][d_c] f32;
     lse_part [B][Q][H][S] f32 (S = num_splits from lse_part's last axis).
     chunk_tokens > 0: fixed-size partitions (mla_decode_paged_chunked)."""
+    _decode(cfg, q_full, cache, page_table, seq_lens, None, o_part, lse_part, max_seq_len, stream,
+            chunk_tokens)
+
+
+def decode_paged_tree(cfg: Config, q_full, cache, page_table, seq_lens, tree_parent, o_part,
+                      lse_part, max_seq_len: int, stream=None, chunk_tokens: int = 0):
+    """a4 verifying a tree of drafted tokens: tree_parent [B][Q] int32, entry i
+    in [-1, i) (the drafted token that token i continues; -1 = the prefix).
+    Other arguments as decode_paged."""
+    _decode(cfg, q_full, cache, page_table, seq_lens, tree_parent, o_part, lse_part, max_seq_len,
+            stream, chunk_tokens)
+
+
+def _decode(cfg, q_full, cache, page_table, seq_lens, tree_parent, o_part, lse_part, max_seq_len,
+            stream, chunk_tokens):
     t = _torch()
     if q_full.dim() != 4:
         raise ValueError("q_full: expected [batch][q_len][H][D]")
@@ -280,6 +327,13 @@ def decode_paged(cfg: Config, q_full, cache, page_table, seq_lens, o_part, lse_p
     sl = _need(seq_lens, "seq_lens", t.int32, B)
     op = _need(o_part, "o_part", t.float32, B * Q * H * S * cfg.kv_rank)
     lp = _need(lse_part, "lse_part", t.float32, B * Q * H * S)
+    if tree_parent is not None:
+        tp = _need(tree_parent, "tree_parent", t.int32, B * Q)
+        _ck(lib().mla_decode_paged_tree(ctypes.byref(cfg.c()), B, Q, int(chunk_tokens), S,
+                                        int(max_seq_len), args[0], args[1], num_pages, pt,
+                                        max_pages, sl, tp, op, lp, _stream(stream)),
+            "mla_decode_paged_tree")
+        return
     if chunk_tokens:
         _ck(lib().mla_decode_paged_chunked(ctypes.byref(cfg.c()), B, Q, int(chunk_tokens), S,
                                            int(max_seq_len), args[0], args[1], num_pages, pt,

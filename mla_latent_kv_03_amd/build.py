@@ -26,7 +26,7 @@ SOURCES = ["mla_api.cpp", "mla_kernels.hip", "mla_decode_rows16.hip", "mla_decod
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function", "-fvisibility=hidden",
+    "-Wall", "-Wshadow", "-Wno-unused-function", "-fvisibility=hidden",
     # keep MFMA accumulators in ordinary VGPRs: the online softmax rescales
     # them with vector ALU ops, which cannot address the accumulation registers
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",

@@ -15,6 +15,7 @@ namespace {
 
 constexpr int kMaxSplits = 4096;
 constexpr int kChunksPerCu = 6;
+constexpr int kMaxTreeDrafts = 64;  // drafted tokens of a tree (one 64-bit branch mask)
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -102,8 +103,8 @@ mla_status_t check_append(const mla_config_t* cfg, int32_t n_tok, const void* c_
 mla_status_t decode_call(const mla_config_t* cfg, int32_t batch, int32_t q_len, int32_t fixed,
                          int32_t num_splits, int32_t max_seq_len, const void* q_full,
                          const void* cache, int64_t num_pages, const int32_t* page_table,
-                         int32_t max_pages, const int32_t* seq_lens, float* o_part,
-                         float* lse_part, void* stream) {
+                         int32_t max_pages, const int32_t* seq_lens, const int32_t* tree_parent,
+                         float* o_part, float* lse_part, void* stream) {
   mla_status_t st = check_config(cfg);
   if (st != MLA_OK) return st;
   MLA_REQUIRE(batch >= 0 && q_len >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
@@ -118,11 +119,12 @@ mla_status_t decode_call(const mla_config_t* cfg, int32_t batch, int32_t q_len, 
   MLA_CHECK_PTR(seq_lens);
   MLA_CHECK_PTR(o_part);
   MLA_CHECK_PTR(lse_part);
+  if (tree_parent) MLA_CHECK_PTR(tree_parent);
   mla::Shape sh = shape_of(cfg);
   sh.split_fixed = fixed;
   return hip_status(mla::launch_decode(sh, batch, q_len, num_splits, max_seq_len, q_full, cache,
-                                       num_pages, page_table, max_pages, seq_lens, o_part,
-                                       lse_part, stream));
+                                       num_pages, page_table, max_pages, seq_lens, tree_parent,
+                                       o_part, lse_part, stream));
 }
 
 mla_status_t check_combine(const mla_config_t* cfg, int32_t batch, int32_t q_len,
@@ -247,8 +249,22 @@ mla_status_t mla_cache_append(const mla_config_t* cfg, int32_t n_tok, const void
                                  max_pages, cache, num_pages, flags);
   if (st != MLA_OK || n_tok == 0) return st;
   return hip_status(mla::launch_cache_append(shape_of(cfg), n_tok, c_kv, k_rope, seq_idx, pos,
-                                             page_table, batch, max_pages, cache, num_pages,
-                                             flags == MLA_APPEND_ROTATE, stream));
+                                             nullptr, page_table, batch, max_pages, cache,
+                                             num_pages, flags == MLA_APPEND_ROTATE, stream));
+}
+
+mla_status_t mla_cache_append_at(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                                 const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                 const int32_t* rope_pos, const int32_t* page_table,
+                                 int32_t batch, int32_t max_pages, void* cache, int64_t num_pages,
+                                 int32_t flags, void* stream) {
+  mla_status_t st = check_append(cfg, n_tok, c_kv, k_rope, seq_idx, pos, page_table, batch,
+                                 max_pages, cache, num_pages, flags);
+  if (st != MLA_OK || n_tok == 0) return st;
+  if (rope_pos) MLA_CHECK_PTR(rope_pos);
+  return hip_status(mla::launch_cache_append(shape_of(cfg), n_tok, c_kv, k_rope, seq_idx, pos,
+                                             rope_pos, page_table, batch, max_pages, cache,
+                                             num_pages, flags == MLA_APPEND_ROTATE, stream));
 }
 
 mla_status_t mla_absorb_append(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
@@ -264,7 +280,27 @@ mla_status_t mla_absorb_append(const mla_config_t* cfg, int32_t n_tok, const voi
   if (st != MLA_OK || (n_tok == 0 && n_app == 0)) return st;
   return hip_status(mla::launch_absorb_append(
       shape_of(cfg), n_tok, q_nope, q_rope, pos_q, w_uk, q_full, n_app, c_kv, k_rope, seq_idx, pos,
-      page_table, batch, max_pages, cache, num_pages, flags == MLA_APPEND_ROTATE, stream));
+      nullptr, page_table, batch, max_pages, cache, num_pages, flags == MLA_APPEND_ROTATE,
+      stream));
+}
+
+mla_status_t mla_absorb_append_at(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                                  const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                                  void* q_full, int32_t n_app, const void* c_kv,
+                                  const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                  const int32_t* rope_pos, const int32_t* page_table,
+                                  int32_t batch, int32_t max_pages, void* cache,
+                                  int64_t num_pages, int32_t flags, void* stream) {
+  mla_status_t st = check_absorb(cfg, n_tok, q_nope, q_rope, pos_q, w_uk, q_full);
+  if (st != MLA_OK) return st;
+  st = check_append(cfg, n_app, c_kv, k_rope, seq_idx, pos, page_table, batch, max_pages, cache,
+                    num_pages, flags);
+  if (st != MLA_OK || (n_tok == 0 && n_app == 0)) return st;
+  if (n_app > 0 && rope_pos) MLA_CHECK_PTR(rope_pos);
+  return hip_status(mla::launch_absorb_append(
+      shape_of(cfg), n_tok, q_nope, q_rope, pos_q, w_uk, q_full, n_app, c_kv, k_rope, seq_idx, pos,
+      rope_pos, page_table, batch, max_pages, cache, num_pages, flags == MLA_APPEND_ROTATE,
+      stream));
 }
 
 mla_status_t mla_decode_paged(const mla_config_t* cfg, int32_t batch, int32_t q_len,
@@ -273,7 +309,7 @@ mla_status_t mla_decode_paged(const mla_config_t* cfg, int32_t batch, int32_t q_
                               int32_t max_pages, const int32_t* seq_lens, float* o_part,
                               float* lse_part, void* stream) {
   return decode_call(cfg, batch, q_len, 0, num_splits, max_seq_len, q_full, cache, num_pages,
-                     page_table, max_pages, seq_lens, o_part, lse_part, stream);
+                     page_table, max_pages, seq_lens, nullptr, o_part, lse_part, stream);
 }
 
 mla_status_t mla_decode_paged_chunked(const mla_config_t* cfg, int32_t batch, int32_t q_len,
@@ -289,7 +325,29 @@ mla_status_t mla_decode_paged_chunked(const mla_config_t* cfg, int32_t batch, in
   MLA_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
   MLA_REQUIRE((int64_t)chunk_tokens * num_splits >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
   return decode_call(cfg, batch, q_len, chunk_tokens, num_splits, max_seq_len, q_full, cache,
-                     num_pages, page_table, max_pages, seq_lens, o_part, lse_part, stream);
+                     num_pages, page_table, max_pages, seq_lens, nullptr, o_part, lse_part,
+                     stream);
+}
+
+mla_status_t mla_decode_paged_tree(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                   int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
+                                   const void* q_full, const void* cache, int64_t num_pages,
+                                   const int32_t* page_table, int32_t max_pages,
+                                   const int32_t* seq_lens, const int32_t* tree_parent,
+                                   float* o_part, float* lse_part, void* stream) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(q_len >= 1 && q_len <= kMaxTreeDrafts, MLA_ERR_SHAPE);
+  MLA_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
+  if (chunk_tokens != 0) {
+    MLA_REQUIRE(chunk_tokens >= cfg->page_size && chunk_tokens % cfg->page_size == 0,
+                MLA_ERR_SHAPE);
+    MLA_REQUIRE((int64_t)chunk_tokens * num_splits >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
+  }
+  if (batch > 0) MLA_CHECK_PTR(tree_parent);
+  return decode_call(cfg, batch, q_len, chunk_tokens, num_splits, max_seq_len, q_full, cache,
+                     num_pages, page_table, max_pages, seq_lens, tree_parent, o_part, lse_part,
+                     stream);
 }
 
 mla_status_t mla_chunk_plan(const mla_config_t* cfg, int64_t total_tokens, int32_t max_seq_len,

@@ -1,7 +1,9 @@
 // Paged cache append of one row (a2; "The Architecture of Memory",
 // "PagedAttention: Virtual Memory for LLMs"): row n of c_kv / k_rope goes to
 // physical row page_table[seq_idx[n]][pos[n] / page] * page + pos[n] % page,
-// its RoPE part rotated by pos[n] when `rotate` is set. Rows whose sequence,
+// its RoPE part rotated by rope_pos[n] when `rotate` is set (by pos[n] when
+// rope_pos is NULL; a drafted tree's token sits at a slot that need not be
+// its position, "The Architecture of Memory", "Tree Attention Verification"). Rows whose sequence,
 // position or page entry is out of range are skipped. The row's values do not
 // depend on where it goes, so they are loaded (16 bytes per lane when `vec`:
 // every source and destination row 16-byte aligned) before the page-table
@@ -17,6 +19,7 @@ __device__ __forceinline__ void append_row(int n, int dc, int dr, int page, cons
                                            const T* __restrict__ k_rope,
                                            const int32_t* __restrict__ seq_idx,
                                            const int32_t* __restrict__ pos,
+                                           const int32_t* __restrict__ rope_pos,
                                            const int32_t* __restrict__ page_table, int batch,
                                            int max_pages, T* __restrict__ cache, int64_t num_pages,
                                            int rotate, double log2_base, int vec) {
@@ -39,6 +42,7 @@ __device__ __forceinline__ void append_row(int n, int dc, int dr, int page, cons
   const int pg = page_table[(size_t)b * max_pages + p / page];
   if (pg < 0 || (int64_t)pg >= num_pages) return;
   T* row = cache + ((size_t)pg * page + p % page) * D;
+  const int rp = rope_pos ? rope_pos[n] : p;
   if (tid < nvec) reinterpret_cast<uint4*>(row)[tid] = v0;
   for (int i = tid + blockDim.x; i < nvec; i += blockDim.x)
     reinterpret_cast<uint4*>(row)[i] = reinterpret_cast<const uint4*>(src)[i];
@@ -46,7 +50,7 @@ __device__ __forceinline__ void append_row(int n, int dc, int dr, int page, cons
   if (tid < dr / 2) {
     if (rotate) {
       double y0, y1;
-      rope_pair(x0, x1, p, tid, dr, log2_base, &y0, &y1);
+      rope_pair(x0, x1, rp, tid, dr, log2_base, &y0, &y1);
       Elt<T>::st(row + dc + 2 * tid, (float)y0);
       Elt<T>::st(row + dc + 2 * tid + 1, (float)y1);
     } else {
@@ -57,7 +61,8 @@ __device__ __forceinline__ void append_row(int n, int dc, int dr, int page, cons
   for (int i = tid + blockDim.x; i < dr / 2; i += blockDim.x) {
     if (rotate) {
       double y0, y1;
-      rope_pair(Elt<T>::ld(kr + 2 * i), Elt<T>::ld(kr + 2 * i + 1), p, i, dr, log2_base, &y0, &y1);
+      rope_pair(Elt<T>::ld(kr + 2 * i), Elt<T>::ld(kr + 2 * i + 1), rp, i, dr, log2_base, &y0,
+                &y1);
       Elt<T>::st(row + dc + 2 * i, (float)y0);
       Elt<T>::st(row + dc + 2 * i + 1, (float)y1);
     } else {

@@ -61,4 +61,26 @@ __device__ __forceinline__ void split_range(int L, int S, int page, int fixed, i
   *t1 = (int)e;
 }
 
+// Tree verification ("The Architecture of Memory", "Tree Attention
+// Verification"): the last Q cached tokens of a sequence are drafted tokens
+// forming a tree, parent[i] in [-1, i) being the drafted token that token i
+// continues (-1: the prefix). Query j sees every prefix token and the drafted
+// tokens on its own branch: bit i of its branch mask is set when i is j or an
+// ancestor of j. The walk stops after Q steps (Q <= 64) whatever the entries
+// hold; tree_entry_ok is the validity the kernels check first.
+__device__ __forceinline__ bool tree_entry_ok(const int32_t* __restrict__ parent, int i) {
+  const int p = parent[i];
+  return p >= -1 && p < i;
+}
+__device__ __forceinline__ uint64_t tree_branch_mask(const int32_t* __restrict__ parent, int Q,
+                                                     int j) {
+  uint64_t m = 0;
+  int i = j;
+  for (int step = 0; step < Q && i >= 0 && i < Q; ++step) {
+    m |= 1ull << i;
+    i = parent[i];
+  }
+  return m;
+}
+
 }  // namespace mla

@@ -29,6 +29,9 @@
 // The block's queries arrive by the same direct-to-LDS path (through the ring
 // slot that tile 3 later takes), so the waits for the first tiles never
 // include ordinary loads.
+// With a drafted tree (tree_parent, "Tree Attention Verification") a row
+// sees the prefix and the drafted tokens on its query's branch; only tiles
+// that reach the drafted tokens test the branch mask.
 #include "mla_decode_common.h"
 #include "mla_launch.h"
 
@@ -61,7 +64,8 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
                           const bf16_t* __restrict__ q_full,
                           const bf16_t* __restrict__ cache, int64_t num_pages,
                           const int32_t* __restrict__ page_table, int max_pages,
-                          const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
+                          const int32_t* __restrict__ seq_lens,
+                          const int32_t* __restrict__ tree_parent, float* __restrict__ o_part,
                           float* __restrict__ lse_part) {
   extern __shared__ u32x4_t lds[];
   int unit, grp;
@@ -75,7 +79,10 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   const int s = unit % S;
   int L;
   const int b = seq_by_rank(seq_lens, units / S, unit / S, lane, &L);
-  const bool bad_len = (L < Q) || (L > max_seq_len);
+  const int32_t* par = tree_parent ? tree_parent + (size_t)b * Q : nullptr;
+  // a malformed tree makes the sequence invalid (the same verdict in every wave)
+  const bool bad_tree = par && !__all(lane >= Q || tree_entry_ok(par, lane));
+  const bool bad_len = (L < Q) || (L > max_seq_len) || bad_tree;
   int t0 = 0, t1 = 0;
   if (!bad_len) split_range(L, S, page, fixed, s, &t0, &t1);
   const int ntiles = (t1 - t0 + kT - 1) / kT;
@@ -107,8 +114,11 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[f][m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const int p_lim = L - Q + (row0 + n) / H;
-  const int lim = min(p_lim, t1 - 1);  // last token this row may see in this partition
+  // tokens row n sees in this partition: t <= lim, and with a drafted tree
+  // also the drafted tokens (t >= t_draft) on its query's branch
+  const int t_draft = L - Q;
+  const int lim = min(par ? t_draft - 1 : t_draft + (row0 + n) / H, t1 - 1);
+  const uint64_t branch = (par && !bad_len) ? tree_branch_mask(par, Q, (row0 + n) / H) : 0ull;
 
   if (ntiles > 0) {
     // ---- prologue: queries (waves 0, 1: 8 rows each, into slot 3), tiles 0..2
@@ -202,10 +212,23 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
       const f32x4_t s0 = sk[0] + sk[128];   // subtile 0: column halves 0 + 1
       const f32x4_t s1 = sk[64] + sk[192];  // subtile 1
       float sv[8];
+      if (par && ts + kT > t_draft) {  // the tile reaches the drafted tokens
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv[r] = (ts + 4 * kg + r <= lim) ? s0[r] * scale_log2 : -INFINITY;
-        sv[4 + r] = (ts + 16 + 4 * kg + r <= lim) ? s1[r] * scale_log2 : -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const int ta = ts + 4 * kg + r, tb = ta + 16;
+          const bool va =
+              ta <= lim || (ta >= t_draft && ta < t1 && ((branch >> (ta - t_draft)) & 1ull));
+          const bool vb =
+              tb <= lim || (tb >= t_draft && tb < t1 && ((branch >> (tb - t_draft)) & 1ull));
+          sv[r] = va ? s0[r] * scale_log2 : -INFINITY;
+          sv[4 + r] = vb ? s1[r] * scale_log2 : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sv[r] = (ts + 4 * kg + r <= lim) ? s0[r] * scale_log2 : -INFINITY;
+          sv[4 + r] = (ts + 16 + 4 * kg + r <= lim) ? s1[r] * scale_log2 : -INFINITY;
+        }
       }
       float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                          fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
@@ -305,7 +328,8 @@ bool decode_rows16_ok(const Shape& s, int q_len) {
 int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
                          const void* q_full, const void* cache, int64_t num_pages,
                          const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                         float* o_part, float* lse_part, void* stream) {
+                         const int32_t* tree_parent, float* o_part, float* lse_part,
+                         void* stream) {
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_rows16_kernel),
@@ -320,7 +344,7 @@ int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, i
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page,
                      s.split_fixed, max_seq_len, s.scale * 1.4426950408889634f, units, groups,
                      (const bf16_t*)q_full, (const bf16_t*)cache, num_pages, page_table, max_pages,
-                     seq_lens, o_part, lse_part);
+                     seq_lens, tree_parent, o_part, lse_part);
   return (int)hipGetLastError();
 }
 

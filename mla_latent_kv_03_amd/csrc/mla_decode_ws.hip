@@ -35,6 +35,9 @@
 // computed in the same step as the softmax and P.C of tile k; tiles stream
 // through a 4-slot LDS ring and one block barrier per tile covers the tile's
 // arrival, the score hand-over and the reuse of the slot two tiles back.
+// With a drafted tree (tree_parent, "Tree Attention Verification") a row sees
+// the prefix and the drafted tokens on its query's branch; only tiles that
+// reach the drafted tokens test the branch mask.
 #include "mla_decode_common.h"
 #include "mla_launch.h"
 
@@ -65,7 +68,8 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
                       float scale_log2, int units, int groups, const bf16_t* __restrict__ q_full,
                       const bf16_t* __restrict__ cache, int64_t num_pages,
                       const int32_t* __restrict__ page_table, int max_pages,
-                      const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
+                      const int32_t* __restrict__ seq_lens,
+                      const int32_t* __restrict__ tree_parent, float* __restrict__ o_part,
                       float* __restrict__ lse_part) {
   extern __shared__ u32x4_t lds[];
   int unit, grp;
@@ -86,7 +90,10 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   f32x4_t* sbuf = reinterpret_cast<f32x4_t*>(reinterpret_cast<char*>(lds) + kWRingBytes);
   auto slot = [&](int k) { return lds + (k & (kWRing - 1)) * kWTChunks; };
 
-  const bool bad_len = (L < Q) || (L > max_seq_len);
+  const int32_t* par = tree_parent ? tree_parent + (size_t)b * Q : nullptr;
+  // a malformed tree makes the sequence invalid (the same verdict in every wave)
+  const bool bad_tree = par && !__all(lane >= Q || tree_entry_ok(par, lane));
+  const bool bad_len = (L < Q) || (L > max_seq_len) || bad_tree;
   int t0 = 0, t1 = 0;
   if (!bad_len) split_range(L, S, page, fixed, s, &t0, &t1);
   const int ntiles = (t1 - t0 + kWT - 1) / kWT;
@@ -242,9 +249,17 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[rg][fb][m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
-  int lim[2];  // last token each row of this lane may see in this partition
+  // tokens each row of this lane sees in this partition: t <= lim, and with a
+  // drafted tree also the drafted tokens (t >= t_draft) on its query's branch
+  const int t_draft = L - Q;
+  int lim[2];
+  uint64_t branch[2];
 #pragma unroll
-  for (int rg = 0; rg < 2; ++rg) lim[rg] = min(L - Q + (row0 + 16 * rg + n) / H, t1 - 1);
+  for (int rg = 0; rg < 2; ++rg) {
+    const int j = (row0 + 16 * rg + n) / H;
+    lim[rg] = min(par ? t_draft - 1 : t_draft + j, t1 - 1);
+    branch[rg] = (par && !bad_len) ? tree_branch_mask(par, Q, j) : 0ull;
+  }
 
   __syncthreads();  // tile 0 landed
   for (int k = 0; k < ntiles; ++k) {
@@ -263,10 +278,23 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
       const f32x4_t s0 = sk[rg * 64];        // tokens 4 kg + r
       const f32x4_t s1 = sk[128 + rg * 64];  // tokens 16 + 4 kg + r
       float sv[8];
+      if (par && ts + kWT > t_draft) {  // the tile reaches the drafted tokens
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv[r] = (ts + 4 * kg + r <= lim[rg]) ? s0[r] * scale_log2 : -INFINITY;
-        sv[4 + r] = (ts + 16 + 4 * kg + r <= lim[rg]) ? s1[r] * scale_log2 : -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const int ta = ts + 4 * kg + r, tb = ta + 16;
+          const bool va = ta <= lim[rg] ||
+                          (ta >= t_draft && ta < t1 && ((branch[rg] >> (ta - t_draft)) & 1ull));
+          const bool vb = tb <= lim[rg] ||
+                          (tb >= t_draft && tb < t1 && ((branch[rg] >> (tb - t_draft)) & 1ull));
+          sv[r] = va ? s0[r] * scale_log2 : -INFINITY;
+          sv[4 + r] = vb ? s1[r] * scale_log2 : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sv[r] = (ts + 4 * kg + r <= lim[rg]) ? s0[r] * scale_log2 : -INFINITY;
+          sv[4 + r] = (ts + 16 + 4 * kg + r <= lim[rg]) ? s1[r] * scale_log2 : -INFINITY;
+        }
       }
       float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                          fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
@@ -368,7 +396,7 @@ bool decode_ws_ok(const Shape& s, int q_len) {
 int launch_decode_ws(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
                      const void* q_full, const void* cache, int64_t num_pages,
                      const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                     float* o_part, float* lse_part, void* stream) {
+                     const int32_t* tree_parent, float* o_part, float* lse_part, void* stream) {
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_ws_kernel),
@@ -383,7 +411,7 @@ int launch_decode_ws(const Shape& s, int batch, int q_len, int num_splits, int m
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page,
                      s.split_fixed, max_seq_len, s.scale * 1.4426950408889634f, units, groups,
                      (const bf16_t*)q_full, (const bf16_t*)cache, num_pages, page_table, max_pages,
-                     seq_lens, o_part, lse_part);
+                     seq_lens, tree_parent, o_part, lse_part);
   return (int)hipGetLastError();
 }
 

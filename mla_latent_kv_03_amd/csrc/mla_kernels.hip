@@ -105,28 +105,29 @@ __global__ __launch_bounds__(128) void append_kernel(int dc, int dr, int page,
                                                      const T* __restrict__ k_rope,
                                                      const int32_t* __restrict__ seq_idx,
                                                      const int32_t* __restrict__ pos,
+                                                     const int32_t* __restrict__ rope_pos,
                                                      const int32_t* __restrict__ page_table,
                                                      int batch, int max_pages, T* __restrict__ cache,
                                                      int64_t num_pages, int rotate, double log2_base,
                                                      int vec) {
-  append_row<T>(blockIdx.x, dc, dr, page, c_kv, k_rope, seq_idx, pos, page_table, batch, max_pages,
-                cache, num_pages, rotate, log2_base, vec);
+  append_row<T>(blockIdx.x, dc, dr, page, c_kv, k_rope, seq_idx, pos, rope_pos, page_table, batch,
+                max_pages, cache, num_pages, rotate, log2_base, vec);
 }
 
 int launch_cache_append(const Shape& s, int n_tok, const void* c_kv, const void* k_rope,
-                        const int32_t* seq_idx, const int32_t* pos, const int32_t* page_table,
-                        int batch, int max_pages, void* cache, int64_t num_pages, int rotate,
-                        void* stream) {
+                        const int32_t* seq_idx, const int32_t* pos, const int32_t* rope_pos,
+                        const int32_t* page_table, int batch, int max_pages, void* cache,
+                        int64_t num_pages, int rotate, void* stream) {
   const int vec = append_vectorizable(s, c_kv, cache);
   if (s.dtype == 0)
     hipLaunchKernelGGL(append_kernel<float>, dim3(n_tok), dim3(128), 0, as_stream(stream), s.dc,
                        s.dr, s.page, (const float*)c_kv, (const float*)k_rope, seq_idx, pos,
-                       page_table, batch, max_pages, (float*)cache, num_pages, rotate, s.log2_base,
-                       vec);
+                       rope_pos, page_table, batch, max_pages, (float*)cache, num_pages, rotate,
+                       s.log2_base, vec);
   else
     hipLaunchKernelGGL(append_kernel<bf16_t>, dim3(n_tok), dim3(128), 0, as_stream(stream), s.dc,
                        s.dr, s.page, (const bf16_t*)c_kv, (const bf16_t*)k_rope, seq_idx, pos,
-                       page_table, batch, max_pages, (bf16_t*)cache, num_pages, rotate,
+                       rope_pos, page_table, batch, max_pages, (bf16_t*)cache, num_pages, rotate,
                        s.log2_base, vec);
   return (int)hipGetLastError();
 }
@@ -148,7 +149,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
     int Q, int H, int dc, int dr, int page, int S, int fixed, int max_seq_len, float scale,
     const T* __restrict__ q_full, const T* __restrict__ cache, int64_t num_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
+    const int32_t* __restrict__ tree_parent, float* __restrict__ o_part,
+    float* __restrict__ lse_part) {
   extern __shared__ float smem[];
   const int s = blockIdx.x, b = blockIdx.y;
   const int R = Q * H;
@@ -163,6 +165,10 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 
   const int L = seq_lens[b];
   bool bad = (L < Q) || (L > max_seq_len);
+  const int32_t* par = tree_parent ? tree_parent + (size_t)b * Q : nullptr;
+  if (par) {  // every thread checks every entry: the verdict is block-uniform
+    for (int i = 0; i < Q; ++i) bad |= !tree_entry_ok(par, i);
+  }
   int t0 = 0, t1 = 0;
   if (!bad) split_range(L, S, page, fixed, s, &t0, &t1);
 
@@ -178,7 +184,11 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   const int my_r = tid / kGenTok, my_k = tid % kGenTok;
   float m_run = -INFINITY, l_run = 0.0f;
   const int my_j = (r0 + my_r) / H;   // query index of this thread's row
-  const int my_p = L - Q + my_j;      // its position
+  // tokens this row sees: t <= lim, and with a drafted tree also the drafted
+  // tokens (t >= L - Q) on its branch
+  const int t_draft = L - Q;  // first drafted token
+  const int lim = par ? t_draft - 1 : t_draft + my_j;
+  const uint64_t branch = (par && !bad && my_j < Q) ? tree_branch_mask(par, Q, my_j) : 0ull;
 
   for (int t = t0; t < t1 && !bad; t += kGenTok) {
     const int nt = min(kGenTok, t1 - t);
@@ -192,7 +202,10 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
     for (int i = tid; i < nt * D; i += blockDim.x) cs[(i / D) * Dp + (i % D)] = Elt<T>::ld(src + i);
     __syncthreads();
     float sc = -INFINITY;
-    if (my_r < nr && my_k < nt && t + my_k <= my_p) {
+    const int tk = t + my_k;
+    const bool seen =
+        tk <= lim || (par && tk >= t_draft && ((branch >> (tk - t_draft)) & 1ull));
+    if (my_r < nr && my_k < nt && seen) {
       const float* qr = qs + my_r * D;
       const float* cr = cs + my_k * Dp;
       float dot = 0.0f;
@@ -255,8 +268,8 @@ template <typename T>
 static int decode_generic_impl(const Shape& s, int batch, int q_len, int num_splits,
                                int max_seq_len, const void* q_full, const void* cache,
                                int64_t num_pages, const int32_t* page_table, int max_pages,
-                               const int32_t* seq_lens, float* o_part, float* lse_part,
-                               void* stream) {
+                               const int32_t* seq_lens, const int32_t* tree_parent, float* o_part,
+                               float* lse_part, void* stream) {
   const int D = s.D();
   const size_t lds = sizeof(float) * ((size_t)kGenRows * D + (size_t)kGenTok * (D + 1) +
                                       kGenRows * kGenTok + kGenRows);
@@ -271,7 +284,8 @@ static int decode_generic_impl(const Shape& s, int batch, int q_len, int num_spl
   hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(256), lds, as_stream(stream), q_len, s.H,
                      s.dc, s.dr, s.page, num_splits, s.split_fixed, max_seq_len, s.scale,
                      (const T*)q_full,
-                     (const T*)cache, num_pages, page_table, max_pages, seq_lens, o_part, lse_part);
+                     (const T*)cache, num_pages, page_table, max_pages, seq_lens, tree_parent,
+                     o_part, lse_part);
   return (int)hipGetLastError();
 }
 
@@ -279,12 +293,13 @@ bool decode_rows16_ok(const Shape& s, int q_len);
 int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
                          const void* q_full, const void* cache, int64_t num_pages,
                          const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                         float* o_part, float* lse_part, void* stream);
+                         const int32_t* tree_parent, float* o_part, float* lse_part,
+                         void* stream);
 bool decode_ws_ok(const Shape& s, int q_len);
 int launch_decode_ws(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
                      const void* q_full, const void* cache, int64_t num_pages,
                      const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                     float* o_part, float* lse_part, void* stream);
+                     const int32_t* tree_parent, float* o_part, float* lse_part, void* stream);
 
 // bf16 MFMA kernels for the 576-wide DeepSeek row: 64 query rows per block
 // (specialised QK and PV waves) when the row count and page size allow it,
@@ -298,25 +313,26 @@ int decode_kernel_kind(const Shape& s, int q_len) {
 int launch_decode(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
                   const void* q_full, const void* cache, int64_t num_pages,
                   const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                  float* o_part, float* lse_part, void* stream) {
+                  const int32_t* tree_parent, float* o_part, float* lse_part, void* stream) {
   switch (decode_kernel_kind(s, q_len)) {
     case 2:
       return launch_decode_ws(s, batch, q_len, num_splits, max_seq_len, q_full, cache, num_pages,
-                              page_table, max_pages, seq_lens, o_part, lse_part, stream);
+                              page_table, max_pages, seq_lens, tree_parent, o_part, lse_part,
+                              stream);
     case 1:
       return launch_decode_rows16(s, batch, q_len, num_splits, max_seq_len, q_full, cache,
-                                  num_pages, page_table, max_pages, seq_lens, o_part, lse_part,
-                                  stream);
+                                  num_pages, page_table, max_pages, seq_lens, tree_parent, o_part,
+                                  lse_part, stream);
     default:
       break;
   }
   return s.dtype == 0
              ? decode_generic_impl<float>(s, batch, q_len, num_splits, max_seq_len, q_full, cache,
-                                          num_pages, page_table, max_pages, seq_lens, o_part,
-                                          lse_part, stream)
+                                          num_pages, page_table, max_pages, seq_lens, tree_parent,
+                                          o_part, lse_part, stream)
              : decode_generic_impl<bf16_t>(s, batch, q_len, num_splits, max_seq_len, q_full, cache,
-                                           num_pages, page_table, max_pages, seq_lens, o_part,
-                                           lse_part, stream);
+                                           num_pages, page_table, max_pages, seq_lens, tree_parent,
+                                           o_part, lse_part, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -28,10 +28,11 @@ inline int append_vectorizable(const Shape& s, const void* c_kv, const void* cac
 int launch_absorb_q(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
                     const int32_t* pos, const void* w_uk, void* q_full, void* stream);
 
+// rope_pos may be NULL (rotate by pos)
 int launch_cache_append(const Shape& s, int n_tok, const void* c_kv, const void* k_rope,
-                        const int32_t* seq_idx, const int32_t* pos, const int32_t* page_table,
-                        int batch, int max_pages, void* cache, int64_t num_pages, int rotate,
-                        void* stream);
+                        const int32_t* seq_idx, const int32_t* pos, const int32_t* rope_pos,
+                        const int32_t* page_table, int batch, int max_pages, void* cache,
+                        int64_t num_pages, int rotate, void* stream);
 
 // a1 and a2 of one decode step in one launch when the absorption takes the
 // bf16 MFMA kernel, else the two launches in order; results identical to
@@ -39,13 +40,16 @@ int launch_cache_append(const Shape& s, int n_tok, const void* c_kv, const void*
 int launch_absorb_append(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
                          const int32_t* pos_q, const void* w_uk, void* q_full, int n_app,
                          const void* c_kv, const void* k_rope, const int32_t* seq_idx,
-                         const int32_t* pos, const int32_t* page_table, int batch, int max_pages,
-                         void* cache, int64_t num_pages, int rotate, void* stream);
+                         const int32_t* pos, const int32_t* rope_pos, const int32_t* page_table,
+                         int batch, int max_pages, void* cache, int64_t num_pages, int rotate,
+                         void* stream);
 
+// tree_parent: [batch][q_len] drafted-token tree (q_len <= 64), or NULL for
+// the chain of drafted tokens
 int launch_decode(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
                   const void* q_full, const void* cache, int64_t num_pages,
                   const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                  float* o_part, float* lse_part, void* stream);
+                  const int32_t* tree_parent, float* o_part, float* lse_part, void* stream);
 
 int launch_combine(const Shape& s, int rows, int num_splits, const float* o_part,
                    const float* lse_part, void* o_lat, float* lse, void* stream);

@@ -162,15 +162,15 @@ __global__ __launch_bounds__(256) void absorb_append_kernel(
     const bf16_t* __restrict__ w_uk, bf16_t* __restrict__ q_full, int ny, int n_abs, int page,
     const bf16_t* __restrict__ c_kv, const bf16_t* __restrict__ k_rope,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
-    const int32_t* __restrict__ page_table, int batch, int max_pages, bf16_t* __restrict__ cache,
-    int64_t num_pages, int rotate, int vec) {
+    const int32_t* __restrict__ rope_pos, const int32_t* __restrict__ page_table, int batch,
+    int max_pages, bf16_t* __restrict__ cache, int64_t num_pages, int rotate, int vec) {
   const int id = blockIdx.x;
   if (id < n_abs) {
     absorb_block(id % H, (id / H) % ny, id / (H * ny), n_tok, H, dn, dc, dr, log2_base, q_nope,
                  q_rope, pos_q, w_uk, q_full);
   } else {
-    append_row<bf16_t>(id - n_abs, dc, dr, page, c_kv, k_rope, seq_idx, pos, page_table, batch,
-                       max_pages, cache, num_pages, rotate, log2_base, vec);
+    append_row<bf16_t>(id - n_abs, dc, dr, page, c_kv, k_rope, seq_idx, pos, rope_pos, page_table,
+                       batch, max_pages, cache, num_pages, rotate, log2_base, vec);
   }
 }
 
@@ -241,14 +241,15 @@ __global__ __launch_bounds__(256) void up_v_mfma_kernel(int n_tok, int H, int dc
 int launch_absorb_append(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
                          const int32_t* pos_q, const void* w_uk, void* q_full, int n_app,
                          const void* c_kv, const void* k_rope, const int32_t* seq_idx,
-                         const int32_t* pos, const int32_t* page_table, int batch, int max_pages,
-                         void* cache, int64_t num_pages, int rotate, void* stream) {
+                         const int32_t* pos, const int32_t* rope_pos, const int32_t* page_table,
+                         int batch, int max_pages, void* cache, int64_t num_pages, int rotate,
+                         void* stream) {
   if (!absorb_mfma_ok(s) || n_tok == 0 || n_app == 0) {
     int rc = 0;
     if (n_tok > 0) rc = launch_absorb_q(s, n_tok, q_nope, q_rope, pos_q, w_uk, q_full, stream);
     if (rc == 0 && n_app > 0)
-      rc = launch_cache_append(s, n_app, c_kv, k_rope, seq_idx, pos, page_table, batch, max_pages,
-                               cache, num_pages, rotate, stream);
+      rc = launch_cache_append(s, n_app, c_kv, k_rope, seq_idx, pos, rope_pos, page_table, batch,
+                               max_pages, cache, num_pages, rotate, stream);
     return rc;
   }
   const int ny = s.dc / 64 + 1;
@@ -257,7 +258,7 @@ int launch_absorb_append(const Shape& s, int n_tok, const void* q_nope, const vo
                      reinterpret_cast<hipStream_t>(stream), n_tok, s.H, s.dn, s.dc, s.dr,
                      s.log2_base, (const bf16_t*)q_nope, (const bf16_t*)q_rope, pos_q,
                      (const bf16_t*)w_uk, (bf16_t*)q_full, ny, n_abs, s.page, (const bf16_t*)c_kv,
-                     (const bf16_t*)k_rope, seq_idx, pos, page_table, batch, max_pages,
+                     (const bf16_t*)k_rope, seq_idx, pos, rope_pos, page_table, batch, max_pages,
                      (bf16_t*)cache, num_pages, rotate, append_vectorizable(s, c_kv, cache));
   return (int)hipGetLastError();
 }

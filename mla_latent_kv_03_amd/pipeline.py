@@ -26,6 +26,44 @@ def upload(x, dtype, device="cuda"):
     return t.from_numpy(x).to(device=device).to(dtype).contiguous()
 
 
+def tree_depths(parents):
+    """Depth of each drafted token of a tree (0 when its parent is -1, else
+    one more than its parent's); parents must precede their children."""
+    d = []
+    for j, p in enumerate(int(x) for x in parents):
+        if not -1 <= p < j:
+            raise ValueError(f"tree: drafted token {j} has parent {p}")
+        d.append(0 if p < 0 else d[p] + 1)
+    return d
+
+
+def draft_positions(seq_lens, q_len: int, tree_parents=None):
+    """(slot, position) of the q_len drafted tokens of every sequence, flat
+    [B*Q] lists: token j of sequence b is cached at slot L_b - Q + j; its
+    position (query RoPE and cached RoPE key) is that slot for a chain, and
+    L_b - Q + depth(j) for a tree ("Tree Attention Verification")."""
+    slot, pos = [], []
+    for b, L in enumerate(int(x) for x in seq_lens):
+        dep = (list(range(q_len)) if tree_parents is None
+               else tree_depths(tree_parents[b]))
+        for j in range(q_len):
+            slot.append(L - q_len + j)
+            pos.append(L - q_len + dep[j])
+    return slot, pos
+
+
+def token_rope_positions(seq_lens, q_len: int, tree_parents=None):
+    """Position of every cached token of the batch (sequence-major, the order
+    of a setup fill): t for prefix tokens, the draft_positions of the last
+    q_len."""
+    out = []
+    _, dpos = draft_positions(seq_lens, q_len, tree_parents)
+    for b, L in enumerate(int(x) for x in seq_lens):
+        out.extend(range(L - q_len))
+        out.extend(dpos[b * q_len:(b + 1) * q_len])
+    return out
+
+
 class DecodeStep:
     """Device state of one decode step for ``batch`` sequences of ``q_len`` tokens.
 
@@ -35,7 +73,7 @@ class DecodeStep:
     """
 
     def __init__(self, cfg: B.Config, batch: int, q_len: int, num_splits: int,
-                 seq_lens_host, device="cuda", split_chunk: int = 0):
+                 seq_lens_host, device="cuda", split_chunk: int = 0, tree_parents=None):
         t = _torch()
         self.cfg, self.batch, self.q_len, self.num_splits = cfg, batch, q_len, num_splits
         self.split_chunk = split_chunk  # > 0: fixed-size partitions
@@ -43,9 +81,14 @@ class DecodeStep:
         dt = dtype_of(cfg)
         lens = [int(x) for x in seq_lens_host]
         self.max_seq_len = max(lens)
-        # query j of sequence b sits at position L_b - Q + j
-        pos = [L - q_len + j for L in lens for j in range(q_len)]
+        # drafted token j of sequence b: cached at slot L_b - Q + j, positioned
+        # there for a chain and at L_b - Q + depth(j) for a tree
+        slot, pos = draft_positions(lens, q_len, tree_parents)
         self.qpos = t.tensor(pos, dtype=t.int32, device=device)
+        self.slot = t.tensor(slot, dtype=t.int32, device=device)
+        self.tree = (None if tree_parents is None else
+                     t.tensor([[int(p) for p in row] for row in tree_parents], dtype=t.int32,
+                              device=device))
         self.seq_idx = t.tensor([b for b in range(batch) for _ in range(q_len)], dtype=t.int32,
                                 device=device)
         self.q_full = t.empty((batch, q_len, H, D), dtype=dt, device=device)
@@ -59,13 +102,22 @@ class DecodeStep:
         B.absorb_q(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, stream)
 
     def append(self, c_new, k_new, page_table, cache, stream=None):
-        B.cache_append(self.cfg, c_new, k_new, self.seq_idx, self.qpos, page_table, cache,
-                       B.APPEND_ROTATE, stream)
+        if self.tree is None:
+            B.cache_append(self.cfg, c_new, k_new, self.seq_idx, self.slot, page_table, cache,
+                           B.APPEND_ROTATE, stream)
+        else:
+            B.cache_append_at(self.cfg, c_new, k_new, self.seq_idx, self.slot, self.qpos,
+                              page_table, cache, B.APPEND_ROTATE, stream)
 
     def decode(self, cache, page_table, seq_lens, stream=None, max_seq_len: Optional[int] = None):
-        B.decode_paged(self.cfg, self.q_full, cache, page_table, seq_lens, self.o_part,
-                       self.lse_part, max_seq_len or self.max_seq_len, stream,
-                       chunk_tokens=self.split_chunk)
+        if self.tree is None:
+            B.decode_paged(self.cfg, self.q_full, cache, page_table, seq_lens, self.o_part,
+                           self.lse_part, max_seq_len or self.max_seq_len, stream,
+                           chunk_tokens=self.split_chunk)
+        else:
+            B.decode_paged_tree(self.cfg, self.q_full, cache, page_table, seq_lens, self.tree,
+                                self.o_part, self.lse_part, max_seq_len or self.max_seq_len,
+                                stream, chunk_tokens=self.split_chunk)
 
     def combine(self, stream=None):
         B.splitkv_combine(self.cfg, self.o_part, self.lse_part, self.o_lat, self.lse, stream)
@@ -74,8 +126,13 @@ class DecodeStep:
         B.up_project_v(self.cfg, self.o_lat, w_uv, self.out, stream)
 
     def absorb_append(self, q_nope, q_rope, w_uk, c_new, k_new, page_table, cache, stream=None):
-        B.absorb_append(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, c_new, k_new,
-                        self.seq_idx, self.qpos, page_table, cache, B.APPEND_ROTATE, stream)
+        if self.tree is None:
+            B.absorb_append(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, c_new, k_new,
+                            self.seq_idx, self.slot, page_table, cache, B.APPEND_ROTATE, stream)
+        else:
+            B.absorb_append_at(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, c_new,
+                               k_new, self.seq_idx, self.slot, self.qpos, page_table, cache,
+                               B.APPEND_ROTATE, stream)
 
     def combine_up_project(self, w_uv, stream=None):
         B.combine_up_project(self.cfg, self.o_part, self.lse_part, self.o_lat, w_uv, self.out,
@@ -102,10 +159,15 @@ class DecodeStep:
 
 
 def fill_cache(cfg: B.Config, cache, page_table, c_all, k_all, seq_idx, pos, stream=None,
-               rows_per_call: int = 1 << 20):
-    """Write every cached row (setup): rows n go to (seq_idx[n], pos[n]), keys rotated."""
+               rows_per_call: int = 1 << 20, rope_pos=None):
+    """Write every cached row (setup): rows n go to (seq_idx[n], pos[n]), keys
+    rotated by pos[n] (rope_pos[n] when given: see token_rope_positions)."""
     n = int(pos.numel())
     for a in range(0, n, rows_per_call):
         e = min(n, a + rows_per_call)
-        B.cache_append(cfg, c_all[a:e], k_all[a:e], seq_idx[a:e], pos[a:e], page_table, cache,
-                       B.APPEND_ROTATE, stream)
+        if rope_pos is None:
+            B.cache_append(cfg, c_all[a:e], k_all[a:e], seq_idx[a:e], pos[a:e], page_table, cache,
+                           B.APPEND_ROTATE, stream)
+        else:
+            B.cache_append_at(cfg, c_all[a:e], k_all[a:e], seq_idx[a:e], pos[a:e],
+                              rope_pos[a:e], page_table, cache, B.APPEND_ROTATE, stream)

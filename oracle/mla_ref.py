@@ -436,14 +436,16 @@ def cache_slot(page_table, seq: int, pos: int, page: int = 64) -> int:
 
 
 def cache_append_image(pool, c, k_rope, seq_idx, pos, page_table, kv_rank: int,
-                       page: int = 64, rotate: bool = False, base: float = 10000.0):
+                       page: int = 64, rotate: bool = False, base: float = 10000.0,
+                       rope_pos=None):
     """The pool after appending rows [c_n ; k^R_n] at (seq_idx[n], pos[n]).
 
     ``pool`` is [P][page][D] in any dtype and is copied, never modified. Raw
     mode copies the values as given (so a bit pattern array gives a byte-exact
     image); rotate mode stores RoPE(k^R_n, pos[n]) in fp64 instead, the rotated
     positional key the cache carries ("Beyond the Attention Bottleneck", "The
-    RoPE Compatibility Problem").
+    RoPE Compatibility Problem"). With ``rope_pos`` the key is rotated by
+    rope_pos[n] while pos[n] still picks the slot (a drafted tree's token).
     """
     out = np.array(pool, copy=True)
     P, pg, D = out.shape
@@ -454,5 +456,6 @@ def cache_append_image(pool, c, k_rope, seq_idx, pos, page_table, kv_rank: int,
     for n in range(len(pos)):
         slot = cache_slot(page_table, int(seq_idx[n]), int(pos[n]), page)
         flat[slot, :kv_rank] = c[n]
-        flat[slot, kv_rank:] = rope(k_rope[n], pos[n], base) if rotate else k_rope[n]
+        rp = pos[n] if rope_pos is None else rope_pos[n]
+        flat[slot, kv_rank:] = rope(k_rope[n], rp, base) if rotate else k_rope[n]
     return flat.reshape(P, page, D)

@@ -12,7 +12,8 @@ import torch
 import oracle
 import workload
 import mla_latent_kv_03_amd as mla
-from mla_latent_kv_03_amd.pipeline import DecodeStep, dtype_of, fill_cache, upload
+from mla_latent_kv_03_amd.pipeline import (DecodeStep, dtype_of, fill_cache, token_rope_positions,
+                                           upload)
 
 NAN_BF16 = 0x7FC1      # quiet NaN with a payload: poison for unused cache slots
 NAN_F32 = 0x7FC00001
@@ -58,8 +59,12 @@ class Case:
         self.pt = upload(inp.page_table, torch.int32)
         self.seq_lens = upload(inp.seq_lens, torch.int32)
         si, pos = tok_index(inp)
+        rope_pos = None
+        if inp.parents is not None:  # drafted tree: keys rotated at prefix + depth
+            rope_pos = upload(np.asarray(token_rope_positions(inp.seq_lens, Q, inp.parents),
+                                         np.int32), torch.int32)
         fill_cache(cfg, self.pool, self.pt, upload(inp.c, dt), upload(inp.k_rope, dt),
-                   upload(si, torch.int32), upload(pos, torch.int32))
+                   upload(si, torch.int32), upload(pos, torch.int32), rope_pos=rope_pos)
         self.q_nope = upload(np.ascontiguousarray(inp.q_nope), dt)
         self.q_rope = upload(np.ascontiguousarray(inp.q_rope), dt)
         self.w_uk = upload(inp.w_uk, dt)
@@ -70,7 +75,8 @@ class Case:
         self.c_new = upload(inp.c[rows], dt)
         self.k_new = upload(inp.k_rope[rows], dt)
         self.chunk = wl.split_chunk if num_splits is None else 0
-        self.step = DecodeStep(cfg, B, Q, self.S, inp.seq_lens, split_chunk=self.chunk)
+        self.step = DecodeStep(cfg, B, Q, self.S, inp.seq_lens, split_chunk=self.chunk,
+                               tree_parents=inp.parents)
         torch.cuda.synchronize()
 
     def run(self, max_seq_len=None, fused=True):

@@ -189,3 +189,51 @@ def test_fused_call_errors(L):
     assert L.mla_combine_up_project(_c(V2), 2, 1, 4, A16, A16, A16, MIS, A16, A16, None) == 4
     assert L.mla_combine_up_project(_c(V2), 0, 1, 4, None, None, None, None, None, None,
                                     None) == 0
+
+
+def test_tree_decode_errors(L):
+    def call(q_len=8, chunk=0, S=4, max_seq=256, batch=2, tree=A16, o=A16):
+        return L.mla_decode_paged_tree(_c(V2), batch, q_len, chunk, S, max_seq, A16, A16, 8, A16,
+                                       4, A16, tree, o, A16, None)
+    assert call(tree=None) == 1
+    assert call(tree=MIS) == 4
+    assert call(q_len=65) == 2 and call(q_len=0) == 2        # one 64-bit branch mask per query
+    assert call(chunk=100) == 2 and call(chunk=64, S=2) == 5  # as the fixed-size plan
+    assert call(S=0) == 2
+    assert call(o=None) == 1
+    assert call(batch=0, tree=None) == 0                     # nothing to do
+
+
+def test_append_at_errors(L):
+    args = [A16, A16, A16, A16]
+    # c_kv, k_rope, seq_idx, pos, rope_pos, page_table, batch, max_pages, cache, num_pages, flags
+    assert L.mla_cache_append_at(_c(V2), 8, *args, MIS, A16, 2, 4, A16, 16, 1, None) == 4
+    assert L.mla_cache_append_at(_c(V2), 8, *args, A16, None, 2, 4, A16, 16, 1, None) == 1
+    assert L.mla_cache_append_at(_c(V2), 8, *args, A16, A16, 2, 4, A16, 16, 3, None) == 2
+    assert L.mla_cache_append_at(_c(V2), 0, *args, None, A16, 2, 4, A16, 16, 1, None) == 0
+    a = [A16] * 5
+    assert L.mla_absorb_append_at(_c(V2), 4, *a, 4, *args, MIS, A16, 2, 4, A16, 16, 1,
+                                  None) == 4
+    assert L.mla_absorb_append_at(_c(V2), 4, None, *a[:4], 4, *args, A16, A16, 2, 4, A16, 16, 1,
+                                  None) == 1
+
+
+def test_pipeline_tree_positions_agree_with_oracle():
+    import oracle
+    import workload
+    from mla_latent_kv_03_amd.pipeline import draft_positions, token_rope_positions
+    wl = workload.WORKLOADS["tiny_f32"].replace(batch=4, q_len=7, seq_len=None, len_range=(7, 90),
+                                                tree="random")
+    inp = workload.make(wl, 6, with_latents=False)
+    slot, pos = draft_positions(inp.seq_lens, 7, inp.parents)
+    allpos = token_rope_positions(inp.seq_lens, 7, inp.parents)
+    off = 0
+    for b, L in enumerate(inp.seq_lens):
+        kp, qp = oracle.tree_positions(int(L), inp.parents[b])
+        assert pos[7 * b:7 * b + 7] == qp.tolist()
+        assert slot[7 * b:7 * b + 7] == list(range(int(L) - 7, int(L)))
+        assert allpos[off:off + int(L)] == kp.tolist()
+        off += int(L)
+    # a chain: positions are the slots
+    slot, pos = draft_positions(inp.seq_lens, 7)
+    assert slot == pos

@@ -1,0 +1,161 @@
+"""GPU parity of tree-structured speculative verification, through the C ABI.
+
+The drafted tokens (the last q_len of each sequence) form a tree; query j sees
+the whole prefix and the drafted tokens on its own branch, and a drafted
+token's position is prefix + depth ("The Architecture of Memory", "Tree
+Attention Verification"). Compared with the fp64 oracle (oracle.mla_ref with
+``parents``) under the same bounds as the chain: max|err| <= 1e-4 * max|ref|
+(fp32) and 1e-2 * max|ref| (bf16), lse within 1e-5 / 1e-2. Every decode
+kernel class is exercised (generic fp32 and bf16, 16 and 64 query rows per
+block), with random trees of several roots, a fixed tree, and the fixed-size
+partition plan; a chain-shaped tree must give the chain call's bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+import mla_latent_kv_03_amd as mla
+from mla_latent_kv_03_amd.pipeline import upload
+
+from gpu_case import Case, check_against_oracle, poisoned_pool, to64
+
+pytestmark = pytest.mark.gpu
+
+W = workload.WORKLOADS
+
+
+def small(name, **kw):
+    return W[name].replace(**kw)
+
+
+TREES = {
+    "f32_generic": small("tiny_f32", batch=3, q_len=5, seq_len=None, len_range=(5, 300),
+                         paged=True, num_splits=3, tree="random"),
+    "bf16_generic_h4": small("v2lite_32k", batch=2, q_len=3, heads=4, seq_len=None,
+                             len_range=(3, 500), paged=True, num_splits=2, tree="random"),
+    "rows16_h16_q5": small("v2lite_paged_varlen", batch=3, q_len=5, len_range=(30, 900),
+                           num_splits=4, tree="random"),
+    "ws_h16_q8": small("v2lite_32k_tree8", batch=2, seq_len=700, num_splits=3),
+    "ws_h128_q4": small("v2_h128_8k", batch=2, q_len=4, seq_len=1000, num_splits=3,
+                        tree="random"),
+    "ws_h16_q8_chunked": small("v2lite_paged_varlen", batch=4, q_len=8, len_range=(8, 700),
+                               num_splits=6, split_chunk=128, tree="random"),
+    "ws_q64": small("v2lite_paged_varlen", batch=2, q_len=64, heads=16, len_range=(64, 400),
+                    num_splits=2, tree="random"),
+}
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu] {request.node.name}", flush=True)
+    yield
+
+
+@pytest.mark.parametrize("name", list(TREES))
+def test_tree_decode_step_matches_oracle(name):
+    wl = TREES[name]
+    case = Case(wl, seed=3)
+    kinds = {"f32_generic": "generic", "bf16_generic_h4": "generic"}
+    if name in kinds:
+        assert mla.decode_kernel_kind(case.cfg, wl.q_len) == kinds[name]
+    case.run()
+    check_against_oracle(case, case.results(), case.oracle())
+    case.run(fused=False)
+    check_against_oracle(case, case.results(), case.oracle())
+
+
+def test_full_size_tree_sampled():
+    wl = W["v2lite_32k_tree8"]
+    case = Case(wl, seed=0)
+    case.run()
+    got = case.results()
+    ref = case.oracle(heads=[0, 7, 15], seqs=[0, 7])
+    check_against_oracle(case, got, ref, heads=[0, 7, 15], seqs=[0, 7])
+    for k in got:
+        assert np.all(np.isfinite(got[k]))
+
+
+@pytest.mark.parametrize("heads,Q", [(16, 5), (16, 8), (4, 3), (128, 4)])
+def test_chain_shaped_tree_gives_chain_bits(heads, Q):
+    wl = small("v2lite_paged_varlen", batch=3, q_len=Q, heads=heads, len_range=(Q, 600),
+               num_splits=3)
+    case = Case(wl, seed=5)
+    st = case.step
+    st.absorb(case.q_nope, case.q_rope, case.w_uk)
+    st.decode(case.pool, case.pt, case.seq_lens)
+    torch.cuda.synchronize()
+    o0, l0 = st.o_part.clone(), st.lse_part.clone()
+    chain = torch.tensor([[i - 1 for i in range(Q)]] * wl.batch, dtype=torch.int32, device="cuda")
+    mla.decode_paged_tree(case.cfg, st.q_full, case.pool, case.pt, case.seq_lens, chain,
+                          st.o_part, st.lse_part, st.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(l0.view(torch.int32), st.lse_part.view(torch.int32))
+    lens = case.inp.seq_lens
+    for b in range(wl.batch):  # partitions with tokens (empty ones stay unwritten)
+        ok = np.isfinite(to64(l0[b]))
+        assert torch.equal(o0[b].view(torch.int32)[torch.from_numpy(ok)],
+                           st.o_part[b].view(torch.int32)[torch.from_numpy(ok)]), (b, lens[b])
+
+
+@pytest.mark.parametrize("heads,Q", [(16, 8), (16, 5), (4, 3)])
+def test_malformed_tree_poisons_only_its_sequence(heads, Q):
+    wl = small("v2lite_paged_varlen", batch=3, q_len=Q, heads=heads, len_range=(50, 400),
+               num_splits=2, tree="random")
+    inp = workload.make(wl, 9)
+    case = Case(wl, inputs=inp)
+    st = case.step
+    st.tree[1, Q - 1] = Q - 1      # sequence 1: a drafted token that continues itself
+    st.absorb(case.q_nope, case.q_rope, case.w_uk)
+    st.decode(case.pool, case.pt, case.seq_lens)
+    st.combine()
+    torch.cuda.synchronize()
+    lse = to64(st.lse)
+    assert np.all(np.isnan(lse[1])) and np.all(np.isnan(to64(st.o_lat)[1]))
+    ref = oracle.mla_decode_ref(inp, seqs=[0, 2])
+    got = {"o": to64(st.out), "o_lat": to64(st.o_lat), "lse": lse}
+    st.up_project(case.w_uv)
+    torch.cuda.synchronize()
+    got["o"] = to64(st.out)
+    check_against_oracle(case, got, ref, seqs=[0, 2])
+
+
+def test_append_at_slot_and_rope_position():
+    wl = small("v2lite_paged_varlen", batch=2, len_range=(100, 300))
+    inp = workload.make(wl, 4)
+    cfg = mla.Config.from_workload(wl)
+    rng = np.random.default_rng(2)
+    n = 24
+    seq = rng.integers(0, 2, n).astype(np.int32)
+    pos = np.array([rng.integers(0, int(inp.seq_lens[b])) for b in seq], np.int32)
+    rope_pos = rng.integers(0, 1 << 20, n).astype(np.int32)
+    c = workload.round_bf16(rng.standard_normal((n, wl.kv_rank)).astype(np.float32))
+    k = workload.round_bf16(rng.standard_normal((n, wl.rope_dim)).astype(np.float32))
+    # distinct slots, so no two rows race
+    _, first = np.unique(np.stack([seq, pos], 1), axis=0, return_index=True)
+    first = np.sort(first)
+    seq, pos, rope_pos, c, k = seq[first], pos[first], rope_pos[first], c[first], k[first]
+    pool = poisoned_pool(cfg, inp.num_pages)
+    pt = upload(inp.page_table, torch.int32)
+    mla.cache_append_at(cfg, upload(c, torch.bfloat16), upload(k, torch.bfloat16),
+                        upload(seq, torch.int32), upload(pos, torch.int32),
+                        upload(rope_pos, torch.int32), pt, pool, mla.APPEND_ROTATE)
+    torch.cuda.synchronize()
+    got = pool.float().cpu().numpy().astype(np.float64)
+    base = got.copy()
+    ref = oracle.cache_append_image(base, c, k, seq, pos, inp.page_table, wl.kv_rank,
+                                    wl.page_size, rotate=True, rope_pos=rope_pos)
+    flat_g = got.reshape(-1, wl.dim)
+    flat_r = ref.reshape(-1, wl.dim)
+    for i in range(len(seq)):
+        slot = oracle.cache_slot(inp.page_table, int(seq[i]), int(pos[i]), wl.page_size)
+        assert np.array_equal(flat_g[slot, :wl.kv_rank], c[i])
+        # the rotated key, rounded once to bf16: within half a bf16 ulp of fp64
+        r = flat_r[slot, wl.kv_rank:]
+        assert np.all(np.abs(flat_g[slot, wl.kv_rank:] - r) <= np.abs(r) * 2.0 ** -8 + 1e-30)
+    # nothing else written: every other slot still holds the poison
+    mask = np.ones(flat_g.shape[0], bool)
+    mask[[oracle.cache_slot(inp.page_table, int(s), int(p), wl.page_size)
+          for s, p in zip(seq, pos)]] = False
+    assert np.all(np.isnan(flat_g[mask]))

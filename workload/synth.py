@@ -102,6 +102,12 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("v2_h128_1m_q4", batch=1, q_len=4, heads=128, kv_rank=512, rope_dim=64,
                  nope_dim=128, v_dim=128, dtype="bf16", seq_len=1048576, num_splits=256,
                  description="1M-token context, Q=4 chain verify, H=128, contiguous"),
+        # tree-structured speculative verification: 8 drafted tokens, a root
+        # with two children, each with two children, one of which has a child
+        Workload("v2lite_32k_tree8", batch=8, q_len=8, heads=16, kv_rank=512, rope_dim=64,
+                 nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=16,
+                 tree=(-1, 0, 0, 1, 1, 2, 2, 3),
+                 description="V2-Lite shape, B=8, L=32768, 8 drafted tokens in a tree, one pass"),
     ]
 }
 
