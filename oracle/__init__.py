@@ -25,5 +25,12 @@ from .mla_ref import (  # noqa: F401
     lse_combine,
     cache_slot,
     cache_append_image,
+    Q8_LEVELS,
+    quantize_q8,
+    dequantize_q8,
+    quantize_cache_rows,
+    rotated_keys_f32,
+    attend_sequence_rotated,
+    mla_decode_ref_q8,
 )
 from .brute import brute_sequence  # noqa: F401

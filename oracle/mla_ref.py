@@ -31,6 +31,11 @@ What it computes, and where the pages define it:
   L - Q, a child one position after its parent (position = L - Q + depth),
   for its query and its cached RoPE key alike, so that every branch is scored
   exactly as the chain of its tokens decoded one by one would be.
+* A low-precision latent cache: rows quantized to 8 bits between their own
+  minimum and maximum ("KV Cache Optimization: Scaling to Million-Token
+  Contexts", technique 3 "KV Cache Quantization", and its comparison table:
+  an INT8 cache halves the bytes). Reading: per cached token, separately for
+  the latent part and the (rotated) RoPE part, in float32.
 * Split-KV partials merged by a log-sum-exp reduction ("The Architecture of
   Memory", "Flash-Decoding and FlashInfer").
 * Paged cache: fixed-size pages mapped logical -> physical through a page
@@ -424,6 +429,130 @@ def lse_combine(o_part, lse_part):
     lse = (m + np.log(tot))[..., 0]
     o = np.einsum("...s,...sd->...d", w / tot, o_part)
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# 8-bit latent cache
+# --------------------------------------------------------------------------
+Q8_LEVELS = 255  # codes 0 .. 255
+
+
+def quantize_q8(x):
+    """Asymmetric 8-bit codes of one row part between its min and max.
+
+    The row's minimum and maximum fix the range; the step is (max - min) /
+    255; a value's code is its distance from the minimum in steps, rounded to
+    the nearest integer (ties to even). All in float32, the precision the
+    codes are decided in. A constant part (max == min) has step 0 and codes 0.
+    Returns (codes uint8 [n], minimum float32, step float32).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    mn, mx = np.float32(x.min()), np.float32(x.max())
+    step = np.float32((mx - mn) / np.float32(Q8_LEVELS))
+    if step == 0:
+        return np.zeros(x.shape, dtype=np.uint8), mn, step
+    codes = np.rint((x - mn) / step)
+    return np.clip(codes, 0, Q8_LEVELS).astype(np.uint8), mn, step
+
+
+def dequantize_q8(codes, mn, step):
+    """The value a code stands for: min + code * step (float64)."""
+    return F64(mn) + np.asarray(codes, F64) * F64(step)
+
+
+def quantize_cache_rows(c, k_rope_rotated_f32):
+    """Quantize cached rows [c ; k^R] per token, the latent part and the RoPE
+    part each on its own range. Inputs float32 [T][d_c], [T][d_r] (the RoPE
+    keys already rotated and in float32). Returns dict(codes uint8 [T][D],
+    lat_min, lat_step, rope_min, rope_step float32 [T]) and the dequantized
+    rows float64 (c_hat [T][d_c], k_hat [T][d_r])."""
+    c = np.asarray(c, np.float32)
+    k = np.asarray(k_rope_rotated_f32, np.float32)
+    T, dc = c.shape
+    dr = k.shape[1]
+    codes = np.empty((T, dc + dr), np.uint8)
+    meta = {n: np.empty(T, np.float32) for n in ("lat_min", "lat_step", "rope_min", "rope_step")}
+    c_hat = np.empty((T, dc), F64)
+    k_hat = np.empty((T, dr), F64)
+    for t in range(T):
+        q, mn, st = quantize_q8(c[t])
+        codes[t, :dc], meta["lat_min"][t], meta["lat_step"][t] = q, mn, st
+        c_hat[t] = dequantize_q8(q, mn, st)
+        q, mn, st = quantize_q8(k[t])
+        codes[t, dc:], meta["rope_min"][t], meta["rope_step"][t] = q, mn, st
+        k_hat[t] = dequantize_q8(q, mn, st)
+    return dict(codes=codes, **meta), c_hat, k_hat
+
+
+def rotated_keys_f32(k_rope_raw, positions, base: float = 10000.0) -> np.ndarray:
+    """RoPE keys rotated at their positions in float64, then rounded to float32
+    (the values an 8-bit cache row quantizes)."""
+    return rope(k_rope_raw, positions, base).astype(np.float32)
+
+
+def attend_sequence_rotated(c, k_rotated, q_nope, q_rope, w_uk, w_uv, scale,
+                            base: float = 10000.0, parents=None):
+    """attend_sequence over a cache whose RoPE keys are given already rotated
+    (as an 8-bit cache stores them): the same unabsorbed attention, the key
+    positions entering only through the stored rotation."""
+    c = np.asarray(c, F64)
+    k_rotated = np.asarray(k_rotated, F64)
+    L = c.shape[0]
+    q_nope = np.asarray(q_nope, F64)
+    Q, H, _ = q_nope.shape
+    if parents is None:
+        pq = query_positions(L, Q)
+        masked = causal_mask(L, pq)
+    else:
+        _, pq = tree_positions(L, parents)
+        masked = tree_excluded(L, parents)
+    q = np.concatenate([q_nope, rope(q_rope, pq[:, None], base)], axis=-1)   # [Q][H][dk]
+    w_uk = np.asarray(w_uk, F64)
+    Hk, dn, dc = w_uk.shape
+    kc = (c @ w_uk.reshape(Hk * dn, dc).T).reshape(L, Hk, dn)
+    k = np.concatenate([kc, np.broadcast_to(k_rotated[:, None, :], (L, Hk, k_rotated.shape[1]))],
+                       axis=-1)                                               # [L][H][dk]
+    s = scale * np.einsum("qhd,thd->qht", q, k)
+    s[np.broadcast_to(masked[:, None, :], s.shape)] = -np.inf
+    m = s.max(-1, keepdims=True)
+    e = np.exp(s - m)
+    den = e.sum(-1, keepdims=True)
+    p = e / den
+    w_uv = np.asarray(w_uv, F64)
+    v = (c @ w_uv.reshape(-1, dc).T).reshape(L, w_uv.shape[0], w_uv.shape[1])
+    o = np.einsum("qht,thv->qhv", p, v)
+    o_lat = np.einsum("qht,tc->qhc", p, c)
+    return o, o_lat, m[..., 0] + np.log(den[..., 0])
+
+
+def mla_decode_ref_q8(inputs, heads: Optional[Sequence[int]] = None,
+                      seqs: Optional[Sequence[int]] = None):
+    """The oracle over an 8-bit latent cache: every cached row of ``inputs`` is
+    quantized as the cache stores it (quantize_cache_rows, RoPE keys rotated
+    at their positions first) and the decode attends over the dequantized
+    rows. Returns the dict of mla_decode_ref plus "codes" per selected
+    sequence for the append checks."""
+    wl = inputs.wl
+    hs = list(range(wl.heads)) if heads is None else list(heads)
+    bs = list(range(wl.batch)) if seqs is None else list(seqs)
+    B, Q = wl.batch, wl.q_len
+    o = np.full((B, Q, len(hs), wl.v_dim), np.nan)
+    o_lat = np.full((B, Q, len(hs), wl.kv_rank), np.nan)
+    lse = np.full((B, Q, len(hs)), np.nan)
+    w_uk = np.asarray(inputs.w_uk, F64)[hs]
+    w_uv = np.asarray(inputs.w_uv, F64)[hs]
+    rows = {}
+    for b in bs:
+        c, kr = inputs.seq(b)
+        L = c.shape[0]
+        par = None if getattr(inputs, "parents", None) is None else inputs.parents[b]
+        kpos = np.arange(L) if par is None else tree_positions(L, par)[0]
+        qrows, c_hat, k_hat = quantize_cache_rows(c, rotated_keys_f32(kr, kpos, wl.rope_base))
+        rows[b] = qrows
+        o[b], o_lat[b], lse[b] = attend_sequence_rotated(
+            c_hat, k_hat, inputs.q_nope[b][:, hs], inputs.q_rope[b][:, hs], w_uk, w_uv,
+            wl.softmax_scale, wl.rope_base, parents=par)
+    return {"o": o, "o_lat": o_lat, "lse": lse, "rows": rows}
 
 
 # --------------------------------------------------------------------------
