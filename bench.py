@@ -34,13 +34,14 @@ METRIC = "MLA decode latent-cache GB/s (% of HBM peak) + decode tokens/s, V2-Lit
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LAYERS = {"v2lite_32k": 27, "v2lite_paged_varlen": 27, "v2_h128_8k": 4, "v2_h128_1m_q4": 2,
-          "v2lite_32k_tree8": 27, "tiny_f32": 4}
+          "v2lite_32k_tree8": 27, "v2lite_32k_q8": 27, "tiny_f32": 4}
 CSRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc")
 # decode kernel name (mla_decode_kernel_name) -> (kernel symbol, the sources that define it)
 DECODE_KERNELS = {
     "mfma_rows16": ("decode_rows16_kernel", ["mla_decode_common.h", "mla_decode_rows16.hip"]),
     "mfma_ws": ("decode_ws_kernel", ["mla_decode_common.h", "mla_decode_ws.hip"]),
     "generic": ("decode_generic_kernel", ["mla_kernels.hip"]),
+    "mfma_q8": ("decode_q8_kernel", ["mla_decode_common.h", "mla_q8.hip"]),
 }
 
 
@@ -113,15 +114,17 @@ def cpu_baseline(wl, inp, budget_flops=2.4e12):
             break
         seqs.append(b)
         spent += seq_cost(b, heads)
+    ref = oracle.mla_decode_ref_q8 if wl.cache == "q8" else oracle.mla_decode_ref
     t = time.perf_counter()
-    oracle.mla_decode_ref(inp, heads=list(range(heads)), seqs=seqs)
+    ref(inp, heads=list(range(heads)), seqs=seqs)
     dt = time.perf_counter() - t
     tokens = sum(int(inp.seq_lens[b]) for b in seqs)
-    nbytes = tokens * wl.dim * wl.elem_bytes * heads / wl.heads
+    nbytes = tokens * wl.cache_row_bytes * heads / wl.heads
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{len(seqs)} of {wl.batch} sequences ({tokens} cached tokens), "
-                      f"{heads} of {wl.heads} heads, {dt:.1f} s; fp64 unabsorbed NumPy oracle; "
+                      f"{heads} of {wl.heads} heads, {dt:.1f} s; fp64 unabsorbed NumPy oracle"
+                      f"{' (rows coded to 8 bits first)' if wl.cache == 'q8' else ''}; "
                       f"bytes counted x {heads}/{wl.heads}",
             "seconds": round(dt, 2),
             "decode_tokens_per_s": round(len(seqs) * wl.q_len * heads / wl.heads / dt, 4)}
@@ -138,7 +141,8 @@ def main():
 
     import workload
     import mla_latent_kv_03_amd as mla
-    from mla_latent_kv_03_amd.pipeline import DecodeStep, fill_cache, token_rope_positions, upload
+    from mla_latent_kv_03_amd.pipeline import (DecodeStep, fill_cache, fill_cache_q8,
+                                               token_rope_positions, upload)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -162,15 +166,22 @@ def main():
     # ---- device state: one cache pool per layer (same bytes, distinct addresses)
     pt = upload(inp.page_table, torch.int32)
     seq_lens = upload(inp.seq_lens, torch.int32)
-    pool0 = torch.full((inp.num_pages, wl.page_size, wl.dim), float("nan"), dtype=dt, device="cuda")
+    q8 = wl.cache == "q8"
+    if q8:  # 8-bit rows: codes plus (min, step) pairs
+        pool0 = torch.full((inp.num_pages, wl.page_size, wl.dim + 16), 255, dtype=torch.uint8,
+                           device="cuda")
+    else:
+        pool0 = torch.full((inp.num_pages, wl.page_size, wl.dim), float("nan"), dtype=dt,
+                           device="cuda")
     si = np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(inp.seq_lens)])
     pos = np.concatenate([np.arange(int(L), dtype=np.int32) for L in inp.seq_lens])
     rope_pos = None
     if inp.parents is not None:  # a drafted tree: its keys sit at prefix + depth
         rope_pos = upload(np.asarray(token_rope_positions(inp.seq_lens, wl.q_len, inp.parents),
                                      np.int32), torch.int32)
-    fill_cache(cfg, pool0, pt, upload(inp.c, dt), upload(inp.k_rope, dt), upload(si, torch.int32),
-               upload(pos, torch.int32), rope_pos=rope_pos)
+    (fill_cache_q8 if q8 else fill_cache)(cfg, pool0, pt, upload(inp.c, dt), upload(inp.k_rope, dt),
+                                          upload(si, torch.int32), upload(pos, torch.int32),
+                                          rope_pos=rope_pos)
     pools = [pool0] + [pool0.clone() for _ in range(n_layers - 1)]
     q_nope, q_rope = upload(inp.q_nope, dt), upload(inp.q_rope, dt)
     w_uk, w_uv = upload(inp.w_uk, dt), upload(inp.w_uv, dt)
@@ -178,7 +189,7 @@ def main():
                            for b, L in enumerate(inp.seq_lens)])
     c_new, k_new = upload(inp.c[rows], dt), upload(inp.k_rope[rows], dt)
     steps = [DecodeStep(cfg, B, Q, wl.num_splits, inp.seq_lens, split_chunk=wl.split_chunk,
-                        tree_parents=inp.parents) for _ in range(1)]
+                        tree_parents=inp.parents, cache_q8=q8) for _ in range(1)]
     st = steps[0]
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
@@ -272,14 +283,14 @@ def main():
 
     # ---- algorithmic work
     total_tokens = int(inp.seq_lens.astype(np.int64).sum())
-    cache_bytes = total_tokens * wl.dim * wl.elem_bytes            # read once per step
+    cache_bytes = total_tokens * wl.cache_row_bytes                # read once per step
     flops = total_tokens * Q * H * (2 * wl.dim + 2 * wl.kv_rank)
     gbs_step = cache_bytes / (ms_step * 1e-3) / 1e9
     gbs_decode = cache_bytes / (decode_ms * 1e-3) / 1e9
     tflops_decode = flops / (decode_ms * 1e-3) / 1e12
     ai = flops / cache_bytes
     bound = "hbm" if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
-    kernel = mla.decode_kernel_kind(cfg, Q)
+    kernel = "mfma_q8" if q8 else mla.decode_kernel_kind(cfg, Q)
     ksym, ksrc = DECODE_KERNELS[kernel]
     khash = src_hash(ksrc)
     if bound == "hbm":
@@ -319,6 +330,7 @@ def main():
                    "layer_caches_rotated": n_layers, "hip_graph": bool(args.graph),
                    "library_calls_per_step": 5 if args.unfused else 3,
                    "drafted_tree": None if wl.tree is None else list(wl.tree),
+                   "cache_format": wl.cache, "cache_bytes_per_token": wl.cache_row_bytes,
                    "decode_kernel": kernel},
         "pct_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B * Q / (ms_step * 1e-3), 1),

@@ -259,6 +259,42 @@ mla_status_t mla_decode_paged_tree(const mla_config_t* cfg, int32_t batch, int32
 mla_status_t mla_chunk_plan(const mla_config_t* cfg, int64_t total_tokens, int32_t max_seq_len,
                             int32_t num_cus, int32_t* chunk_tokens, int32_t* num_splits);
 
+/* 8-bit latent cache (f2; "KV Cache Optimization: Scaling to Million-Token
+ * Contexts", technique 3 "KV Cache Quantization" and its comparison table):
+ * a row of cache_q8 [num_pages][page_size][D + 16] bytes is the d_c + d_r
+ * codes (uint8) of the row's latent part and rotated RoPE part, each coded
+ * between its own minimum and maximum, followed by four fp32: latent min,
+ * latent step, RoPE min, RoPE step. step = (max - min) / 255, code =
+ * rint((x - min) / step) in float32 (0 when step is 0); a code stands for
+ * min + code * step. 592 bytes per token for d_c = 512, d_r = 64 (1,152 in
+ * bf16). mla_cache_q8_bytes_per_token: D + 16, or 0 for an invalid config or
+ * when D is not a multiple of 16. */
+size_t mla_cache_q8_bytes_per_token(const mla_config_t* cfg);
+
+/* a2 into an 8-bit cache: row n is coded as above and written to the slot
+ * that mla_cache_append_at picks (seq_idx[n], pos[n]); its RoPE key rotated
+ * by rope_pos[n] (NULL: pos[n]) before coding (MLA_APPEND_ROTATE) or coded
+ * as given (MLA_APPEND_RAW). c_kv, k_rope as for mla_cache_append (type T).
+ * Errors as mla_cache_append; MLA_ERR_UNSUPPORTED when D % 16 != 0. */
+mla_status_t mla_cache_append_q8(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                                 const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                 const int32_t* rope_pos, const int32_t* page_table,
+                                 int32_t batch, int32_t max_pages, void* cache_q8,
+                                 int64_t num_pages, int32_t flags, void* stream);
+
+/* a4 over an 8-bit cache: mla_decode_paged (chunk_tokens = 0) or
+ * mla_decode_paged_chunked (chunk_tokens > 0), with tree_parent as in
+ * mla_decode_paged_tree (NULL: the chain), reading each cached row as its
+ * decoded values min + code * step. The same outputs, layouts and errors;
+ * MLA_ERR_UNSUPPORTED unless bf16, d_c = 512, d_r = 64, page_size a
+ * multiple of 64 and q_len * H a multiple of 16. */
+mla_status_t mla_decode_paged_q8(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                 int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
+                                 const void* q_full, const void* cache_q8, int64_t num_pages,
+                                 const int32_t* page_table, int32_t max_pages,
+                                 const int32_t* seq_lens, const int32_t* tree_parent,
+                                 float* o_part, float* lse_part, void* stream);
+
 /* a5. Log-sum-exp merge of the partitions ("The Architecture of Memory",
  * "Flash-Decoding and FlashInfer"), per row r = (b, j, h):
  *   LSE = ln sum_s e^(lse_s),  o_lat[r] = sum_s e^(lse_s - LSE) o_part[r][s]

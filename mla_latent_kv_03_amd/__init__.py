@@ -16,7 +16,9 @@ fallback. If the library is missing, every call raises.
 absorb_append and combine_up_project run the first two and the last two of
 these calls in one launch each, with the same results. A tree of drafted
 tokens is verified with cache_append_at / absorb_append_at (slot and RoPE
-position differ) and decode_paged_tree.
+position differ) and decode_paged_tree. An 8-bit latent cache (uint8 rows
+of codes plus per-part min and step) is written by cache_append_q8 and read
+by decode_paged_q8.
 """
 from ._binding import (  # noqa: F401
     F32,
@@ -46,4 +48,7 @@ from ._binding import (  # noqa: F401
     cache_append_at,
     absorb_append_at,
     decode_paged_tree,
+    cache_q8_bytes_per_token,
+    cache_append_q8,
+    decode_paged_q8,
 )

@@ -109,6 +109,11 @@ def lib() -> ctypes.CDLL:
                                                 VP, VP, I32, I32, VP, I64, I32, VP]),
         "mla_decode_paged_tree": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32,
                                                  VP, VP, FP, FP, VP]),
+        "mla_cache_q8_bytes_per_token": (ctypes.c_size_t, [P]),
+        "mla_cache_append_q8": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, VP, I32, I32, VP, I64,
+                                               I32, VP]),
+        "mla_decode_paged_q8": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32,
+                                               VP, VP, FP, FP, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -211,23 +216,24 @@ def _absorb_args(cfg: Config, q_nope, q_rope, pos, w_uk, q_full):
             _need(q_full, "q_full", dt, n * H * cfg.dim))
 
 
-def _append_args(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache, mode):
+def _append_args(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache, mode, q8=False):
     t = _torch()
     n = int(pos.numel())
     dt = _elem_dtype(cfg)
     if page_table.dim() != 2:
         raise ValueError("page_table: expected [batch][max_pages]")
     batch, max_pages = page_table.shape
-    if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != cfg.dim:
-        raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{cfg.dim}]")
+    row = cfg.dim + 16 if q8 else cfg.dim
+    if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != row:
+        raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{row}]")
     num_pages = int(cache.shape[0])
     return (n, _need(c_kv, "c_kv", dt, n * cfg.kv_rank),
             _need(k_rope, "k_rope", dt, n * cfg.rope_dim),
             _need(seq_idx, "seq_idx", t.int32, n),
             _need(pos, "pos", t.int32, n),
             _need(page_table, "page_table", t.int32, batch * max_pages),
-            int(batch), int(max_pages), _need(cache, "cache", dt, cache.numel()), num_pages,
-            int(mode))
+            int(batch), int(max_pages),
+            _need(cache, "cache", t.uint8 if q8 else dt, cache.numel()), num_pages, int(mode))
 
 
 def absorb_q(cfg: Config, q_nope, q_rope, pos, w_uk, q_full, stream=None):
@@ -279,6 +285,21 @@ def absorb_append_at(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_r
                                    _stream(stream)), "mla_absorb_append_at")
 
 
+def cache_q8_bytes_per_token(cfg: Config) -> int:
+    """Bytes of one 8-bit cache row: d_c + d_r codes + 16 bytes of (min, step)."""
+    return lib().mla_cache_q8_bytes_per_token(ctypes.byref(cfg.c()))
+
+
+def cache_append_q8(cfg: Config, c_kv, k_rope, seq_idx, pos, rope_pos, page_table, cache_q8,
+                    mode: int = APPEND_ROTATE, stream=None):
+    """a2 into an 8-bit cache: cache_q8 uint8 [num_pages][page][D + 16]; each row
+    coded per part between its own min and max; rope_pos as cache_append_at."""
+    a = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache_q8, mode, q8=True)
+    rp = _rope_pos_arg(rope_pos, a[0])
+    _ck(lib().mla_cache_append_q8(ctypes.byref(cfg.c()), *a[:5], rp, *a[5:], _stream(stream)),
+        "mla_cache_append_q8")
+
+
 def chunk_plan(cfg: Config, total_tokens: int, max_seq_len: int, num_cus: int = 256):
     """A fixed-size partition plan (chunk_tokens, num_splits) for decode_paged(chunk_tokens=...)."""
     ck, ns = ctypes.c_int32(0), ctypes.c_int32(0)
@@ -296,6 +317,14 @@ def decode_paged(cfg: Config, q_full, cache, page_table, seq_lens, o_part, lse_p
             chunk_tokens)
 
 
+def decode_paged_q8(cfg: Config, q_full, cache_q8, page_table, seq_lens, o_part, lse_part,
+                    max_seq_len: int, stream=None, chunk_tokens: int = 0, tree_parent=None):
+    """a4 over an 8-bit cache (cache_q8 uint8 [num_pages][page][D + 16]); other
+    arguments as decode_paged / decode_paged_tree."""
+    _decode(cfg, q_full, cache_q8, page_table, seq_lens, tree_parent, o_part, lse_part,
+            max_seq_len, stream, chunk_tokens, q8=True)
+
+
 def decode_paged_tree(cfg: Config, q_full, cache, page_table, seq_lens, tree_parent, o_part,
                       lse_part, max_seq_len: int, stream=None, chunk_tokens: int = 0):
     """a4 verifying a tree of drafted tokens: tree_parent [B][Q] int32, entry i
@@ -306,7 +335,7 @@ def decode_paged_tree(cfg: Config, q_full, cache, page_table, seq_lens, tree_par
 
 
 def _decode(cfg, q_full, cache, page_table, seq_lens, tree_parent, o_part, lse_part, max_seq_len,
-            stream, chunk_tokens):
+            stream, chunk_tokens, q8=False):
     t = _torch()
     if q_full.dim() != 4:
         raise ValueError("q_full: expected [batch][q_len][H][D]")
@@ -318,15 +347,23 @@ def _decode(cfg, q_full, cache, page_table, seq_lens, tree_parent, o_part, lse_p
     if page_table.dim() != 2 or page_table.shape[0] != B:
         raise ValueError("page_table: expected [batch][max_pages]")
     max_pages = int(page_table.shape[1])
-    if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != cfg.dim:
-        raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{cfg.dim}]")
+    row = cfg.dim + 16 if q8 else cfg.dim
+    if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != row:
+        raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{row}]")
     num_pages = int(cache.shape[0])
     args = (_need(q_full, "q_full", dt, B * Q * H * cfg.dim),
-            _need(cache, "cache", dt, cache.numel()))
+            _need(cache, "cache", t.uint8 if q8 else dt, cache.numel()))
     pt = _need(page_table, "page_table", t.int32, B * max_pages)
     sl = _need(seq_lens, "seq_lens", t.int32, B)
     op = _need(o_part, "o_part", t.float32, B * Q * H * S * cfg.kv_rank)
     lp = _need(lse_part, "lse_part", t.float32, B * Q * H * S)
+    if q8:
+        tp = None if tree_parent is None else _need(tree_parent, "tree_parent", t.int32, B * Q)
+        _ck(lib().mla_decode_paged_q8(ctypes.byref(cfg.c()), B, Q, int(chunk_tokens), S,
+                                      int(max_seq_len), args[0], args[1], num_pages, pt,
+                                      max_pages, sl, tp, op, lp, _stream(stream)),
+            "mla_decode_paged_q8")
+        return
     if tree_parent is not None:
         tp = _need(tree_parent, "tree_parent", t.int32, B * Q)
         _ck(lib().mla_decode_paged_tree(ctypes.byref(cfg.c()), B, Q, int(chunk_tokens), S,

@@ -350,6 +350,62 @@ mla_status_t mla_decode_paged_tree(const mla_config_t* cfg, int32_t batch, int32
                      stream);
 }
 
+size_t mla_cache_q8_bytes_per_token(const mla_config_t* cfg) {
+  if (check_config(cfg) != MLA_OK || (cfg->kv_rank + cfg->rope_dim) % 16) return 0;
+  return (size_t)(cfg->kv_rank + cfg->rope_dim) + 16;
+}
+
+mla_status_t mla_cache_append_q8(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                                 const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                 const int32_t* rope_pos, const int32_t* page_table,
+                                 int32_t batch, int32_t max_pages, void* cache_q8,
+                                 int64_t num_pages, int32_t flags, void* stream) {
+  mla_status_t st = check_append(cfg, n_tok, c_kv, k_rope, seq_idx, pos, page_table, batch,
+                                 max_pages, cache_q8, num_pages, flags);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE((cfg->kv_rank + cfg->rope_dim) % 16 == 0, MLA_ERR_UNSUPPORTED);
+  if (n_tok == 0) return MLA_OK;
+  if (rope_pos) MLA_CHECK_PTR(rope_pos);
+  return hip_status(mla::launch_cache_append_q8(shape_of(cfg), n_tok, c_kv, k_rope, seq_idx, pos,
+                                                rope_pos, page_table, batch, max_pages, cache_q8,
+                                                num_pages, flags == MLA_APPEND_ROTATE, stream));
+}
+
+mla_status_t mla_decode_paged_q8(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                 int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
+                                 const void* q_full, const void* cache_q8, int64_t num_pages,
+                                 const int32_t* page_table, int32_t max_pages,
+                                 const int32_t* seq_lens, const int32_t* tree_parent,
+                                 float* o_part, float* lse_part, void* stream) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(batch >= 0 && q_len >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)q_len * cfg->num_heads <= 65536, MLA_ERR_SHAPE);
+  if (tree_parent) MLA_REQUIRE(q_len <= kMaxTreeDrafts, MLA_ERR_SHAPE);
+  MLA_REQUIRE(max_seq_len >= q_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
+  if (chunk_tokens != 0) {
+    MLA_REQUIRE(chunk_tokens >= cfg->page_size && chunk_tokens % cfg->page_size == 0,
+                MLA_ERR_SHAPE);
+    MLA_REQUIRE((int64_t)chunk_tokens * num_splits >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
+  }
+  mla::Shape sh = shape_of(cfg);
+  MLA_REQUIRE(mla::decode_q8_ok(sh, q_len), MLA_ERR_UNSUPPORTED);
+  if (batch == 0) return MLA_OK;
+  MLA_CHECK_PTR(q_full);
+  MLA_CHECK_PTR(cache_q8);
+  MLA_CHECK_PTR(page_table);
+  MLA_CHECK_PTR(seq_lens);
+  MLA_CHECK_PTR(o_part);
+  MLA_CHECK_PTR(lse_part);
+  if (tree_parent) MLA_CHECK_PTR(tree_parent);
+  sh.split_fixed = chunk_tokens;
+  return hip_status(mla::launch_decode_q8(sh, batch, q_len, num_splits, max_seq_len, q_full,
+                                          cache_q8, num_pages, page_table, max_pages, seq_lens,
+                                          tree_parent, o_part, lse_part, stream));
+}
+
 mla_status_t mla_chunk_plan(const mla_config_t* cfg, int64_t total_tokens, int32_t max_seq_len,
                             int32_t num_cus, int32_t* chunk_tokens, int32_t* num_splits) {
   mla_status_t st = check_config(cfg);

@@ -64,6 +64,19 @@ int launch_combine_up_project(const Shape& s, int n_tok, int num_splits, const f
                               const float* lse_part, void* o_lat, float* lse, const void* w_uv,
                               void* out, void* stream);
 
+// 8-bit latent cache: rows of d_c + d_r codes plus 16 bytes of (min, step)
+// pairs. The decode needs the DeepSeek row (bf16, 512 + 64), page % 64 == 0
+// and q_len * H % 16 == 0 (decode_q8_ok).
+int launch_cache_append_q8(const Shape& s, int n_tok, const void* c_kv, const void* k_rope,
+                           const int32_t* seq_idx, const int32_t* pos, const int32_t* rope_pos,
+                           const int32_t* page_table, int batch, int max_pages, void* cache,
+                           int64_t num_pages, int rotate, void* stream);
+bool decode_q8_ok(const Shape& s, int q_len);
+int launch_decode_q8(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
+                     const void* q_full, const void* cache, int64_t num_pages,
+                     const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                     const int32_t* tree_parent, float* o_part, float* lse_part, void* stream);
+
 // Which decode kernel a shape takes (for tests and tools): 0 = generic VALU
 // kernel, 1 = bf16 MFMA kernel with 16 query rows per block, 2 = bf16 MFMA
 // kernel with 64 query rows per block.

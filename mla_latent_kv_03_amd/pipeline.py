@@ -73,10 +73,12 @@ class DecodeStep:
     """
 
     def __init__(self, cfg: B.Config, batch: int, q_len: int, num_splits: int,
-                 seq_lens_host, device="cuda", split_chunk: int = 0, tree_parents=None):
+                 seq_lens_host, device="cuda", split_chunk: int = 0, tree_parents=None,
+                 cache_q8: bool = False):
         t = _torch()
         self.cfg, self.batch, self.q_len, self.num_splits = cfg, batch, q_len, num_splits
         self.split_chunk = split_chunk  # > 0: fixed-size partitions
+        self.cache_q8 = cache_q8        # the cache holds 8-bit rows
         H, D, dc, dv = cfg.num_heads, cfg.dim, cfg.kv_rank, cfg.v_dim
         dt = dtype_of(cfg)
         lens = [int(x) for x in seq_lens_host]
@@ -102,7 +104,11 @@ class DecodeStep:
         B.absorb_q(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, stream)
 
     def append(self, c_new, k_new, page_table, cache, stream=None):
-        if self.tree is None:
+        if self.cache_q8:
+            B.cache_append_q8(self.cfg, c_new, k_new, self.seq_idx, self.slot,
+                              None if self.tree is None else self.qpos, page_table, cache,
+                              B.APPEND_ROTATE, stream)
+        elif self.tree is None:
             B.cache_append(self.cfg, c_new, k_new, self.seq_idx, self.slot, page_table, cache,
                            B.APPEND_ROTATE, stream)
         else:
@@ -110,7 +116,11 @@ class DecodeStep:
                               page_table, cache, B.APPEND_ROTATE, stream)
 
     def decode(self, cache, page_table, seq_lens, stream=None, max_seq_len: Optional[int] = None):
-        if self.tree is None:
+        if self.cache_q8:
+            B.decode_paged_q8(self.cfg, self.q_full, cache, page_table, seq_lens, self.o_part,
+                              self.lse_part, max_seq_len or self.max_seq_len, stream,
+                              chunk_tokens=self.split_chunk, tree_parent=self.tree)
+        elif self.tree is None:
             B.decode_paged(self.cfg, self.q_full, cache, page_table, seq_lens, self.o_part,
                            self.lse_part, max_seq_len or self.max_seq_len, stream,
                            chunk_tokens=self.split_chunk)
@@ -126,7 +136,10 @@ class DecodeStep:
         B.up_project_v(self.cfg, self.o_lat, w_uv, self.out, stream)
 
     def absorb_append(self, q_nope, q_rope, w_uk, c_new, k_new, page_table, cache, stream=None):
-        if self.tree is None:
+        if self.cache_q8:  # no fused call for the 8-bit append: the two calls in order
+            self.absorb(q_nope, q_rope, w_uk, stream)
+            self.append(c_new, k_new, page_table, cache, stream)
+        elif self.tree is None:
             B.absorb_append(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, c_new, k_new,
                             self.seq_idx, self.slot, page_table, cache, B.APPEND_ROTATE, stream)
         else:
@@ -156,6 +169,17 @@ class DecodeStep:
             self.combine(stream)
             self.up_project(w_uv, stream)
         return self.out
+
+
+def fill_cache_q8(cfg: B.Config, cache_q8, page_table, c_all, k_all, seq_idx, pos, stream=None,
+                  rows_per_call: int = 1 << 20, rope_pos=None):
+    """fill_cache for an 8-bit cache (cache_q8 uint8 [num_pages][page][D + 16])."""
+    n = int(pos.numel())
+    for a in range(0, n, rows_per_call):
+        e = min(n, a + rows_per_call)
+        B.cache_append_q8(cfg, c_all[a:e], k_all[a:e], seq_idx[a:e], pos[a:e],
+                          None if rope_pos is None else rope_pos[a:e], page_table, cache_q8,
+                          B.APPEND_ROTATE, stream)
 
 
 def fill_cache(cfg: B.Config, cache, page_table, c_all, k_all, seq_idx, pos, stream=None,

@@ -12,8 +12,8 @@ import torch
 import oracle
 import workload
 import mla_latent_kv_03_amd as mla
-from mla_latent_kv_03_amd.pipeline import (DecodeStep, dtype_of, fill_cache, token_rope_positions,
-                                           upload)
+from mla_latent_kv_03_amd.pipeline import (DecodeStep, dtype_of, fill_cache, fill_cache_q8,
+                                           token_rope_positions, upload)
 
 NAN_BF16 = 0x7FC1      # quiet NaN with a payload: poison for unused cache slots
 NAN_F32 = 0x7FC00001
@@ -55,7 +55,12 @@ class Case:
         dt = dtype_of(cfg)
         self.dt = dt
         B, Q, H = wl.batch, wl.q_len, wl.heads
-        self.pool = poisoned_pool(cfg, inp.num_pages)
+        self.q8 = wl.cache == "q8"
+        if self.q8:  # poison: every byte 0xFF (codes 255, NaN minima and steps)
+            self.pool = torch.full((inp.num_pages, cfg.page_size, cfg.dim + 16), 255,
+                                   dtype=torch.uint8, device="cuda")
+        else:
+            self.pool = poisoned_pool(cfg, inp.num_pages)
         self.pt = upload(inp.page_table, torch.int32)
         self.seq_lens = upload(inp.seq_lens, torch.int32)
         si, pos = tok_index(inp)
@@ -63,8 +68,9 @@ class Case:
         if inp.parents is not None:  # drafted tree: keys rotated at prefix + depth
             rope_pos = upload(np.asarray(token_rope_positions(inp.seq_lens, Q, inp.parents),
                                          np.int32), torch.int32)
-        fill_cache(cfg, self.pool, self.pt, upload(inp.c, dt), upload(inp.k_rope, dt),
-                   upload(si, torch.int32), upload(pos, torch.int32), rope_pos=rope_pos)
+        fill = fill_cache_q8 if self.q8 else fill_cache
+        fill(cfg, self.pool, self.pt, upload(inp.c, dt), upload(inp.k_rope, dt),
+             upload(si, torch.int32), upload(pos, torch.int32), rope_pos=rope_pos)
         self.q_nope = upload(np.ascontiguousarray(inp.q_nope), dt)
         self.q_rope = upload(np.ascontiguousarray(inp.q_rope), dt)
         self.w_uk = upload(inp.w_uk, dt)
@@ -76,7 +82,7 @@ class Case:
         self.k_new = upload(inp.k_rope[rows], dt)
         self.chunk = wl.split_chunk if num_splits is None else 0
         self.step = DecodeStep(cfg, B, Q, self.S, inp.seq_lens, split_chunk=self.chunk,
-                               tree_parents=inp.parents)
+                               tree_parents=inp.parents, cache_q8=self.q8)
         torch.cuda.synchronize()
 
     def run(self, max_seq_len=None, fused=True):
@@ -91,6 +97,8 @@ class Case:
         return {"o": to64(s.out), "o_lat": to64(s.o_lat), "lse": to64(s.lse)}
 
     def oracle(self, heads=None, seqs=None):
+        if self.q8:  # the attention over the rows the 8-bit cache encodes
+            return oracle.mla_decode_ref_q8(self.inp, heads=heads, seqs=seqs)
         return oracle.mla_decode_ref(self.inp, heads=heads, seqs=seqs)
 
 

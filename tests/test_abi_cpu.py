@@ -237,3 +237,23 @@ def test_pipeline_tree_positions_agree_with_oracle():
     # a chain: positions are the slots
     slot, pos = draft_positions(inp.seq_lens, 7)
     assert slot == pos
+
+
+def test_q8_entry_errors(L):
+    assert L.mla_cache_q8_bytes_per_token(_c(V2)) == 592
+    assert L.mla_cache_q8_bytes_per_token(_c(TINY)) == 96          # 64 + 16 codes + 16
+    def dec(cfg=V2, q_len=1, batch=2, chunk=0, S=4, tree=None, o=A16, max_pages=4):
+        return L.mla_decode_paged_q8(_c(cfg), batch, q_len, chunk, S, 256, A16, A16, 8, A16,
+                                     max_pages, A16, tree, o, A16, None)
+    assert dec(o=None) == 1
+    assert dec(tree=MIS) == 4
+    assert dec(q_len=65, tree=A16) == 2                              # tree mask limit
+    assert dec(cfg=mla.Config(num_heads=16, page_size=32), max_pages=8) == 6  # tile > page
+    assert dec(cfg=mla.Config(num_heads=8)) == 6                     # 8 rows: no kernel
+    assert dec(cfg=TINY) == 6                                        # fp32 / other shapes
+    assert dec(batch=0) == 0
+    args = [A16, A16, A16, A16]
+    assert L.mla_cache_append_q8(_c(V2), 8, *args, MIS, A16, 2, 4, A16, 16, 1, None) == 4
+    assert L.mla_cache_append_q8(_c(V2), 8, *args, None, A16, 2, 4, None, 16, 1, None) == 1
+    odd = mla.Config(num_heads=4, kv_rank=64, rope_dim=8, nope_dim=32, v_dim=32, dtype=mla.F32)
+    assert L.mla_cache_append_q8(_c(odd), 8, *args, None, A16, 2, 4, A16, 16, 1, None) == 6

@@ -54,6 +54,9 @@ class Workload:
     # tuple = that parent array for every sequence; "random" = a seeded
     # random tree per sequence (parent of token j uniform in [-1, j-1])
     tree: object = None
+    # cache format: "native" = rows in the workload dtype; "q8" = 8-bit codes
+    # per row part plus (min, step) pairs, D + 16 bytes per token
+    cache: str = "native"
     description: str = ""
 
     @property
@@ -69,6 +72,11 @@ class Workload:
     @property
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def cache_row_bytes(self) -> int:
+        """Bytes one cached token occupies (per layer)."""
+        return self.dim + 16 if self.cache == "q8" else self.dim * self.elem_bytes
 
     @property
     def max_seq_len(self) -> int:
@@ -104,6 +112,10 @@ WORKLOADS: Dict[str, Workload] = {
                  description="1M-token context, Q=4 chain verify, H=128, contiguous"),
         # tree-structured speculative verification: 8 drafted tokens, a root
         # with two children, each with two children, one of which has a child
+        Workload("v2lite_32k_q8", batch=8, q_len=1, heads=16, kv_rank=512, rope_dim=64,
+                 nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=32,
+                 cache="q8",
+                 description="DeepSeek-V2-Lite layer shape, B=8, L=32768, 8-bit latent cache"),
         Workload("v2lite_32k_tree8", batch=8, q_len=8, heads=16, kv_rank=512, rope_dim=64,
                  nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=16,
                  tree=(-1, 0, 0, 1, 1, 2, 2, 3),
