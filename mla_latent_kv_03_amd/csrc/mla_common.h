@@ -68,12 +68,12 @@ __device__ __forceinline__ void split_range(int L, int S, int page, int fixed, i
 // tokens on its own branch: bit i of its branch mask is set when i is j or an
 // ancestor of j. The walk stops after Q steps (Q <= 64) whatever the entries
 // hold; tree_entry_ok is the validity the kernels check first.
-__device__ __forceinline__ bool tree_entry_ok(const int32_t* __restrict__ parent, int i) {
+__host__ __device__ __forceinline__ bool tree_entry_ok(const int32_t* __restrict__ parent, int i) {
   const int p = parent[i];
   return p >= -1 && p < i;
 }
-__device__ __forceinline__ uint64_t tree_branch_mask(const int32_t* __restrict__ parent, int Q,
-                                                     int j) {
+__host__ __device__ __forceinline__ uint64_t tree_branch_mask(const int32_t* __restrict__ parent, int Q,
+                                                              int j) {
   uint64_t m = 0;
   int i = j;
   for (int step = 0; step < Q && i >= 0 && i < Q; ++step) {
@@ -81,6 +81,23 @@ __device__ __forceinline__ uint64_t tree_branch_mask(const int32_t* __restrict__
     i = parent[i];
   }
   return m;
+}
+
+// Tokens ts .. ts + 63 that one query row sees, as bits (bit o = token ts + o):
+// every token up to lim, and with a drafted tree the drafts on the row's branch
+// (bit i of `branch` = token t_draft + i) that lie below t1. Shifts and selects
+// only: a per-token short-circuit form of this test lost one of its masked
+// stores in gfx950 code generation.
+__host__ __device__ __forceinline__ uint64_t tile_visible(int ts, int lim, int t_draft, int t1,
+                                                          uint64_t branch) {
+  const int npre = lim - ts + 1;  // prefix tokens from ts on
+  const uint64_t pre = npre >= 64 ? ~0ull : (npre <= 0 ? 0ull : (1ull << npre) - 1ull);
+  const int rel = ts - t_draft;   // offset o holds draft o + rel
+  uint64_t drafts = rel >= 0 ? (rel < 64 ? branch >> rel : 0ull)
+                             : (-rel < 64 ? branch << -rel : 0ull);
+  const int nin = t1 - ts;        // offsets below t1
+  if (nin < 64) drafts &= nin <= 0 ? 0ull : (1ull << nin) - 1ull;
+  return pre | drafts;
 }
 
 }  // namespace mla

@@ -278,23 +278,14 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
       const f32x4_t s0 = sk[rg * 64];        // tokens 4 kg + r
       const f32x4_t s1 = sk[128 + rg * 64];  // tokens 16 + 4 kg + r
       float sv[8];
-      if (par && ts + kWT > t_draft) {  // the tile reaches the drafted tokens
+      // lane's tokens: ts + 4 kg + r (subtile 0) and ts + 16 + 4 kg + r (subtile 1)
+      uint64_t vl = ~0ull;
+      if (!__all(ts + kWT - 1 <= lim[rg]))
+        vl = tile_visible(ts, lim[rg], t_draft, t1, branch[rg]) >> (4 * kg);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ta = ts + 4 * kg + r, tb = ta + 16;
-          const bool va = ta <= lim[rg] ||
-                          (ta >= t_draft && ta < t1 && ((branch[rg] >> (ta - t_draft)) & 1ull));
-          const bool vb = tb <= lim[rg] ||
-                          (tb >= t_draft && tb < t1 && ((branch[rg] >> (tb - t_draft)) & 1ull));
-          sv[r] = va ? s0[r] * scale_log2 : -INFINITY;
-          sv[4 + r] = vb ? s1[r] * scale_log2 : -INFINITY;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sv[r] = (ts + 4 * kg + r <= lim[rg]) ? s0[r] * scale_log2 : -INFINITY;
-          sv[4 + r] = (ts + 16 + 4 * kg + r <= lim[rg]) ? s1[r] * scale_log2 : -INFINITY;
-        }
+      for (int r = 0; r < 4; ++r) {
+        sv[r] = ((vl >> r) & 1ull) ? s0[r] * scale_log2 : -INFINITY;
+        sv[4 + r] = ((vl >> (16 + r)) & 1ull) ? s1[r] * scale_log2 : -INFINITY;
       }
       float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                          fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));

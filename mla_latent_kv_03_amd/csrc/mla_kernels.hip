@@ -202,9 +202,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
     for (int i = tid; i < nt * D; i += blockDim.x) cs[(i / D) * Dp + (i % D)] = Elt<T>::ld(src + i);
     __syncthreads();
     float sc = -INFINITY;
-    const int tk = t + my_k;
-    const bool seen =
-        tk <= lim || (par && tk >= t_draft && ((branch >> (tk - t_draft)) & 1ull));
+    const bool seen = (tile_visible(t, lim, t_draft, t1, branch) >> my_k) & 1ull;
     if (my_r < nr && my_k < nt && seen) {
       const float* qr = qs + my_r * D;
       const float* cr = cs + my_k * Dp;

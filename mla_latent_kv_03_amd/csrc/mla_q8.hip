@@ -395,20 +395,7 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
         for (int r = 0; r < 4; ++r) sv[4 * u + r] = su[r];
       }
       if (!__all(ts + kQT - 1 <= lim)) {  // some token of the tile is masked for some row
-        // tile offsets this row sees, as one 64-bit mask: the prefix up to lim,
-        // and with a drafted tree the drafted tokens on the row's branch (kept
-        // below t1). Plain shifts and selects: a short-circuit form of this
-        // test lost one of its -inf stores in code generation.
-        const int nvis = min(max(lim - ts + 1, 0), kQT);
-        uint64_t vis = nvis >= 64 ? ~0ull : (1ull << nvis) - 1ull;
-        if (par && ts + kQT > t_draft) {
-          const int rel = ts - t_draft;  // tile offset o holds draft o + rel
-          uint64_t bm = rel >= 0 ? (rel < 64 ? branch >> rel : 0ull)
-                                 : (-rel < 64 ? branch << -rel : 0ull);
-          const int nin = t1 - ts;  // offsets below t1
-          if (nin < 64) bm &= (1ull << max(nin, 0)) - 1ull;
-          vis |= bm;
-        }
+        const uint64_t vis = tile_visible(ts, lim, t_draft, t1, branch);
         const uint64_t vl = vis >> (4 * kg);
 #pragma unroll
         for (int j = 0; j < 16; ++j)
