@@ -32,5 +32,9 @@ from .mla_ref import (  # noqa: F401
     rotated_keys_f32,
     attend_sequence_rotated,
     mla_decode_ref_q8,
+    indexer_scores,
+    topk_tokens,
+    dsa_selection,
+    mla_decode_ref_sparse,
 )
-from .brute import brute_sequence  # noqa: F401
+from .brute import brute_sequence, brute_index_scores  # noqa: F401

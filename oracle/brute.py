@@ -60,8 +60,12 @@ def _on_branch(parents, j, i):
     return False
 
 
-def brute_sequence(c, k_rope, q_nope, q_rope, w_uk, w_uv, scale, base=10000.0, parents=None):
-    """Nested lists in, nested lists out: (o [Q][H][d_v], o_lat [Q][H][d_c], lse [Q][H])."""
+def brute_sequence(c, k_rope, q_nope, q_rope, w_uk, w_uv, scale, base=10000.0, parents=None,
+                   selected=None):
+    """Nested lists in, nested lists out: (o [Q][H][d_v], o_lat [Q][H][d_c], lse [Q][H]).
+
+    ``selected``: per query, the cached tokens it reads (a sparse read); each
+    keeps its own position."""
     L = len(c)
     Q = len(q_nope)
     H = len(w_uk)
@@ -73,6 +77,9 @@ def brute_sequence(c, k_rope, q_nope, q_rope, w_uk, w_uv, scale, base=10000.0, p
         return pre + _links_to_prefix(parents, t - pre)
 
     def sees(j, t):
+        if selected is not None:
+            assert parents is None
+            return t in selected[j] and t <= pre + j
         if parents is None:
             return t <= pre + j
         return t < pre or _on_branch(parents, j, t - pre)
@@ -109,3 +116,21 @@ def brute_sequence(c, k_rope, q_nope, q_rope, w_uk, w_uv, scale, base=10000.0, p
         o_lat.append(olj)
         lse.append(lj)
     return o, o_lat, lse
+
+
+def brute_index_scores(q_idx, w_idx, k_idx):
+    """Scalar loops: score[j][t] = sum over scorer heads h of
+    w[j][h] * max(0, q[j][h] . k[t]) ("DeepSeek's Config Says 16 KV Heads",
+    section 6, "Sparse attention"; the weighted-ReLU form is a reading)."""
+    out = []
+    for qj, wj in zip(q_idx, w_idx):
+        row = []
+        for kt in k_idx:
+            acc = 0.0
+            for qh, wh in zip(qj, wj):
+                d = _dot(qh, kt)
+                if d > 0.0:
+                    acc += wh * d
+            row.append(acc)
+        out.append(row)
+    return out

@@ -36,6 +36,11 @@ What it computes, and where the pages define it:
   Contexts", technique 3 "KV Cache Quantization", and its comparison table:
   an INT8 cache halves the bytes). Reading: per cached token, separately for
   the latent part and the (rotated) RoPE part, in float32.
+* A sparse read: a small scorer rates every cached token and attention reads
+  only the top-scored ones ("DeepSeek's Config Says 16 KV Heads, Its Cache
+  Holds a Ninth of That", section 6, "Sparse attention"). Reading: the score
+  is a weighted sum over the scorer's heads of ReLU(q . k), ties in the top-k
+  go to the smaller token index.
 * Split-KV partials merged by a log-sum-exp reduction ("The Architecture of
   Memory", "Flash-Decoding and FlashInfer").
 * Paged cache: fixed-size pages mapped logical -> physical through a page
@@ -249,7 +254,7 @@ def attend_scores(c, k_rope_raw, q_nope, q_rope, w_uk, scale, base=10000.0,
 
 
 def attend_sequence(c, k_rope_raw, q_nope, q_rope, w_uk, w_uv, scale,
-                    base: float = 10000.0, chunk: int = 1024, parents=None):
+                    base: float = 10000.0, chunk: int = 1024, parents=None, keep=None):
     """Decode attention of one sequence, without absorption.
 
     c [L][d_c], k_rope_raw [L][d_r] (unrotated, positions 0..L-1),
@@ -258,10 +263,19 @@ def attend_sequence(c, k_rope_raw, q_nope, q_rope, w_uk, w_uv, scale,
     Returns o [Q][H][d_v] = sum_t p_t V_t,h, o_lat [Q][H][d_c] = sum_t p_t c_t
     (the same weights applied to the latents) and lse [Q][H] = m + ln sum e^(s-m).
     ``parents``: the drafted tokens form this tree instead of a chain.
+    ``keep``: [Q][L] bool, the cached tokens each query reads (a sparse read);
+    every kept token must be visible to its query, and the others are left
+    out of the softmax.
     """
     c = np.asarray(c, F64)
     L = c.shape[0]
     s = attend_scores(c, k_rope_raw, q_nope, q_rope, w_uk, scale, base, chunk, parents=parents)
+    if keep is not None:
+        keep = np.asarray(keep, dtype=bool)
+        assert keep.shape == (s.shape[0], L)
+        if np.any(keep[:, None, :] & np.isneginf(s)):
+            raise ValueError("a kept token lies after its query")
+        s[np.broadcast_to(~keep[:, None, :], s.shape)] = -np.inf
     m = s.max(axis=-1, keepdims=True)
     e = np.exp(s - m)
     den = e.sum(axis=-1, keepdims=True)
@@ -553,6 +567,83 @@ def mla_decode_ref_q8(inputs, heads: Optional[Sequence[int]] = None,
             c_hat, k_hat, inputs.q_nope[b][:, hs], inputs.q_rope[b][:, hs], w_uk, w_uv,
             wl.softmax_scale, wl.rope_base, parents=par)
     return {"o": o, "o_lat": o_lat, "lse": lse, "rows": rows}
+
+
+# --------------------------------------------------------------------------
+# sparse read: a small scorer picks the cached tokens attention reads
+# --------------------------------------------------------------------------
+def indexer_scores(q_idx, w_idx, k_idx) -> np.ndarray:
+    """Index scores [Q][L] that rate every cached token for each query token.
+
+    The pages fix the scorer's size (64 heads of 128 dimensions) and its role:
+    it rates all earlier tokens and attention then reads only the best ones
+    ("DeepSeek's Config Says 16 KV Heads, Its Cache Holds a Ninth of That",
+    section 6, "Sparse attention"). Reading (the DSA published form, the pages
+    print no formula): I[j][t] = sum_h w[j][h] * max(0, q[j][h] . k[t]), with
+    q_idx [Q][H_I][d_I], per-query head weights w_idx [Q][H_I] and one indexer
+    key per cached token, k_idx [L][d_I].
+    """
+    q = np.asarray(q_idx, F64)
+    w = np.asarray(w_idx, F64)
+    k = np.asarray(k_idx, F64)
+    dots = np.matmul(q, k.T)                                      # [Q][H_I][L]
+    return np.einsum("qh,qht->qt", w, np.maximum(dots, 0.0))
+
+
+def topk_tokens(scores, k: int, visible: int) -> np.ndarray:
+    """Cached tokens one query reads: of tokens 0 .. visible-1, the k with the
+    highest index scores (every one when visible <= k), in increasing token
+    order (same page and section: attention runs only over the top 2,048).
+    Reading: equal scores go to the smaller token index; NaN among the
+    visible scores makes the selection undefined (ValueError)."""
+    s = np.asarray(scores, F64)[:visible]
+    if np.isnan(s).any():
+        raise ValueError("NaN index score")
+    if visible <= k:
+        return np.arange(visible)
+    order = np.lexsort((np.arange(visible), -s))                  # score desc, index asc
+    return np.sort(order[:k])
+
+
+def dsa_selection(inputs) -> List[List[np.ndarray]]:
+    """[B][Q] selected token arrays of a workload with a sparse read: indexer
+    scores of every cached token, then the top index_topk among those query j
+    sees (t <= L - Q + j)."""
+    wl = inputs.wl
+    out = []
+    for b in range(wl.batch):
+        L = int(inputs.seq_lens[b])
+        sc = indexer_scores(inputs.q_idx[b], inputs.w_idx[b], inputs.seq_index_keys(b))
+        out.append([topk_tokens(sc[j], wl.index_topk, L - wl.q_len + j + 1)
+                    for j in range(wl.q_len)])
+    return out
+
+
+def mla_decode_ref_sparse(inputs, selection=None, heads: Optional[Sequence[int]] = None,
+                          seqs: Optional[Sequence[int]] = None):
+    """The oracle of a sparse read: query j of sequence b attends only over the
+    cached tokens selection[b][j] (dsa_selection by default). Returns the dict
+    of mla_decode_ref plus "selection"."""
+    wl = inputs.wl
+    sel = dsa_selection(inputs) if selection is None else selection
+    hs = list(range(wl.heads)) if heads is None else list(heads)
+    bs = list(range(wl.batch)) if seqs is None else list(seqs)
+    B, Q = wl.batch, wl.q_len
+    o = np.full((B, Q, len(hs), wl.v_dim), np.nan)
+    o_lat = np.full((B, Q, len(hs), wl.kv_rank), np.nan)
+    lse = np.full((B, Q, len(hs)), np.nan)
+    w_uk = np.asarray(inputs.w_uk, F64)[hs]
+    w_uv = np.asarray(inputs.w_uv, F64)[hs]
+    for b in bs:
+        c, kr = inputs.seq(b)
+        L = c.shape[0]
+        keep = np.zeros((Q, L), dtype=bool)
+        for j in range(Q):
+            keep[j, np.asarray(sel[b][j], dtype=np.int64)] = True
+        o[b], o_lat[b], lse[b] = attend_sequence(c, kr, inputs.q_nope[b][:, hs],
+                                                 inputs.q_rope[b][:, hs], w_uk, w_uv,
+                                                 wl.softmax_scale, wl.rope_base, keep=keep)
+    return {"o": o, "o_lat": o_lat, "lse": lse, "selection": sel}
 
 
 # --------------------------------------------------------------------------

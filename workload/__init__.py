@@ -11,6 +11,9 @@ from .synth import (  # noqa: F401
     Inputs,
     make,
     seq_latents,
+    seq_index_keys,
+    random_selection,
+    score_rows,
     round_bf16,
     bf16_bits,
 )

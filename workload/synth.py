@@ -30,6 +30,7 @@ PAGE = 64
 
 # stream tags: one independent generator per tensor (and per sequence)
 _T_LENS, _T_WUK, _T_WUV, _T_QN, _T_QR, _T_C, _T_KR, _T_PERM, _T_TREE = range(9)
+_T_QI, _T_WI, _T_KI, _T_SEL, _T_SCORES = range(9, 14)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -57,6 +58,11 @@ class Workload:
     # cache format: "native" = rows in the workload dtype; "q8" = 8-bit codes
     # per row part plus (min, step) pairs, D + 16 bytes per token
     cache: str = "native"
+    # sparse read: > 0 = each query reads only the index_topk cached tokens an
+    # indexer of index_heads heads x index_dim rates highest
+    index_topk: int = 0
+    index_heads: int = 64
+    index_dim: int = 128
     description: str = ""
 
     @property
@@ -116,6 +122,11 @@ WORKLOADS: Dict[str, Workload] = {
                  nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=32,
                  cache="q8",
                  description="DeepSeek-V2-Lite layer shape, B=8, L=32768, 8-bit latent cache"),
+        Workload("v2lite_32k_dsa", batch=8, q_len=1, heads=16, kv_rank=512, rope_dim=64,
+                 nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=16,
+                 index_topk=2048,
+                 description="V2-Lite shape, B=8, L=32768, sparse read of the top 2,048 tokens "
+                             "chosen by a 64-head x 128 indexer"),
         Workload("v2lite_32k_tree8", batch=8, q_len=8, heads=16, kv_rank=512, rope_dim=64,
                  nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=16,
                  tree=(-1, 0, 0, 1, 1, 2, 2, 3),
@@ -170,6 +181,35 @@ def seq_latents(wl: Workload, seed: int, b: int, length: int):
     return c, kr
 
 
+def seq_index_keys(wl: Workload, seed: int, b: int, length: int) -> np.ndarray:
+    """Indexer keys [length][d_I] of sequence b: N(0, 1), in the workload dtype."""
+    return _normal(_rng(seed, _T_KI, b), (length, wl.index_dim), 1.0, wl.dtype)
+
+
+def random_selection(seed: int, b: int, j: int, visible: int, k: int) -> np.ndarray:
+    """A seeded set of min(k, visible) distinct tokens of 0 .. visible-1, in
+    increasing order: an index list for a sparse read drawn without any
+    scores (for testing the sparse decode on its own)."""
+    rng = _rng(seed, _T_SEL, b * 4096 + j)
+    if visible <= k:
+        return np.arange(visible, dtype=np.int32)
+    return np.sort(rng.choice(visible, size=k, replace=False)).astype(np.int32)
+
+
+def score_rows(seed: int, rows: int, length: int, ties: bool = True) -> np.ndarray:
+    """float32 [rows][length] index scores for testing top-k selection alone:
+    N(0, 4) values, and with ``ties`` a quarter of them copied from a few
+    shared values (exact ties, +0.0 and -0.0 among them) so that the tie rule
+    decides the boundary."""
+    rng = _rng(seed, _T_SCORES, rows * 65536 + length)
+    x = rng.standard_normal(size=(rows, length), dtype=np.float32) * np.float32(2.0)
+    if ties:
+        shared = np.array([0.0, -0.0, 1.5, 2.25, 3.0, -1.0], dtype=np.float32)
+        pick = rng.random((rows, length)) < 0.25
+        x[pick] = shared[rng.integers(0, len(shared), size=int(pick.sum()))]
+    return x
+
+
 def tree_parents(wl: Workload, seed: int = 0) -> Optional[np.ndarray]:
     """[B][Q] int32 parent of each drafted token (-1: attached to the prefix),
     or None for a chain. Parents always precede their children."""
@@ -221,6 +261,9 @@ class Inputs:
     c: Optional[np.ndarray] = None        # [sum L_b][d_c]
     k_rope: Optional[np.ndarray] = None   # [sum L_b][d_r], unrotated
     parents: Optional[np.ndarray] = None  # int32 [B][Q] drafted tree (None: chain)
+    q_idx: Optional[np.ndarray] = None    # [B][Q][H_I][d_I] indexer queries
+    w_idx: Optional[np.ndarray] = None    # float32 [B][Q][H_I] indexer head weights
+    k_idx: Optional[np.ndarray] = None    # [sum L_b][d_I] indexer keys
 
     def seq(self, b: int):
         """Latents and unrotated RoPE keys of sequence b (views or fresh draws)."""
@@ -228,6 +271,12 @@ class Inputs:
             s, e = int(self.offsets[b]), int(self.offsets[b + 1])
             return self.c[s:e], self.k_rope[s:e]
         return seq_latents(self.wl, self.seed, b, int(self.seq_lens[b]))
+
+    def seq_index_keys(self, b: int) -> np.ndarray:
+        """Indexer keys [L_b][d_I] of sequence b."""
+        if self.k_idx is not None:
+            return self.k_idx[int(self.offsets[b]):int(self.offsets[b + 1])]
+        return seq_index_keys(self.wl, self.seed, b, int(self.seq_lens[b]))
 
 
 def make(wl: Workload, seed: int = 0, with_latents: bool = True,
@@ -251,6 +300,11 @@ def make(wl: Workload, seed: int = 0, with_latents: bool = True,
     pt, total = page_table_for(wl, lens, seed)
     inp = Inputs(wl, seed, lens, offsets, w_uk, w_uv, q_nope, q_rope, pt, total,
                  parents=tree_parents(wl, seed))
+    if wl.index_topk > 0:
+        Hi, di = wl.index_heads, wl.index_dim
+        inp.q_idx = _normal(_rng(seed, _T_QI), (wl.batch, wl.q_len, Hi, di), 1.0, wl.dtype)
+        inp.w_idx = _normal(_rng(seed, _T_WI), (wl.batch, wl.q_len, Hi), 1.0 / math.sqrt(Hi),
+                            "f32")
     if with_latents:
         T = int(offsets[-1])
         fdt = np.float32
@@ -260,4 +314,8 @@ def make(wl: Workload, seed: int = 0, with_latents: bool = True,
             c, kr = seq_latents(wl, seed, b, int(lens[b]))
             inp.c[offsets[b]:offsets[b + 1]] = c
             inp.k_rope[offsets[b]:offsets[b + 1]] = kr
+        if wl.index_topk > 0:
+            inp.k_idx = np.empty((T, wl.index_dim), dtype=fdt)
+            for b in range(wl.batch):
+                inp.k_idx[offsets[b]:offsets[b + 1]] = seq_index_keys(wl, seed, b, int(lens[b]))
     return inp
