@@ -18,7 +18,10 @@
  *                       two pairs of the above, each in one launch
  * Verifying a tree of drafted tokens instead of a chain takes
  * mla_absorb_append_at / mla_cache_append_at (a token's cache slot and its
- * RoPE position differ) and mla_decode_paged_tree (the tree mask).
+ * RoPE position differ) and mla_decode_paged_tree (the tree mask). An 8-bit
+ * cache takes mla_cache_append_q8 / mla_decode_paged_q8; a sparse read
+ * (attention over the top-scored tokens only) takes mla_index_append,
+ * mla_index_scores, mla_topk_select and mla_decode_sparse.
  *
  * Conventions shared by every call
  *   - Every pointer argument except `cfg` is a DEVICE pointer; `cfg` is a host
@@ -294,6 +297,86 @@ mla_status_t mla_decode_paged_q8(const mla_config_t* cfg, int32_t batch, int32_t
                                  const int32_t* page_table, int32_t max_pages,
                                  const int32_t* seq_lens, const int32_t* tree_parent,
                                  float* o_part, float* lse_part, void* stream);
+
+/* Sparse read (f3; "DeepSeek's Config Says 16 KV Heads, Its Cache Holds a
+ * Ninth of That", section 6 "Sparse attention"): a small scorer (the pages:
+ * 64 heads of 128 dimensions) rates every cached token for each query, and
+ * attention reads only the topk best (the pages: 2,048); the latent cache
+ * keeps every token, next to one indexer key per token. A step runs
+ *   mla_index_append   the new tokens' indexer keys into their cache
+ *   mla_index_scores   I[b][j][t] for every cached token t
+ *   mla_topk_select    the topk tokens each query reads
+ *   mla_decode_sparse  split-KV attention over those tokens only
+ * then mla_combine_up_project as for the dense decode.
+ * The score is a reading (the pages give the scorer's size only):
+ *   I[b][j][t] = sum_h w_idx[b][j][h] * max(0, q_idx[b][j][h] . k_idx(b, t))
+ * with fp32 accumulation; a NaN dot stays NaN. */
+
+/* Indexer keys into index_cache [num_pages][page_size][index_dim] T through
+ * the page table, exactly as mla_cache_append places latent rows (pos[n]
+ * picks the slot; no rotation). k_idx [n_tok][index_dim] T. index_dim a
+ * multiple of 8 (bf16) or 4 (fp32), at most 1,024. Rows whose seq_idx, pos or
+ * page entry is out of range are skipped. */
+mla_status_t mla_index_append(const mla_config_t* cfg, int32_t index_dim, int32_t n_tok,
+                              const void* k_idx, const int32_t* seq_idx, const int32_t* pos,
+                              const int32_t* page_table, int32_t batch, int32_t max_pages,
+                              void* index_cache, int64_t num_pages, void* stream);
+
+/* Index scores of every cached token t < L_b for each query j:
+ * scores[b][j][t] (row stride ld_scores >= max_seq_len floats) as above;
+ * entries t >= L_b are not written. q_idx [batch][q_len][index_heads]
+ * [index_dim] T, w_idx [batch][q_len][index_heads] f32, index_cache and
+ * page_table as for mla_index_append, seq_lens [batch]. A token whose page
+ * entry is invalid scores NaN; a sequence with an invalid length is not
+ * written (mla_topk_select reports it). bf16 with 64 heads x 128 runs on
+ * MFMA; other shapes need index_heads * (index_dim + 1) * 4 <= 160 KiB
+ * (MLA_ERR_UNSUPPORTED otherwise). index_heads in [1, 256]. */
+mla_status_t mla_index_scores(const mla_config_t* cfg, int32_t index_heads, int32_t index_dim,
+                              int32_t batch, int32_t q_len, int32_t max_seq_len,
+                              const void* q_idx, const float* w_idx, const void* index_cache,
+                              int64_t num_pages, const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_lens, float* scores, int32_t ld_scores,
+                              void* stream);
+
+/* The tokens each query reads: of the n = L_b - q_len + j + 1 tokens query
+ * j sees, the topk with the highest scores (all n when n <= topk), equal
+ * scores going to the smaller token index (-0.0 equals +0.0), written to
+ * indices[b][j][0 .. count) in increasing token order, count =
+ * min(topk, n) into counts[b][j]. counts[b][j] = -1 (indices unwritten)
+ * when L_b is outside [q_len, max_seq_len] or a score among the n is NaN.
+ * scores [batch][q_len][ld_scores] f32, indices [batch][q_len][topk] int32,
+ * counts [batch][q_len] int32. 1 <= topk <= 65,536. */
+mla_status_t mla_topk_select(int32_t batch, int32_t q_len, int32_t max_seq_len, int32_t topk,
+                             const float* scores, int32_t ld_scores, const int32_t* seq_lens,
+                             int32_t* indices, int32_t* counts, void* stream);
+
+/* List entries per partition of mla_decode_sparse: ceil(topk / num_splits)
+ * rounded up to a multiple of 32; 0 for invalid arguments. */
+int32_t mla_sparse_chunk(int32_t topk, int32_t num_splits);
+
+/* Name of the kernel mla_decode_sparse takes: "mfma_rows16_gather" for bf16,
+ * d_c = 512, d_r = 64, H a multiple of 16 and mla_sparse_chunk <= 1,984;
+ * else "generic_gather"; "invalid" for invalid arguments. Static string. */
+const char* mla_decode_sparse_kernel_name(const mla_config_t* cfg, int32_t topk,
+                                          int32_t num_splits);
+
+/* a4 over the selected tokens: query j of sequence b attends only over the
+ * cached tokens indices[b][j][0 .. counts[b][j]) (each keeping its own
+ * position; the cached RoPE keys are already rotated). Partition s covers
+ * list entries [s*chunk, min(count, (s+1)*chunk)), chunk = mla_sparse_chunk;
+ * the outputs, their layouts and the empty / masked conventions are those of
+ * mla_decode_paged, merged the same way by mla_splitkv_combine. A query
+ * whose count is outside [0, topk], or whose list holds a token it cannot
+ * see (outside [0, L_b - q_len + j]) or one with an invalid page, gets NaN
+ * outputs. indices, counts as written by mla_topk_select. Other arguments
+ * and errors as mla_decode_paged. */
+mla_status_t mla_decode_sparse(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                               int32_t topk, int32_t num_splits, int32_t max_seq_len,
+                               const void* q_full, const void* cache, int64_t num_pages,
+                               const int32_t* page_table, int32_t max_pages,
+                               const int32_t* seq_lens, const int32_t* indices,
+                               const int32_t* counts, float* o_part, float* lse_part,
+                               void* stream);
 
 /* a5. Log-sum-exp merge of the partitions ("The Architecture of Memory",
  * "Flash-Decoding and FlashInfer"), per row r = (b, j, h):

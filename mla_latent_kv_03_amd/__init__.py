@@ -18,7 +18,8 @@ these calls in one launch each, with the same results. A tree of drafted
 tokens is verified with cache_append_at / absorb_append_at (slot and RoPE
 position differ) and decode_paged_tree. An 8-bit latent cache (uint8 rows
 of codes plus per-part min and step) is written by cache_append_q8 and read
-by decode_paged_q8.
+by decode_paged_q8. A sparse read (attention over the top-scored tokens
+only) runs index_append, index_scores, topk_select and decode_sparse.
 """
 from ._binding import (  # noqa: F401
     F32,
@@ -51,4 +52,10 @@ from ._binding import (  # noqa: F401
     cache_q8_bytes_per_token,
     cache_append_q8,
     decode_paged_q8,
+    index_append,
+    index_scores,
+    topk_select,
+    sparse_chunk,
+    decode_sparse_kernel_kind,
+    decode_sparse,
 )

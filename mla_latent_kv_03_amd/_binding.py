@@ -114,6 +114,14 @@ def lib() -> ctypes.CDLL:
                                                I32, VP]),
         "mla_decode_paged_q8": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32,
                                                VP, VP, FP, FP, VP]),
+        "mla_index_append": (ctypes.c_int, [P, I32, I32, VP, VP, VP, VP, I32, I32, VP, I64, VP]),
+        "mla_index_scores": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, FP, VP, I64, VP, I32,
+                                            VP, FP, I32, VP]),
+        "mla_topk_select": (ctypes.c_int, [I32, I32, I32, I32, FP, I32, VP, VP, VP, VP]),
+        "mla_sparse_chunk": (ctypes.c_int32, [I32, I32]),
+        "mla_decode_sparse_kernel_name": (ctypes.c_char_p, [P, I32, I32]),
+        "mla_decode_sparse": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32, VP,
+                                             VP, VP, FP, FP, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -380,6 +388,108 @@ def _decode(cfg, q_full, cache, page_table, seq_lens, tree_parent, o_part, lse_p
     _ck(lib().mla_decode_paged(ctypes.byref(cfg.c()), B, Q, S, int(max_seq_len), args[0], args[1],
                                num_pages, pt, max_pages, sl, op, lp, _stream(stream)),
         "mla_decode_paged")
+
+
+# --------------------------------------------------------------------------
+# sparse read
+# --------------------------------------------------------------------------
+def _index_cache_dims(cfg: Config, index_cache):
+    if index_cache.dim() != 3 or index_cache.shape[1] != cfg.page_size:
+        raise ValueError(f"index_cache: expected [num_pages][{cfg.page_size}][index_dim]")
+    return int(index_cache.shape[0]), int(index_cache.shape[2])
+
+
+def index_append(cfg: Config, k_idx, seq_idx, pos, page_table, index_cache, stream=None):
+    """Indexer keys k_idx [n][index_dim] into index_cache [num_pages][page][index_dim]
+    at the slots mla_cache_append would pick (no rotation)."""
+    t = _torch()
+    n = int(pos.numel())
+    num_pages, dI = _index_cache_dims(cfg, index_cache)
+    if page_table.dim() != 2:
+        raise ValueError("page_table: expected [batch][max_pages]")
+    batch, max_pages = (int(x) for x in page_table.shape)
+    dt = _elem_dtype(cfg)
+    _ck(lib().mla_index_append(ctypes.byref(cfg.c()), dI, n, _need(k_idx, "k_idx", dt, n * dI),
+                               _need(seq_idx, "seq_idx", t.int32, n), _need(pos, "pos", t.int32, n),
+                               _need(page_table, "page_table", t.int32, batch * max_pages), batch,
+                               max_pages, _need(index_cache, "index_cache", dt, index_cache.numel()),
+                               num_pages, _stream(stream)), "mla_index_append")
+
+
+def index_scores(cfg: Config, q_idx, w_idx, index_cache, page_table, seq_lens, scores,
+                 max_seq_len: int, stream=None):
+    """Index scores [B][Q][ld] f32 (ld = scores.shape[2] >= max_seq_len):
+    sum_h w_idx[b][j][h] * max(0, q_idx[b][j][h] . k_idx(b, t)) for t < L_b.
+    q_idx [B][Q][H_I][d_I] (cfg dtype), w_idx [B][Q][H_I] f32."""
+    t = _torch()
+    if q_idx.dim() != 4 or scores.dim() != 3:
+        raise ValueError("q_idx: expected [batch][q_len][heads][dim]; scores [batch][q_len][ld]")
+    B, Q, Hi, dI = (int(x) for x in q_idx.shape)
+    num_pages, dI2 = _index_cache_dims(cfg, index_cache)
+    if dI2 != dI:
+        raise ValueError("index_cache width does not match q_idx")
+    max_pages = int(page_table.shape[1])
+    ld = int(scores.shape[2])
+    dt = _elem_dtype(cfg)
+    _ck(lib().mla_index_scores(ctypes.byref(cfg.c()), Hi, dI, B, Q, int(max_seq_len),
+                               _need(q_idx, "q_idx", dt, B * Q * Hi * dI),
+                               _need(w_idx, "w_idx", t.float32, B * Q * Hi),
+                               _need(index_cache, "index_cache", dt, index_cache.numel()),
+                               num_pages, _need(page_table, "page_table", t.int32, B * max_pages),
+                               max_pages, _need(seq_lens, "seq_lens", t.int32, B),
+                               _need(scores, "scores", t.float32, B * Q * ld), ld,
+                               _stream(stream)), "mla_index_scores")
+
+
+def topk_select(scores, seq_lens, indices, counts, max_seq_len: int, stream=None):
+    """The topk (= indices.shape[2]) best-scored tokens each query sees, in
+    increasing token order; counts [B][Q] int32 (-1: invalid sequence)."""
+    t = _torch()
+    if scores.dim() != 3 or indices.dim() != 3:
+        raise ValueError("scores: expected [batch][q_len][ld]; indices [batch][q_len][topk]")
+    B, Q, ld = (int(x) for x in scores.shape)
+    K = int(indices.shape[2])
+    _ck(lib().mla_topk_select(B, Q, int(max_seq_len), K,
+                              _need(scores, "scores", t.float32, B * Q * ld), ld,
+                              _need(seq_lens, "seq_lens", t.int32, B),
+                              _need(indices, "indices", t.int32, B * Q * K),
+                              _need(counts, "counts", t.int32, B * Q), _stream(stream)),
+        "mla_topk_select")
+
+
+def sparse_chunk(topk: int, num_splits: int) -> int:
+    """List entries per partition of decode_sparse."""
+    return int(lib().mla_sparse_chunk(int(topk), int(num_splits)))
+
+
+def decode_sparse_kernel_kind(cfg: Config, topk: int, num_splits: int) -> str:
+    """"mfma_rows16_gather" or "generic_gather"."""
+    return lib().mla_decode_sparse_kernel_name(ctypes.byref(cfg.c()), int(topk),
+                                               int(num_splits)).decode()
+
+
+def decode_sparse(cfg: Config, q_full, cache, page_table, seq_lens, indices, counts, o_part,
+                  lse_part, max_seq_len: int, stream=None):
+    """a4 over the selected tokens indices [B][Q][topk] (counts [B][Q]); other
+    arguments and outputs as decode_paged."""
+    t = _torch()
+    B, Q = int(q_full.shape[0]), int(q_full.shape[1])
+    S = int(lse_part.shape[3])
+    K = int(indices.shape[2])
+    H, dt = cfg.num_heads, _elem_dtype(cfg)
+    if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != cfg.dim:
+        raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{cfg.dim}]")
+    max_pages = int(page_table.shape[1])
+    _ck(lib().mla_decode_sparse(ctypes.byref(cfg.c()), B, Q, K, S, int(max_seq_len),
+                                _need(q_full, "q_full", dt, B * Q * H * cfg.dim),
+                                _need(cache, "cache", dt, cache.numel()), int(cache.shape[0]),
+                                _need(page_table, "page_table", t.int32, B * max_pages), max_pages,
+                                _need(seq_lens, "seq_lens", t.int32, B),
+                                _need(indices, "indices", t.int32, B * Q * K),
+                                _need(counts, "counts", t.int32, B * Q),
+                                _need(o_part, "o_part", t.float32, B * Q * H * S * cfg.kv_rank),
+                                _need(lse_part, "lse_part", t.float32, B * Q * H * S),
+                                _stream(stream)), "mla_decode_sparse")
 
 
 def _combine_args(cfg: Config, o_part, lse_part, o_lat, lse):

@@ -406,6 +406,138 @@ mla_status_t mla_decode_paged_q8(const mla_config_t* cfg, int32_t batch, int32_t
                                           tree_parent, o_part, lse_part, stream));
 }
 
+namespace {
+constexpr int kMaxIndexHeads = 256;
+constexpr int kMaxIndexDim = 1024;
+constexpr int kMaxTopk = 65536;
+
+mla_status_t check_index_shape(const mla_config_t* cfg, int32_t index_heads, int32_t index_dim) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(index_heads >= 1 && index_heads <= kMaxIndexHeads, MLA_ERR_SHAPE);
+  MLA_REQUIRE(index_dim >= 1 && index_dim <= kMaxIndexDim, MLA_ERR_SHAPE);
+  MLA_REQUIRE(index_dim % (cfg->dtype == MLA_F32 ? 4 : 8) == 0, MLA_ERR_SHAPE);
+  return MLA_OK;
+}
+
+// list entries per partition of the sparse decode: ceil(topk / S) rounded up
+// to a whole 32-token tile
+int32_t sparse_chunk(int32_t topk, int32_t num_splits) {
+  const int32_t per = (topk + num_splits - 1) / num_splits;
+  return ((per + 31) / 32) * 32;
+}
+}  // namespace
+
+mla_status_t mla_index_append(const mla_config_t* cfg, int32_t index_dim, int32_t n_tok,
+                              const void* k_idx, const int32_t* seq_idx, const int32_t* pos,
+                              const int32_t* page_table, int32_t batch, int32_t max_pages,
+                              void* index_cache, int64_t num_pages, void* stream) {
+  mla_status_t st = check_index_shape(cfg, 1, index_dim);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(n_tok >= 0 && batch >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size <= INT32_MAX, MLA_ERR_CAPACITY);
+  if (n_tok == 0) return MLA_OK;
+  MLA_CHECK_PTR(k_idx);
+  MLA_CHECK_PTR(seq_idx);
+  MLA_CHECK_PTR(pos);
+  MLA_CHECK_PTR(page_table);
+  MLA_CHECK_PTR(index_cache);
+  return hip_status(mla::launch_index_append(shape_of(cfg), index_dim, n_tok, k_idx, seq_idx, pos,
+                                             page_table, batch, max_pages, index_cache, num_pages,
+                                             stream));
+}
+
+mla_status_t mla_index_scores(const mla_config_t* cfg, int32_t index_heads, int32_t index_dim,
+                              int32_t batch, int32_t q_len, int32_t max_seq_len,
+                              const void* q_idx, const float* w_idx, const void* index_cache,
+                              int64_t num_pages, const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_lens, float* scores, int32_t ld_scores,
+                              void* stream) {
+  mla_status_t st = check_index_shape(cfg, index_heads, index_dim);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(batch >= 0 && q_len >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(q_len <= 65535, MLA_ERR_SHAPE);
+  MLA_REQUIRE(max_seq_len >= q_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE(ld_scores >= max_seq_len, MLA_ERR_SHAPE);
+  mla::Shape sh = shape_of(cfg);
+  if (!mla::index_scores_mfma_ok(sh, index_heads, index_dim))
+    MLA_REQUIRE(mla::index_scores_generic_lds(index_heads, index_dim) <= 160 * 1024,
+                MLA_ERR_UNSUPPORTED);
+  if (batch == 0) return MLA_OK;
+  MLA_CHECK_PTR(q_idx);
+  MLA_CHECK_PTR(w_idx);
+  MLA_CHECK_PTR(index_cache);
+  MLA_CHECK_PTR(page_table);
+  MLA_CHECK_PTR(seq_lens);
+  MLA_CHECK_PTR(scores);
+  return hip_status(mla::launch_index_scores(sh, index_heads, index_dim, batch, q_len, max_seq_len,
+                                             q_idx, w_idx, index_cache, num_pages, page_table,
+                                             max_pages, seq_lens, scores, ld_scores, stream));
+}
+
+mla_status_t mla_topk_select(int32_t batch, int32_t q_len, int32_t max_seq_len, int32_t topk,
+                             const float* scores, int32_t ld_scores, const int32_t* seq_lens,
+                             int32_t* indices, int32_t* counts, void* stream) {
+  MLA_REQUIRE(batch >= 0 && q_len >= 1 && topk >= 1 && topk <= kMaxTopk, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)batch * q_len <= INT32_MAX, MLA_ERR_SHAPE);
+  MLA_REQUIRE(max_seq_len >= q_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE(ld_scores >= max_seq_len, MLA_ERR_SHAPE);
+  if (batch == 0) return MLA_OK;
+  MLA_CHECK_PTR(scores);
+  MLA_CHECK_PTR(seq_lens);
+  MLA_CHECK_PTR(indices);
+  MLA_CHECK_PTR(counts);
+  return hip_status(mla::launch_topk(batch, q_len, max_seq_len, topk, scores, ld_scores, seq_lens,
+                                     indices, counts, stream));
+}
+
+int32_t mla_sparse_chunk(int32_t topk, int32_t num_splits) {
+  if (topk < 1 || topk > kMaxTopk || num_splits < 1 || num_splits > kMaxSplits) return 0;
+  return sparse_chunk(topk, num_splits);
+}
+
+const char* mla_decode_sparse_kernel_name(const mla_config_t* cfg, int32_t topk,
+                                          int32_t num_splits) {
+  if (check_config(cfg) != MLA_OK || topk < 1 || topk > kMaxTopk || num_splits < 1 ||
+      num_splits > kMaxSplits)
+    return "invalid";
+  return mla::decode_sparse_kind(shape_of(cfg), sparse_chunk(topk, num_splits)) == 1
+             ? "mfma_rows16_gather"
+             : "generic_gather";
+}
+
+mla_status_t mla_decode_sparse(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                               int32_t topk, int32_t num_splits, int32_t max_seq_len,
+                               const void* q_full, const void* cache, int64_t num_pages,
+                               const int32_t* page_table, int32_t max_pages,
+                               const int32_t* seq_lens, const int32_t* indices,
+                               const int32_t* counts, float* o_part, float* lse_part,
+                               void* stream) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(batch >= 0 && q_len >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits, MLA_ERR_SHAPE);
+  MLA_REQUIRE(topk >= 1 && topk <= kMaxTopk, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)q_len * cfg->num_heads <= 65536, MLA_ERR_SHAPE);
+  MLA_REQUIRE(max_seq_len >= q_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
+  if (batch == 0) return MLA_OK;
+  MLA_CHECK_PTR(q_full);
+  MLA_CHECK_PTR(cache);
+  MLA_CHECK_PTR(page_table);
+  MLA_CHECK_PTR(seq_lens);
+  MLA_CHECK_PTR(indices);
+  MLA_CHECK_PTR(counts);
+  MLA_CHECK_PTR(o_part);
+  MLA_CHECK_PTR(lse_part);
+  return hip_status(mla::launch_decode_sparse(shape_of(cfg), batch, q_len, topk,
+                                              sparse_chunk(topk, num_splits), num_splits,
+                                              max_seq_len, q_full, cache, num_pages, page_table,
+                                              max_pages, seq_lens, indices, counts, o_part,
+                                              lse_part, stream));
+}
+
 mla_status_t mla_chunk_plan(const mla_config_t* cfg, int64_t total_tokens, int32_t max_seq_len,
                             int32_t num_cus, int32_t* chunk_tokens, int32_t* num_splits) {
   mla_status_t st = check_config(cfg);

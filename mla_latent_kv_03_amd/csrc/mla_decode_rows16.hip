@@ -32,6 +32,12 @@
 // With a drafted tree (tree_parent, "Tree Attention Verification") a row
 // sees the prefix and the drafted tokens on its query's branch; only tiles
 // that reach the drafted tokens test the branch mask.
+// Sparse read (kGather; "DeepSeek's Config Says 16 KV Heads", section 6):
+// the partition is a slice of the query's list of selected tokens instead of
+// a token range. The block resolves its slice to physical cache rows once
+// (index list, then page table, into LDS); each tile load then gathers its 8
+// rows per wave with per-lane 64-bit addresses. The 16 rows of a block are
+// heads of one query (H % 16 == 0), so they share one list.
 #include "mla_decode_common.h"
 #include "mla_launch.h"
 
@@ -52,12 +58,17 @@ constexpr int kHalfSteps = kKSteps / 2;             // 9 QK k-steps per wave
 constexpr size_t kRingBytes = (size_t)kRing * kTChunks * 16;   // 147,456 B
 constexpr size_t kScoreBytes = (size_t)2 * kWaves * 64 * 16;   // 8,192 B
 constexpr size_t kLdsBytes = kRingBytes + kScoreBytes;         // 155,648 B
+constexpr int kGatherMaxChunk = 1984;                          // list entries per partition
+constexpr size_t kGatherLdsBytes = kLdsBytes + 4 * kGatherMaxChunk;  // + resolved rows
+constexpr size_t kStaticLds = 256;  // the block reductions' own LDS
 
 static_assert(kPartChunks % 64 == 0, "a wave's share of a tile is whole loads");
-static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
+static_assert(kGatherLdsBytes + kStaticLds <= 160 * 1024, "LDS of one CU");
+static_assert(kGatherMaxChunk % kT == 0, "whole tiles");
 
 }  // namespace
 
+template <bool kGather>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
                           float scale_log2, int units, int groups,
@@ -65,8 +76,9 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
                           const bf16_t* __restrict__ cache, int64_t num_pages,
                           const int32_t* __restrict__ page_table, int max_pages,
                           const int32_t* __restrict__ seq_lens,
-                          const int32_t* __restrict__ tree_parent, float* __restrict__ o_part,
-                          float* __restrict__ lse_part) {
+                          const int32_t* __restrict__ tree_parent,
+                          const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+                          int topk, float* __restrict__ o_part, float* __restrict__ lse_part) {
   extern __shared__ u32x4_t lds[];
   int unit, grp;
   if (!map_block(units, groups, &unit, &grp)) return;
@@ -77,35 +89,100 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   const int n = lane & 15, kg = lane >> 4;
   const int sub = wave & 1, khalf = wave >> 1;  // QK share: subtile, half of the columns
   const int s = unit % S;
-  int L;
-  const int b = seq_by_rank(seq_lens, units / S, unit / S, lane, &L);
-  const int32_t* par = tree_parent ? tree_parent + (size_t)b * Q : nullptr;
+  int L, b;
+  if constexpr (kGather) {
+    b = unit / S;
+    L = seq_lens[b];
+  } else {
+    b = seq_by_rank(seq_lens, units / S, unit / S, lane, &L);
+  }
+  const int jq = row0 / H;  // the query of every row of the block (gather: H % 16 == 0)
+  const int32_t* par = (!kGather && tree_parent) ? tree_parent + (size_t)b * Q : nullptr;
   // a malformed tree makes the sequence invalid (the same verdict in every wave)
   const bool bad_tree = par && !__all(lane >= Q || tree_entry_ok(par, lane));
-  const bool bad_len = (L < Q) || (L > max_seq_len) || bad_tree;
-  int t0 = 0, t1 = 0;
-  if (!bad_len) split_range(L, S, page, fixed, s, &t0, &t1);
+  bool bad_len = (L < Q) || (L > max_seq_len) || bad_tree;
+  int cnt = 0;  // gather: length of the query's list
+  if constexpr (kGather) {
+    cnt = sel_cnt[(size_t)b * Q + jq];
+    bad_len = bad_len || cnt < 0 || cnt > topk;
+  }
+  int t0 = 0, t1 = 0;  // tokens (gather: list entries) of this partition
+  if (!bad_len) {
+    if constexpr (kGather) {
+      t0 = min(s * fixed, cnt);
+      t1 = min(t0 + fixed, cnt);
+    } else {
+      split_range(L, S, page, fixed, s, &t0, &t1);
+    }
+  }
   const int ntiles = (t1 - t0 + kT - 1) / kT;
   bool bad = bad_len;
 
   f32x4_t* sc = reinterpret_cast<f32x4_t*>(reinterpret_cast<char*>(lds) + kRingBytes);
+  int* const rows = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + kLdsBytes);
   auto slot = [&](int k) { return lds + (k & (kRing - 1)) * kTChunks; };
 
   PageWindow pw;
-  pw.init(page_table + (size_t)b * max_pages + t0 / page, (t1 - t0 + page - 1) / page, lane);
-  settle(pw.reg);
+  if constexpr (!kGather) {
+    pw.init(page_table + (size_t)b * max_pages + t0 / page, (t1 - t0 + page - 1) / page, lane);
+    settle(pw.reg);
+  } else {
+    // the partition's list entries -> cache rows (0 past the end or for an
+    // entry that is not visible to the query or whose page is invalid)
+    const int32_t* lst = sel_idx + ((size_t)b * Q + jq) * topk;
+    const int vis = L - Q + jq;  // the query's own position
+    const int nfill = ntiles * kT;
+    for (int i = threadIdx.x; i < nfill; i += 256) {
+      int row = 0;
+      if (i < t1 - t0) {
+        const int t = lst[t0 + i];
+        const int pg = (t >= 0 && t <= vis) ? page_table[(size_t)b * max_pages + t / page] : -1;
+        if (pg < 0 || (int64_t)pg >= num_pages)
+          bad = true;
+        else
+          row = pg * page + t % page;
+      }
+      rows[i] = row;
+    }
+    __syncthreads();
+  }
   RowDma<kPartLoads> dma;
   dma.init(wave * kPartChunks, lane, wave * kPartRows);
   // this wave's rows [8 wave, 8 wave + 8) of tile k (never across a page: 8 | page)
   auto issue = [&](int k) {
-    const int t = t0 + k * kT + wave * kPartRows;
-    int pg = pw.get((t - t0) / page, lane);
-    if (pg < 0 || (int64_t)pg >= num_pages) {
-      bad = true;
-      pg = 0;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(slot(k) + wave * kPartChunks));
+    if constexpr (kGather) {
+      // load i covers part chunks [64 i, 64 i + 64): rows ra and ra + 1, lane
+      // l of load i reading row ra + (l >= split); dma.off[i] holds
+      // (that row) * row bytes + the swizzled chunk offset
+      const int lt = k * kT + wave * kPartRows;
+      const int4 r03 = *reinterpret_cast<const int4*>(rows + lt);
+      const int4 r47 = *reinterpret_cast<const int4*>(rows + lt + 4);
+      const int rr[kPartRows] = {r03.x, r03.y, r03.z, r03.w, r47.x, r47.y, r47.z, r47.w};
+      const char* cb = reinterpret_cast<const char*>(cache);
+#pragma unroll
+      for (int i = 0; i < kPartLoads; ++i) {
+        const int ra = (64 * i) / kChunks;
+        const int split = kChunks * (ra + 1) - 64 * i;
+        const bool second = lane >= split;
+        const int rsel = second ? rr[ra + 1 < kPartRows ? ra + 1 : ra] : rr[ra];
+        const int rrel = second ? ra + 1 : ra;
+        const char* src = cb + ((int64_t)rsel - rrel) * (int64_t)(kD * 2) + dma.off[i];
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                     :
+                     : "s"(dst + i * 1024), "v"(src)
+                     : "memory");
+      }
+    } else {
+      const int t = t0 + k * kT + wave * kPartRows;
+      int pg = pw.get((t - t0) / page, lane);
+      if (pg < 0 || (int64_t)pg >= num_pages) {
+        bad = true;
+        pg = 0;
+      }
+      const bf16_t* src = cache + ((size_t)pg * page + (t % page)) * kD;
+      dma.issue(src, dst);
     }
-    const bf16_t* src = cache + ((size_t)pg * page + (t % page)) * kD;
-    dma.issue(src, __builtin_amdgcn_readfirstlane(lds_addr(slot(k) + wave * kPartChunks)));
   };
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -117,7 +194,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   // tokens row n sees in this partition: t <= lim, and with a drafted tree
   // also the drafted tokens (t >= t_draft) on its query's branch
   const int t_draft = L - Q;
-  const int lim = min(par ? t_draft - 1 : t_draft + (row0 + n) / H, t1 - 1);
+  const int lim = kGather ? t1 - 1 : min(par ? t_draft - 1 : t_draft + (row0 + n) / H, t1 - 1);
   const uint64_t branch = (par && !bad_len) ? tree_branch_mask(par, Q, (row0 + n) / H) : 0ull;
 
   if (ntiles > 0) {
@@ -315,6 +392,11 @@ bool decode_rows16_ok(const Shape& s, int q_len) {
          (q_len * s.H) % kRows == 0;
 }
 
+bool decode_sparse_rows16_ok(const Shape& s, int chunk) {
+  return s.dtype == 1 && s.dc == kDC && s.dr == kD - kDC && s.H % kRows == 0 && chunk > 0 &&
+         chunk <= kGatherMaxChunk && chunk % kT == 0;
+}
+
 int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
                          const void* q_full, const void* cache, int64_t num_pages,
                          const int32_t* page_table, int max_pages, const int32_t* seq_lens,
@@ -322,7 +404,7 @@ int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, i
                          void* stream) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_rows16_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_rows16_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return (int)e;
     attr = true;
@@ -330,11 +412,36 @@ int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, i
   const int units = batch * num_splits;
   const int groups = q_len * s.H / kRows;
   const int blocks = ((units + 7) / 8) * 8 * groups;
-  hipLaunchKernelGGL(decode_rows16_kernel, dim3(blocks), dim3(256), kLdsBytes,
+  hipLaunchKernelGGL(decode_rows16_kernel<false>, dim3(blocks), dim3(256), kLdsBytes,
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page,
                      s.split_fixed, max_seq_len, s.scale * 1.4426950408889634f, units, groups,
                      (const bf16_t*)q_full, (const bf16_t*)cache, num_pages, page_table, max_pages,
-                     seq_lens, tree_parent, o_part, lse_part);
+                     seq_lens, tree_parent, nullptr, nullptr, 0, o_part, lse_part);
+  return (int)hipGetLastError();
+}
+
+int launch_decode_sparse_rows16(const Shape& s, int batch, int q_len, int topk, int chunk,
+                                int num_splits, int max_seq_len, const void* q_full,
+                                const void* cache, int64_t num_pages, const int32_t* page_table,
+                                int max_pages, const int32_t* seq_lens, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, float* o_part, float* lse_part,
+                                void* stream) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_rows16_kernel<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kGatherLdsBytes);
+    if (e != hipSuccess) return (int)e;
+    attr = true;
+  }
+  const int units = batch * num_splits;
+  const int groups = q_len * s.H / kRows;
+  const int blocks = ((units + 7) / 8) * 8 * groups;
+  hipLaunchKernelGGL(decode_rows16_kernel<true>, dim3(blocks), dim3(256), kGatherLdsBytes,
+                     reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page, chunk,
+                     max_seq_len, s.scale * 1.4426950408889634f, units, groups,
+                     (const bf16_t*)q_full, (const bf16_t*)cache, num_pages, page_table, max_pages,
+                     seq_lens, nullptr, sel_idx, sel_cnt, topk, o_part, lse_part);
   return (int)hipGetLastError();
 }
 

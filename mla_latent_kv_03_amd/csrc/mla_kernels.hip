@@ -139,38 +139,63 @@ int launch_cache_append(const Shape& s, int n_tok, const void* c_kv, const void*
 // stride); scores use one thread per (row, token); the online softmax keeps a
 // running max m and sum l per row; thread f accumulates output columns
 // f, f + 256, ... of all rows.
+// kGather (sparse read, "DeepSeek's Config Says 16 KV Heads", section 6): the
+// partition is a slice of its query's list of selected tokens; a block's rows
+// are heads of one query, and each staged token is looked up through the list
+// and the page table.
 // ---------------------------------------------------------------------------
 constexpr int kGenRows = 8;
 constexpr int kGenTok = 16;
 constexpr int kGenMaxF = 4;  // d_c <= 1024
 
-template <typename T>
+template <typename T, bool kGather>
 __global__ __launch_bounds__(256) void decode_generic_kernel(
     int Q, int H, int dc, int dr, int page, int S, int fixed, int max_seq_len, float scale,
     const T* __restrict__ q_full, const T* __restrict__ cache, int64_t num_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ tree_parent, float* __restrict__ o_part,
+    const int32_t* __restrict__ tree_parent, const int32_t* __restrict__ sel_idx,
+    const int32_t* __restrict__ sel_cnt, int topk, float* __restrict__ o_part,
     float* __restrict__ lse_part) {
   extern __shared__ float smem[];
   const int s = blockIdx.x, b = blockIdx.y;
   const int R = Q * H;
-  const int r0 = blockIdx.z * kGenRows;
-  const int nr = min(kGenRows, R - r0);
+  int r0, nr, jq = 0;  // jq: the block's query (gather)
+  if constexpr (kGather) {
+    const int hg = (H + kGenRows - 1) / kGenRows;
+    jq = blockIdx.z / hg;
+    r0 = jq * H + (blockIdx.z % hg) * kGenRows;
+    nr = min(kGenRows, (jq + 1) * H - r0);
+  } else {
+    r0 = blockIdx.z * kGenRows;
+    nr = min(kGenRows, R - r0);
+  }
   const int D = dc + dr, Dp = D + 1;
   float* qs = smem;                    // [kGenRows][D]
   float* cs = qs + kGenRows * D;       // [kGenTok][Dp]
   float* ps = cs + kGenTok * Dp;       // [kGenRows][kGenTok]
   float* al = ps + kGenRows * kGenTok; // [kGenRows] rescale factors
+  int64_t* rs = reinterpret_cast<int64_t*>(al + 2 * kGenRows);  // [kGenTok] gathered rows
   const int tid = threadIdx.x;
 
   const int L = seq_lens[b];
   bool bad = (L < Q) || (L > max_seq_len);
-  const int32_t* par = tree_parent ? tree_parent + (size_t)b * Q : nullptr;
+  const int32_t* par = (!kGather && tree_parent) ? tree_parent + (size_t)b * Q : nullptr;
   if (par) {  // every thread checks every entry: the verdict is block-uniform
     for (int i = 0; i < Q; ++i) bad |= !tree_entry_ok(par, i);
   }
-  int t0 = 0, t1 = 0;
-  if (!bad) split_range(L, S, page, fixed, s, &t0, &t1);
+  int t0 = 0, t1 = 0;  // tokens (gather: list entries) of this partition
+  const int32_t* lst = nullptr;
+  if constexpr (kGather) {
+    const int cnt = sel_cnt[(size_t)b * Q + jq];
+    bad = bad || cnt < 0 || cnt > topk;
+    lst = sel_idx + ((size_t)b * Q + jq) * topk;
+    if (!bad) {
+      t0 = min(s * fixed, cnt);
+      t1 = min(t0 + fixed, cnt);
+    }
+  } else {
+    if (!bad) split_range(L, S, page, fixed, s, &t0, &t1);
+  }
 
   for (int i = tid; i < nr * D; i += blockDim.x)
     qs[i] = Elt<T>::ld(q_full + ((size_t)b * R + r0) * D + i);
@@ -187,20 +212,41 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   // tokens this row sees: t <= lim, and with a drafted tree also the drafted
   // tokens (t >= L - Q) on its branch
   const int t_draft = L - Q;  // first drafted token
-  const int lim = par ? t_draft - 1 : t_draft + my_j;
+  const int lim = kGather ? t1 - 1 : (par ? t_draft - 1 : t_draft + my_j);
   const uint64_t branch = (par && !bad && my_j < Q) ? tree_branch_mask(par, Q, my_j) : 0ull;
 
   for (int t = t0; t < t1 && !bad; t += kGenTok) {
     const int nt = min(kGenTok, t1 - t);
-    const int pg = page_table[(size_t)b * max_pages + t / page];
-    if (pg < 0 || (int64_t)pg >= num_pages) {
-      bad = true;  // uniform across the block: every thread read the same entry
-      break;
+    if constexpr (kGather) {
+      __syncthreads();  // previous step done with cs / ps / al / rs
+      if (tid < nt) {   // list entry -> cache row; -1 when not visible or its page is invalid
+        const int tk = lst[t + tid];
+        const int pg =
+            (tk >= 0 && tk <= L - Q + jq) ? page_table[(size_t)b * max_pages + tk / page] : -1;
+        rs[tid] = (pg < 0 || (int64_t)pg >= num_pages) ? -1 : (int64_t)pg * page + tk % page;
+      }
+      __syncthreads();
+      bool badrow = false;  // every thread reads every entry: block-uniform
+      for (int u = 0; u < nt; ++u) badrow |= rs[u] < 0;
+      if (badrow) {
+        bad = true;
+        break;
+      }
+      for (int i = tid; i < nt * D; i += blockDim.x)
+        cs[(i / D) * Dp + (i % D)] = Elt<T>::ld(cache + rs[i / D] * D + (i % D));
+      __syncthreads();
+    } else {
+      const int pg = page_table[(size_t)b * max_pages + t / page];
+      if (pg < 0 || (int64_t)pg >= num_pages) {
+        bad = true;  // uniform across the block: every thread read the same entry
+        break;
+      }
+      __syncthreads();  // previous step done with cs / ps / al
+      const T* src = cache + ((size_t)pg * page + (t % page)) * D;
+      for (int i = tid; i < nt * D; i += blockDim.x)
+        cs[(i / D) * Dp + (i % D)] = Elt<T>::ld(src + i);
+      __syncthreads();
     }
-    __syncthreads();  // previous step done with cs / ps / al
-    const T* src = cache + ((size_t)pg * page + (t % page)) * D;
-    for (int i = tid; i < nt * D; i += blockDim.x) cs[(i / D) * Dp + (i % D)] = Elt<T>::ld(src + i);
-    __syncthreads();
     float sc = -INFINITY;
     const bool seen = (tile_visible(t, lim, t_draft, t1, branch) >> my_k) & 1ull;
     if (my_r < nr && my_k < nt && seen) {
@@ -262,6 +308,15 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   }
 }
 
+// dynamic LDS of the generic decode: queries, staged tokens, P, rescale
+// factors (2 x kGenRows floats keep what follows 8-byte aligned) and the
+// gathered row numbers
+static size_t generic_lds_bytes(int D) {
+  return sizeof(float) * ((size_t)kGenRows * D + (size_t)kGenTok * (D + 1) + kGenRows * kGenTok +
+                          2 * kGenRows) +
+         sizeof(int64_t) * kGenTok;
+}
+
 template <typename T>
 static int decode_generic_impl(const Shape& s, int batch, int q_len, int num_splits,
                                int max_seq_len, const void* q_full, const void* cache,
@@ -269,22 +324,73 @@ static int decode_generic_impl(const Shape& s, int batch, int q_len, int num_spl
                                const int32_t* seq_lens, const int32_t* tree_parent, float* o_part,
                                float* lse_part, void* stream) {
   const int D = s.D();
-  const size_t lds = sizeof(float) * ((size_t)kGenRows * D + (size_t)kGenTok * (D + 1) +
-                                      kGenRows * kGenTok + kGenRows);
   static bool attr_set = false;
   if (!attr_set) {
-    HIPCHK(hipFuncSetAttribute((const void*)decode_generic_kernel<T>,
+    HIPCHK(hipFuncSetAttribute((const void*)decode_generic_kernel<T, false>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024));
     attr_set = true;
   }
   const int R = q_len * s.H;
   dim3 grid(num_splits, batch, (R + kGenRows - 1) / kGenRows);
-  hipLaunchKernelGGL(decode_generic_kernel<T>, grid, dim3(256), lds, as_stream(stream), q_len, s.H,
-                     s.dc, s.dr, s.page, num_splits, s.split_fixed, max_seq_len, s.scale,
-                     (const T*)q_full,
-                     (const T*)cache, num_pages, page_table, max_pages, seq_lens, tree_parent,
-                     o_part, lse_part);
+  hipLaunchKernelGGL((decode_generic_kernel<T, false>), grid, dim3(256), generic_lds_bytes(D),
+                     as_stream(stream), q_len, s.H, s.dc, s.dr, s.page, num_splits, s.split_fixed,
+                     max_seq_len, s.scale, (const T*)q_full, (const T*)cache, num_pages,
+                     page_table, max_pages, seq_lens, tree_parent, nullptr, nullptr, 0, o_part,
+                     lse_part);
   return (int)hipGetLastError();
+}
+
+template <typename T>
+static int decode_sparse_generic_impl(const Shape& s, int batch, int q_len, int topk, int chunk,
+                                      int num_splits, int max_seq_len, const void* q_full,
+                                      const void* cache, int64_t num_pages,
+                                      const int32_t* page_table, int max_pages,
+                                      const int32_t* seq_lens, const int32_t* sel_idx,
+                                      const int32_t* sel_cnt, float* o_part, float* lse_part,
+                                      void* stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    HIPCHK(hipFuncSetAttribute((const void*)decode_generic_kernel<T, true>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024));
+    attr_set = true;
+  }
+  dim3 grid(num_splits, batch, q_len * ((s.H + kGenRows - 1) / kGenRows));
+  hipLaunchKernelGGL((decode_generic_kernel<T, true>), grid, dim3(256), generic_lds_bytes(s.D()),
+                     as_stream(stream), q_len, s.H, s.dc, s.dr, s.page, num_splits, chunk,
+                     max_seq_len, s.scale, (const T*)q_full, (const T*)cache, num_pages,
+                     page_table, max_pages, seq_lens, nullptr, sel_idx, sel_cnt, topk, o_part,
+                     lse_part);
+  return (int)hipGetLastError();
+}
+
+bool decode_sparse_rows16_ok(const Shape& s, int chunk);
+int launch_decode_sparse_rows16(const Shape& s, int batch, int q_len, int topk, int chunk,
+                                int num_splits, int max_seq_len, const void* q_full,
+                                const void* cache, int64_t num_pages, const int32_t* page_table,
+                                int max_pages, const int32_t* seq_lens, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, float* o_part, float* lse_part,
+                                void* stream);
+
+int decode_sparse_kind(const Shape& s, int chunk) { return decode_sparse_rows16_ok(s, chunk) ? 1 : 0; }
+
+int launch_decode_sparse(const Shape& s, int batch, int q_len, int topk, int chunk, int num_splits,
+                         int max_seq_len, const void* q_full, const void* cache, int64_t num_pages,
+                         const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                         const int32_t* sel_idx, const int32_t* sel_cnt, float* o_part,
+                         float* lse_part, void* stream) {
+  if (decode_sparse_kind(s, chunk) == 1)
+    return launch_decode_sparse_rows16(s, batch, q_len, topk, chunk, num_splits, max_seq_len,
+                                       q_full, cache, num_pages, page_table, max_pages, seq_lens,
+                                       sel_idx, sel_cnt, o_part, lse_part, stream);
+  return s.dtype == 0
+             ? decode_sparse_generic_impl<float>(s, batch, q_len, topk, chunk, num_splits,
+                                                 max_seq_len, q_full, cache, num_pages, page_table,
+                                                 max_pages, seq_lens, sel_idx, sel_cnt, o_part,
+                                                 lse_part, stream)
+             : decode_sparse_generic_impl<bf16_t>(s, batch, q_len, topk, chunk, num_splits,
+                                                  max_seq_len, q_full, cache, num_pages,
+                                                  page_table, max_pages, seq_lens, sel_idx,
+                                                  sel_cnt, o_part, lse_part, stream);
 }
 
 bool decode_rows16_ok(const Shape& s, int q_len);

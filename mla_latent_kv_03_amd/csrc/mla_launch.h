@@ -82,4 +82,29 @@ int launch_decode_q8(const Shape& s, int batch, int q_len, int num_splits, int m
 // kernel with 64 query rows per block.
 int decode_kernel_kind(const Shape& s, int q_len);
 
+// Sparse read. Indexer keys: rows of dI elements of type T through the same
+// page table; scores: [batch][q_len][ld] f32; selection: indices
+// [batch][q_len][topk] int32 and counts [batch][q_len] int32 (-1: invalid).
+int launch_index_append(const Shape& s, int dI, int n_tok, const void* k_new,
+                        const int32_t* seq_idx, const int32_t* pos, const int32_t* page_table,
+                        int batch, int max_pages, void* icache, int64_t num_pages, void* stream);
+bool index_scores_mfma_ok(const Shape& s, int Hi, int dI);
+size_t index_scores_generic_lds(int Hi, int dI);
+int launch_index_scores(const Shape& s, int Hi, int dI, int batch, int q_len, int max_seq_len,
+                        const void* q_idx, const float* w_idx, const void* icache,
+                        int64_t num_pages, const int32_t* page_table, int max_pages,
+                        const int32_t* seq_lens, float* scores, int ld, void* stream);
+int launch_topk(int batch, int q_len, int max_seq_len, int topk, const float* scores, int ld,
+                const int32_t* seq_lens, int32_t* indices, int32_t* counts, void* stream);
+// decode over the selected tokens: partition s of query (b, j) covers list
+// entries [s * chunk, min(count, (s + 1) * chunk)); kind 1 = the bf16 MFMA
+// kernel (16 rows per block, H % 16 == 0, chunk a multiple of 32 up to
+// 1,984), 0 = generic
+int decode_sparse_kind(const Shape& s, int chunk);
+int launch_decode_sparse(const Shape& s, int batch, int q_len, int topk, int chunk, int num_splits,
+                         int max_seq_len, const void* q_full, const void* cache, int64_t num_pages,
+                         const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                         const int32_t* sel_idx, const int32_t* sel_cnt, float* o_part,
+                         float* lse_part, void* stream);
+
 }  // namespace mla

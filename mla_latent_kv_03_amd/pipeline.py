@@ -74,7 +74,7 @@ class DecodeStep:
 
     def __init__(self, cfg: B.Config, batch: int, q_len: int, num_splits: int,
                  seq_lens_host, device="cuda", split_chunk: int = 0, tree_parents=None,
-                 cache_q8: bool = False):
+                 cache_q8: bool = False, index_topk: int = 0):
         t = _torch()
         self.cfg, self.batch, self.q_len, self.num_splits = cfg, batch, q_len, num_splits
         self.split_chunk = split_chunk  # > 0: fixed-size partitions
@@ -99,6 +99,12 @@ class DecodeStep:
         self.o_lat = t.empty((batch, q_len, H, dc), dtype=dt, device=device)
         self.lse = t.empty((batch, q_len, H), dtype=t.float32, device=device)
         self.out = t.empty((batch, q_len, H, dv), dtype=dt, device=device)
+        # sparse read: index scores, then the index_topk tokens each query reads
+        self.index_topk = index_topk
+        if index_topk > 0:
+            self.scores = t.empty((batch, q_len, self.max_seq_len), dtype=t.float32, device=device)
+            self.indices = t.empty((batch, q_len, index_topk), dtype=t.int32, device=device)
+            self.counts = t.empty((batch, q_len), dtype=t.int32, device=device)
 
     def absorb(self, q_nope, q_rope, w_uk, stream=None):
         B.absorb_q(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, stream)
@@ -115,8 +121,23 @@ class DecodeStep:
             B.cache_append_at(self.cfg, c_new, k_new, self.seq_idx, self.slot, self.qpos,
                               page_table, cache, B.APPEND_ROTATE, stream)
 
+    def index_append(self, k_idx_new, page_table, index_cache, stream=None):
+        B.index_append(self.cfg, k_idx_new, self.seq_idx, self.slot, page_table, index_cache,
+                       stream)
+
+    def index_scores(self, q_idx, w_idx, index_cache, page_table, seq_lens, stream=None):
+        B.index_scores(self.cfg, q_idx, w_idx, index_cache, page_table, seq_lens, self.scores,
+                       self.max_seq_len, stream)
+
+    def select(self, seq_lens, stream=None):
+        B.topk_select(self.scores, seq_lens, self.indices, self.counts, self.max_seq_len, stream)
+
     def decode(self, cache, page_table, seq_lens, stream=None, max_seq_len: Optional[int] = None):
-        if self.cache_q8:
+        if self.index_topk > 0:
+            B.decode_sparse(self.cfg, self.q_full, cache, page_table, seq_lens, self.indices,
+                            self.counts, self.o_part, self.lse_part,
+                            max_seq_len or self.max_seq_len, stream)
+        elif self.cache_q8:
             B.decode_paged_q8(self.cfg, self.q_full, cache, page_table, seq_lens, self.o_part,
                               self.lse_part, max_seq_len or self.max_seq_len, stream,
                               chunk_tokens=self.split_chunk, tree_parent=self.tree)
@@ -152,16 +173,24 @@ class DecodeStep:
                              self.lse, stream)
 
     def run(self, q_nope, q_rope, w_uk, w_uv, c_new, k_new, cache, page_table, seq_lens,
-            stream=None, max_seq_len: Optional[int] = None, fused: bool = True):
+            stream=None, max_seq_len: Optional[int] = None, fused: bool = True, sparse=None):
         """absorb -> append (B*Q new rows) -> decode -> combine -> up-project.
 
         fused: the first two and the last two calls each as one library call
-        (mla_absorb_append, mla_combine_up_project; same results)."""
+        (mla_absorb_append, mla_combine_up_project; same results).
+        sparse: (q_idx, w_idx, k_idx_new, index_cache) for a sparse read: the
+        new indexer keys are appended, every cached token scored, the top
+        index_topk selected, and the decode reads only those."""
         if fused:
             self.absorb_append(q_nope, q_rope, w_uk, c_new, k_new, page_table, cache, stream)
         else:
             self.absorb(q_nope, q_rope, w_uk, stream)
             self.append(c_new, k_new, page_table, cache, stream)
+        if self.index_topk > 0:
+            q_idx, w_idx, k_idx_new, index_cache = sparse
+            self.index_append(k_idx_new, page_table, index_cache, stream)
+            self.index_scores(q_idx, w_idx, index_cache, page_table, seq_lens, stream)
+            self.select(seq_lens, stream)
         self.decode(cache, page_table, seq_lens, stream, max_seq_len)
         if fused:
             self.combine_up_project(w_uv, stream)
@@ -169,6 +198,15 @@ class DecodeStep:
             self.combine(stream)
             self.up_project(w_uv, stream)
         return self.out
+
+
+def fill_index_cache(cfg: B.Config, index_cache, page_table, k_all, seq_idx, pos, stream=None,
+                     rows_per_call: int = 1 << 20):
+    """Write every cached token's indexer key (setup), rows n at (seq_idx[n], pos[n])."""
+    n = int(pos.numel())
+    for a in range(0, n, rows_per_call):
+        e = min(n, a + rows_per_call)
+        B.index_append(cfg, k_all[a:e], seq_idx[a:e], pos[a:e], page_table, index_cache, stream)
 
 
 def fill_cache_q8(cfg: B.Config, cache_q8, page_table, c_all, k_all, seq_idx, pos, stream=None,

@@ -13,7 +13,7 @@ import oracle
 import workload
 import mla_latent_kv_03_amd as mla
 from mla_latent_kv_03_amd.pipeline import (DecodeStep, dtype_of, fill_cache, fill_cache_q8,
-                                           token_rope_positions, upload)
+                                           fill_index_cache, token_rope_positions, upload)
 
 NAN_BF16 = 0x7FC1      # quiet NaN with a payload: poison for unused cache slots
 NAN_F32 = 0x7FC00001
@@ -33,6 +33,14 @@ def poisoned_pool(cfg, num_pages, device="cuda"):
         t = torch.full((num_pages, cfg.page_size, cfg.dim), NAN_F32, dtype=torch.int32, device=device)
         return t.view(torch.float32)
     t = torch.full((num_pages, cfg.page_size, cfg.dim), NAN_BF16, dtype=torch.int16, device=device)
+    return t.view(torch.bfloat16)
+
+
+def poisoned_index_pool(cfg, num_pages, dim, device="cuda"):
+    if cfg.dtype == mla.F32:
+        t = torch.full((num_pages, cfg.page_size, dim), NAN_F32, dtype=torch.int32, device=device)
+        return t.view(torch.float32)
+    t = torch.full((num_pages, cfg.page_size, dim), NAN_BF16, dtype=torch.int16, device=device)
     return t.view(torch.bfloat16)
 
 
@@ -81,14 +89,24 @@ class Case:
         self.c_new = upload(inp.c[rows], dt)
         self.k_new = upload(inp.k_rope[rows], dt)
         self.chunk = wl.split_chunk if num_splits is None else 0
+        self.sparse = None
+        if wl.index_topk > 0:  # sparse read: indexer keys cached beside the latent rows
+            self.index_pool = poisoned_index_pool(cfg, inp.num_pages, wl.index_dim)
+            fill_index_cache(cfg, self.index_pool, self.pt, upload(inp.k_idx, dt),
+                             upload(si, torch.int32), upload(pos, torch.int32))
+            self.q_idx = upload(np.ascontiguousarray(inp.q_idx), dt)
+            self.w_idx = upload(np.ascontiguousarray(inp.w_idx), torch.float32)
+            self.k_idx_new = upload(inp.k_idx[rows], dt)
+            self.sparse = (self.q_idx, self.w_idx, self.k_idx_new, self.index_pool)
         self.step = DecodeStep(cfg, B, Q, self.S, inp.seq_lens, split_chunk=self.chunk,
-                               tree_parents=inp.parents, cache_q8=self.q8)
+                               tree_parents=inp.parents, cache_q8=self.q8,
+                               index_topk=wl.index_topk)
         torch.cuda.synchronize()
 
     def run(self, max_seq_len=None, fused=True):
         out = self.step.run(self.q_nope, self.q_rope, self.w_uk, self.w_uv, self.c_new, self.k_new,
                             self.pool, self.pt, self.seq_lens, max_seq_len=max_seq_len,
-                            fused=fused)
+                            fused=fused, sparse=self.sparse)
         torch.cuda.synchronize()
         return out
 
@@ -96,7 +114,9 @@ class Case:
         s = self.step
         return {"o": to64(s.out), "o_lat": to64(s.o_lat), "lse": to64(s.lse)}
 
-    def oracle(self, heads=None, seqs=None):
+    def oracle(self, heads=None, seqs=None, selection=None):
+        if self.wl.index_topk > 0:  # attention over the oracle's own selection
+            return oracle.mla_decode_ref_sparse(self.inp, selection, heads=heads, seqs=seqs)
         if self.q8:  # the attention over the rows the 8-bit cache encodes
             return oracle.mla_decode_ref_q8(self.inp, heads=heads, seqs=seqs)
         return oracle.mla_decode_ref(self.inp, heads=heads, seqs=seqs)

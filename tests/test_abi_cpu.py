@@ -257,3 +257,49 @@ def test_q8_entry_errors(L):
     assert L.mla_cache_append_q8(_c(V2), 8, *args, None, A16, 2, 4, None, 16, 1, None) == 1
     odd = mla.Config(num_heads=4, kv_rank=64, rope_dim=8, nope_dim=32, v_dim=32, dtype=mla.F32)
     assert L.mla_cache_append_q8(_c(odd), 8, *args, None, A16, 2, 4, A16, 16, 1, None) == 6
+
+
+def test_sparse_entry_errors(L):
+    c = _c(V2)
+    # indexer key append: width rule, pointers, alignment, empty call
+    assert L.mla_index_append(c, 130, 4, A16, A16, A16, A16, 2, 4, A16, 16, None) == 2
+    assert L.mla_index_append(c, 128, 4, None, A16, A16, A16, 2, 4, A16, 16, None) == 1
+    assert L.mla_index_append(c, 128, 4, A16, A16, MIS, A16, 2, 4, A16, 16, None) == 4
+    assert L.mla_index_append(c, 128, 0, None, None, None, None, 2, 4, None, 16, None) == 0
+    # index scores: heads range, ld below max_seq_len, capacity, unsupported LDS size
+    def sc(heads=64, dim=128, ld=256, max_len=256, max_pages=4, scores=A16, cfg=V2):
+        return L.mla_index_scores(_c(cfg), heads, dim, 2, 1, max_len, A16, A16, A16, 8, A16,
+                                  max_pages, A16, scores, ld, None)
+    assert sc(heads=0) == 2 and sc(heads=257) == 2
+    assert sc(ld=255) == 2
+    assert sc(max_len=300) == 5                                     # 4 pages x 64 < 300
+    assert sc(scores=None) == 1 and sc(scores=MIS) == 4
+    assert sc(heads=256, dim=1024, cfg=TINY) == 6                   # generic needs > 160 KiB
+    # top-k
+    assert L.mla_topk_select(2, 1, 256, 0, A16, 256, A16, A16, A16, None) == 2
+    assert L.mla_topk_select(2, 1, 256, 65537, A16, 256, A16, A16, A16, None) == 2
+    assert L.mla_topk_select(2, 1, 256, 64, A16, 200, A16, A16, A16, None) == 2
+    assert L.mla_topk_select(2, 1, 256, 64, A16, 256, A16, None, A16, None) == 1
+    assert L.mla_topk_select(0, 1, 256, 64, None, 256, None, None, None, None) == 0
+    # sparse decode
+    def dec(topk=2048, S=16, counts=A16, batch=2):
+        return L.mla_decode_sparse(c, batch, 1, topk, S, 256, A16, A16, 8, A16, 4, A16, A16,
+                                   counts, A16, A16, None)
+    assert dec(topk=0) == 2 and dec(S=0) == 2
+    assert dec(counts=None) == 1 and dec(counts=MIS) == 4
+    assert dec(batch=0) == 0
+
+
+def test_sparse_chunk_and_kernel_choice(L):
+    assert mla.sparse_chunk(2048, 16) == 128
+    assert mla.sparse_chunk(2048, 3) == 704                # ceil(2048/3) = 683 -> 704
+    assert mla.sparse_chunk(100, 1) == 128
+    assert mla.sparse_chunk(0, 4) == 0 and mla.sparse_chunk(64, 0) == 0
+    assert mla.decode_sparse_kernel_kind(V2, 2048, 16) == "mfma_rows16_gather"
+    assert mla.decode_sparse_kernel_kind(V2, 2048, 2) == "mfma_rows16_gather"  # chunk 1024
+    assert mla.decode_sparse_kernel_kind(V2, 2048, 1) == "generic_gather"      # chunk > 1,984
+    assert mla.decode_sparse_kernel_kind(mla.Config(num_heads=8), 2048, 16) == "generic_gather"
+    assert mla.decode_sparse_kernel_kind(mla.Config(num_heads=128), 2048, 16) == \
+        "mfma_rows16_gather"
+    assert mla.decode_sparse_kernel_kind(TINY, 64, 2) == "generic_gather"
+    assert mla.decode_sparse_kernel_kind(V2, 0, 2) == "invalid"

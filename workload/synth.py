@@ -63,6 +63,10 @@ class Workload:
     index_topk: int = 0
     index_heads: int = 64
     index_dim: int = 128
+    # True: indexer queries and keys are integers in [-2, 2] and head weights
+    # multiples of 1/8 in [-2, 2], so every index score is exact in float32
+    # whatever the summation order (both sides then rank identical values)
+    index_exact: bool = False
     description: str = ""
 
     @property
@@ -181,8 +185,16 @@ def seq_latents(wl: Workload, seed: int, b: int, length: int):
     return c, kr
 
 
+def _small_ints(rng, shape, lo, hi, scale=1.0):
+    return (rng.integers(lo, hi, endpoint=True, size=shape).astype(np.float32)
+            * np.float32(scale))
+
+
 def seq_index_keys(wl: Workload, seed: int, b: int, length: int) -> np.ndarray:
-    """Indexer keys [length][d_I] of sequence b: N(0, 1), in the workload dtype."""
+    """Indexer keys [length][d_I] of sequence b: N(0, 1) in the workload dtype,
+    or integers in [-2, 2] with ``index_exact``."""
+    if wl.index_exact:
+        return _small_ints(_rng(seed, _T_KI, b), (length, wl.index_dim), -2, 2)
     return _normal(_rng(seed, _T_KI, b), (length, wl.index_dim), 1.0, wl.dtype)
 
 
@@ -302,9 +314,13 @@ def make(wl: Workload, seed: int = 0, with_latents: bool = True,
                  parents=tree_parents(wl, seed))
     if wl.index_topk > 0:
         Hi, di = wl.index_heads, wl.index_dim
-        inp.q_idx = _normal(_rng(seed, _T_QI), (wl.batch, wl.q_len, Hi, di), 1.0, wl.dtype)
-        inp.w_idx = _normal(_rng(seed, _T_WI), (wl.batch, wl.q_len, Hi), 1.0 / math.sqrt(Hi),
-                            "f32")
+        if wl.index_exact:
+            inp.q_idx = _small_ints(_rng(seed, _T_QI), (wl.batch, wl.q_len, Hi, di), -2, 2)
+            inp.w_idx = _small_ints(_rng(seed, _T_WI), (wl.batch, wl.q_len, Hi), -16, 16, 0.125)
+        else:
+            inp.q_idx = _normal(_rng(seed, _T_QI), (wl.batch, wl.q_len, Hi, di), 1.0, wl.dtype)
+            inp.w_idx = _normal(_rng(seed, _T_WI), (wl.batch, wl.q_len, Hi), 1.0 / math.sqrt(Hi),
+                                "f32")
     if with_latents:
         T = int(offsets[-1])
         fdt = np.float32
