@@ -14,6 +14,10 @@ has) so every step reads its latent cache from HBM rather than from the
 Prints one JSON line. value = latent-cache bytes read per step / step time
 (GB/s); the decode kernel's own rate against the 8 TB/s HBM peak is in
 "roofline"; the fp64 oracle timed on the host cores is in "cpu_baseline".
+A sparse-read workload (v2lite_32k_dsa) adds the indexer-key append, the
+index scores and the top-k selection to the step, and its decode reads only
+the selected rows: value = (indexer keys + selected latent rows) per step
+time, and "roofline" is the indexer pass, the step's dominant kernel.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
 """
@@ -34,7 +38,7 @@ METRIC = "MLA decode latent-cache GB/s (% of HBM peak) + decode tokens/s, V2-Lit
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LAYERS = {"v2lite_32k": 27, "v2lite_paged_varlen": 27, "v2_h128_8k": 4, "v2_h128_1m_q4": 2,
-          "v2lite_32k_tree8": 27, "v2lite_32k_q8": 27, "tiny_f32": 4}
+          "v2lite_32k_tree8": 27, "v2lite_32k_q8": 27, "v2lite_32k_dsa": 27, "tiny_f32": 4}
 CSRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc")
 # decode kernel name (mla_decode_kernel_name) -> (kernel symbol, the sources that define it)
 DECODE_KERNELS = {
@@ -42,6 +46,8 @@ DECODE_KERNELS = {
     "mfma_ws": ("decode_ws_kernel", ["mla_decode_common.h", "mla_decode_ws.hip"]),
     "generic": ("decode_generic_kernel", ["mla_kernels.hip"]),
     "mfma_q8": ("decode_q8_kernel", ["mla_decode_common.h", "mla_q8.hip"]),
+    # sparse read: the indexer pass is the step's dominant kernel
+    "index_scores_mfma": ("index_scores_mfma_kernel", ["mla_decode_common.h", "mla_sparse.hip"]),
 }
 
 
@@ -114,20 +120,48 @@ def cpu_baseline(wl, inp, budget_flops=2.4e12):
             break
         seqs.append(b)
         spent += seq_cost(b, heads)
-    ref = oracle.mla_decode_ref_q8 if wl.cache == "q8" else oracle.mla_decode_ref
+    sparse = wl.index_topk > 0
+    if sparse:  # indexer scores + selection of every sequence of the sample, then attention
+        ref = lambda x, heads, seqs: oracle.mla_decode_ref_sparse(  # noqa: E731
+            x, sparse_selection(x, seqs), heads=heads, seqs=seqs)
+    else:
+        ref = oracle.mla_decode_ref_q8 if wl.cache == "q8" else oracle.mla_decode_ref
     t = time.perf_counter()
     ref(inp, heads=list(range(heads)), seqs=seqs)
     dt = time.perf_counter() - t
     tokens = sum(int(inp.seq_lens[b]) for b in seqs)
-    nbytes = tokens * wl.cache_row_bytes * heads / wl.heads
+    if sparse:  # indexer keys of every token + the selected latent rows
+        sel = sum(min(wl.index_topk, int(inp.seq_lens[b]) - wl.q_len + j + 1)
+                  for b in seqs for j in range(wl.q_len))
+        nbytes = (tokens * wl.index_dim * wl.elem_bytes
+                  + sel * wl.cache_row_bytes * heads / wl.heads)
+    else:
+        nbytes = tokens * wl.cache_row_bytes * heads / wl.heads
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{len(seqs)} of {wl.batch} sequences ({tokens} cached tokens), "
                       f"{heads} of {wl.heads} heads, {dt:.1f} s; fp64 unabsorbed NumPy oracle"
-                      f"{' (rows coded to 8 bits first)' if wl.cache == 'q8' else ''}; "
+                      f"{' (rows coded to 8 bits first)' if wl.cache == 'q8' else ''}"
+                      f"{' (indexer scores and top-k selection first)' if sparse else ''}; "
                       f"bytes counted x {heads}/{wl.heads}",
             "seconds": round(dt, 2),
             "decode_tokens_per_s": round(len(seqs) * wl.q_len * heads / wl.heads / dt, 4)}
+
+
+def sparse_selection(inp, seqs):
+    """The oracle's selection for the sampled sequences only (others empty)."""
+    import oracle
+    wl = inp.wl
+    out = []
+    for b in range(wl.batch):
+        if b not in seqs:
+            out.append([[] for _ in range(wl.q_len)])
+            continue
+        L = int(inp.seq_lens[b])
+        sc = oracle.indexer_scores(inp.q_idx[b], inp.w_idx[b], inp.seq_index_keys(b))
+        out.append([oracle.topk_tokens(sc[j], wl.index_topk, L - wl.q_len + j + 1)
+                    for j in range(wl.q_len)])
+    return out
 
 
 def main():
@@ -142,7 +176,7 @@ def main():
     import workload
     import mla_latent_kv_03_amd as mla
     from mla_latent_kv_03_amd.pipeline import (DecodeStep, fill_cache, fill_cache_q8,
-                                               token_rope_positions, upload)
+                                               fill_index_cache, token_rope_positions, upload)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -188,9 +222,17 @@ def main():
     rows = np.concatenate([inp.offsets[b] + np.arange(int(L) - Q, int(L))
                            for b, L in enumerate(inp.seq_lens)])
     c_new, k_new = upload(inp.c[rows], dt), upload(inp.k_rope[rows], dt)
-    steps = [DecodeStep(cfg, B, Q, wl.num_splits, inp.seq_lens, split_chunk=wl.split_chunk,
-                        tree_parents=inp.parents, cache_q8=q8) for _ in range(1)]
-    st = steps[0]
+    sparse = wl.index_topk > 0
+    if sparse:  # indexer keys: one pool per layer, like the latent cache
+        ipool0 = torch.full((inp.num_pages, wl.page_size, wl.index_dim), float("nan"), dtype=dt,
+                            device="cuda")
+        fill_index_cache(cfg, ipool0, pt, upload(inp.k_idx, dt), upload(si, torch.int32),
+                         upload(pos, torch.int32))
+        ipools = [ipool0] + [ipool0.clone() for _ in range(n_layers - 1)]
+        q_idx, w_idx = upload(inp.q_idx, dt), upload(inp.w_idx, torch.float32)
+        k_idx_new = upload(inp.k_idx[rows], dt)
+    st = DecodeStep(cfg, B, Q, wl.num_splits, inp.seq_lens, split_chunk=wl.split_chunk,
+                    tree_parents=inp.parents, cache_q8=q8, index_topk=wl.index_topk)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
 
@@ -203,6 +245,11 @@ def main():
             st.append(c_new, k_new, pt, pool)
         else:
             st.absorb_append(q_nope, q_rope, w_uk, c_new, k_new, pt, pool)
+        if sparse:
+            ipool = ipools[layer % n_layers]
+            st.index_append(k_idx_new, pt, ipool)
+            st.index_scores(q_idx, w_idx, ipool, pt, seq_lens)
+            st.select(seq_lens)
         st.decode(pool, pt, seq_lens)
         if args.unfused:
             st.combine()
@@ -253,10 +300,30 @@ def main():
     eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     eb0.record(stream)
     for i in range(kd):
-        st.decode(pools[i % n_layers], pt, seq_lens)
+        if sparse:  # the dominant kernel of a sparse step: the indexer pass
+            st.index_scores(q_idx, w_idx, ipools[i % n_layers], pt, seq_lens)
+        else:
+            st.decode(pools[i % n_layers], pt, seq_lens)
     eb1.record(stream)
     torch.cuda.synchronize()
     decode_ms = eb0.elapsed_time(eb1) / kd
+    sparse_calls = None
+    if sparse:  # per-call events around the selection and the gather decode
+        se = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(kd)]
+        for i in range(kd):
+            st.index_scores(q_idx, w_idx, ipools[i % n_layers], pt, seq_lens)
+            se[i][0].record(stream)
+            st.select(seq_lens)
+            se[i][1].record(stream)
+            st.decode(pools[i % n_layers], pt, seq_lens)
+            se[i][2].record(stream)
+        torch.cuda.synchronize()
+        tk = sorted(a.elapsed_time(b) for a, b, _ in se)
+        sd = sorted(b.elapsed_time(c) for _, b, c in se)
+        sparse_calls = {"topk_median_us": round(tk[len(tk) // 2] * 1e3, 2),
+                        "sparse_decode_median_us": round(sd[len(sd) // 2] * 1e3, 2),
+                        "sparse_decode_kernel": mla.decode_sparse_kernel_kind(
+                            cfg, wl.index_topk, wl.num_splits)}
 
     # ---- per-call durations of the decode kernel and of decode + combine:
     # HIP events around each call of a third pass (there the merge and the
@@ -269,7 +336,7 @@ def main():
         pool = pools[i % n_layers]
         st.absorb_append(q_nope, q_rope, w_uk, c_new, k_new, pt, pool)
         evs[i][0].record(stream)
-        st.decode(pool, pt, seq_lens)
+        st.decode(pool, pt, seq_lens)  # (sparse: over the last selection)
         evs[i][1].record(stream)
         st.combine()
         evs[i][2].record(stream)
@@ -283,14 +350,25 @@ def main():
 
     # ---- algorithmic work
     total_tokens = int(inp.seq_lens.astype(np.int64).sum())
-    cache_bytes = total_tokens * wl.cache_row_bytes                # read once per step
-    flops = total_tokens * Q * H * (2 * wl.dim + 2 * wl.kv_rank)
-    gbs_step = cache_bytes / (ms_step * 1e-3) / 1e9
+    if sparse:
+        # a sparse step reads every indexer key and the selected latent rows;
+        # the indexer pass (the timed kernel) reads the keys
+        sel_rows = sum(min(wl.index_topk, int(L) - Q + j + 1)
+                       for L in inp.seq_lens for j in range(Q))
+        kernel_bytes = total_tokens * wl.index_dim * wl.elem_bytes
+        step_bytes = kernel_bytes + sel_rows * wl.cache_row_bytes
+        flops = total_tokens * Q * 2 * wl.index_heads * wl.index_dim
+        kernel = "index_scores_mfma"
+    else:
+        kernel_bytes = step_bytes = total_tokens * wl.cache_row_bytes  # read once per step
+        flops = total_tokens * Q * H * (2 * wl.dim + 2 * wl.kv_rank)
+        kernel = "mfma_q8" if q8 else mla.decode_kernel_kind(cfg, Q)
+    cache_bytes = kernel_bytes
+    gbs_step = step_bytes / (ms_step * 1e-3) / 1e9
     gbs_decode = cache_bytes / (decode_ms * 1e-3) / 1e9
     tflops_decode = flops / (decode_ms * 1e-3) / 1e12
     ai = flops / cache_bytes
     bound = "hbm" if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
-    kernel = "mfma_q8" if q8 else mla.decode_kernel_kind(cfg, Q)
     ksym, ksrc = DECODE_KERNELS[kernel]
     khash = src_hash(ksrc)
     if bound == "hbm":
@@ -320,7 +398,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
-        "data": "synthetic: seeded N(0,1) latents/keys/queries, N(0,1/d_c) weights",
+        "data": "synthetic: seeded N(0,1) latents/keys/queries, N(0,1/d_c) weights"
+                + ("; indexer queries/keys N(0,1), head weights N(0,1/H_I)" if sparse else ""),
         "config": {"workload": wl.name, "batch": B, "q_len": Q, "heads": H,
                    "seq_len": wl.seq_len if wl.seq_len else list(wl.len_range),
                    "total_cached_tokens": total_tokens, "kv_rank": wl.kv_rank,
@@ -331,7 +410,9 @@ def main():
                    "library_calls_per_step": 5 if args.unfused else 3,
                    "drafted_tree": None if wl.tree is None else list(wl.tree),
                    "cache_format": wl.cache, "cache_bytes_per_token": wl.cache_row_bytes,
-                   "decode_kernel": kernel},
+                   "decode_kernel": kernel,
+                   "index_topk": wl.index_topk or None,
+                   "indexer": ([wl.index_heads, wl.index_dim] if sparse else None)},
         "pct_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B * Q / (ms_step * 1e-3), 1),
         "decode_gbs": round(gbs_decode, 1),
@@ -342,6 +423,10 @@ def main():
         "setup_s": round(t_setup, 1),
         "decode_src_sha256_16": khash,
     }
+    if sparse:
+        out["sparse"] = dict(sparse_calls, selected_rows_per_step=sel_rows,
+                             step_bytes=step_bytes,
+                             dense_equivalent_cache_bytes=total_tokens * wl.cache_row_bytes)
     if wl.name.startswith("v2lite"):
         out["v2lite_attention_tokens_per_s_27_layers"] = round(B / (27 * ms_step * 1e-3), 1)
     props = torch.cuda.get_device_properties(0)

@@ -345,10 +345,18 @@ mla_status_t mla_index_scores(const mla_config_t* cfg, int32_t index_heads, int3
  * min(topk, n) into counts[b][j]. counts[b][j] = -1 (indices unwritten)
  * when L_b is outside [q_len, max_seq_len] or a score among the n is NaN.
  * scores [batch][q_len][ld_scores] f32, indices [batch][q_len][topk] int32,
- * counts [batch][q_len] int32. 1 <= topk <= 65,536. */
+ * counts [batch][q_len] int32. 1 <= topk <= 65,536.
+ * workspace: mla_topk_workspace_bytes(batch, q_len) bytes of device memory
+ * that are all zero before the first call; every call leaves them all zero
+ * again, so one zeroing at allocation serves every later call (calls that
+ * share a workspace must not overlap). */
 mla_status_t mla_topk_select(int32_t batch, int32_t q_len, int32_t max_seq_len, int32_t topk,
                              const float* scores, int32_t ld_scores, const int32_t* seq_lens,
-                             int32_t* indices, int32_t* counts, void* stream);
+                             void* workspace, int32_t* indices, int32_t* counts, void* stream);
+
+/* Bytes of the workspace of mla_topk_select (per query: 4,096 histogram
+ * counts and a flag); 0 for invalid arguments. */
+size_t mla_topk_workspace_bytes(int32_t batch, int32_t q_len);
 
 /* List entries per partition of mla_decode_sparse: ceil(topk / num_splits)
  * rounded up to a multiple of 32; 0 for invalid arguments. */

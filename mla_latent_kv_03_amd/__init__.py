@@ -55,6 +55,7 @@ from ._binding import (  # noqa: F401
     index_append,
     index_scores,
     topk_select,
+    topk_workspace_bytes,
     sparse_chunk,
     decode_sparse_kernel_kind,
     decode_sparse,

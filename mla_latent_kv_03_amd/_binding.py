@@ -117,7 +117,8 @@ def lib() -> ctypes.CDLL:
         "mla_index_append": (ctypes.c_int, [P, I32, I32, VP, VP, VP, VP, I32, I32, VP, I64, VP]),
         "mla_index_scores": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, FP, VP, I64, VP, I32,
                                             VP, FP, I32, VP]),
-        "mla_topk_select": (ctypes.c_int, [I32, I32, I32, I32, FP, I32, VP, VP, VP, VP]),
+        "mla_topk_select": (ctypes.c_int, [I32, I32, I32, I32, FP, I32, VP, VP, VP, VP, VP]),
+        "mla_topk_workspace_bytes": (ctypes.c_size_t, [I32, I32]),
         "mla_sparse_chunk": (ctypes.c_int32, [I32, I32]),
         "mla_decode_sparse_kernel_name": (ctypes.c_char_p, [P, I32, I32]),
         "mla_decode_sparse": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32, VP,
@@ -441,9 +442,16 @@ def index_scores(cfg: Config, q_idx, w_idx, index_cache, page_table, seq_lens, s
                                _stream(stream)), "mla_index_scores")
 
 
-def topk_select(scores, seq_lens, indices, counts, max_seq_len: int, stream=None):
+def topk_workspace_bytes(batch: int, q_len: int) -> int:
+    """Bytes of the top-k workspace (allocate zeroed once; every call leaves it zero)."""
+    return int(lib().mla_topk_workspace_bytes(int(batch), int(q_len)))
+
+
+def topk_select(scores, seq_lens, indices, counts, max_seq_len: int, workspace, stream=None):
     """The topk (= indices.shape[2]) best-scored tokens each query sees, in
-    increasing token order; counts [B][Q] int32 (-1: invalid sequence)."""
+    increasing token order; counts [B][Q] int32 (-1: invalid sequence).
+    workspace: a uint8 device tensor of topk_workspace_bytes(B, Q), zero on
+    the first call (the call leaves it zero)."""
     t = _torch()
     if scores.dim() != 3 or indices.dim() != 3:
         raise ValueError("scores: expected [batch][q_len][ld]; indices [batch][q_len][topk]")
@@ -452,6 +460,7 @@ def topk_select(scores, seq_lens, indices, counts, max_seq_len: int, stream=None
     _ck(lib().mla_topk_select(B, Q, int(max_seq_len), K,
                               _need(scores, "scores", t.float32, B * Q * ld), ld,
                               _need(seq_lens, "seq_lens", t.int32, B),
+                              _need(workspace, "workspace", t.uint8, topk_workspace_bytes(B, Q)),
                               _need(indices, "indices", t.int32, B * Q * K),
                               _need(counts, "counts", t.int32, B * Q), _stream(stream)),
         "mla_topk_select")

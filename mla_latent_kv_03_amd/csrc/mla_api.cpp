@@ -476,9 +476,14 @@ mla_status_t mla_index_scores(const mla_config_t* cfg, int32_t index_heads, int3
                                              max_pages, seq_lens, scores, ld_scores, stream));
 }
 
+size_t mla_topk_workspace_bytes(int32_t batch, int32_t q_len) {
+  if (batch < 0 || q_len < 1 || (int64_t)batch * q_len > INT32_MAX) return 0;
+  return mla::topk_workspace_bytes(batch, q_len);
+}
+
 mla_status_t mla_topk_select(int32_t batch, int32_t q_len, int32_t max_seq_len, int32_t topk,
                              const float* scores, int32_t ld_scores, const int32_t* seq_lens,
-                             int32_t* indices, int32_t* counts, void* stream) {
+                             void* workspace, int32_t* indices, int32_t* counts, void* stream) {
   MLA_REQUIRE(batch >= 0 && q_len >= 1 && topk >= 1 && topk <= kMaxTopk, MLA_ERR_SHAPE);
   MLA_REQUIRE((int64_t)batch * q_len <= INT32_MAX, MLA_ERR_SHAPE);
   MLA_REQUIRE(max_seq_len >= q_len, MLA_ERR_CAPACITY);
@@ -486,10 +491,11 @@ mla_status_t mla_topk_select(int32_t batch, int32_t q_len, int32_t max_seq_len, 
   if (batch == 0) return MLA_OK;
   MLA_CHECK_PTR(scores);
   MLA_CHECK_PTR(seq_lens);
+  MLA_CHECK_PTR(workspace);
   MLA_CHECK_PTR(indices);
   MLA_CHECK_PTR(counts);
   return hip_status(mla::launch_topk(batch, q_len, max_seq_len, topk, scores, ld_scores, seq_lens,
-                                     indices, counts, stream));
+                                     workspace, indices, counts, stream));
 }
 
 int32_t mla_sparse_chunk(int32_t topk, int32_t num_splits) {

@@ -122,11 +122,17 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   int* const rows = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + kLdsBytes);
   auto slot = [&](int k) { return lds + (k & (kRing - 1)) * kTChunks; };
 
+  RowDma<kPartLoads> dma;
+  dma.init(wave * kPartChunks, lane, wave * kPartRows);
   PageWindow pw;
   if constexpr (!kGather) {
     pw.init(page_table + (size_t)b * max_pages + t0 / page, (t1 - t0 + page - 1) / page, lane);
     settle(pw.reg);
   } else {
+    // the queries go out first (their latency overlaps the lookups below)
+    if (wave < 2 && ntiles > 0)
+      dma.issue(q_full + ((size_t)b * R + row0 + wave * kPartRows) * kD,
+                __builtin_amdgcn_readfirstlane(lds_addr(slot(kRing - 1) + wave * kPartChunks)));
     // the partition's list entries -> cache rows (0 past the end or for an
     // entry that is not visible to the query or whose page is invalid)
     const int32_t* lst = sel_idx + ((size_t)b * Q + jq) * topk;
@@ -146,8 +152,6 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
     }
     __syncthreads();
   }
-  RowDma<kPartLoads> dma;
-  dma.init(wave * kPartChunks, lane, wave * kPartRows);
   // this wave's rows [8 wave, 8 wave + 8) of tile k (never across a page: 8 | page)
   auto issue = [&](int k) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(slot(k) + wave * kPartChunks));
@@ -200,7 +204,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   if (ntiles > 0) {
     // ---- prologue: queries (waves 0, 1: 8 rows each, into slot 3), tiles 0..2
     const int pre = min(ntiles, kRing - 1);
-    if (wave < 2)
+    if (!kGather && wave < 2)  // (gather: already on its way)
       dma.issue(q_full + ((size_t)b * R + row0 + wave * kPartRows) * kD,
                 __builtin_amdgcn_readfirstlane(lds_addr(slot(kRing - 1) + wave * kPartChunks)));
     issue(0);

@@ -23,11 +23,23 @@ namespace {
 
 constexpr int kIH = 64;   // indexer heads of the MFMA kernel
 constexpr int kID = 128;  // indexer key width of the MFMA kernel
-constexpr int kIdxTok = 256;  // tokens per index-score block (4 waves x 64)
+constexpr int kIdxChunks = 2;               // 64-token chunks per wave
+constexpr int kIdxTok = 4 * 64 * kIdxChunks;  // tokens per index-score block
 
 constexpr int kTkThreads = 1024;
-constexpr int kTkBins = 1024;
-constexpr int kTkLdsKeys = 36864;  // sequences up to this many visible tokens keep their keys in LDS
+constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kTkCoarseBits = 12;              // coarse bins: the top 12 bits of a key
+constexpr int kTkCoarse = 1 << kTkCoarseBits;
+constexpr int kTkWsRow = kTkCoarse + 4;        // workspace words per query: counts, NaN flag
+constexpr int kTkHistTok = 4096;               // scores per histogram block (16 per thread)
+constexpr int kTkCand = 8192;                  // keys of the k-th key's coarse bin gathered in LDS
+constexpr int kTkBinBits = 10;
+constexpr int kTkBins = 1 << kTkBinBits;
+constexpr int kTkBatch = 16;                   // score loads in flight per thread
+constexpr int kTkOut = 8;                      // 64-key chunks read ahead in the output passes
+constexpr int kTkRegKeys = 32;                 // register-resident keys per lane
+constexpr int kTkRegSpan = 64 * kTkRegKeys;    // tokens per wave
+constexpr int kTkRegTok = kTkWaves * kTkRegSpan;  // 32,768 tokens per block
 
 // ---------------------------------------------------------------------------
 // indexer key append: row n -> slot pos[n] of sequence seq_idx[n]
@@ -55,42 +67,30 @@ __global__ __launch_bounds__(64) void index_append_kernel(int dI, int page,
 __device__ __forceinline__ float relu_nan(float x) { return x < 0.0f ? 0.0f : x; }
 
 // ---------------------------------------------------------------------------
-// index scores, bf16 MFMA: 64 heads x 128 dims. Block = 256 tokens of one
-// (sequence, query); wave w takes tokens [64 w, 64 w + 64) in 4 groups of 16.
-// Per group: D[head][token] = q_idx[head][:] . k[token][:] on
-// v_mfma_f32_16x16x32_bf16 (M = 16 heads, N = 16 tokens, 4 head blocks x 4
-// k-steps), then lane (token n, head quarter kg) folds its 16 heads with
-// w * max(0, D) and the four quarters are summed with lane swaps.
+// index scores, bf16 MFMA: 64 heads x 128 dims. Block = kIdxTok tokens of one
+// (sequence, query); wave w takes kIdxChunks chunks of 64 tokens, chunk c
+// covering [kIdxTok * block + 64 (kIdxChunks w + c), + 64), in groups of 16.
+// Every load goes out before the first MFMA: queries and weights, then the
+// page entries of all chunks, then all their keys, so one wave keeps
+// kIdxChunks x 16 KB in flight. Per group: D[head][token] = q_idx[head][:] .
+// k[token][:] on v_mfma_f32_16x16x32_bf16 (M = 16 heads, N = 16 tokens, 4 head
+// blocks x 4 k-steps), then lane (token n, head quarter kg) folds its 16 heads
+// with w * max(0, D) and the four quarters are summed with lane swaps.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void index_scores_mfma_kernel(
-    int Q, int page, int max_seq_len, const bf16_t* __restrict__ q_idx,
-    const float* __restrict__ w_idx, const bf16_t* __restrict__ icache, int64_t num_pages,
-    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, int ld) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void index_scores_mfma_kernel(int Q, int page, int max_seq_len, const bf16_t* __restrict__ q_idx,
+                              const float* __restrict__ w_idx, const bf16_t* __restrict__ icache,
+                              int64_t num_pages, const int32_t* __restrict__ page_table,
+                              int max_pages, const int32_t* __restrict__ seq_lens,
+                              float* __restrict__ scores, int ld) {
   const int b = blockIdx.y, j = blockIdx.z;
   const int L = seq_lens[b];
   if (L < Q || L > max_seq_len) return;  // the selection reports the sequence invalid
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
-  const int tw = blockIdx.x * kIdxTok + wave * 64;
+  const int tw = blockIdx.x * kIdxTok + wave * 64 * kIdxChunks;
   if (tw >= L) return;
 
-  // keys first (the long loads): group g, token tw + 16 g + n, dims 32 ks + 8 kg
-  bf16x8_t kv[4][4];
-  bool okp[4];
-  const bf16x8_t zero = {};
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int t = tw + 16 * g + n;
-    const bool in = t < L;
-    int pg = in ? page_table[(size_t)b * max_pages + t / page] : 0;
-    okp[g] = pg >= 0 && (int64_t)pg < num_pages;
-    if (!okp[g]) pg = 0;
-    const bf16_t* kp = icache + ((size_t)pg * page + (in ? t % page : 0)) * kID + 8 * kg;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      kv[g][ks] = in ? *reinterpret_cast<const bf16x8_t*>(kp + 32 * ks) : zero;
-  }
   // queries: head 16 mt + n, dims 32 ks + 8 kg; weights of heads 16 mt + 4 kg + r
   const bf16_t* qb = q_idx + ((size_t)b * Q + j) * kIH * kID;
   const float* wb = w_idx + ((size_t)b * Q + j) * kIH;
@@ -104,9 +104,33 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) wv[mt][r] = wb[16 * mt + 4 * kg + r];
   }
+  // page entries of every group (token tw + 16 g + n)
+  constexpr int kG = 4 * kIdxChunks;
+  int pgs[kG];
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const int t = tw + 16 * g + n;
+    pgs[g] = t < L ? page_table[(size_t)b * max_pages + t / page] : 0;
+  }
+  // keys: dims 32 ks + 8 kg of token tw + 16 g + n
+  bf16x8_t kv[kG][4];
+  bool okp[kG];
+  const bf16x8_t zero = {};
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const int t = tw + 16 * g + n;
+    const bool in = t < L;
+    int pg = pgs[g];
+    okp[g] = pg >= 0 && (int64_t)pg < num_pages;
+    if (!okp[g]) pg = 0;
+    const bf16_t* kp = icache + ((size_t)pg * page + (in ? t % page : 0)) * kID + 8 * kg;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kv[g][ks] = in ? *reinterpret_cast<const bf16x8_t*>(kp + 32 * ks) : zero;
+  }
   float* out = scores + ((size_t)b * Q + j) * ld;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < kG; ++g) {
     float part = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -161,16 +185,24 @@ __global__ __launch_bounds__(256) void index_scores_generic_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// top-k selection: one block of 1,024 threads per (sequence, query).
-// Scores map to order-preserving 32-bit keys (-0 taken as +0). The k-th
-// largest key T is found by narrowing a key range [lo, hi]: a histogram of
-// 1,024 equal-width bins over the range, the bin where the count from the
-// top reaches the number still needed becomes the new range (at most four
-// rounds, each dividing the width by ~1,024). Then every thread takes an
-// equal slice of the tokens in order (slices of odd length, so that the
-// slices' LDS reads fall in distinct banks), counts keys > T and == T, and
-// one block scan gives each slice its output position: all keys > T, and the
-// first (topk - count(> T)) keys == T in token order.
+// top-k selection in two launches.
+// Scores map to order-preserving 32-bit keys (-0 taken as +0); the top 12
+// bits of a key (sign, exponent, 3 mantissa bits) name one of 4,096 coarse
+// bins, in key order.
+//  1. topk_hist_kernel: blocks of 256 threads take 4,096 visible scores each,
+//     count them per coarse bin in LDS and add the non-empty bins to the
+//     query's histogram in the workspace (global atomics); a NaN sets the
+//     query's flag there.
+//  2. topk_select_kernel: one block of 1,024 threads (16 waves) per query
+//     reads the histogram and clears it (the workspace is all zero between
+//     calls), finds the coarse bin of the k-th largest key and gathers that
+//     bin's keys into LDS with wave ballots; the exact k-th key T is found by
+//     narrowing [lo, hi] over those keys with histograms of 1,024 bins of 2^s
+//     keys (a shift, no division). When the bin holds more keys than LDS
+//     takes, the narrowing reads every score instead. The output is written
+//     in token order: wave w owns a contiguous span of tokens, counts its keys
+//     > T and == T, and after a prefix over the 16 waves writes every key > T
+//     and the first (topk - count(> T)) keys == T.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t score_key(float v) {
   uint32_t u = __float_as_uint(v);
@@ -190,71 +222,111 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, u
   if (lane == 63) tmp[wave] = inc;
   __syncthreads();
   if (wave == 0) {
-    uint32_t w = lane < kTkThreads / 64 ? tmp[lane] : 0u;
+    uint32_t w = lane < kTkWaves ? tmp[lane] : 0u;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
+    for (int o = 1; o < kTkWaves; o <<= 1) {
       const uint32_t u = __shfl_up(w, o, 64);
       if (lane >= o) w += u;
     }
-    if (lane < kTkThreads / 64) tmp[16 + lane] = w;  // inclusive over waves
+    if (lane < kTkWaves) tmp[kTkWaves + lane] = w;  // inclusive over waves
   }
   __syncthreads();
-  const uint32_t off = wave ? tmp[16 + wave - 1] : 0u;
-  *total = tmp[16 + kTkThreads / 64 - 1];
+  const uint32_t off = wave ? tmp[kTkWaves + wave - 1] : 0u;
+  *total = tmp[2 * kTkWaves - 1];
   __syncthreads();  // tmp free for the next scan
   return off + inc - v;
 }
 
-__device__ __forceinline__ uint32_t block_min_max(uint32_t v, bool want_max, uint32_t* tmp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t u = __shfl_xor(v, o, 64);
-    v = want_max ? max(v, u) : min(v, u);
-  }
-  if (lane == 0) tmp[wave] = v;
-  __syncthreads();
-  uint32_t r = tmp[0];
-  for (int w = 1; w < kTkThreads / 64; ++w) r = want_max ? max(r, tmp[w]) : min(r, tmp[w]);
-  __syncthreads();
-  return r;
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__global__ __launch_bounds__(kTkThreads) void topk_kernel(int Q, int max_seq_len, int K,
-                                                         int lds_keys,
-                                                         const float* __restrict__ scores, int ld,
-                                                         const int32_t* __restrict__ seq_lens,
-                                                         int32_t* __restrict__ indices,
-                                                         int32_t* __restrict__ counts) {
-  extern __shared__ uint32_t skeys[];
+// grid (ceil(max_seq_len / kTkHistTok), batch * q_len); workspace row of the
+// query: kTkCoarse bin counts, then its NaN flag
+__global__ __launch_bounds__(256) void topk_hist_kernel(int Q, int max_seq_len,
+                                                       const float* __restrict__ scores, int ld,
+                                                       const int32_t* __restrict__ seq_lens,
+                                                       uint32_t* __restrict__ ws) {
+  __shared__ uint32_t h[kTkCoarse];
+  const int bj = blockIdx.y;
+  const int b = bj / Q, j = bj % Q;
+  const int L = seq_lens[b];
+  if (L < Q || L > max_seq_len) return;  // the select kernel reports it
+  const int n = L - Q + j + 1;
+  const int t0 = blockIdx.x * kTkHistTok;
+  if (t0 >= n) return;
+  for (int i = threadIdx.x; i < kTkCoarse; i += 256) h[i] = 0u;
+  __syncthreads();
+  const float* sc = scores + (size_t)bj * ld;
+  float v[kTkHistTok / 256];
+#pragma unroll
+  for (int u = 0; u < kTkHistTok / 256; ++u) {
+    const int t = t0 + u * 256 + threadIdx.x;
+    v[u] = t < n ? sc[t] : 0.0f;
+  }
+  bool nan = false;
+#pragma unroll
+  for (int u = 0; u < kTkHistTok / 256; ++u) {
+    const int t = t0 + u * 256 + threadIdx.x;
+    if (t < n) {
+      nan |= v[u] != v[u];
+      atomicAdd(&h[score_key(v[u]) >> (32 - kTkCoarseBits)], 1u);
+    }
+  }
+  uint32_t* row = ws + (size_t)bj * kTkWsRow;
+  if (__syncthreads_or(nan ? 1 : 0) && threadIdx.x == 0) row[kTkCoarse] = 1u;
+  for (int i = threadIdx.x; i < kTkCoarse; i += 256)
+    if (h[i]) atomicAdd(&row[i], h[i]);
+}
+
+// kReg: the query sees at most kTkRegTok tokens and every key stays in
+// registers after one read of the scores: wave w holds tokens
+// [kTkRegSpan w, kTkRegSpan (w + 1)), key v of lane l being token
+// kTkRegSpan w + 64 v + l (each load and each ballot covers 64 consecutive
+// tokens). Else every pass reads the scores again.
+template <bool kReg>
+__global__ __launch_bounds__(kTkThreads) void topk_select_kernel(
+    int Q, int max_seq_len, int K, const float* __restrict__ scores, int ld,
+    const int32_t* __restrict__ seq_lens, uint32_t* __restrict__ ws, int32_t* __restrict__ indices,
+    int32_t* __restrict__ counts) {
   __shared__ uint32_t hist[kTkBins];
-  __shared__ uint32_t tmp[48];
-  __shared__ uint32_t pick[2];
+  __shared__ uint32_t cand[kTkCand];
+  __shared__ uint32_t tmp[4 * kTkWaves];
+  __shared__ uint32_t pick[4];
   const int bj = blockIdx.x;
   const int b = bj / Q, j = bj % Q;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = seq_lens[b];
   int32_t* out = indices + (size_t)bj * K;
-  if (L < Q || L > max_seq_len) {
-    if (tid == 0) counts[bj] = -1;
-    return;
-  }
-  const int n = L - Q + j + 1;  // tokens the query sees
+  uint32_t* row = ws + (size_t)bj * kTkWsRow;
+  // the coarse counts, four bins per thread from the top (bins 4095 - 4 tid ..)
+  uint32_t c4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c4[i] = row[kTkCoarse - 1 - (4 * tid + i)];
+  const bool nan = row[kTkCoarse] != 0u;
+  const bool valid = !(L < Q || L > max_seq_len);
+  const int n = valid ? L - Q + j + 1 : 0;  // tokens the query sees
   const float* sc = scores + (size_t)bj * ld;
-  const bool inlds = n <= lds_keys;
-
-  // keys (kept in LDS when they fit), NaN check, key range
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  bool nan = false;
-  for (int t = tid; t < n; t += kTkThreads) {
-    const float v = sc[t];
-    nan |= v != v;
-    const uint32_t k = score_key(v);
-    if (inlds) skeys[t] = k;
-    kmin = min(kmin, k);
-    kmax = max(kmax, k);
+  // kReg: all keys of this wave's span, one read of the scores
+  uint32_t kr[kReg ? kTkRegKeys : 1];
+  const int rbase = wave * kTkRegSpan + lane;
+  if constexpr (kReg) {
+    float v[kTkRegKeys];
+#pragma unroll
+    for (int u = 0; u < kTkRegKeys; ++u) {
+      const int t = rbase + 64 * u;
+      v[u] = t < n ? sc[t] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kTkRegKeys; ++u)
+      kr[u] = rbase + 64 * u < n ? score_key(v[u]) : 0u;  // 0: below every real key
   }
-  if (__syncthreads_or(nan ? 1 : 0)) {
+  __syncthreads();  // every thread has read its counts and the flag
+#pragma unroll
+  for (int i = 0; i < 4; ++i) row[kTkCoarse - 1 - (4 * tid + i)] = 0u;
+  if (tid == 0) row[kTkCoarse] = 0u;
+  if (!valid || nan) {
     if (tid == 0) counts[bj] = -1;
     return;
   }
@@ -263,20 +335,97 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int Q, int max_seq_len
     if (tid == 0) counts[bj] = n;
     return;
   }
-  kmin = block_min_max(kmin, false, tmp);
-  kmax = block_min_max(kmax, true, tmp);
-  auto key_at = [&](int t) { return inlds ? skeys[t] : score_key(sc[t]); };
+  auto key_at = [&](int t) -> uint32_t { return t < n ? score_key(sc[t]) : 0u; };
+
+  // the coarse bin of the K-th largest key: running counts from the top
+  uint32_t need = (uint32_t)K;
+  {
+    const uint32_t s4 = c4[0] + c4[1] + c4[2] + c4[3];
+    uint32_t tot;
+    uint32_t ex = block_excl_scan(s4, tmp, &tot);
+    if (ex < need && ex + s4 >= need) {  // exactly one thread holds it
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (ex < need && ex + c4[i] >= need) {
+          pick[0] = (uint32_t)(kTkCoarse - 1 - (4 * tid + i));
+          pick[1] = ex;
+          pick[2] = c4[i];
+        }
+        ex += c4[i];
+      }
+      pick[3] = 0u;
+    }
+    __syncthreads();
+  }
+  need -= pick[1];
+  const int csh = 32 - kTkCoarseBits;
+  uint32_t lo = pick[0] << csh;
+  uint32_t hi = lo + ((1u << csh) - 1u);
+  int ncand = -1;  // >= 0: the keys in [lo, hi] are cand[0 .. ncand)
+  if (!kReg && pick[2] <= (uint32_t)kTkCand) {
+    // gather the bin's keys (in any order): one LDS atomic per wave and batch
+    auto gather = [&](const uint32_t* kk, const bool* ok) {
+      uint64_t m[kTkBatch];
+      uint32_t cnt = 0u;
+#pragma unroll
+      for (int u = 0; u < kTkBatch; ++u) {
+        m[u] = __ballot(ok[u] && kk[u] >= lo && kk[u] <= hi);
+        cnt += __builtin_popcountll(m[u]);
+      }
+      if (cnt) {
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&pick[3], cnt);
+        base = __shfl(base, 0, 64);
+#pragma unroll
+        for (int u = 0; u < kTkBatch; ++u) {
+          if ((m[u] >> lane) & 1ull) cand[base + lanes_below(m[u])] = kk[u];
+          base += __builtin_popcountll(m[u]);
+        }
+      }
+    };
+    {
+      for (int t0 = wave * 64; t0 < n; t0 += kTkBatch * kTkThreads) {
+        uint32_t kk[kTkBatch];
+        bool ok[kTkBatch];
+#pragma unroll
+        for (int u = 0; u < kTkBatch; ++u) {
+          const int t = t0 + u * kTkThreads + lane;
+          kk[u] = key_at(t);
+          ok[u] = t < n;
+        }
+        gather(kk, ok);
+      }
+    }
+    ncand = (int)pick[2];
+  }
+  __syncthreads();  // cand complete; pick read by all
 
   // narrow [lo, hi] to the single key T of the K-th largest score; `need` =
   // how many tokens with keys in [lo, hi] still belong to the selection
-  uint32_t lo = kmin, hi = kmax, need = (uint32_t)K;
   while (lo < hi) {
+    const uint32_t d = hi - lo;
+    const int sh = max(0, (32 - __builtin_clz(d)) - kTkBinBits);
     for (int i = tid; i < kTkBins; i += kTkThreads) hist[i] = 0u;
     __syncthreads();
-    const uint64_t w = (uint64_t)(hi - lo) + 1u;
-    for (int t = tid; t < n; t += kTkThreads) {
-      const uint32_t k = key_at(t);
-      if (k >= lo && k <= hi) atomicAdd(&hist[(uint32_t)(((uint64_t)(k - lo) * kTkBins) / w)], 1u);
+    if (ncand >= 0) {
+      for (int i = tid; i < ncand; i += kTkThreads) {
+        const uint32_t k = cand[i];
+        if (k >= lo && k <= hi) atomicAdd(&hist[(k - lo) >> sh], 1u);
+      }
+    } else if constexpr (kReg) {  // padding keys are 0, never in range
+#pragma unroll
+      for (int i = 0; i < kTkRegKeys; ++i)
+        if (kr[i] >= lo && kr[i] <= hi) atomicAdd(&hist[(kr[i] - lo) >> sh], 1u);
+    } else {
+      for (int t0 = tid; t0 < n; t0 += kTkBatch * kTkThreads) {
+        uint32_t kk[kTkBatch];
+#pragma unroll
+        for (int u = 0; u < kTkBatch; ++u) kk[u] = key_at(t0 + u * kTkThreads);
+#pragma unroll
+        for (int u = 0; u < kTkBatch; ++u)
+          if (t0 + u * kTkThreads < n && kk[u] >= lo && kk[u] <= hi)
+            atomicAdd(&hist[(kk[u] - lo) >> sh], 1u);
+      }
     }
     __syncthreads();
     const uint32_t h = hist[kTkBins - 1 - tid];  // thread i: the i-th bin from the top
@@ -287,38 +436,84 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int Q, int max_seq_len
       pick[1] = ex;
     }
     __syncthreads();
-    const uint64_t bin = pick[0];
     need -= pick[1];
-    const uint64_t a = (bin * w + kTkBins - 1) / kTkBins;        // first key offset of the bin
-    const uint64_t e = ((bin + 1) * w + kTkBins - 1) / kTkBins;  // one past its last
-    hi = lo + (uint32_t)(e - 1);
-    lo = lo + (uint32_t)a;
+    const uint32_t nlo = lo + (pick[0] << sh);
+    // the bin's last key, cut at hi (in 64 bits: the top bin may end past 2^32)
+    hi = (uint32_t)min((uint64_t)hi, (uint64_t)nlo + ((1ull << sh) - 1ull));
+    lo = nlo;
     __syncthreads();  // pick and hist are rewritten next round
   }
   const uint32_t T = lo;
 
-  // ordered compaction over per-thread slices of odd length
-  int seg = (n + kTkThreads - 1) / kTkThreads;
-  seg |= 1;
-  const int s0 = min(n, tid * seg), s1 = min(n, s0 + seg);
-  uint32_t gt = 0u, eq = 0u;
-  for (int t = s0; t < s1; ++t) {
-    const uint32_t k = key_at(t);
-    gt += k > T;
-    eq += k == T;
-  }
-  uint32_t gtot, etot;
-  const uint32_t gb = block_excl_scan(gt, tmp, &gtot);
-  const uint32_t eb = block_excl_scan(eq, tmp, &etot);
-  uint32_t pos = gb + min(eb, need);
-  uint32_t eseen = eb;
-  for (int t = s0; t < s1; ++t) {
-    const uint32_t k = key_at(t);
-    if (k > T) {
-      out[pos++] = t;
-    } else if (k == T) {
-      if (eseen < need) out[pos++] = t;
-      ++eseen;
+  if constexpr (kReg) {
+    // ordered output from the registers: this wave's span in 64-token steps
+    uint32_t gtw = 0u, eqw = 0u;
+#pragma unroll
+    for (int u = 0; u < kTkRegKeys; ++u) {
+      gtw += __builtin_popcountll(__ballot(kr[u] > T));
+      eqw += __builtin_popcountll(__ballot(kr[u] == T));
+    }
+    if (lane == 0) {
+      tmp[2 * kTkWaves + wave] = gtw;
+      tmp[3 * kTkWaves + wave] = eqw;
+    }
+    __syncthreads();
+    uint32_t gb = 0u, eb = 0u;  // keys > T and == T before this wave's span
+    for (int w = 0; w < wave; ++w) {
+      gb += tmp[2 * kTkWaves + w];
+      eb += tmp[3 * kTkWaves + w];
+    }
+#pragma unroll
+    for (int u = 0; u < kTkRegKeys; ++u) {
+      const bool gt = kr[u] > T, eq = kr[u] == T;
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      const uint32_t eq_before = eb + lanes_below(me);
+      if (gt || (eq && eq_before < need))
+        out[gb + lanes_below(mg) + min(eq_before, need)] = rbase + 64 * u;
+      gb += __builtin_popcountll(mg);
+      eb += __builtin_popcountll(me);
+    }
+  } else {
+    // ordered output: wave w owns tokens [w * span, (w + 1) * span), span a
+    // multiple of 64 * kTkOut
+    const int span = ((n + kTkWaves * 64 * kTkOut - 1) / (kTkWaves * 64 * kTkOut)) * 64 * kTkOut;
+    const int w0 = min(n, wave * span), w1 = min(n, w0 + span);
+    uint32_t gtw = 0u, eqw = 0u;
+    for (int t0 = w0; t0 < w1; t0 += 64 * kTkOut) {
+      uint32_t kk[kTkOut];
+#pragma unroll
+      for (int u = 0; u < kTkOut; ++u) kk[u] = key_at(t0 + 64 * u + lane);  // 0 past n
+#pragma unroll
+      for (int u = 0; u < kTkOut; ++u) {
+        gtw += __builtin_popcountll(__ballot(kk[u] > T));
+        eqw += __builtin_popcountll(__ballot(kk[u] == T));
+      }
+    }
+    if (lane == 0) {
+      tmp[2 * kTkWaves + wave] = gtw;
+      tmp[3 * kTkWaves + wave] = eqw;
+    }
+    __syncthreads();
+    uint32_t gb = 0u, eb = 0u;  // keys > T and == T in the waves before this one
+    for (int w = 0; w < wave; ++w) {
+      gb += tmp[2 * kTkWaves + w];
+      eb += tmp[3 * kTkWaves + w];
+    }
+    for (int t0 = w0; t0 < w1; t0 += 64 * kTkOut) {
+      uint32_t kk[kTkOut];
+#pragma unroll
+      for (int u = 0; u < kTkOut; ++u) kk[u] = key_at(t0 + 64 * u + lane);
+#pragma unroll
+      for (int u = 0; u < kTkOut; ++u) {
+        const int t = t0 + 64 * u + lane;
+        const bool gt = kk[u] > T, eq = kk[u] == T;
+        const uint64_t mg = __ballot(gt), me = __ballot(eq);
+        const uint32_t eq_before = eb + lanes_below(me);
+        if (gt || (eq && eq_before < need))
+          out[gb + lanes_below(mg) + min(eq_before, need)] = t;
+        gb += __builtin_popcountll(mg);
+        eb += __builtin_popcountll(me);
+      }
     }
   }
   if (tid == 0) counts[bj] = K;
@@ -389,20 +584,24 @@ int launch_index_scores(const Shape& s, int Hi, int dI, int batch, int q_len, in
   return (int)hipGetLastError();
 }
 
+size_t topk_workspace_bytes(int batch, int q_len) {
+  return sizeof(uint32_t) * (size_t)kTkWsRow * batch * q_len;
+}
+
 int launch_topk(int batch, int q_len, int max_seq_len, int topk, const float* scores, int ld,
-                const int32_t* seq_lens, int32_t* indices, int32_t* counts, void* stream) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(sizeof(uint32_t) * kTkLdsKeys));
-    if (e != hipSuccess) return (int)e;
-    attr = true;
-  }
-  const int lds_keys = max_seq_len <= kTkLdsKeys ? max_seq_len : 0;
-  hipLaunchKernelGGL(topk_kernel, dim3(batch * q_len), dim3(kTkThreads),
-                     sizeof(uint32_t) * (size_t)lds_keys, reinterpret_cast<hipStream_t>(stream),
-                     q_len, max_seq_len, topk, lds_keys, scores, ld, seq_lens, indices, counts);
+                const int32_t* seq_lens, void* workspace, int32_t* indices, int32_t* counts,
+                void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* ws = reinterpret_cast<uint32_t*>(workspace);
+  hipLaunchKernelGGL(topk_hist_kernel, dim3((max_seq_len + kTkHistTok - 1) / kTkHistTok,
+                                            batch * q_len),
+                     dim3(256), 0, st, q_len, max_seq_len, scores, ld, seq_lens, ws);
+  if (max_seq_len <= kTkRegTok)
+    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(batch * q_len), dim3(kTkThreads), 0, st,
+                       q_len, max_seq_len, topk, scores, ld, seq_lens, ws, indices, counts);
+  else
+    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(batch * q_len), dim3(kTkThreads), 0, st,
+                       q_len, max_seq_len, topk, scores, ld, seq_lens, ws, indices, counts);
   return (int)hipGetLastError();
 }
 

@@ -105,6 +105,9 @@ class DecodeStep:
             self.scores = t.empty((batch, q_len, self.max_seq_len), dtype=t.float32, device=device)
             self.indices = t.empty((batch, q_len, index_topk), dtype=t.int32, device=device)
             self.counts = t.empty((batch, q_len), dtype=t.int32, device=device)
+            # zero once: every selection leaves it zero
+            self.topk_ws = t.zeros(B.topk_workspace_bytes(batch, q_len), dtype=t.uint8,
+                                   device=device)
 
     def absorb(self, q_nope, q_rope, w_uk, stream=None):
         B.absorb_q(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, stream)
@@ -130,7 +133,8 @@ class DecodeStep:
                        self.max_seq_len, stream)
 
     def select(self, seq_lens, stream=None):
-        B.topk_select(self.scores, seq_lens, self.indices, self.counts, self.max_seq_len, stream)
+        B.topk_select(self.scores, seq_lens, self.indices, self.counts, self.max_seq_len,
+                      self.topk_ws, stream)
 
     def decode(self, cache, page_table, seq_lens, stream=None, max_seq_len: Optional[int] = None):
         if self.index_topk > 0:

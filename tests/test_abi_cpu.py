@@ -276,11 +276,15 @@ def test_sparse_entry_errors(L):
     assert sc(scores=None) == 1 and sc(scores=MIS) == 4
     assert sc(heads=256, dim=1024, cfg=TINY) == 6                   # generic needs > 160 KiB
     # top-k
-    assert L.mla_topk_select(2, 1, 256, 0, A16, 256, A16, A16, A16, None) == 2
-    assert L.mla_topk_select(2, 1, 256, 65537, A16, 256, A16, A16, A16, None) == 2
-    assert L.mla_topk_select(2, 1, 256, 64, A16, 200, A16, A16, A16, None) == 2
-    assert L.mla_topk_select(2, 1, 256, 64, A16, 256, A16, None, A16, None) == 1
-    assert L.mla_topk_select(0, 1, 256, 64, None, 256, None, None, None, None) == 0
+    assert L.mla_topk_select(2, 1, 256, 0, A16, 256, A16, A16, A16, A16, None) == 2
+    assert L.mla_topk_select(2, 1, 256, 65537, A16, 256, A16, A16, A16, A16, None) == 2
+    assert L.mla_topk_select(2, 1, 256, 64, A16, 200, A16, A16, A16, A16, None) == 2
+    assert L.mla_topk_select(2, 1, 256, 64, A16, 256, A16, A16, None, A16, None) == 1
+    assert L.mla_topk_select(2, 1, 256, 64, A16, 256, A16, None, A16, A16, None) == 1
+    assert L.mla_topk_select(2, 1, 256, 64, A16, 256, A16, MIS, A16, A16, None) == 4
+    assert L.mla_topk_select(0, 1, 256, 64, None, 256, None, None, None, None, None) == 0
+    assert L.mla_topk_workspace_bytes(8, 1) == 8 * 4100 * 4
+    assert L.mla_topk_workspace_bytes(0, 1) == 0 and L.mla_topk_workspace_bytes(2, 0) == 0
     # sparse decode
     def dec(topk=2048, S=16, counts=A16, batch=2):
         return L.mla_decode_sparse(c, batch, 1, topk, S, 256, A16, A16, 8, A16, 4, A16, A16,

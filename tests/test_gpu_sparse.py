@@ -52,8 +52,11 @@ def _topk_gpu(scores, lens, Q, K, max_len):
     sl = upload(np.asarray(lens, np.int32), torch.int32)
     idx = torch.full((B, Q, K), -7, dtype=torch.int32, device="cuda")
     cnt = torch.full((B, Q), -9, dtype=torch.int32, device="cuda")
-    mla.topk_select(sc, sl, idx, cnt, max_len)
+    ws = torch.zeros(mla.topk_workspace_bytes(B, Q), dtype=torch.uint8, device="cuda")
+    mla.topk_select(sc, sl, idx, cnt, max_len, ws)
+    mla.topk_select(sc, sl, idx, cnt, max_len, ws)   # a second call on the same workspace
     torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0, "the workspace must be left all zero"
     return idx.cpu().numpy(), cnt.cpu().numpy()
 
 
@@ -75,19 +78,43 @@ def test_topk_matches_oracle_bit_exact(length, K, Q):
 
 def test_topk_special_values_and_invalid_sequences():
     L, K = 600, 50
-    rows = workload.score_rows(12, 4, L, ties=False)
+    rows = workload.score_rows(12, 5, L, ties=False)
     rows[0] = 1.0                              # all equal: the first K tokens
     rows[1, ::2] = -np.inf                     # half -inf
     rows[2, :] = np.where(np.arange(L) % 3 == 0, -0.0, 0.0)  # signed zeros only
     rows[3, 17] = np.nan                       # NaN: sequence reported invalid
-    idx, cnt = _topk_gpu(rows, [L, L, L, L], 1, K, L)
-    for b in range(3):
+    fmax = np.finfo(np.float32).max            # keys over nearly the whole 32-bit range
+    rows[4, ::7] = np.inf
+    rows[4, 1::7] = -np.inf
+    rows[4, 2::7] = fmax
+    rows[4, 3::7] = -fmax
+    rows[4, 4::7] = np.float32(1e-40)          # denormals
+    idx, cnt = _topk_gpu(rows, [L] * 5, 1, K, L)
+    for b in (0, 1, 2, 4):
         want = oracle.topk_tokens(rows[b], K, L)
         assert cnt[b, 0] == K and idx[b, 0, :K].tolist() == want.tolist()
+    want = oracle.topk_tokens(rows[4], 150, L)           # the cut inside the +-FLT_MAX copies
+    idx4, cnt4 = _topk_gpu(rows[4:5], [L], 1, 150, L)
+    assert cnt4[0, 0] == 150 and idx4[0, 0].tolist() == want.tolist()
     assert cnt[3, 0] == -1 and np.all(idx[3] == -7)
     # lengths outside [Q, max_seq_len]
     idx, cnt = _topk_gpu(rows[:2], [L + 1, 0], 1, K, L)
     assert cnt.tolist() == [[-1], [-1]]
+
+
+def test_topk_crowded_bin_reads_every_score():
+    # 20,000 scores in one coarse bin (same sign, exponent and top mantissa
+    # bits): more than the gathered-key array holds, so the narrowing reads
+    # every score; one row of equal values, one spread inside [1, 1.125)
+    L, K = 20000, 777
+    rng = np.random.default_rng(3)
+    rows = np.empty((2, L), np.float32)
+    rows[0] = 1.0
+    rows[1] = (1.0 + rng.integers(0, 1 << 17, L) * 2.0 ** -20).astype(np.float32)
+    idx, cnt = _topk_gpu(rows, [L, L], 1, K, L)
+    for b in range(2):
+        want = oracle.topk_tokens(rows[b], K, L)
+        assert cnt[b, 0] == K and idx[b, 0].tolist() == want.tolist()
 
 
 # ---------------------------------------------------------------- index scores
