@@ -36,5 +36,6 @@ from .mla_ref import (  # noqa: F401
     topk_tokens,
     dsa_selection,
     mla_decode_ref_sparse,
+    prefill_in_chunks,
 )
 from .brute import brute_sequence, brute_index_scores  # noqa: F401

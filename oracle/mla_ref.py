@@ -36,6 +36,10 @@ What it computes, and where the pages define it:
   Contexts", technique 3 "KV Cache Quantization", and its comparison table:
   an INT8 cache halves the bytes). Reading: per cached token, separately for
   the latent part and the (rotated) RoPE part, in float32.
+* Chunked prefill: the prompt enters the cache in chunks, each chunk's
+  queries attending causally to everything cached so far ("Beyond the
+  Attention Bottleneck", "Chunked Prefilling"); in the absorbed form a chunk
+  of C tokens is the Q = C chain of the decode above.
 * A sparse read: a small scorer rates every cached token and attention reads
   only the top-scored ones ("DeepSeek's Config Says 16 KV Heads, Its Cache
   Holds a Ninth of That", section 6, "Sparse attention"). Reading: the score
@@ -567,6 +571,32 @@ def mla_decode_ref_q8(inputs, heads: Optional[Sequence[int]] = None,
             c_hat, k_hat, inputs.q_nope[b][:, hs], inputs.q_rope[b][:, hs], w_uk, w_uv,
             wl.softmax_scale, wl.rope_base, parents=par)
     return {"o": o, "o_lat": o_lat, "lse": lse, "rows": rows}
+
+
+# --------------------------------------------------------------------------
+# chunked prefill: the prompt enters the cache chunk by chunk
+# --------------------------------------------------------------------------
+def prefill_in_chunks(c, k_rope_raw, q_nope, q_rope, w_uk, w_uv, scale, chunk: int,
+                      base: float = 10000.0, cached: int = 0):
+    """Prefill of a prompt in chunks of ``chunk`` tokens ("Beyond the Attention
+    Bottleneck", "Chunked Prefilling": the prompt is split into chunks that
+    are processed one after another, each adding its tokens to the cache).
+
+    c [N][d_c], k_rope_raw [N][d_r]: every token of the sequence, the first
+    ``cached`` already in the cache; q_nope [N - cached][H][d_n], q_rope
+    [N - cached][H][d_r]: the queries of the prompt tokens that are still to
+    be prefilled. Chunk by chunk, tokens [s, e) join the cache and their
+    queries attend to the cache as it then stands (tokens 0 .. e-1), query i
+    at position s + i seeing t <= s + i. Returns (o, o_lat, lse) for the
+    prompt's queries in order.
+    """
+    N = len(c)
+    outs = []
+    for s in range(cached, N, chunk):
+        e = min(N, s + chunk)
+        outs.append(attend_sequence(c[:e], k_rope_raw[:e], q_nope[s - cached:e - cached],
+                                    q_rope[s - cached:e - cached], w_uk, w_uv, scale, base))
+    return tuple(np.concatenate([o[i] for o in outs]) for i in range(3))
 
 
 # --------------------------------------------------------------------------
