@@ -38,7 +38,9 @@ METRIC = "MLA decode latent-cache GB/s (% of HBM peak) + decode tokens/s, V2-Lit
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LAYERS = {"v2lite_32k": 27, "v2lite_paged_varlen": 27, "v2_h128_8k": 4, "v2_h128_1m_q4": 2,
-          "v2lite_32k_tree8": 27, "v2lite_32k_q8": 27, "v2lite_32k_dsa": 27, "tiny_f32": 4}
+          "v2lite_32k_tree8": 27, "v2lite_32k_q8": 27, "v2lite_32k_dsa": 27,
+          "v2lite_prefill_32k_c4k": 2, "tiny_f32": 4}
+PREFILL_MIN_Q = 64             # q_len from which a step is a prefill chunk
 CSRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc")
 # decode kernel name (mla_decode_kernel_name) -> (kernel symbol, the sources that define it)
 DECODE_KERNELS = {
@@ -92,6 +94,46 @@ def traffic_from_profile(wl_name, kernel_src_hash):
     if d.get("decode_src_sha256_16") != kernel_src_hash:
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def visible_pairs(wl, inp):
+    """(query, cached token) pairs the attention scores: query j of sequence b
+    sees tokens 0 .. L_b - Q + j (a drafted tree sees no more than that)."""
+    Q = wl.q_len
+    return sum(Q * (int(L) - Q) + Q * (Q + 1) // 2 for L in inp.seq_lens)
+
+
+def cpu_baseline_prefill(wl, inp, flops_step, bytes_step, n_queries=8):
+    """Prefill chunk: the oracle on sampled queries of the chunk (each one a
+    one-token decode over the tokens it sees, head 0 only), scaled by the
+    share of the step's algorithmic work they represent."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    L, Q = int(inp.seq_lens[0]), wl.q_len
+    P = L - Q
+    js = [int(x) for x in np.linspace(0, Q - 1, n_queries)]
+    c, kr = inp.seq(0)
+    t = time.perf_counter()
+    for j in js:
+        oracle.attend_sequence(c[:P + j + 1], kr[:P + j + 1], inp.q_nope[0][j:j + 1][:, :1],
+                               inp.q_rope[0][j:j + 1][:, :1], inp.w_uk[:1], inp.w_uv[:1],
+                               wl.softmax_scale, wl.rope_base)
+    dt = time.perf_counter() - t
+    flops = sum(P + j + 1 for j in js) * (2 * wl.dim + 2 * wl.kv_rank)
+    share = flops / flops_step
+    return {"value": round(bytes_step * share / dt / 1e9, 6), "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(js)} of {Q} queries of sequence 0 (each a one-token decode over the "
+                      f"tokens it sees), head 0 of {wl.heads}, {dt:.1f} s; fp64 unabsorbed NumPy "
+                      f"oracle; scaled by the sample's share {share:.2e} of the step's "
+                      f"algorithmic flops",
+            "seconds": round(dt, 2),
+            "prefill_tokens_per_s": round(wl.batch * Q * share / dt, 6)}
 
 
 def cpu_baseline(wl, inp, budget_flops=2.4e12):
@@ -361,7 +403,8 @@ def main():
         kernel = "index_scores_mfma"
     else:
         kernel_bytes = step_bytes = total_tokens * wl.cache_row_bytes  # read once per step
-        flops = total_tokens * Q * H * (2 * wl.dim + 2 * wl.kv_rank)
+        # every (query row, visible token) pair: 2 * D for the score, 2 * d_c for P.V
+        flops = visible_pairs(wl, inp) * H * (2 * wl.dim + 2 * wl.kv_rank)
         kernel = "mfma_q8" if q8 else mla.decode_kernel_kind(cfg, Q)
     cache_bytes = kernel_bytes
     gbs_step = step_bytes / (ms_step * 1e-3) / 1e9
@@ -427,7 +470,10 @@ def main():
         out["sparse"] = dict(sparse_calls, selected_rows_per_step=sel_rows,
                              step_bytes=step_bytes,
                              dense_equivalent_cache_bytes=total_tokens * wl.cache_row_bytes)
-    if wl.name.startswith("v2lite"):
+    if Q >= PREFILL_MIN_Q:
+        out["prefill_tokens_per_s"] = round(B * Q / (ms_step * 1e-3), 1)
+        out["prefill_step_tflops"] = round(flops / (ms_step * 1e-3) / 1e12, 2)
+    elif wl.name.startswith("v2lite"):
         out["v2lite_attention_tokens_per_s_27_layers"] = round(B / (27 * ms_step * 1e-3), 1)
     props = torch.cuda.get_device_properties(0)
     out["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
@@ -441,7 +487,8 @@ def main():
         torch.cuda.synchronize()
         out["calibration_copy_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp)
+        out["cpu_baseline"] = (cpu_baseline_prefill(wl, inp, flops, cache_bytes)
+                               if Q >= PREFILL_MIN_Q else cpu_baseline(wl, inp))
     print(json.dumps(out), flush=True)
 
 

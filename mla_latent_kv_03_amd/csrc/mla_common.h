@@ -83,6 +83,16 @@ __host__ __device__ __forceinline__ uint64_t tree_branch_mask(const int32_t* __r
   return m;
 }
 
+// Tiles of `tile` tokens a block streams from its partition [t0, t1): up to
+// the last token any of its rows sees. With a chain of drafted tokens (or a
+// chunk of prefill queries) query j sees up to t_draft + j, so a block whose
+// last query is jmax stops there; a tree's rows may see any drafted token.
+__host__ __device__ __forceinline__ int tiles_needed(int t0, int t1, int tile, bool tree,
+                                                     int t_draft, int jmax) {
+  const int end = tree ? t1 : min(t1, t_draft + jmax + 1);
+  return end > t0 ? (end - t0 + tile - 1) / tile : 0;
+}
+
 // Tokens ts .. ts + 63 that one query row sees, as bits (bit o = token ts + o):
 // every token up to lim, and with a drafted tree the drafts on the row's branch
 // (bit i of `branch` = token t_draft + i) that lie below t1. Shifts and selects

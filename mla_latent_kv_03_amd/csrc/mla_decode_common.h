@@ -136,9 +136,9 @@ struct PageWindow {
     base = 0;
     reg = lane < npages ? row[lane] : 0;
   }
-  // physical page of unit page u (wave-uniform u)
+  // physical page of unit page u (wave-uniform u; u may also move back)
   __device__ __forceinline__ int get(int u, int lane) {
-    if (u - base >= 64) {
+    if ((unsigned)(u - base) >= 64u) {
       base = u & ~63;
       reg = base + lane < upages ? row[base + lane] : 0;
       asm volatile("" ::"v"(reg));  // complete this load here, inside the rare branch
@@ -189,10 +189,23 @@ __device__ __forceinline__ int seq_by_rank(const int32_t* __restrict__ seq_lens,
   return b;
 }
 
-// block id -> (unit, row group): all groups of one unit share id % 8, i.e.
-// run on the same XCD and share its L2
+// block id -> (unit, row group). With 8 units or more, all groups of one unit
+// share id % 8, i.e. run on the same XCD and share its L2. With fewer (one
+// long prefill chunk is one unit with many row groups) that would leave XCDs
+// idle, so the work items (unit, group) are split into 8 contiguous ranges,
+// one per XCD: block 8 r + x takes item x * per + r.
+__host__ __device__ __forceinline__ int grid_blocks(int units, int groups) {
+  return units >= 8 ? ((units + 7) / 8) * 8 * groups : 8 * ((units * groups + 7) / 8);
+}
 __device__ __forceinline__ bool map_block(int units, int groups, int* unit, int* grp) {
   const int id = blockIdx.x;
+  if (units < 8) {
+    const int per = (units * groups + 7) / 8;
+    const int f = (id & 7) * per + (id >> 3);
+    *unit = f % units;
+    *grp = f / units;
+    return f < units * groups;
+  }
   const int kk = id >> 3;
   *unit = (kk / groups) * 8 + (id & 7);
   *grp = kk % groups;

@@ -115,7 +115,10 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
       split_range(L, S, page, fixed, s, &t0, &t1);
     }
   }
-  const int ntiles = (t1 - t0 + kT - 1) / kT;
+  // (gather: every listed token is visible, the list slice is the range)
+  const int ntiles =
+      kGather ? (t1 - t0 + kT - 1) / kT
+              : tiles_needed(t0, t1, kT, par != nullptr, L - Q, (row0 + kRows - 1) / H);
   bool bad = bad_len;
 
   f32x4_t* sc = reinterpret_cast<f32x4_t*>(reinterpret_cast<char*>(lds) + kRingBytes);
@@ -415,7 +418,7 @@ int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, i
   }
   const int units = batch * num_splits;
   const int groups = q_len * s.H / kRows;
-  const int blocks = ((units + 7) / 8) * 8 * groups;
+  const int blocks = grid_blocks(units, groups);
   hipLaunchKernelGGL(decode_rows16_kernel<false>, dim3(blocks), dim3(256), kLdsBytes,
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page,
                      s.split_fixed, max_seq_len, s.scale * 1.4426950408889634f, units, groups,
@@ -440,7 +443,7 @@ int launch_decode_sparse_rows16(const Shape& s, int batch, int q_len, int topk, 
   }
   const int units = batch * num_splits;
   const int groups = q_len * s.H / kRows;
-  const int blocks = ((units + 7) / 8) * 8 * groups;
+  const int blocks = grid_blocks(units, groups);
   hipLaunchKernelGGL(decode_rows16_kernel<true>, dim3(blocks), dim3(256), kGatherLdsBytes,
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page, chunk,
                      max_seq_len, s.scale * 1.4426950408889634f, units, groups,

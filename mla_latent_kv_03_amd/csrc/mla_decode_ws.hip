@@ -96,7 +96,9 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   const bool bad_len = (L < Q) || (L > max_seq_len) || bad_tree;
   int t0 = 0, t1 = 0;
   if (!bad_len) split_range(L, S, page, fixed, s, &t0, &t1);
-  const int ntiles = (t1 - t0 + kWT - 1) / kWT;
+  const int ntiles =
+      tiles_needed(t0, t1, kWT, par != nullptr, L - Q, (grp * kWRows + kWRows - 1) / H);
+  auto tstart = [&](int k) { return t0 + k * kWT; };
   // after the last tile the score buffer of step ntiles & 1 carries the QK
   // waves' out-of-range flags
   int* flags = reinterpret_cast<int*>(sbuf + (ntiles & 1) * kWScoreVecs);
@@ -112,7 +114,7 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
     dma.init(w4 * kWPartChunks, lane, w4 * kWPartRows);
     // rows [8 w, 8 w + 8) of tile k (never across a page: 8 | page)
     auto issue = [&](int k) {
-      const int t = t0 + k * kWT + w4 * kWPartRows;
+      const int t = tstart(k) + w4 * kWPartRows;
       int pg = pw.get((t - t0) / page, lane);
       if (pg < 0 || (int64_t)pg >= num_pages) {
         bad = true;
@@ -153,7 +155,7 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
       const bf16_t* isrc = cache;
       uint32_t ilds = 0;
       if (kiss >= 0) {
-        const int t = t0 + kiss * kWT + w4 * kWPartRows;
+        const int t = tstart(kiss) + w4 * kWPartRows;
         int pg = pw.get((t - t0) / page, lane);
         if (pg < 0 || (int64_t)pg >= num_pages) {
           bad = true;
@@ -190,8 +192,9 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
         wait_vmcnt<kWPartLoads>();
       else
         wait_vmcnt<0>();
-      if (t0 + kWT > t1)
-        zero_rows<kWPartLoads>(slot(0) + w4 * kWPartChunks, w4 * kWPartChunks, lane, t1 - t0);
+      if (tstart(0) + kWT > t1)
+        zero_rows<kWPartLoads>(slot(0) + w4 * kWPartChunks, w4 * kWPartChunks, lane,
+                               t1 - tstart(0));
     }
     __syncthreads();  // tile 0 landed
     if (ntiles > 0) qk(0, -1);
@@ -201,7 +204,7 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
           wait_vmcnt<kWPartLoads>();
         else
           wait_vmcnt<0>();
-        const int ts1 = t0 + (k + 1) * kWT;
+        const int ts1 = tstart(k + 1);
         if (ts1 + kWT > t1)
           zero_rows<kWPartLoads>(slot(k + 1) + w4 * kWPartChunks, w4 * kWPartChunks, lane,
                                  t1 - ts1);
@@ -270,7 +273,7 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
     for (int m = 0; m < 4; ++m) bcur[m] = bop(tbase, 0, m);
 
     // ---- online softmax of both row groups (lane: row n, tokens sigma(kg, j))
-    const int ts = t0 + k * kWT;
+    const int ts = tstart(k);
     const f32x4_t* sk = sbuf + (k & 1) * kWScoreVecs + rh * 256 + lane;
     bf16x8_t pa[2];
 #pragma unroll
@@ -397,7 +400,7 @@ int launch_decode_ws(const Shape& s, int batch, int q_len, int num_splits, int m
   }
   const int units = batch * num_splits;
   const int groups = q_len * s.H / kWRows;
-  const int blocks = ((units + 7) / 8) * 8 * groups;
+  const int blocks = grid_blocks(units, groups);
   hipLaunchKernelGGL(decode_ws_kernel, dim3(blocks), dim3(512), kWLds,
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page,
                      s.split_fixed, max_seq_len, s.scale * 1.4426950408889634f, units, groups,

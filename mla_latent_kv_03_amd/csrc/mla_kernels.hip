@@ -215,7 +215,10 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   const int lim = kGather ? t1 - 1 : (par ? t_draft - 1 : t_draft + my_j);
   const uint64_t branch = (par && !bad && my_j < Q) ? tree_branch_mask(par, Q, my_j) : 0ull;
 
-  for (int t = t0; t < t1 && !bad; t += kGenTok) {
+  // a chain stops after the last token the block's last query sees
+  const int t_end = kGather ? t1 : t0 + kGenTok * tiles_needed(t0, t1, kGenTok, par != nullptr,
+                                                                  L - Q, (r0 + nr - 1) / H);
+  for (int t = t0; t < t_end && !bad; t += kGenTok) {
     const int nt = min(kGenTok, t1 - t);
     if constexpr (kGather) {
       __syncthreads();  // previous step done with cs / ps / al / rs

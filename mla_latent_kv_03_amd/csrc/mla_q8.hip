@@ -226,7 +226,7 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   const bool bad_len = (L < Q) || (L > max_seq_len) || bad_tree;
   int t0 = 0, t1 = 0;
   if (!bad_len) split_range(L, S, page, fixed, s, &t0, &t1);
-  const int ntiles = (t1 - t0 + kQT - 1) / kQT;
+  const int ntiles = tiles_needed(t0, t1, kQT, par != nullptr, L - Q, (row0 + 15) / H);
   bool bad = bad_len;
 
   char* const lbase = reinterpret_cast<char*>(lds);
@@ -530,7 +530,7 @@ int launch_decode_q8(const Shape& s, int batch, int q_len, int num_splits, int m
   }
   const int units = batch * num_splits;
   const int groups = q_len * s.H / 16;
-  const int blocks = ((units + 7) / 8) * 8 * groups;
+  const int blocks = grid_blocks(units, groups);
   hipLaunchKernelGGL(decode_q8_kernel, dim3(blocks), dim3(256), kQLds,
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page,
                      s.split_fixed, max_seq_len, s.scale * 1.4426950408889634f, units, groups,

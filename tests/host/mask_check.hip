@@ -5,6 +5,7 @@
 //   V ts lim t_draft t1 branch   -> tile_visible(...) as an unsigned decimal
 //   T Q p0 p1 ... p(Q-1)         -> Q masks tree_branch_mask(p, Q, j), then
 //                                   1/0 for every entry's tree_entry_ok
+//   N t0 t1 tile tree t_draft jmax -> tiles_needed(...)
 #include <cstdio>
 #include <cinttypes>
 #include <vector>
@@ -29,6 +30,10 @@ int main() {
         std::printf("%llu ", (unsigned long long)mla::tree_branch_mask(p.data(), Q, j));
       for (int i = 0; i < Q; ++i) std::printf("%d ", mla::tree_entry_ok(p.data(), i) ? 1 : 0);
       std::printf("\n");
+    } else if (op[0] == 'N') {
+      int t0, t1, tile, tree, t_draft, jmax;
+      if (std::scanf("%d %d %d %d %d %d", &t0, &t1, &tile, &tree, &t_draft, &jmax) != 6) return 2;
+      std::printf("%d\n", mla::tiles_needed(t0, t1, tile, tree != 0, t_draft, jmax));
     } else {
       return 2;
     }

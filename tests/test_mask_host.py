@@ -111,3 +111,24 @@ def test_malformed_entries_are_flagged_and_the_walk_ends(driver):
         assert ok == [1 if -1 <= e < i else 0 for i, e in enumerate(p)], p
         for m in vals[:Q]:
             assert 0 <= m < (1 << Q)  # bounded walk, bits only inside the draft
+
+
+def test_tiles_needed_stops_at_the_blocks_last_visible_token(driver):
+    rng = random.Random(21)
+    cases = []
+    for _ in range(3000):
+        Q = rng.randint(1, 5000)
+        L = rng.randint(Q, 40000)
+        t0 = rng.randrange(0, L)
+        t1 = rng.randint(t0, L)
+        tile = rng.choice([16, 32, 64])
+        tree = int(rng.random() < 0.2)
+        jmax = rng.randrange(Q)
+        cases.append((t0, t1, tile, tree, L - Q, jmax))
+    out = driver([f"N {a} {b} {c} {d} {e} {f}" for a, b, c, d, e, f in cases])
+    for (t0, t1, tile, tree, t_draft, jmax), g in zip(cases, out):
+        # tokens the block's rows can see in [t0, t1): up to t_draft + jmax
+        # for a chain, everything for a tree
+        last = t1 - 1 if tree else min(t1 - 1, t_draft + jmax)
+        want = 0 if last < t0 else -(-(last - t0 + 1) // tile)
+        assert int(g) == want, (t0, t1, tile, tree, t_draft, jmax)

@@ -131,6 +131,14 @@ WORKLOADS: Dict[str, Workload] = {
                  index_topk=2048,
                  description="V2-Lite shape, B=8, L=32768, sparse read of the top 2,048 tokens "
                              "chosen by a 64-head x 128 indexer"),
+        # chunked prefill: the last 4,096-token chunk of a 32,768-token prompt
+        # (its queries attend causally to the 28,672 cached tokens and to the
+        # chunk itself)
+        Workload("v2lite_prefill_32k_c4k", batch=1, q_len=4096, heads=16, kv_rank=512,
+                 rope_dim=64, nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768,
+                 num_splits=1,
+                 description="V2-Lite shape, prefill of the last 4,096-token chunk of a "
+                             "32,768-token prompt"),
         Workload("v2lite_32k_tree8", batch=8, q_len=8, heads=16, kv_rank=512, rope_dim=64,
                  nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=16,
                  tree=(-1, 0, 0, 1, 1, 2, 2, 3),
