@@ -10,23 +10,21 @@
 // float32 (IEEE division, ties to even), 0 for a constant part; a code stands
 // for min + code * step.
 //
-// The decode kernel is the 16-row split-KV kernel of the bf16 cache (one
-// staged tile shared by all 16 query rows, one block barrier per tile, QK of
-// tile k+1 beside P.C of tile k) on 64-token tiles: a tile is one contiguous
-// 37,888-byte copy (37 direct-to-LDS loads), rows 592 bytes apart, a stride
-// at which both operand read patterns below are free of LDS bank conflicts.
-// A wave64 vector instruction occupies the SIMD for 4 cycles, so the codes
-// are not decoded element by element: the MFMAs take them as the fp16 values
-// 1024 + code (one v_perm per two), and the code -> value map is applied per
-// score and per output row (see decode_q8_kernel):
-//   QK  wave w scores the 16 tokens [16 w, 16 w + 16) of the tile over all
-//       576 columns (18 v_mfma_f32_16x16x32_f16; A = 8 codes of one token
-//       per lane, B = the query row in fp16 registers) and leaves S^T in LDS
-//   max every wave reads the four subtiles' scores, takes the row max over
-//       the 64 tokens and forms P (the lazy rescale of the bf16 kernel)
-//   PV  wave w accumulates latent columns [128 w, 128 w + 128) of all 16
-//       rows, two K = 32 blocks per tile; the B operand takes 4 codes of each
-//       of its 8 tokens (ds_read_b32), interleaved and lifted by v_perm.
+// The decode kernel keeps 16 query rows per block and splits the partition
+// into 16-token subtiles that the block's four waves stream independently:
+// each wave has its own 4-slot LDS ring (a subtile is one contiguous
+// 9,472-byte copy, rows 592 bytes apart, a stride at which both operand read
+// patterns are free of LDS bank conflicts), its own loads and waits and its
+// own online-softmax state, so the token loop has no block barrier; the four
+// states are merged once at the end. A wave64 vector instruction occupies the
+// SIMD for 4 cycles, so the codes are not decoded element by element: the
+// MFMAs take them as the fp16 subnormals code * 2^-24 (one v_perm per two),
+// and the code -> value map is applied per score and per output row (see
+// decode_q8_kernel):
+//   QK  16 tokens x 16 rows over all 576 columns (18 v_mfma_f32_16x16x32_f16)
+//   PV  all 512 latent columns of the 16 rows over the 16 tokens
+//       (32 v_mfma_f32_16x16x16_f16); the A operand is P over the 4 tokens
+//       whose scores the lane holds after QK, so P never leaves registers.
 #include "mla_append.h"
 #include "mla_decode_common.h"
 #include "mla_launch.h"
@@ -153,53 +151,77 @@ int launch_cache_append_q8(const Shape& s, int n_tok, const void* c_kv, const vo
 }
 
 // ---------------------------------------------------------------------------
-// Decode over the 8-bit cache, 16 query rows per block.
+// Decode over the 8-bit cache, 16 query rows per block, four waves that
+// stream independently.
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int kQRow = kD + kQ8Meta;                 // 592 bytes per cached row
-constexpr int kQT = 64;                             // tokens per tile
-constexpr int kQTileBytes = kQT * kQRow;            // 37,888
-constexpr int kQRing = 4;
-constexpr int kQQLoads = 8 * kChunks / 64;          // 9 loads: 8 query rows of 1,152 B
-constexpr size_t kQRingBytes = (size_t)kQRing * kQTileBytes;  // 151,552
-constexpr size_t kQScoreBytes = (size_t)2 * kWaves * 64 * 16; // 8,192
-constexpr size_t kQLds = kQRingBytes + kQScoreBytes;         // 159,744
+constexpr int kQRow = kD + kQ8Meta;                  // 592 bytes per cached row
+constexpr int kQT = 16;                              // tokens per wave subtile
+constexpr int kQSubBytes = kQT * kQRow;              // 9,472
+constexpr int kQRing = 3;                            // ring slots per wave
+constexpr int kQWaveBytes = kQRing * kQSubBytes;     // 28,416
+constexpr int kQQBytes = kKSteps * 64 * 16;          // 18,432: the query B operands in fp16
+constexpr size_t kQLds = (size_t)kWaves * kQWaveBytes + kQQBytes;  // 132,096
+constexpr int kQWide = kQSubBytes / 1024;            // 9 loads of 16 B per lane ...
+constexpr int kQSubLoads = kQWide + 1;               // ... and one of 4 B per lane
+constexpr int kQQueryLoads = 16 * kD * 2 / 1024;     // 18: the 16 query rows in bf16
+constexpr int kQAcc = 16 * kDC * 4;                  // 32,768: one wave's accumulators
 
-static_assert(kQTileBytes % 1024 == 0, "a tile is whole 1 KB loads");
-static_assert(kQLds + 256 <= 160 * 1024, "LDS of one CU");
-static_assert(8 * kChunks * 16 <= kQTileBytes, "the query rows fit a ring slot");
-
-// tile loads of wave w: [first, first + count), 10 + 9 + 9 + 9
-__device__ __forceinline__ int q8_first_load(int w) { return w == 0 ? 0 : 1 + 9 * w; }
-__device__ __forceinline__ int q8_load_count(int w) { return w == 0 ? 10 : 9; }
+static_assert(kQSubBytes - kQWide * 1024 == 256, "a subtile is 9 wide loads and one narrow");
+static_assert(kQRow % 16 == 0, "a 16-byte chunk never straddles two rows");
+static_assert((kQQueryLoads + kWaves - 1) / kWaves * 1024 <= kQSubBytes,
+              "a wave's share of the query rows fits one ring slot");
+static_assert((size_t)kWaves * kQAcc <= kQLds, "the four waves' accumulators fit the LDS");
+static_assert(kQLds + 4096 <= 160 * 1024, "LDS of one CU, with the static arrays");
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
-constexpr uint32_t kF16Hi = 0x64646464u;  // high byte of the fp16 value 1024 + v, v < 256
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
 
-// 4 codes (one dword) -> the fp16 values 1024 + code, two per dword: one
-// v_perm each places a code under the 0x64 exponent byte (bytes 0..3 of the
-// selector's space are c, bytes 4..7 the constant)
-__device__ __forceinline__ u32x2_t codes_f16(uint32_t c) {
-  return u32x2_t{__builtin_amdgcn_perm(kF16Hi, c, 0x04010400u),
-                 __builtin_amdgcn_perm(kF16Hi, c, 0x04030402u)};
+// A code byte under a zero high byte is the fp16 subnormal code * 2^-24,
+// exact, and the MFMA takes subnormal fp16 inputs as they are. One v_perm
+// lifts two codes of a dword (selector byte 0x0c yields a zero byte).
+__device__ __forceinline__ f16x8_t codes8_sub(u32x2_t c) {
+  return __builtin_bit_cast(f16x8_t, u32x4_t{__builtin_amdgcn_perm(0u, c.x, 0x0c010c00u),
+                                              __builtin_amdgcn_perm(0u, c.x, 0x0c030c02u),
+                                              __builtin_amdgcn_perm(0u, c.y, 0x0c010c00u),
+                                              __builtin_amdgcn_perm(0u, c.y, 0x0c030c02u)});
 }
-__device__ __forceinline__ f16x8_t codes8_f16(u32x2_t c) {
-  const u32x2_t lo = codes_f16(c.x), hi = codes_f16(c.y);
-  return __builtin_bit_cast(f16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+
+// The MFMA's k index 8 kg + i of step ks stands for code column
+// q8_col(ks, kg) + i: in the latent part a lane's four steps 4 G .. 4 G + 3
+// cover 32 contiguous codes (two 16-byte LDS reads), in the RoPE part its two
+// steps cover 16. The query rows take the same columns, so the dot products
+// are unchanged.
+__device__ __forceinline__ int q8_col(int ks, int kg) {
+  return ks < kDC / 32 ? 128 * (ks >> 2) + 32 * kg + 8 * (ks & 3)
+                       : kDC + 16 * kg + 8 * (ks - kDC / 32);
 }
+constexpr int kQAReads = kKSteps / 2;                // 9 reads of 16 B per subtile
 
 }  // namespace
 
-// The contractions run on fp16 MFMA over the values 1024 + code (exact in
-// fp16, and one v_perm per two of them), and the affine code -> value map is
-// applied per score and per output row instead of per element:
-//   score: q . (min + step c) = step (q . (1024 + c)) + (min - 1024 step) sum q
-//          per part (latent, RoPE), each with its own accumulator
+// Block: 16 query rows (row0 .. row0 + 15) of one (sequence, partition)
+// unit, 4 waves. The partition is cut into 16-token subtiles; wave w takes
+// subtiles w, w + 4, w + 8, ... and streams them through a 3-slot ring of its
+// own (one subtile = 9,472 contiguous bytes of one page, 10 direct-to-LDS
+// loads), so the token loop has no block barrier: each wave waits only for
+// its own loads and keeps its own online-softmax state for all 16 rows. The
+// four states are merged at the end through LDS. The query rows' fp16 MFMA
+// operands (18 KB) sit in LDS beside the rings: in registers they would
+// leave too few for the 128 accumulators and a subtile's operands.
+//
+// The contractions run on fp16 MFMA with the codes as the subnormals
+// code * 2^-24, and the affine code -> value map (min + step * code, per row
+// and part) is applied per score and per output row:
+//   score: q . (min + step c) = step 2^24 (q . c 2^-24) + min sum q, per part
+//          (latent, RoPE), QK^T = 18 v_mfma_f32_16x16x32_f16 per subtile
+//          (A = 8 codes of token n per lane, B = the query rows in fp16)
 //   P.C:   sum_t p_t (min_t + step_t c_t)
-//            = sum_t P_t (1024 + c_t) + sum_t p_t min_t - 1024 sum_t P_t,
-//          P_t = fp16(p_t step_t), the A operand; sum_t P_t of exactly those
-//          fp16 values comes from one more MFMA against an all-ones operand
+//            = 2^24 sum_t P_t (c_t 2^-24) + sum_t p_t min_t, P_t = fp16(p_t step_t)
+//          32 v_mfma_f32_16x16x16_f16 per subtile: A = P of row n over the 4
+//          tokens whose scores the lane already holds, B = one column of those
+//          4 tokens' codes (two v_perm), columns 64 g + 4 n + r
 // The query rows are converted to fp16 once per block (exact for bf16 values
 // within fp16 range).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -211,6 +233,9 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
                       const int32_t* __restrict__ tree_parent, float* __restrict__ o_part,
                       float* __restrict__ lse_part) {
   extern __shared__ u32x4_t lds[];
+  __shared__ float st_m[kWaves][16], st_l[kWaves][16], st_o[kWaves][16];
+  __shared__ int pwin[kWaves][64];     // each wave's copy of the page window
+  __shared__ float sqp[kWaves][16][2];  // each wave's part of the query row sums
   int unit, grp;
   if (!map_block(units, groups, &unit, &grp)) return;
   const int R = Q * H;
@@ -226,185 +251,206 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   const bool bad_len = (L < Q) || (L > max_seq_len) || bad_tree;
   int t0 = 0, t1 = 0;
   if (!bad_len) split_range(L, S, page, fixed, s, &t0, &t1);
-  const int ntiles = tiles_needed(t0, t1, kQT, par != nullptr, L - Q, (row0 + 15) / H);
+  // block-uniform: subtiles any row of the block sees; this wave's share
+  const int nsub = tiles_needed(t0, t1, kQT, par != nullptr, L - Q, (row0 + 15) / H);
+  const int nk = nsub > wave ? (nsub - wave + kWaves - 1) / kWaves : 0;
   bool bad = bad_len;
 
   char* const lbase = reinterpret_cast<char*>(lds);
-  f32x4_t* sc = reinterpret_cast<f32x4_t*>(lbase + kQRingBytes);
-  auto slot = [&](int k) { return lbase + (k & (kQRing - 1)) * kQTileBytes; };
+  char* const wbase = lbase + wave * kQWaveBytes;
+  char* const qop = lbase + kWaves * kQWaveBytes;  // the query B operands
 
+  // The page-table window (lane i: unit page i of the partition) is copied
+  // into LDS ahead of the query rows, so that waiting for it leaves the
+  // query copy in flight.
   PageWindow pw;
-  pw.init(page_table + (size_t)b * max_pages + t0 / page, (t1 - t0 + page - 1) / page, lane);
-  settle(pw.reg);
-  const int l0 = q8_first_load(wave), lc = q8_load_count(wave);
-  // this wave's loads of tile k: tile bytes [1024 i, 1024 i + 1024), i in
-  // [l0, l0 + lc); a tile never crosses a page (64 | page)
-  auto issue = [&](int k) {
-    const int t = t0 + k * kQT;
-    int pg = pw.get((t - t0) / page, lane);
-    if (pg < 0 || (int64_t)pg >= num_pages) {
+  pw.row = page_table + (size_t)b * max_pages + t0 / page;
+  pw.upages = (t1 - t0 + page - 1) / page;
+  pw.base = 0;
+  pw.reg = 0;
+  // Subtiles are issued in order, k = 0, 1, 2, ...: subtile k of this wave is
+  // tokens [t0 + 16 (4 k + wave), + 16), inside one page (t0 is a multiple of
+  // the page size, which is a multiple of 64). The next one to issue is row
+  // i_off of unit page i_up, into slot i_slot; each step moves 64 tokens on,
+  // which crosses at most one page boundary.
+  int i_up = 0, i_off = kQT * wave, i_slot = 0;
+  const int pg_lim = (int)min(num_pages, (int64_t)0x7fffffff);
+  const size_t page_bytes = (size_t)page * kQRow;
+  auto issue_next = [&]() {
+    int pg = pw.get(i_up, lane);
+    if (pg < 0 || pg >= pg_lim) {
       bad = true;
       pg = 0;
     }
-    const uint8_t* src = cache + ((size_t)pg * page + (t % page)) * (size_t)kQRow;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(slot(k)));
-    for (int i = l0; i < l0 + lc; ++i)  // wave-uniform bounds
+    const uint8_t* src = cache + (size_t)pg * page_bytes + (size_t)i_off * kQRow;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(wbase + i_slot * kQSubBytes));
+#pragma unroll
+    for (int i = 0; i < kQWide; ++i)
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                    :
                    : "s"(dst + i * 1024), "v"((uint32_t)(i * 1024 + 16 * lane)), "s"(src)
                    : "memory");
-  };
-  // wait until at most `in_flight` later tiles of this wave are in flight
-  auto wait_tiles = [&](int in_flight) {
-    if (wave == 0) {
-      if (in_flight >= 2) wait_vmcnt<20>();
-      else if (in_flight == 1) wait_vmcnt<10>();
-      else wait_vmcnt<0>();
-    } else {
-      if (in_flight >= 2) wait_vmcnt<18>();
-      else if (in_flight == 1) wait_vmcnt<9>();
-      else wait_vmcnt<0>();
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 nt"
+                 :
+                 : "s"(dst + kQWide * 1024), "v"((uint32_t)(kQWide * 1024 + 4 * lane)), "s"(src)
+                 : "memory");
+    i_off += kWaves * kQT;
+    if (i_off >= page) {
+      i_off -= page;
+      ++i_up;
     }
+    i_slot = i_slot == kQRing - 1 ? 0 : i_slot + 1;
   };
-  // rows past the partition end (another token's bytes, or poison): zero the
-  // 16-byte chunks this wave loaded whose row is >= first_bad (a chunk never
-  // straddles two rows: 16 | 592); a zero row has min = step = 0
-  auto zero_tail = [&](int k, int first_bad) {
-    char* base = slot(k);
-    for (int i = l0; i < l0 + lc; ++i) {
-      const int o = i * 1024 + 16 * lane;
-      if (o / kQRow >= first_bad) *reinterpret_cast<u32x4_t*>(base + o) = u32x4_t{0u, 0u, 0u, 0u};
-    }
+  // wait until at most `in_flight` later subtiles of this wave are in flight
+  auto wait_subs = [&](int in_flight) {
+    static_assert(kQRing == 3, "waits for up to two later subtiles");
+    if (in_flight >= 2) wait_vmcnt<2 * kQSubLoads>();
+    else if (in_flight == 1) wait_vmcnt<kQSubLoads>();
+    else wait_vmcnt<0>();
   };
 
   float m_run = -INFINITY, l_run = 0.0f;
-  float off = 0.0f;  // this lane's part of sum_t p_t min_t - 1024 sum_t P_t (row n)
-  f32x4_t acc[2][4], psum;
+  float off = 0.0f;  // this lane's part of sum_t p_t min_t (row n)
+  float sq_lat = 0.0f, sq_rope = 0.0f;             // row sums of the query parts
+  const float c24 = scale_log2 * 16777216.0f;
+  f32x4_t acc[kFB][4];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int g = 0; g < kFB; ++g)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc[f][m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  psum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = 0; r < 4; ++r) acc[g][r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const int t_draft = L - Q;
   const int lim = min(par ? t_draft - 1 : t_draft + (row0 + n) / H, t1 - 1);
   const uint64_t branch = (par && !bad_len) ? tree_branch_mask(par, Q, (row0 + n) / H) : 0ull;
 
-  if (ntiles > 0) {
-    // ---- prologue: queries (waves 0, 1: 8 rows each, into slot 3), tiles 0..2
-    const int npre = min(ntiles, kQRing - 1);
-    RowDma<kQQLoads> qdma;
-    qdma.init(wave * 8 * kChunks, lane, wave * 8);
-    if (wave < 2)
-      qdma.issue(q_full + ((size_t)b * R + row0 + wave * 8) * kD,
-                 __builtin_amdgcn_readfirstlane(lds_addr(slot(kQRing - 1) + wave * 8 * kChunks * 16)));
-    issue(0);
-    if (npre > 1) issue(1);
-    if (npre > 2) issue(2);
-    if (wave < 2) wait_vmcnt<0>();  // own query rows (and the tiles behind them)
-    __syncthreads();
-    // queries in fp16: row n, chunk 4 ks + kg (stored with the bf16 tile's
-    // swizzle), and the row's sums over the latent and RoPE columns
-    f16x8_t qh[kKSteps];
-    float sq_lat = 0.0f, sq_rope = 0.0f;
+  if (nsub > 0) {
+    // ---- prologue: the page window; query load i (1 KB of the 16 bf16 rows)
+    // to the last slot of wave i % 4 at 1 KB * (i / 4); subtiles 0 .. kQRing - 2
     {
-      const u32x4_t* qb = reinterpret_cast<const u32x4_t*>(slot(kQRing - 1));
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        const int c = 4 * ks + kg;
-        const bf16x8_t qv = __builtin_bit_cast(bf16x8_t, qb[n * kChunks + (c ^ (n & 7))]);
+      const int* src = pw.row + min(lane, pw.upages - 1);  // pw.upages >= 1 here
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(&pwin[wave][0]));
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                   :
+                   : "s"(dst), "v"(src)
+                   : "memory");
+      const bf16_t* qsrc = q_full + ((size_t)b * R + row0) * kD;
+      const uint32_t qdst =
+          __builtin_amdgcn_readfirstlane(lds_addr(wbase + (kQRing - 1) * kQSubBytes));
+      for (int i = wave; i < kQQueryLoads; i += kWaves)  // wave-uniform bounds
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                     :
+                     : "s"(qdst + (i / kWaves) * 1024), "v"((uint32_t)(i * 1024 + 16 * lane)),
+                       "s"(qsrc)
+                     : "memory");
+      // the window has landed when at most this wave's query loads are pending
+      static_assert(kQQueryLoads == 4 * kWaves + 2, "waves 0, 1 issue 5 query loads, 2, 3 four");
+      if (wave < 2)
+        wait_vmcnt<kQQueryLoads / kWaves + 1>();
+      else
+        wait_vmcnt<kQQueryLoads / kWaves>();
+      pw.reg = pwin[wave][lane];
+    }
+    const int npre = min(nk, kQRing - 1);
+    for (int k = 0; k < npre; ++k) issue_next();
+    wait_subs(npre);  // own query loads (issued before the subtiles)
+    __syncthreads();
+    // the B operand of step ks for lane (row n, kg), columns q8_col(ks, kg) .. + 7,
+    // in fp16 at qop + 1 KB * ks + 16 * lane: wave w converts the steps
+    // ks = w mod 4 and its part of the row sums, which meet in LDS
+    {
+      float sl = 0.0f, sr = 0.0f;
+      for (int ks = wave; ks < kKSteps; ks += kWaves) {  // wave-uniform bounds
+        const int gb = n * kD * 2 + 2 * q8_col(ks, kg);
+        const int li = gb >> 10;
+        const char* p = lbase + (li % kWaves) * kQWaveBytes + (kQRing - 1) * kQSubBytes +
+                        (li / kWaves) * 1024 + (gb & 1023);
+        const bf16x8_t qv = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+        f16x8_t h;
         float part = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const _Float16 h = (_Float16)(float)qv[j];
-          qh[ks][j] = h;
-          part += (float)h;
+          h[j] = (_Float16)(float)qv[j];
+          part += (float)h[j];
         }
+        *reinterpret_cast<f16x8_t*>(qop + ks * 1024 + 16 * lane) = h;
         if (ks < kDC / 32)
-          sq_lat += part;
+          sl += part;
         else
-          sq_rope += part;
+          sr += part;
       }
-      sq_lat = row_sum4(sq_lat) * scale_log2;    // the softmax scale folded in
-      sq_rope = row_sum4(sq_rope) * scale_log2;
+      sl = row_sum4(sl);
+      sr = row_sum4(sr);
+      if (kg == 0) {
+        sqp[wave][n][0] = sl;
+        sqp[wave][n][1] = sr;
+      }
     }
-    // own part of tile 0
-    wait_tiles(npre - 1);
-    if (t0 + kQT > t1) zero_tail(0, t1 - t0);
-    __syncthreads();
+    __syncthreads();  // the operands are written and the staging slots are free
+    sq_lat = (sqp[0][n][0] + sqp[1][n][0] + sqp[2][n][0] + sqp[3][n][0]) * scale_log2;
+    sq_rope = (sqp[0][n][1] + sqp[1][n][1] + sqp[2][n][1] + sqp[3][n][1]) * scale_log2;
+    if (nk > kQRing - 1) issue_next();
 
-    // QK: A operand of lane (token 16 wave + n, kg) at byte (16 wave + n) * 592 + 32 ks + 8 kg
-    const int arow = (16 * wave + n) * kQRow;
-    // PV: tokens sigma(kg, j) of a K-block; codes of columns 128 wave + 64 f + 4 n .. + 3
-    int pvt[8];
+    // QK: A operand of lane (token n, kg) at bytes n * 592 + q8_col(ks, kg);
+    // PV: B operand of lane (column 64 g + 4 n + r, kg) from tokens 4 kg + j
+    const int arow = n * kQRow;
+    const int brow = 4 * kg * kQRow + 4 * n;
+    const char* const qb = qop + 16 * lane;
+    int c_slot = 0;  // slot of subtile k
+    for (int k = 0; k < nk; ++k) {
+      wait_subs(min(nk - 1 - k, kQRing - 1));
+      const int ts = t0 + kQT * (kWaves * k + wave);
+      char* tile = wbase + c_slot * kQSubBytes;
+      c_slot = c_slot == kQRing - 1 ? 0 : c_slot + 1;
+      if (ts + kQT > t1) {  // rows past the partition end (another token, or poison) -> 0
+        for (int c = (t1 - ts) * (kQRow / 16) + lane; c < kQSubBytes / 16; c += 64)
+          reinterpret_cast<u32x4_t*>(tile)[c] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      // the QK operands and the row metadata first
+      u32x4_t cv[kQAReads];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pvt[j] = ((j < 4) ? 4 * kg + j : 16 + 4 * kg + (j - 4)) * kQRow;
-    const f16x8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
+      for (int i = 0; i < kQAReads; ++i)
+        cv[i] = *reinterpret_cast<const u32x4_t*>(tile + arow + q8_col(2 * i, kg));
+      float4 mt[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        mt[r] = *reinterpret_cast<const float4*>(tile + (4 * kg + r) * kQRow + kD);
 
-    // scores (log2 units) of subtile `wave` of tile k into score buffer k & 1
-    auto qk = [&](int k) {
-      const char* tile = slot(k);
-      const char* buf = tile + arow;
       f32x4_t cl[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
       f32x4_t cr = {0.0f, 0.0f, 0.0f, 0.0f};
-      u32x2_t cv[kKSteps];
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks)
-        cv[ks] = *reinterpret_cast<const u32x2_t*>(buf + 32 * ks + 8 * kg);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        const f16x8_t a = codes8_f16(cv[ks]);
+        const u32x4_t& w = cv[ks >> 1];
+        const f16x8_t a = codes8_sub((ks & 1) ? u32x2_t{w.z, w.w} : u32x2_t{w.x, w.y});
+        const f16x8_t qk = *reinterpret_cast<const f16x8_t*>(qb + ks * 1024);
         if (ks < kDC / 32)
-          cl[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[ks], cl[ks & 1], 0, 0, 0);
+          cl[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qk, cl[ks & 1], 0, 0, 0);
         else
-          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[ks], cr, 0, 0, 0);
+          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qk, cr, 0, 0, 0);
       }
+      // the PV operands: their reads overlap the score and softmax arithmetic
+      uint32_t u[kFB][4];
+#pragma unroll
+      for (int g = 0; g < kFB; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          u[g][j] = *reinterpret_cast<const uint32_t*>(tile + brow + j * kQRow + 64 * g);
+
+      // ---- scores of row n, tokens 4 kg + r (log2 units)
       const f32x4_t al = cl[0] + cl[1];
-      // lane (row n, kg) holds tokens 16 wave + 4 kg + r
-      f32x4_t out;
+      float sv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float4 mt = *reinterpret_cast<const float4*>(tile + (16 * wave + 4 * kg + r) * kQRow + kD);
-        const float kl = fmaf(-1024.0f, mt.y, mt.x), kr2 = fmaf(-1024.0f, mt.w, mt.z);
-        out[r] = fmaf(mt.y * scale_log2, al[r],
-                      fmaf(mt.w * scale_log2, cr[r], fmaf(kl, sq_lat, kr2 * sq_rope)));
+        sv[r] = fmaf(mt[r].y * c24, al[r],
+                     fmaf(mt[r].w * c24, cr[r], fmaf(mt[r].x, sq_lat, mt[r].z * sq_rope)));
       }
-      sc[((k & 1) * kWaves + wave) * 64 + lane] = out;
-    };
-    qk(0);
+      if (!__all(ts + kQT - 1 <= lim)) {  // some token of the subtile is masked for some row
+        const uint32_t vl =
+            (uint32_t)(tile_visible(ts, lim, t_draft, t1, branch) >> (4 * kg)) & 0xfu;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[r] = ((vl >> r) & 1u) ? sv[r] : -INFINITY;
+      }
 
-    for (int k = 0; k < ntiles; ++k) {
-      if (k + 1 < ntiles) {  // own part of tile k+1 (tile k+2 may stay in flight)
-        wait_tiles(k + 2 < ntiles ? 1 : 0);
-        const int ts1 = t0 + (k + 1) * kQT;
-        if (ts1 + kQT > t1) zero_tail(k + 1, t1 - ts1);
-      }
-      // tile k+1 landed for every wave, the scores of tile k are complete, and
-      // slot k-1 (= slot k+3) is no longer read by anyone
-      __syncthreads();
-      if (k + 3 < ntiles) issue(k + 3);
-      if (k + 1 < ntiles) qk(k + 1);
-
-      // ---- softmax over the tile's 64 tokens (lane: row n, tokens 16 u + 4 kg + r)
-      const int ts = t0 + k * kQT;
-      const f32x4_t* sk = sc + (k & 1) * kWaves * 64 + lane;
-      float sv[16];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f32x4_t su = sk[64 * u];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[4 * u + r] = su[r];
-      }
-      if (!__all(ts + kQT - 1 <= lim)) {  // some token of the tile is masked for some row
-        const uint64_t vis = tile_visible(ts, lim, t_draft, t1, branch);
-        const uint64_t vl = vis >> (4 * kg);
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          sv[j] = ((vl >> (16 * (j >> 2) + (j & 3))) & 1ull) ? sv[j] : -INFINITY;
-      }
-      float mloc = sv[0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mloc = fmaxf(mloc, sv[j]);
-      mloc = row_max4(mloc);
+      // ---- online softmax of this wave's rows (lazy rescale)
+      const float mloc = row_max4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
       const bool raise = mloc > m_run + kLazy;
       if (__any(raise)) {
         const float m_new = raise ? mloc : m_run;
@@ -416,104 +462,137 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
 #pragma unroll
           for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * kg + r, 64);
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
+          for (int g = 0; g < kFB; ++g)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) acc[f][m][r] *= ar[r];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) psum[r] *= ar[r];
+              for (int r = 0; r < 4; ++r) acc[g][c][r] *= ar[r];
         }
         m_run = m_new;
       }
       const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-      const char* tb = slot(k);
-      // P for K-block blk: slots 0..3 = subtile 2 blk, 4..7 = subtile 2 blk + 1
-      f16x8_t pa[2];
-      float ps = 0.0f;
+      f16x4_t pa;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(sv[8 * blk + j] - m_use);
-          const float2 mt = *reinterpret_cast<const float2*>(tb + blk * 32 * kQRow + pvt[j] + kD);
-          ps += p;
-          off = fmaf(p, mt.x, off);
-          pa[blk][j] = (_Float16)(p * mt.y);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sv[r] - m_use);
+        l_run += p;
+        off = fmaf(p, mt[r].x, off);
+        pa[r] = (_Float16)(p * mt[r].y);
       }
-      l_run += ps;
 
-      // ---- PV: this wave's 128 latent columns, two blocks of 64, two K-blocks
+      // the slot is read: subtile k + kQRing may land in it
+      if (k + kQRing < nk) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue_next();
+      }
+
+      // ---- PV: all 512 latent columns of the 16 rows, K = this subtile's 16 tokens
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const char* kb = tb + blk * 32 * kQRow;
-        uint32_t cw[2][8];
+      for (int g = 0; g < kFB; ++g) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            cw[f][j] = *reinterpret_cast<const uint32_t*>(kb + pvt[j] + 128 * wave + 64 * f + 4 * n);
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          // token pairs (2 i, 2 i + 1): interleave their bytes, then lift each
-          // column's byte pair to two fp16 values 1024 + code
-          u32x4_t bm[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t i0 = __builtin_amdgcn_perm(cw[f][2 * i + 1], cw[f][2 * i], 0x05010400u);
-            const uint32_t i1 = __builtin_amdgcn_perm(cw[f][2 * i + 1], cw[f][2 * i], 0x07030602u);
-            const u32x2_t c01 = codes_f16(i0), c23 = codes_f16(i1);
-            bm[0][i] = c01.x;
-            bm[1][i] = c01.y;
-            bm[2][i] = c23.x;
-            bm[3][i] = c23.y;
-          }
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                pa[blk], __builtin_bit_cast(f16x8_t, bm[m]), acc[f][m], 0, 0, 0);
+        for (int r = 0; r < 4; ++r) {
+          // column 64 g + 4 n + r of tokens 4 kg .. 4 kg + 3, as subnormals
+          const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + r) << 16) | (uint32_t)r;
+          const u32x2_t bw = {__builtin_amdgcn_perm(u[g][1], u[g][0], sel),
+                              __builtin_amdgcn_perm(u[g][3], u[g][2], sel)};
+          acc[g][r] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              pa, __builtin_bit_cast(f16x4_t, bw), acc[g][r], 0, 0, 0);
         }
-        psum = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[blk], ones, psum, 0, 0, 0);
       }
     }
   }
   wait_vmcnt<0>();
 
-  // ---- write rows row0 .. row0+15, columns [128 wave, 128 wave + 128) ------
-  const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
-  const float nanv = __int_as_float(0x7fc00000);
+  // ---- merge the four waves' states; wave w writes columns [128 w, 128 w + 128)
   const float l_row = row_sum4(l_run);
-  const float off_row = row_sum4(off);   // sum_t p_t min_t of row n
-  float inv[4], base[4];
+  const float off_row = row_sum4(off);
+  if (kg == 0) {
+    st_m[wave][n] = m_run;
+    st_l[wave][n] = l_row;
+    st_o[wave][n] = off_row;
+  }
+  const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
+  // every loop has ended: the rings and the query operands are free. Each
+  // wave's raw accumulators go to kQAcc * wave, lane-major (entry (g, c) of
+  // lane l at 16 (64 (4 g + c) + l)); the reader applies the streams' factors.
+  {
+    f32x4_t* dst = reinterpret_cast<f32x4_t*>(lbase + wave * kQAcc) + lane;
+#pragma unroll
+    for (int g = 0; g < kFB; ++g)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[64 * (4 * g + c)] = acc[g][c];
+  }
+  __syncthreads();
+  const float nanv = __int_as_float(0x7fc00000);
+  // per output row 4 kg + r: each wave's factor 2^(m_w - m_all), 1 / l and
+  // sum_t p_t min_t, all relative to m_all
+  float fw[kWaves][4], inv[4], base[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float lr = __shfl(l_row, 4 * kg + r, 64);
+    const int rr = 4 * kg + r;
+    float mr = st_m[0][rr];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mr = fmaxf(mr, st_m[w][rr]);
+    float lr = 0.0f, orr = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = st_m[w][rr];
+      const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mr);
+      fw[w][r] = f;
+      lr = fmaf(st_l[w][rr], f, lr);
+      orr = fmaf(st_o[w][rr], f, orr);
+    }
     inv[r] = lr > 0.0f ? 1.0f / lr : 0.0f;
-    // row 4 kg + r: psum holds sum_t P_t of that row in every column
-    base[r] = fmaf(-1024.0f, psum[r], __shfl(off_row, 4 * kg + r, 64));
+    base[r] = orr;
   }
-  // an empty partition (no tokens) leaves its o_part rows unwritten
+  // an empty partition (no tokens) leaves its o_part rows unwritten; wave w
+  // writes columns [128 w, 128 w + 128)
+  if (t1 > t0 || any_bad) {
 #pragma unroll
-  for (int r = 0; r < 4 && (t1 > t0 || any_bad); ++r) {
-    const int orow = row0 + 4 * kg + r;
-    float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + 128 * wave + 4 * n;
+    for (int gg = 0; gg < 2; ++gg) {
+      const int g = 2 * wave + gg;
+      f32x4_t sum[4];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      float4 v = make_float4((acc[f][0][r] + base[r]) * inv[r], (acc[f][1][r] + base[r]) * inv[r],
-                             (acc[f][2][r] + base[r]) * inv[r], (acc[f][3][r] + base[r]) * inv[r]);
-      if (any_bad) v = make_float4(nanv, nanv, nanv, nanv);
-      *reinterpret_cast<float4*>(dst + f * 64) = v;
+      for (int c = 0; c < 4; ++c) {
+        sum[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const f32x4_t v =
+              reinterpret_cast<const f32x4_t*>(lbase + w * kQAcc)[64 * (4 * g + c) + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sum[c][r] = fmaf(fw[w][r], v[r], sum[c][r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int orow = row0 + 4 * kg + r;
+        float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + 64 * g + 4 * n;
+        float4 v = make_float4(fmaf(16777216.0f, sum[0][r], base[r]) * inv[r],
+                               fmaf(16777216.0f, sum[1][r], base[r]) * inv[r],
+                               fmaf(16777216.0f, sum[2][r], base[r]) * inv[r],
+                               fmaf(16777216.0f, sum[3][r], base[r]) * inv[r]);
+        if (any_bad) v = make_float4(nanv, nanv, nanv, nanv);
+        *reinterpret_cast<float4*>(dst) = v;
+      }
     }
   }
   if (wave == 0 && kg == 0) {
-    const float lse = l_row > 0.0f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
+    float m_all = st_m[0][n];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m_all = fmaxf(m_all, st_m[w][n]);
+    float l_all = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = st_m[w][n];
+      l_all = fmaf(st_l[w][n], mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - m_all), l_all);
+    }
+    const float lse = l_all > 0.0f ? (m_all + log2f(l_all)) * 0.69314718055994531f : -INFINITY;
     lse_part[((size_t)b * R + row0 + n) * S + s] = any_bad ? nanv : lse;
   }
 }
 
 bool decode_q8_ok(const Shape& s, int q_len) {
-  return s.dtype == 1 && s.dc == kDC && s.dr == kD - kDC && s.page % kQT == 0 &&
+  return s.dtype == 1 && s.dc == kDC && s.dr == kD - kDC && s.page % 64 == 0 &&
          (q_len * s.H) % 16 == 0;
 }
 
