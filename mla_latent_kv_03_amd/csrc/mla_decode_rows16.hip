@@ -129,8 +129,29 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   dma.init(wave * kPartChunks, lane, wave * kPartRows);
   PageWindow pw;
   if constexpr (!kGather) {
-    pw.init(page_table + (size_t)b * max_pages + t0 / page, (t1 - t0 + page - 1) / page, lane);
-    settle(pw.reg);
+    // the page window (lane i: unit page i of the partition) is copied into
+    // the score buffer, unused until the first scores, ahead of the query
+    // rows, so that waiting for it leaves the query copy in flight
+    pw.row = page_table + (size_t)b * max_pages + t0 / page;
+    pw.upages = (t1 - t0 + page - 1) / page;
+    pw.base = 0;
+    pw.reg = 0;
+    if (ntiles > 0) {  // then pw.upages >= 1
+      const int* win = reinterpret_cast<const int*>(sc) + 64 * wave;
+      const int* src = pw.row + min(lane, pw.upages - 1);
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(lds_addr(win))), "v"(src)
+                   : "memory");
+      if (wave < 2) {
+        dma.issue(q_full + ((size_t)b * R + row0 + wave * kPartRows) * kD,
+                  __builtin_amdgcn_readfirstlane(lds_addr(slot(kRing - 1) + wave * kPartChunks)));
+        wait_vmcnt<kPartLoads>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      pw.reg = win[lane];
+    }
   } else {
     // the queries go out first (their latency overlaps the lookups below)
     if (wave < 2 && ntiles > 0)
@@ -205,11 +226,9 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   const uint64_t branch = (par && !bad_len) ? tree_branch_mask(par, Q, (row0 + n) / H) : 0ull;
 
   if (ntiles > 0) {
-    // ---- prologue: queries (waves 0, 1: 8 rows each, into slot 3), tiles 0..2
-    const int pre = min(ntiles, kRing - 1);
-    if (!kGather && wave < 2)  // (gather: already on its way)
-      dma.issue(q_full + ((size_t)b * R + row0 + wave * kPartRows) * kD,
-                __builtin_amdgcn_readfirstlane(lds_addr(slot(kRing - 1) + wave * kPartChunks)));
+    // ---- prologue: queries (waves 0, 1: 8 rows each, into slot 3, issued
+    // above), tiles 0..2
+    const int pre = min(ntiles, kRing - 1);  // (the queries are already on their way)
     issue(0);
     if (pre > 1) issue(1);
     if (pre > 2) issue(2);
