@@ -23,8 +23,17 @@ namespace {
 
 constexpr int kIH = 64;   // indexer heads of the MFMA kernel
 constexpr int kID = 128;  // indexer key width of the MFMA kernel
-constexpr int kIdxChunks = 2;               // 64-token chunks per wave
-constexpr int kIdxTok = 4 * 64 * kIdxChunks;  // tokens per index-score block
+constexpr int kIRow = kID * 2;                         // 256 bytes per bf16 key
+constexpr int kIChunk = 32;                            // tokens per chunk: two groups of 16
+constexpr int kIChunkBytes = kIChunk * kIRow;          // 8 KB
+constexpr int kIRing = 4;                              // chunk slots per wave
+constexpr int kIWaveChunks = 8;                        // chunks per wave
+constexpr int kIdxTok = 4 * kIWaveChunks * kIChunk;    // 1,024 tokens per block
+constexpr int kIChunkLoads = kIChunk * kIRow / 1024;   // 8 direct-to-LDS loads per chunk
+constexpr size_t kIRingBytes = (size_t)4 * kIRing * kIChunkBytes;  // 131,072 B
+constexpr int kIQBytes = kIH * kID * 2;                // 16 KB: the query's 64 x 128 bf16
+constexpr size_t kILds = kIRingBytes + kIQBytes + kIH * 4;  // + the 64 head weights
+static_assert(kILds <= 160 * 1024, "LDS of one CU");
 
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / 64;
@@ -68,82 +77,170 @@ __device__ __forceinline__ float relu_nan(float x) { return x < 0.0f ? 0.0f : x;
 
 // ---------------------------------------------------------------------------
 // index scores, bf16 MFMA: 64 heads x 128 dims. Block = kIdxTok tokens of one
-// (sequence, query); wave w takes kIdxChunks chunks of 64 tokens, chunk c
-// covering [kIdxTok * block + 64 (kIdxChunks w + c), + 64), in groups of 16.
-// Every load goes out before the first MFMA: queries and weights, then the
-// page entries of all chunks, then all their keys, so one wave keeps
-// kIdxChunks x 16 KB in flight. Per group: D[head][token] = q_idx[head][:] .
-// k[token][:] on v_mfma_f32_16x16x32_bf16 (M = 16 heads, N = 16 tokens, 4 head
-// blocks x 4 k-steps), then lane (token n, head quarter kg) folds its 16 heads
-// with w * max(0, D) and the four quarters are summed with lane swaps.
+// (sequence, query), four waves without block barriers; chunk c of wave w is
+// the 32 tokens [kIdxTok * block + 32 (4 c + w), + 32), two groups of 16.
+// Chunks stream through a 4-slot LDS ring per wave: a group's 16 keys are
+// 4 KB of one page, copied with four 1 KB direct-to-LDS loads (page entries
+// are scalar loads), chunk c + 4 going out as soon as chunk c's operands are
+// in registers. Chunk k of key row r sits at 16 (k ^ (r & 15)) inside the
+// row, the XOR applied on the global side, so the operand reads hit 16
+// different bank groups. Per group: D[head][token] = q_idx[head][:] .
+// k[token][:] on v_mfma_f32_16x16x32_bf16 (M = 16 heads, N = 16 tokens, 4
+// head blocks x 4 k-steps), then lane (token n, head quarter kg) folds its 16
+// heads with w * max(0, D) and the four quarters are summed with lane swaps.
+// The scores are kept in registers and stored at the end (stores would share
+// the load counter the ring waits on).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void index_scores_mfma_kernel(int Q, int page, int max_seq_len, const bf16_t* __restrict__ q_idx,
                               const float* __restrict__ w_idx, const bf16_t* __restrict__ icache,
                               int64_t num_pages, const int32_t* __restrict__ page_table,
                               int max_pages, const int32_t* __restrict__ seq_lens,
                               float* __restrict__ scores, int ld) {
+  extern __shared__ u32x4_t lds[];
   const int b = blockIdx.y, j = blockIdx.z;
-  const int L = seq_lens[b];
-  if (L < Q || L > max_seq_len) return;  // the selection reports the sequence invalid
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 15, kg = lane >> 4;
-  const int tw = blockIdx.x * kIdxTok + wave * 64 * kIdxChunks;
-  if (tw >= L) return;
+  const int tb = blockIdx.x * kIdxTok + wave * kIChunk;  // chunk 0 of this wave
+  const int L = seq_lens[b];
+  const bool valid = L >= Q && L <= max_seq_len;  // else the selection reports it invalid
+  // chunks of this wave that start before L (every wave stays for the barrier)
+  const int nk =
+      valid && L > tb ? min(kIWaveChunks, (L - tb + 4 * kIChunk - 1) / (4 * kIChunk)) : 0;
+  char* const lbase = reinterpret_cast<char*>(lds);
+  char* const ring = lbase + wave * kIRing * kIChunkBytes;
+  char* const qs = lbase + kIRingBytes;                      // [head][dim] bf16
+  const float* const wsh = reinterpret_cast<const float*>(qs + kIQBytes);
+  // the query and the weights go to LDS once per block (1 KB loads i =
+  // 4 w .. 4 w + 3 of wave w; the weights by wave 0), ahead of the keys
+  {
+    const bf16_t* qb = q_idx + ((size_t)b * Q + j) * kIH * kID;
+    const uint32_t qd = __builtin_amdgcn_readfirstlane(lds_addr(qs));
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 4 * wave + ii;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                   :
+                   : "s"(qd + i * 1024), "v"((uint32_t)(i * 1024 + 16 * lane)), "s"(qb)
+                   : "memory");
+    }
+    if (wave == 0)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 nt"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(lds_addr(wsh))),
+                     "v"((uint32_t)(4 * lane)), "s"(w_idx + ((size_t)b * Q + j) * kIH)
+                   : "memory");
+  }
 
+  // load i of a group: lane l copies row 4 i + l / 16, chunk (l % 16) ^ row
+  uint32_t doff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    doff[i] = (uint32_t)(r * kIRow + (((lane & 15) ^ r) << 4));
+  }
+  uint32_t okbits = 0u;  // bit 2 c + g: group g of chunk c has a valid page
+  auto issue = [&](int c) {
+    char* const slot = ring + (c % kIRing) * kIChunkBytes;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int tg = tb + 4 * kIChunk * c + 16 * g;  // wave-uniform; 16 tokens of one page
+      const int pg = tg < L ? page_table[(size_t)b * max_pages + tg / page] : -1;
+      const bool ok = pg >= 0 && (int64_t)pg < num_pages;
+      okbits |= (ok ? 1u : 0u) << (2 * c + g);
+      // (an invalid or unused group copies the pool's first rows, never read out)
+      const bf16_t* src = icache + (ok ? ((size_t)pg * page + tg % page) * kID : 0);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(slot + g * 16 * kIRow));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                     :
+                     : "s"(dst + i * 1024), "v"(doff[i]), "s"(src)
+                     : "memory");
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < kIRing; ++c)
+    if (c < nk) issue(c);
+  // own query (and weight) loads landed; then everyone's
+  const int first = min(nk, kIRing);
+  if (first >= 4)
+    wait_vmcnt<4 * kIChunkLoads>();
+  else if (first == 3)
+    wait_vmcnt<3 * kIChunkLoads>();
+  else if (first == 2)
+    wait_vmcnt<2 * kIChunkLoads>();
+  else if (first == 1)
+    wait_vmcnt<kIChunkLoads>();
+  else
+    wait_vmcnt<0>();
+  __syncthreads();
+  if (nk == 0) return;
   // queries: head 16 mt + n, dims 32 ks + 8 kg; weights of heads 16 mt + 4 kg + r
-  const bf16_t* qb = q_idx + ((size_t)b * Q + j) * kIH * kID;
-  const float* wb = w_idx + ((size_t)b * Q + j) * kIH;
   bf16x8_t qa[4][4];
   float wv[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      qa[mt][ks] = *reinterpret_cast<const bf16x8_t*>(qb + (16 * mt + n) * kID + 32 * ks + 8 * kg);
+      qa[mt][ks] = *reinterpret_cast<const bf16x8_t*>(qs + (16 * mt + n) * kIRow + 64 * ks + 16 * kg);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wv[mt][r] = wb[16 * mt + 4 * kg + r];
+    for (int r = 0; r < 4; ++r) wv[mt][r] = wsh[16 * mt + 4 * kg + r];
   }
-  // page entries of every group (token tw + 16 g + n)
-  constexpr int kG = 4 * kIdxChunks;
-  int pgs[kG];
+
+  float res[kIWaveChunks][2];  // lanes kg == 0: score of token 16 g + n of chunk c
 #pragma unroll
-  for (int g = 0; g < kG; ++g) {
-    const int t = tw + 16 * g + n;
-    pgs[g] = t < L ? page_table[(size_t)b * max_pages + t / page] : 0;
-  }
-  // keys: dims 32 ks + 8 kg of token tw + 16 g + n
-  bf16x8_t kv[kG][4];
-  bool okp[kG];
-  const bf16x8_t zero = {};
+  for (int c = 0; c < kIWaveChunks; ++c) {
+    if (c >= nk) break;  // wave-uniform
+    // chunk c landed; up to three later chunks may stay in flight
+    const int later = min(nk - 1 - c, kIRing - 1);
+    if (later >= 3)
+      wait_vmcnt<3 * kIChunkLoads>();
+    else if (later == 2)
+      wait_vmcnt<2 * kIChunkLoads>();
+    else if (later == 1)
+      wait_vmcnt<kIChunkLoads>();
+    else
+      wait_vmcnt<0>();
+    const char* const slot = ring + (c % kIRing) * kIChunkBytes;
+    bf16x8_t kv[2][4];
 #pragma unroll
-  for (int g = 0; g < kG; ++g) {
-    const int t = tw + 16 * g + n;
-    const bool in = t < L;
-    int pg = pgs[g];
-    okp[g] = pg >= 0 && (int64_t)pg < num_pages;
-    if (!okp[g]) pg = 0;
-    const bf16_t* kp = icache + ((size_t)pg * page + (in ? t % page : 0)) * kID + 8 * kg;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      kv[g][ks] = in ? *reinterpret_cast<const bf16x8_t*>(kp + 32 * ks) : zero;
-  }
-  float* out = scores + ((size_t)b * Q + j) * ld;
-#pragma unroll
-  for (int g = 0; g < kG; ++g) {
-    float part = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kv[g][ks], d, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(wv[mt][r], relu_nan(d[r]), part);
+        kv[g][ks] = *reinterpret_cast<const bf16x8_t*>(slot + (16 * g + n) * kIRow +
+                                                       (((4 * ks + kg) ^ n) << 4));
+    if (c + kIRing < nk) {  // the slot is read: chunk c + 4 may land in it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(c + kIRing);
     }
-    part = row_sum4(part);
-    const int t = tw + 16 * g + n;
-    if (kg == 0 && t < L) out[t] = okp[g] ? part : __int_as_float(0x7fc00000);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float part = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kv[g][ks], d, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part = fmaf(wv[mt][r], relu_nan(d[r]), part);
+      }
+      res[c][g] = row_sum4(part);
+    }
+  }
+  wait_vmcnt<0>();
+  float* out = scores + ((size_t)b * Q + j) * ld;
+  if (kg == 0) {
+#pragma unroll
+    for (int c = 0; c < kIWaveChunks; ++c)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int t = tb + 4 * kIChunk * c + 16 * g + n;
+        if (c < nk && t < L)
+          out[t] = ((okbits >> (2 * c + g)) & 1u) ? res[c][g] : __int_as_float(0x7fc00000);
+      }
   }
 }
 
@@ -537,7 +634,7 @@ int launch_index_append(const Shape& s, int dI, int n_tok, const void* k_new,
 }
 
 bool index_scores_mfma_ok(const Shape& s, int Hi, int dI) {
-  return s.dtype == 1 && Hi == kIH && dI == kID;
+  return s.dtype == 1 && Hi == kIH && dI == kID && s.page % 16 == 0;
 }
 
 size_t index_scores_generic_lds(int Hi, int dI) {
@@ -551,13 +648,20 @@ int launch_index_scores(const Shape& s, int Hi, int dI, int batch, int q_len, in
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid((max_seq_len + kIdxTok - 1) / kIdxTok, batch, q_len);
   if (index_scores_mfma_ok(s, Hi, dI)) {
-    hipLaunchKernelGGL(index_scores_mfma_kernel, grid, dim3(256), 0, st, q_len, s.page,
+    static bool attr = false;
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(index_scores_mfma_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kILds);
+      if (e != hipSuccess) return (int)e;
+      attr = true;
+    }
+    hipLaunchKernelGGL(index_scores_mfma_kernel, grid, dim3(256), kILds, st, q_len, s.page,
                        max_seq_len, (const bf16_t*)q_idx, w_idx, (const bf16_t*)icache, num_pages,
                        page_table, max_pages, seq_lens, scores, ld);
     return (int)hipGetLastError();
   }
-  const size_t lds = index_scores_generic_lds(Hi, dI);
-  if (lds > 64 * 1024) {
+  const size_t lds_bytes = index_scores_generic_lds(Hi, dI);
+  if (lds_bytes > 64 * 1024) {
     static bool attr[2] = {false, false};
     if (!attr[s.dtype]) {
       hipError_t e = s.dtype == 0
@@ -573,11 +677,11 @@ int launch_index_scores(const Shape& s, int Hi, int dI, int batch, int q_len, in
   }
   const dim3 ggrid((max_seq_len + 255) / 256, batch, q_len);
   if (s.dtype == 0)
-    hipLaunchKernelGGL(index_scores_generic_kernel<float>, ggrid, dim3(256), lds, st, q_len, Hi,
+    hipLaunchKernelGGL(index_scores_generic_kernel<float>, ggrid, dim3(256), lds_bytes, st, q_len, Hi,
                        dI, s.page, max_seq_len, (const float*)q_idx, w_idx, (const float*)icache,
                        num_pages, page_table, max_pages, seq_lens, scores, ld);
   else
-    hipLaunchKernelGGL(index_scores_generic_kernel<bf16_t>, ggrid, dim3(256), lds, st, q_len, Hi,
+    hipLaunchKernelGGL(index_scores_generic_kernel<bf16_t>, ggrid, dim3(256), lds_bytes, st, q_len, Hi,
                        dI, s.page, max_seq_len, (const bf16_t*)q_idx, w_idx,
                        (const bf16_t*)icache, num_pages, page_table, max_pages, seq_lens, scores,
                        ld);
