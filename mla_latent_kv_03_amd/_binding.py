@@ -56,6 +56,14 @@ class Config:
         return _Cfg(self.num_heads, self.kv_rank, self.rope_dim, self.nope_dim, self.v_dim,
                     self.page_size, self.dtype, self.scale, self.rope_base)
 
+    def cptr(self):
+        """A pointer to this config's mla_config_t, built once per Config (the
+        struct is never written)."""
+        p = _CPTR.get(self)
+        if p is None:
+            p = _CPTR[self] = ctypes.pointer(self.c())
+        return p
+
     @staticmethod
     def from_workload(wl) -> "Config":
         return Config(num_heads=wl.heads, kv_rank=wl.kv_rank, rope_dim=wl.rope_dim,
@@ -65,6 +73,7 @@ class Config:
 
 
 _lib = None
+_CPTR = {}  # Config -> pointer to its mla_config_t
 
 
 def lib_path() -> str:
@@ -149,33 +158,33 @@ def _ck(status: int, where: str):
 
 
 def config_validate(cfg: Config) -> int:
-    return lib().mla_config_validate(ctypes.byref(cfg.c()))
+    return lib().mla_config_validate(cfg.cptr())
 
 
 def cache_bytes_per_token(cfg: Config) -> int:
-    return lib().mla_cache_bytes_per_token(ctypes.byref(cfg.c()))
+    return lib().mla_cache_bytes_per_token(cfg.cptr())
 
 
 def split_chunk(cfg: Config, seq_len: int, num_splits: int) -> int:
     out = ctypes.c_int32(0)
-    _ck(lib().mla_split_chunk(ctypes.byref(cfg.c()), seq_len, num_splits, ctypes.byref(out)),
+    _ck(lib().mla_split_chunk(cfg.cptr(), seq_len, num_splits, ctypes.byref(out)),
         "mla_split_chunk")
     return out.value
 
 
 def default_num_splits(cfg: Config, batch: int, q_len: int, max_seq_len: int,
                        num_cus: int = 256) -> int:
-    return lib().mla_default_num_splits(ctypes.byref(cfg.c()), batch, q_len, max_seq_len, num_cus)
+    return lib().mla_default_num_splits(cfg.cptr(), batch, q_len, max_seq_len, num_cus)
 
 
 def decode_partials_bytes(cfg: Config, batch: int, q_len: int, num_splits: int) -> int:
-    return lib().mla_decode_partials_bytes(ctypes.byref(cfg.c()), batch, q_len, num_splits)
+    return lib().mla_decode_partials_bytes(cfg.cptr(), batch, q_len, num_splits)
 
 
 def decode_kernel_kind(cfg: Config, q_len: int) -> str:
     """Which decode kernel libmla takes for this shape: "mfma_ws", "mfma_rows16"
     or "generic"."""
-    return lib().mla_decode_kernel_name(ctypes.byref(cfg.c()), q_len).decode()
+    return lib().mla_decode_kernel_name(cfg.cptr(), q_len).decode()
 
 
 # --------------------------------------------------------------------------
@@ -208,7 +217,10 @@ def _need(x, name: str, dtype, numel: int):
 
 def _stream(stream) -> ctypes.c_void_p:
     t = _torch()
-    if stream is None:
+    if stream is None:  # the current stream of the current device, as a raw handle
+        raw = getattr(t._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return ctypes.c_void_p(raw(t._C._cuda_getDevice()))
         stream = t.cuda.current_stream()
     h = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     return ctypes.c_void_p(h)
@@ -248,14 +260,14 @@ def _append_args(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache, mod
 def absorb_q(cfg: Config, q_nope, q_rope, pos, w_uk, q_full, stream=None):
     """a1: q_full[n][h] = [W_UK[h]^T q_nope[n][h] ; RoPE(q_rope[n][h], pos[n])]."""
     args = _absorb_args(cfg, q_nope, q_rope, pos, w_uk, q_full)
-    _ck(lib().mla_absorb_q(ctypes.byref(cfg.c()), *args, _stream(stream)), "mla_absorb_q")
+    _ck(lib().mla_absorb_q(cfg.cptr(), *args, _stream(stream)), "mla_absorb_q")
 
 
 def cache_append(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache,
                  mode: int = APPEND_ROTATE, stream=None):
     """a2: write rows [c_kv[n] ; k] at page_table[seq_idx[n]][pos[n] // page] ..."""
     args = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode)
-    _ck(lib().mla_cache_append(ctypes.byref(cfg.c()), *args, _stream(stream)), "mla_cache_append")
+    _ck(lib().mla_cache_append(cfg.cptr(), *args, _stream(stream)), "mla_cache_append")
 
 
 def absorb_append(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_rope, seq_idx, pos,
@@ -264,7 +276,7 @@ def absorb_append(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_rope
     cache_append(c_kv, k_rope, seq_idx, pos, page_table, cache, mode)."""
     a = _absorb_args(cfg, q_nope, q_rope, pos_q, w_uk, q_full)
     b = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode)
-    _ck(lib().mla_absorb_append(ctypes.byref(cfg.c()), *a, *b, _stream(stream)),
+    _ck(lib().mla_absorb_append(cfg.cptr(), *a, *b, _stream(stream)),
         "mla_absorb_append")
 
 
@@ -280,7 +292,7 @@ def cache_append_at(cfg: Config, c_kv, k_rope, seq_idx, pos, rope_pos, page_tabl
     still picks the slot (drafted tokens of a tree)."""
     a = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode)
     rp = _rope_pos_arg(rope_pos, a[0])
-    _ck(lib().mla_cache_append_at(ctypes.byref(cfg.c()), *a[:5], rp, *a[5:], _stream(stream)),
+    _ck(lib().mla_cache_append_at(cfg.cptr(), *a[:5], rp, *a[5:], _stream(stream)),
         "mla_cache_append_at")
 
 
@@ -290,13 +302,13 @@ def absorb_append_at(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_r
     a = _absorb_args(cfg, q_nope, q_rope, pos_q, w_uk, q_full)
     b = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode)
     rp = _rope_pos_arg(rope_pos, b[0])
-    _ck(lib().mla_absorb_append_at(ctypes.byref(cfg.c()), *a, *b[:5], rp, *b[5:],
+    _ck(lib().mla_absorb_append_at(cfg.cptr(), *a, *b[:5], rp, *b[5:],
                                    _stream(stream)), "mla_absorb_append_at")
 
 
 def cache_q8_bytes_per_token(cfg: Config) -> int:
     """Bytes of one 8-bit cache row: d_c + d_r codes + 16 bytes of (min, step)."""
-    return lib().mla_cache_q8_bytes_per_token(ctypes.byref(cfg.c()))
+    return lib().mla_cache_q8_bytes_per_token(cfg.cptr())
 
 
 def cache_append_q8(cfg: Config, c_kv, k_rope, seq_idx, pos, rope_pos, page_table, cache_q8,
@@ -305,14 +317,14 @@ def cache_append_q8(cfg: Config, c_kv, k_rope, seq_idx, pos, rope_pos, page_tabl
     coded per part between its own min and max; rope_pos as cache_append_at."""
     a = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache_q8, mode, q8=True)
     rp = _rope_pos_arg(rope_pos, a[0])
-    _ck(lib().mla_cache_append_q8(ctypes.byref(cfg.c()), *a[:5], rp, *a[5:], _stream(stream)),
+    _ck(lib().mla_cache_append_q8(cfg.cptr(), *a[:5], rp, *a[5:], _stream(stream)),
         "mla_cache_append_q8")
 
 
 def chunk_plan(cfg: Config, total_tokens: int, max_seq_len: int, num_cus: int = 256):
     """A fixed-size partition plan (chunk_tokens, num_splits) for decode_paged(chunk_tokens=...)."""
     ck, ns = ctypes.c_int32(0), ctypes.c_int32(0)
-    _ck(lib().mla_chunk_plan(ctypes.byref(cfg.c()), int(total_tokens), int(max_seq_len),
+    _ck(lib().mla_chunk_plan(cfg.cptr(), int(total_tokens), int(max_seq_len),
                              int(num_cus), ctypes.byref(ck), ctypes.byref(ns)), "mla_chunk_plan")
     return ck.value, ns.value
 
@@ -368,25 +380,25 @@ def _decode(cfg, q_full, cache, page_table, seq_lens, tree_parent, o_part, lse_p
     lp = _need(lse_part, "lse_part", t.float32, B * Q * H * S)
     if q8:
         tp = None if tree_parent is None else _need(tree_parent, "tree_parent", t.int32, B * Q)
-        _ck(lib().mla_decode_paged_q8(ctypes.byref(cfg.c()), B, Q, int(chunk_tokens), S,
+        _ck(lib().mla_decode_paged_q8(cfg.cptr(), B, Q, int(chunk_tokens), S,
                                       int(max_seq_len), args[0], args[1], num_pages, pt,
                                       max_pages, sl, tp, op, lp, _stream(stream)),
             "mla_decode_paged_q8")
         return
     if tree_parent is not None:
         tp = _need(tree_parent, "tree_parent", t.int32, B * Q)
-        _ck(lib().mla_decode_paged_tree(ctypes.byref(cfg.c()), B, Q, int(chunk_tokens), S,
+        _ck(lib().mla_decode_paged_tree(cfg.cptr(), B, Q, int(chunk_tokens), S,
                                         int(max_seq_len), args[0], args[1], num_pages, pt,
                                         max_pages, sl, tp, op, lp, _stream(stream)),
             "mla_decode_paged_tree")
         return
     if chunk_tokens:
-        _ck(lib().mla_decode_paged_chunked(ctypes.byref(cfg.c()), B, Q, int(chunk_tokens), S,
+        _ck(lib().mla_decode_paged_chunked(cfg.cptr(), B, Q, int(chunk_tokens), S,
                                            int(max_seq_len), args[0], args[1], num_pages, pt,
                                            max_pages, sl, op, lp, _stream(stream)),
             "mla_decode_paged_chunked")
         return
-    _ck(lib().mla_decode_paged(ctypes.byref(cfg.c()), B, Q, S, int(max_seq_len), args[0], args[1],
+    _ck(lib().mla_decode_paged(cfg.cptr(), B, Q, S, int(max_seq_len), args[0], args[1],
                                num_pages, pt, max_pages, sl, op, lp, _stream(stream)),
         "mla_decode_paged")
 
@@ -410,7 +422,7 @@ def index_append(cfg: Config, k_idx, seq_idx, pos, page_table, index_cache, stre
         raise ValueError("page_table: expected [batch][max_pages]")
     batch, max_pages = (int(x) for x in page_table.shape)
     dt = _elem_dtype(cfg)
-    _ck(lib().mla_index_append(ctypes.byref(cfg.c()), dI, n, _need(k_idx, "k_idx", dt, n * dI),
+    _ck(lib().mla_index_append(cfg.cptr(), dI, n, _need(k_idx, "k_idx", dt, n * dI),
                                _need(seq_idx, "seq_idx", t.int32, n), _need(pos, "pos", t.int32, n),
                                _need(page_table, "page_table", t.int32, batch * max_pages), batch,
                                max_pages, _need(index_cache, "index_cache", dt, index_cache.numel()),
@@ -432,7 +444,7 @@ def index_scores(cfg: Config, q_idx, w_idx, index_cache, page_table, seq_lens, s
     max_pages = int(page_table.shape[1])
     ld = int(scores.shape[2])
     dt = _elem_dtype(cfg)
-    _ck(lib().mla_index_scores(ctypes.byref(cfg.c()), Hi, dI, B, Q, int(max_seq_len),
+    _ck(lib().mla_index_scores(cfg.cptr(), Hi, dI, B, Q, int(max_seq_len),
                                _need(q_idx, "q_idx", dt, B * Q * Hi * dI),
                                _need(w_idx, "w_idx", t.float32, B * Q * Hi),
                                _need(index_cache, "index_cache", dt, index_cache.numel()),
@@ -473,7 +485,7 @@ def sparse_chunk(topk: int, num_splits: int) -> int:
 
 def decode_sparse_kernel_kind(cfg: Config, topk: int, num_splits: int) -> str:
     """"mfma_rows16_gather" or "generic_gather"."""
-    return lib().mla_decode_sparse_kernel_name(ctypes.byref(cfg.c()), int(topk),
+    return lib().mla_decode_sparse_kernel_name(cfg.cptr(), int(topk),
                                                int(num_splits)).decode()
 
 
@@ -489,7 +501,7 @@ def decode_sparse(cfg: Config, q_full, cache, page_table, seq_lens, indices, cou
     if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != cfg.dim:
         raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{cfg.dim}]")
     max_pages = int(page_table.shape[1])
-    _ck(lib().mla_decode_sparse(ctypes.byref(cfg.c()), B, Q, K, S, int(max_seq_len),
+    _ck(lib().mla_decode_sparse(cfg.cptr(), B, Q, K, S, int(max_seq_len),
                                 _need(q_full, "q_full", dt, B * Q * H * cfg.dim),
                                 _need(cache, "cache", dt, cache.numel()), int(cache.shape[0]),
                                 _need(page_table, "page_table", t.int32, B * max_pages), max_pages,
@@ -519,7 +531,7 @@ def _combine_args(cfg: Config, o_part, lse_part, o_lat, lse):
 def splitkv_combine(cfg: Config, o_part, lse_part, o_lat, lse=None, stream=None):
     """a5: LSE merge. o_lat [B][Q][H][d_c] (cfg dtype); lse [B][Q][H] f32 or None."""
     args = _combine_args(cfg, o_part, lse_part, o_lat, lse)
-    _ck(lib().mla_splitkv_combine(ctypes.byref(cfg.c()), *args, _stream(stream)),
+    _ck(lib().mla_splitkv_combine(cfg.cptr(), *args, _stream(stream)),
         "mla_splitkv_combine")
 
 
@@ -530,7 +542,7 @@ def combine_up_project(cfg: Config, o_part, lse_part, o_lat, w_uv, out, lse=None
     H, dt = cfg.num_heads, _elem_dtype(cfg)
     wv = _need(w_uv, "w_uv", dt, H * cfg.v_dim * cfg.kv_rank)
     ot = _need(out, "out", dt, B * Q * H * cfg.v_dim)
-    _ck(lib().mla_combine_up_project(ctypes.byref(cfg.c()), B, Q, S, op, lp, ol, ls, wv, ot,
+    _ck(lib().mla_combine_up_project(cfg.cptr(), B, Q, S, op, lp, ol, ls, wv, ot,
                                      _stream(stream)), "mla_combine_up_project")
 
 
@@ -541,4 +553,4 @@ def up_project_v(cfg: Config, o_lat, w_uv, out, stream=None):
     args = (_need(o_lat, "o_lat", dt, n * H * cfg.kv_rank),
             _need(w_uv, "w_uv", dt, H * cfg.v_dim * cfg.kv_rank),
             _need(out, "out", dt, n * H * cfg.v_dim))
-    _ck(lib().mla_up_project_v(ctypes.byref(cfg.c()), n, *args, _stream(stream)), "mla_up_project_v")
+    _ck(lib().mla_up_project_v(cfg.cptr(), n, *args, _stream(stream)), "mla_up_project_v")
