@@ -328,9 +328,10 @@ mla_status_t mla_index_append(const mla_config_t* cfg, int32_t index_dim, int32_
  * [index_dim] T, w_idx [batch][q_len][index_heads] f32, index_cache and
  * page_table as for mla_index_append, seq_lens [batch]. A token whose page
  * entry is invalid scores NaN; a sequence with an invalid length is not
- * written (mla_topk_select reports it). bf16 with 64 heads x 128 runs on
- * MFMA; other shapes need index_heads * (index_dim + 1) * 4 <= 160 KiB
- * (MLA_ERR_UNSUPPORTED otherwise). index_heads in [1, 256]. */
+ * written (mla_topk_select reports it). bf16 with 64 heads x 128 and a page
+ * size that is a multiple of 16 runs on MFMA; other shapes need
+ * index_heads * (index_dim + 1) * 4 <= 160 KiB (MLA_ERR_UNSUPPORTED
+ * otherwise). index_heads in [1, 256]. */
 mla_status_t mla_index_scores(const mla_config_t* cfg, int32_t index_heads, int32_t index_dim,
                               int32_t batch, int32_t q_len, int32_t max_seq_len,
                               const void* q_idx, const float* w_idx, const void* index_cache,
