@@ -49,7 +49,7 @@ DECODE_KERNELS = {
     "generic": ("decode_generic_kernel", ["mla_kernels.hip"]),
     "mfma_q8": ("decode_q8_kernel", ["mla_decode_common.h", "mla_q8.hip"]),
     # sparse read: the indexer pass is the step's dominant kernel
-    "index_scores_mfma": ("index_scores_mfma_kernel", ["mla_decode_common.h", "mla_sparse.hip"]),
+    "index_scores_mfma": ("index_scores_mfma_kernel<false>", ["mla_decode_common.h", "mla_sparse.hip"]),
 }
 
 
@@ -290,8 +290,11 @@ def main():
         if sparse:
             ipool = ipools[layer % n_layers]
             st.index_append(k_idx_new, pt, ipool)
-            st.index_scores(q_idx, w_idx, ipool, pt, seq_lens)
-            st.select(seq_lens)
+            if args.unfused:
+                st.index_scores(q_idx, w_idx, ipool, pt, seq_lens)
+                st.select(seq_lens)
+            else:
+                st.index_select(q_idx, w_idx, ipool, pt, seq_lens)
         st.decode(pool, pt, seq_lens)
         if args.unfused:
             st.combine()
@@ -450,7 +453,8 @@ def main():
                    "paged": wl.paged, "num_splits": wl.num_splits,
                    "split_chunk": wl.split_chunk,
                    "layer_caches_rotated": n_layers, "hip_graph": bool(args.graph),
-                   "library_calls_per_step": 5 if args.unfused else 3,
+                   "library_calls_per_step": (5 if args.unfused else 3) +
+                                             ((3 if args.unfused else 2) if sparse else 0),
                    "drafted_tree": None if wl.tree is None else list(wl.tree),
                    "cache_format": wl.cache, "cache_bytes_per_token": wl.cache_row_bytes,
                    "decode_kernel": kernel,

@@ -359,6 +359,21 @@ mla_status_t mla_topk_select(int32_t batch, int32_t q_len, int32_t max_seq_len, 
  * counts and a flag); 0 for invalid arguments. */
 size_t mla_topk_workspace_bytes(int32_t batch, int32_t q_len);
 
+/* mla_index_scores followed by mla_topk_select in one call: the same scores,
+ * indices and counts, the same arguments, checks and errors as those two calls
+ * (workspace as for mla_topk_select). With the MFMA indexer (bf16, 64 heads
+ * x 128, page size a multiple of 16) the score kernel also builds the
+ * selection's histogram, one launch fewer; other shapes run the separate
+ * launches. */
+mla_status_t mla_index_scores_topk(const mla_config_t* cfg, int32_t index_heads,
+                                   int32_t index_dim, int32_t batch, int32_t q_len,
+                                   int32_t max_seq_len, const void* q_idx, const float* w_idx,
+                                   const void* index_cache, int64_t num_pages,
+                                   const int32_t* page_table, int32_t max_pages,
+                                   const int32_t* seq_lens, float* scores, int32_t ld_scores,
+                                   int32_t topk, void* workspace, int32_t* indices,
+                                   int32_t* counts, void* stream);
+
 /* List entries per partition of mla_decode_sparse: ceil(topk / num_splits)
  * rounded up to a multiple of 32; 0 for invalid arguments. */
 int32_t mla_sparse_chunk(int32_t topk, int32_t num_splits);

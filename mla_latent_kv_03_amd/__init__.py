@@ -54,6 +54,7 @@ from ._binding import (  # noqa: F401
     decode_paged_q8,
     index_append,
     index_scores,
+    index_scores_topk,
     topk_select,
     topk_workspace_bytes,
     sparse_chunk,

@@ -127,6 +127,8 @@ def lib() -> ctypes.CDLL:
         "mla_index_scores": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, FP, VP, I64, VP, I32,
                                             VP, FP, I32, VP]),
         "mla_topk_select": (ctypes.c_int, [I32, I32, I32, I32, FP, I32, VP, VP, VP, VP, VP]),
+        "mla_index_scores_topk": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, FP, VP, I64, VP,
+                                                 I32, VP, FP, I32, I32, VP, VP, VP, VP]),
         "mla_topk_workspace_bytes": (ctypes.c_size_t, [I32, I32]),
         "mla_sparse_chunk": (ctypes.c_int32, [I32, I32]),
         "mla_decode_sparse_kernel_name": (ctypes.c_char_p, [P, I32, I32]),
@@ -452,6 +454,37 @@ def index_scores(cfg: Config, q_idx, w_idx, index_cache, page_table, seq_lens, s
                                max_pages, _need(seq_lens, "seq_lens", t.int32, B),
                                _need(scores, "scores", t.float32, B * Q * ld), ld,
                                _stream(stream)), "mla_index_scores")
+
+
+def index_scores_topk(cfg: Config, q_idx, w_idx, index_cache, page_table, seq_lens, scores,
+                      max_seq_len: int, indices, counts, workspace, stream=None):
+    """index_scores then topk_select in one library call (the same scores,
+    indices and counts; one launch fewer with the MFMA indexer)."""
+    t = _torch()
+    if q_idx.dim() != 4 or scores.dim() != 3 or indices.dim() != 3:
+        raise ValueError("q_idx: expected [batch][q_len][heads][dim]; scores [batch][q_len][ld]; "
+                         "indices [batch][q_len][topk]")
+    B, Q, Hi, dI = (int(x) for x in q_idx.shape)
+    num_pages, dI2 = _index_cache_dims(cfg, index_cache)
+    if dI2 != dI:
+        raise ValueError("index_cache width does not match q_idx")
+    max_pages = int(page_table.shape[1])
+    ld = int(scores.shape[2])
+    K = int(indices.shape[2])
+    dt = _elem_dtype(cfg)
+    _ck(lib().mla_index_scores_topk(cfg.cptr(), Hi, dI, B, Q, int(max_seq_len),
+                                    _need(q_idx, "q_idx", dt, B * Q * Hi * dI),
+                                    _need(w_idx, "w_idx", t.float32, B * Q * Hi),
+                                    _need(index_cache, "index_cache", dt, index_cache.numel()),
+                                    num_pages,
+                                    _need(page_table, "page_table", t.int32, B * max_pages),
+                                    max_pages, _need(seq_lens, "seq_lens", t.int32, B),
+                                    _need(scores, "scores", t.float32, B * Q * ld), ld, K,
+                                    _need(workspace, "workspace", t.uint8,
+                                          topk_workspace_bytes(B, Q)),
+                                    _need(indices, "indices", t.int32, B * Q * K),
+                                    _need(counts, "counts", t.int32, B * Q), _stream(stream)),
+        "mla_index_scores_topk")
 
 
 def topk_workspace_bytes(batch: int, q_len: int) -> int:

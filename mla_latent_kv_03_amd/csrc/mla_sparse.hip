@@ -75,6 +75,14 @@ __global__ __launch_bounds__(64) void index_append_kernel(int dI, int page,
 // ReLU that keeps a NaN (a NaN dot must not turn into a valid score)
 __device__ __forceinline__ float relu_nan(float x) { return x < 0.0f ? 0.0f : x; }
 
+// order-preserving 32-bit key of a score (-0 taken as +0); its top 12 bits
+// are the top-k's coarse bin
+__device__ __forceinline__ uint32_t score_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // ---------------------------------------------------------------------------
 // index scores, bf16 MFMA: 64 heads x 128 dims. Block = kIdxTok tokens of one
 // (sequence, query), four waves without block barriers; chunk c of wave w is
@@ -90,13 +98,19 @@ __device__ __forceinline__ float relu_nan(float x) { return x < 0.0f ? 0.0f : x;
 // heads with w * max(0, D) and the four quarters are summed with lane swaps.
 // The scores are kept in registers and stored at the end (stores would share
 // the load counter the ring waits on).
+// kHist: the block also counts its visible scores into the top-k's coarse
+// histogram as they are made (LDS atomics into the LDS that staged the
+// query, once the query is in registers) and at the end adds the non-empty
+// bins and the NaN flag to the query's workspace row, as topk_hist_kernel
+// does; every wave then stays to the final barrier.
 // ---------------------------------------------------------------------------
+template <bool kHist>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void index_scores_mfma_kernel(int Q, int page, int max_seq_len, const bf16_t* __restrict__ q_idx,
                               const float* __restrict__ w_idx, const bf16_t* __restrict__ icache,
                               int64_t num_pages, const int32_t* __restrict__ page_table,
                               int max_pages, const int32_t* __restrict__ seq_lens,
-                              float* __restrict__ scores, int ld) {
+                              float* __restrict__ scores, int ld, uint32_t* __restrict__ ws) {
   extern __shared__ u32x4_t lds[];
   const int b = blockIdx.y, j = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -176,7 +190,7 @@ void index_scores_mfma_kernel(int Q, int page, int max_seq_len, const bf16_t* __
   else
     wait_vmcnt<0>();
   __syncthreads();
-  if (nk == 0) return;
+  if (!kHist && nk == 0) return;
   // queries: head 16 mt + n, dims 32 ks + 8 kg; weights of heads 16 mt + 4 kg + r
   bf16x8_t qa[4][4];
   float wv[4][4];
@@ -187,6 +201,15 @@ void index_scores_mfma_kernel(int Q, int page, int max_seq_len, const bf16_t* __
       qa[mt][ks] = *reinterpret_cast<const bf16x8_t*>(qs + (16 * mt + n) * kIRow + 64 * ks + 16 * kg);
 #pragma unroll
     for (int r = 0; r < 4; ++r) wv[mt][r] = wsh[16 * mt + 4 * kg + r];
+  }
+  uint32_t* const hist = reinterpret_cast<uint32_t*>(qs);  // kHist: [kTkCoarse] counts
+  static_assert(kTkCoarse * 4 <= kIQBytes, "the histogram fits the query's staging");
+  const int nvis = valid ? L - Q + j + 1 : 0;  // tokens the query sees
+  bool nan = false;                            // a NaN among this lane's visible scores
+  if constexpr (kHist) {
+    __syncthreads();  // every wave has its query in registers
+    for (int i = threadIdx.x; i < kTkCoarse; i += 256) hist[i] = 0u;
+    __syncthreads();
   }
 
   float res[kIWaveChunks][2];  // lanes kg == 0: score of token 16 g + n of chunk c
@@ -228,6 +251,14 @@ void index_scores_mfma_kernel(int Q, int page, int max_seq_len, const bf16_t* __
         for (int r = 0; r < 4; ++r) part = fmaf(wv[mt][r], relu_nan(d[r]), part);
       }
       res[c][g] = row_sum4(part);
+      if constexpr (kHist) {  // count the visible score into the coarse histogram
+        const int t = tb + 4 * kIChunk * c + 16 * g + n;
+        if (kg == 0 && t < nvis) {
+          const float v = ((okbits >> (2 * c + g)) & 1u) ? res[c][g] : __int_as_float(0x7fc00000);
+          nan |= v != v;
+          atomicAdd(&hist[score_key(v) >> (32 - kTkCoarseBits)], 1u);
+        }
+      }
     }
   }
   wait_vmcnt<0>();
@@ -241,6 +272,12 @@ void index_scores_mfma_kernel(int Q, int page, int max_seq_len, const bf16_t* __
         if (c < nk && t < L)
           out[t] = ((okbits >> (2 * c + g)) & 1u) ? res[c][g] : __int_as_float(0x7fc00000);
       }
+  }
+  if constexpr (kHist) {
+    uint32_t* row = ws + ((size_t)b * Q + j) * kTkWsRow;
+    if (__syncthreads_or(nan ? 1 : 0) && threadIdx.x == 0) row[kTkCoarse] = 1u;
+    for (int i = threadIdx.x; i < kTkCoarse; i += 256)
+      if (hist[i]) atomicAdd(&row[i], hist[i]);
   }
 }
 
@@ -301,12 +338,6 @@ __global__ __launch_bounds__(256) void index_scores_generic_kernel(
 //     > T and == T, and after a prefix over the 16 waves writes every key > T
 //     and the first (topk - count(> T)) keys == T.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t score_key(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // exclusive prefix sum over the block's 1,024 threads; *total = the sum
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -650,14 +681,15 @@ int launch_index_scores(const Shape& s, int Hi, int dI, int batch, int q_len, in
   if (index_scores_mfma_ok(s, Hi, dI)) {
     static bool attr = false;
     if (!attr) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(index_scores_mfma_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kILds);
+      hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(index_scores_mfma_kernel<false>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kILds);
       if (e != hipSuccess) return (int)e;
       attr = true;
     }
-    hipLaunchKernelGGL(index_scores_mfma_kernel, grid, dim3(256), kILds, st, q_len, s.page,
-                       max_seq_len, (const bf16_t*)q_idx, w_idx, (const bf16_t*)icache, num_pages,
-                       page_table, max_pages, seq_lens, scores, ld);
+    hipLaunchKernelGGL((index_scores_mfma_kernel<false>), grid, dim3(256), kILds, st, q_len,
+                       s.page, max_seq_len, (const bf16_t*)q_idx, w_idx, (const bf16_t*)icache,
+                       num_pages, page_table, max_pages, seq_lens, scores, ld, nullptr);
     return (int)hipGetLastError();
   }
   const size_t lds_bytes = index_scores_generic_lds(Hi, dI);
@@ -692,6 +724,12 @@ size_t topk_workspace_bytes(int batch, int q_len) {
   return sizeof(uint32_t) * (size_t)kTkWsRow * batch * q_len;
 }
 
+namespace {
+int launch_topk_select(int batch, int q_len, int max_seq_len, int topk, const float* scores,
+                       int ld, const int32_t* seq_lens, uint32_t* ws, int32_t* indices,
+                       int32_t* counts, hipStream_t st);
+}  // namespace
+
 int launch_topk(int batch, int q_len, int max_seq_len, int topk, const float* scores, int ld,
                 const int32_t* seq_lens, void* workspace, int32_t* indices, int32_t* counts,
                 void* stream) {
@@ -700,6 +738,47 @@ int launch_topk(int batch, int q_len, int max_seq_len, int topk, const float* sc
   hipLaunchKernelGGL(topk_hist_kernel, dim3((max_seq_len + kTkHistTok - 1) / kTkHistTok,
                                             batch * q_len),
                      dim3(256), 0, st, q_len, max_seq_len, scores, ld, seq_lens, ws);
+  return launch_topk_select(batch, q_len, max_seq_len, topk, scores, ld, seq_lens, ws, indices,
+                            counts, st);
+}
+
+int launch_index_scores_topk(const Shape& s, int Hi, int dI, int batch, int q_len,
+                             int max_seq_len, const void* q_idx, const float* w_idx,
+                             const void* icache, int64_t num_pages, const int32_t* page_table,
+                             int max_pages, const int32_t* seq_lens, float* scores, int ld,
+                             int topk, void* workspace, int32_t* indices, int32_t* counts,
+                             void* stream) {
+  if (!index_scores_mfma_ok(s, Hi, dI)) {  // the separate launches
+    const int e = launch_index_scores(s, Hi, dI, batch, q_len, max_seq_len, q_idx, w_idx, icache,
+                                      num_pages, page_table, max_pages, seq_lens, scores, ld,
+                                      stream);
+    if (e != 0) return e;
+    return launch_topk(batch, q_len, max_seq_len, topk, scores, ld, seq_lens, workspace, indices,
+                       counts, stream);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* ws = reinterpret_cast<uint32_t*>(workspace);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(index_scores_mfma_kernel<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kILds);
+    if (e != hipSuccess) return (int)e;
+    attr = true;
+  }
+  const dim3 grid((max_seq_len + kIdxTok - 1) / kIdxTok, batch, q_len);
+  hipLaunchKernelGGL((index_scores_mfma_kernel<true>), grid, dim3(256), kILds, st, q_len, s.page,
+                     max_seq_len, (const bf16_t*)q_idx, w_idx, (const bf16_t*)icache, num_pages,
+                     page_table, max_pages, seq_lens, scores, ld, ws);
+  const int e = (int)hipGetLastError();
+  if (e != 0) return e;
+  return launch_topk_select(batch, q_len, max_seq_len, topk, scores, ld, seq_lens, ws, indices,
+                            counts, st);
+}
+
+namespace {
+int launch_topk_select(int batch, int q_len, int max_seq_len, int topk, const float* scores,
+                       int ld, const int32_t* seq_lens, uint32_t* ws, int32_t* indices,
+                       int32_t* counts, hipStream_t st) {
   if (max_seq_len <= kTkRegTok)
     hipLaunchKernelGGL(topk_select_kernel<true>, dim3(batch * q_len), dim3(kTkThreads), 0, st,
                        q_len, max_seq_len, topk, scores, ld, seq_lens, ws, indices, counts);
@@ -708,5 +787,6 @@ int launch_topk(int batch, int q_len, int max_seq_len, int topk, const float* sc
                        q_len, max_seq_len, topk, scores, ld, seq_lens, ws, indices, counts);
   return (int)hipGetLastError();
 }
+}  // namespace
 
 }  // namespace mla

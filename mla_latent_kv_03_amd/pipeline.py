@@ -136,6 +136,12 @@ class DecodeStep:
         B.topk_select(self.scores, seq_lens, self.indices, self.counts, self.max_seq_len,
                       self.topk_ws, stream)
 
+    def index_select(self, q_idx, w_idx, index_cache, page_table, seq_lens, stream=None):
+        """index_scores then select, as one library call."""
+        B.index_scores_topk(self.cfg, q_idx, w_idx, index_cache, page_table, seq_lens,
+                            self.scores, self.max_seq_len, self.indices, self.counts,
+                            self.topk_ws, stream)
+
     def decode(self, cache, page_table, seq_lens, stream=None, max_seq_len: Optional[int] = None):
         if self.index_topk > 0:
             B.decode_sparse(self.cfg, self.q_full, cache, page_table, seq_lens, self.indices,
@@ -181,7 +187,8 @@ class DecodeStep:
         """absorb -> append (B*Q new rows) -> decode -> combine -> up-project.
 
         fused: the first two and the last two calls each as one library call
-        (mla_absorb_append, mla_combine_up_project; same results).
+        (mla_absorb_append, mla_combine_up_project; same results), and for a
+        sparse read the scoring and the selection (mla_index_scores_topk).
         sparse: (q_idx, w_idx, k_idx_new, index_cache) for a sparse read: the
         new indexer keys are appended, every cached token scored, the top
         index_topk selected, and the decode reads only those."""
@@ -193,8 +200,11 @@ class DecodeStep:
         if self.index_topk > 0:
             q_idx, w_idx, k_idx_new, index_cache = sparse
             self.index_append(k_idx_new, page_table, index_cache, stream)
-            self.index_scores(q_idx, w_idx, index_cache, page_table, seq_lens, stream)
-            self.select(seq_lens, stream)
+            if fused:
+                self.index_select(q_idx, w_idx, index_cache, page_table, seq_lens, stream)
+            else:
+                self.index_scores(q_idx, w_idx, index_cache, page_table, seq_lens, stream)
+                self.select(seq_lens, stream)
         self.decode(cache, page_table, seq_lens, stream, max_seq_len)
         if fused:
             self.combine_up_project(w_uv, stream)

@@ -284,6 +284,13 @@ def test_sparse_entry_errors(L):
     assert L.mla_topk_select(2, 1, 256, 64, A16, 256, A16, MIS, A16, A16, None) == 4
     assert L.mla_topk_select(0, 1, 256, 64, None, 256, None, None, None, None, None) == 0
     assert L.mla_topk_workspace_bytes(8, 1) == 8 * 4100 * 4
+    # index scores + top-k in one call: the union of both calls' checks
+    def st(heads=64, topk=64, ld=256, max_len=256, ws=A16, cfg=V2):
+        return L.mla_index_scores_topk(_c(cfg), heads, 128, 2, 1, max_len, A16, A16, A16, 8, A16,
+                                       4, A16, A16, ld, topk, ws, A16, A16, None)
+    assert st(heads=0) == 2 and st(topk=0) == 2 and st(topk=65537) == 2
+    assert st(ld=255) == 2 and st(max_len=300) == 5
+    assert st(ws=None) == 1 and st(ws=MIS) == 4
     assert L.mla_topk_workspace_bytes(0, 1) == 0 and L.mla_topk_workspace_bytes(2, 0) == 0
     # sparse decode
     def dec(topk=2048, S=16, counts=A16, batch=2):

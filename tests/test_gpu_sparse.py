@@ -198,6 +198,47 @@ def test_index_scores_invalid_page_is_nan():
     assert np.all(np.isfinite(got[1, :, :int(inp.seq_lens[1])]))
 
 
+@pytest.mark.parametrize("name", ["mfma_64x128", "generic_f32"])
+def test_index_scores_topk_equals_the_two_calls(name):
+    # mla_index_scores_topk: the same scores bit for bit and the same selection
+    # as mla_index_scores followed by mla_topk_select, on ragged lengths, an
+    # invalid length and a token whose page entry is invalid (NaN score: the
+    # sequence reported invalid); the workspace is left all zero
+    wl, lens = INDEX_SHAPES[name]
+    inp, cfg, dt, pool, pt = _index_case(wl, 5, lens)
+    B, Q, L = wl.batch, wl.q_len, wl.max_seq_len
+    K = min(wl.index_topk, 300)
+    pt_bad = pt.clone()
+    pt_bad[B - 1, 0] = inp.num_pages + 3               # the last sequence's first page
+    seq_lens = inp.seq_lens.copy()
+    seq_lens[0] = L + 1 if B > 2 else seq_lens[0]      # beyond max_seq_len: invalid
+    sl = upload(seq_lens, torch.int32)
+    q_idx = upload(np.ascontiguousarray(inp.q_idx), dt)
+    w_idx = upload(np.ascontiguousarray(inp.w_idx), torch.float32)
+    out = []
+    for fused in (False, True):
+        sc = torch.full((B, Q, L + 3), 7.0, dtype=torch.float32, device="cuda")
+        idx = torch.full((B, Q, K), -5, dtype=torch.int32, device="cuda")
+        cnt = torch.full((B, Q), -9, dtype=torch.int32, device="cuda")
+        ws = torch.zeros(mla.topk_workspace_bytes(B, Q), dtype=torch.uint8, device="cuda")
+        for _ in range(2):  # a second call on the same workspace
+            if fused:
+                mla.index_scores_topk(cfg, q_idx, w_idx, pool, pt_bad, sl, sc, L, idx, cnt, ws)
+            else:
+                mla.index_scores(cfg, q_idx, w_idx, pool, pt_bad, sl, sc, L)
+                mla.topk_select(sc, sl, idx, cnt, L, ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+        out.append((sc.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()))
+    (s0, i0, c0), (s1, i1, c1) = out
+    assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
+    assert np.array_equal(c0, c1) and np.array_equal(i0, i1)
+    assert np.all(c1[B - 1] == -1)                       # NaN among the visible scores
+    if B > 2:
+        assert np.all(c1[0] == -1)                       # invalid length
+    assert np.any(c1 > 0)
+
+
 # ---------------------------------------------------------------- sparse decode alone
 def _random_selection(inp, K, seed):
     wl = inp.wl
