@@ -396,6 +396,126 @@ __global__ __launch_bounds__(384) void combine_up_v_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// a5 + a6 in one launch for many rows (more than 4,096 of them; bf16,
+// d_c = 512, d_v = 128, S <= 64): one block of 8 waves per (head h, 16
+// tokens), so W_UV[h] is read once per 16 tokens rather than once per row.
+//   merge    wave w merges rows (token n0 + 2 w + i, head h), i = 0, 1, both
+//            256-column halves, with the combine kernel's arithmetic (the
+//            same weights, partitions added in the same order); the loads of
+//            all four (row, half) items are issued before the first is
+//            added. The bf16 rows go to o_lat, lse and an LDS tile (zero rows
+//            for tokens past n_tok).
+//   project  wave w computes v-tile w (rows 16 w .. 16 w + 15 of W_UV[h]) for
+//            the 16 tokens: the four k-step chains of up_v_mfma_kernel's
+//            waves, each in its order, summed as that kernel sums them, so
+//            the output has the bits of the two separate launches.
+// Blocks of one head share blockIdx % 8 (one XCD, one L2) when H % 8 == 0.
+// ---------------------------------------------------------------------------
+constexpr int kGrpTok = 16;
+constexpr int kGrpSplits = 64;
+constexpr int kGrpWaves = kFusedDv / 16;          // one v-tile per wave
+constexpr int kGrpRowBytes = kFusedDc * 2 + 16;   // padded: rows start 4 banks apart
+static_assert(2 * kGrpWaves == kGrpTok, "two merged rows per wave");
+
+template <int kCH>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+void combine_up_v_group_kernel(
+    int n_tok, int H, int S, const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    bf16_t* __restrict__ o_lat, float* __restrict__ lse, const bf16_t* __restrict__ w_uv,
+    bf16_t* __restrict__ out) {
+  __shared__ float w[kGrpWaves][2][kGrpSplits];
+  __shared__ u32x4_t tile[kGrpTok * kGrpRowBytes / 16];
+  const int ngrp = (n_tok + kGrpTok - 1) / kGrpTok;
+  const int id = blockIdx.x;
+  int grp, h;
+  if (H % 8 == 0) {
+    const int rest = id >> 3;
+    grp = rest % ngrp;
+    h = (rest / ngrp) * 8 + (id & 7);
+  } else {
+    grp = id / H;
+    h = id % H;
+  }
+  const int n0 = grp * kGrpTok;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nn = lane & 15, g = lane >> 4;
+  char* tb = reinterpret_cast<char*>(tile);
+
+  // ---- merge: item j = (row 2 wave + (j >> 1), half j & 1)
+  CombineCols<kCH> cc[4];  // kCH partitions in flight per item (2 when S <= 2)
+  float lv[2];
+  size_t rr[2];
+  bool ok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int n = n0 + 2 * wave + i;
+    ok[i] = n < n_tok;
+    rr[i] = (size_t)(ok[i] ? n : 0) * H + h;  // rows past n_tok load row (0, h) and drop it
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    cc[j].start(o_part + rr[j >> 1] * S * kFusedDc, S, kFusedDc, (j & 1) * kCombCols + 4 * lane);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) lv[i] = lane < S ? lse_part[rr[i] * S + lane] : 0.0f;
+  CombineWeights cw[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) cw[i] = combine_weights_one(lv[i], S, w[wave][i], lane);
+  __syncthreads();  // weights visible to every lane
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = j >> 1;
+    const int col = (j & 1) * kCombCols + 4 * lane;
+    const float4 v = cc[j].finish(w[wave][i], cw[i], lane);
+    if (ok[i]) {
+      store4<bf16_t>(o_lat + rr[i] * kFusedDc + col, v);
+      if (lse && (j & 1) == 0 && lane == 0) lse[rr[i]] = cw[i].lse();
+    }
+    uint2 u = {0u, 0u};
+    if (ok[i]) {
+      u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+      u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    }
+    *reinterpret_cast<uint2*>(tb + (2 * wave + i) * kGrpRowBytes + 2 * col) = u;
+  }
+  // W_UV[h] operands of v-tile `wave`: chain c, step i covers latent columns
+  // 32 c + 128 i + 8 g .. + 7 of row 16 wave + nn. Loaded after the merge
+  // (the other block on the CU covers their latency), which keeps the
+  // register peak low enough for two blocks per CU.
+  const bf16_t* brow = w_uv + ((size_t)h * kFusedDv + 16 * wave + nn) * kFusedDc + 8 * g;
+  u32x4_t bv[4][4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      bv[c][i] = *reinterpret_cast<const u32x4_t*>(brow + 32 * c + 128 * i);
+  __syncthreads();  // the 16 rows are in LDS
+
+  // ---- project: v_mfma_f32_16x16x32_bf16, M = 16 tokens, N = 16 rows of W_UV
+  f32x4_t acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4_t av =
+          *reinterpret_cast<const u32x4_t*>(tb + nn * kGrpRowBytes + 2 * (32 * c + 128 * i + 8 * g));
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                       __builtin_bit_cast(bf16x8_t, bv[c][i]),
+                                                       acc[c], 0, 0, 0);
+    }
+  f32x4_t sum = acc[0] + acc[1];
+  sum += acc[2] + acc[3];
+  // lane holds tokens n0 + 4 g + r, value column 16 wave + nn
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = n0 + 4 * g + r;
+    if (t < n_tok) out[((size_t)t * H + h) * kFusedDv + 16 * wave + nn] = f2bf(sum[r]);
+  }
+}
+
 bool combine_up_v_fused_ok(const Shape& s, int n_tok, int num_splits) {
   return s.dtype == 1 && s.dc == kFusedDc && s.dv == kFusedDv && n_tok * s.H <= 4096 &&
          num_splits <= kFusedSplits;
@@ -404,6 +524,15 @@ bool combine_up_v_fused_ok(const Shape& s, int n_tok, int num_splits) {
 int launch_combine_up_project(const Shape& s, int n_tok, int num_splits, const float* o_part,
                               const float* lse_part, void* o_lat, float* lse, const void* w_uv,
                               void* out, void* stream) {
+  if (s.dtype == 1 && s.dc == kFusedDc && s.dv == kFusedDv && n_tok * s.H > 4096 &&
+      num_splits <= kGrpSplits) {
+    const int blocks = s.H * ((n_tok + kGrpTok - 1) / kGrpTok);
+    auto kern = num_splits <= 2 ? combine_up_v_group_kernel<2> : combine_up_v_group_kernel<4>;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kGrpWaves), 0,
+                       reinterpret_cast<hipStream_t>(stream), n_tok, s.H, num_splits, o_part,
+                       lse_part, (bf16_t*)o_lat, lse, (const bf16_t*)w_uv, (bf16_t*)out);
+    return (int)hipGetLastError();
+  }
   if (!combine_up_v_fused_ok(s, n_tok, num_splits)) {
     int rc = launch_combine(s, n_tok * s.H, num_splits, o_part, lse_part, o_lat, lse, stream);
     if (rc == 0) rc = launch_up_project_v(s, n_tok, o_lat, w_uv, out, stream);

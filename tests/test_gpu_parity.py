@@ -280,15 +280,30 @@ def test_paged_equals_identity_bit_exact():
     assert np.array_equal(to64(a.step.o_part), to64(b.step.o_part))
 
 
+# above 4,096 query rows the merge + up-projection runs one block per (head,
+# 16 tokens): ragged last token groups, 128 and 12 heads (both block orders),
+# several query tokens per sequence, 1 to 64 partitions (empty ones included)
+FUSED_WIDE = {
+    "h128_4480_rows_s2": small("v2_h128_8k", batch=35, seq_len=120, num_splits=2),
+    "h128_4224_rows_s1": small("v2_h128_8k", batch=33, seq_len=90, num_splits=1),
+    "paged_q8_5120_rows": small("v2lite_paged_varlen", batch=40, q_len=8, len_range=(8, 300),
+                                num_splits=5),
+    "h12_q12_4320_rows_s64": small("v2lite_32k", batch=30, heads=12, q_len=12, seq_len=700,
+                                   num_splits=64),
+}
 FUSED = ["tiny_f32", "v2lite_small", "v2lite_paged_small", "v2_h128_small", "q4_h128_small",
-         "bf16_generic_h8", "bf16_h12"]
+         "bf16_generic_h8", "bf16_h12"] + list(FUSED_WIDE)
 
 
 @pytest.mark.parametrize("name", FUSED)
 def test_fused_calls_bit_exact(name):
     """mla_absorb_append and mla_combine_up_project give the bits of the calls they fuse."""
-    wl = SMALL[name] if name in SMALL else small("v2lite_32k", batch=3, heads=12, seq_len=500,
-                                                  num_splits=4)
+    if name in FUSED_WIDE:
+        wl = FUSED_WIDE[name]
+        assert wl.batch * wl.q_len * wl.heads > 4096
+    else:
+        wl = SMALL[name] if name in SMALL else small("v2lite_32k", batch=3, heads=12, seq_len=500,
+                                                      num_splits=4)
     case = Case(wl, seed=3)
     case.run(fused=False)
     s = case.step
