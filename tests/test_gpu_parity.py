@@ -395,3 +395,29 @@ def test_invalid_sequence_gives_nan_only_there(fault):
     ol = to64(case.step.o_lat)
     assert np.all(np.isnan(ol[1]))
     assert np.all(np.isfinite(ol[[0, 2]]))
+
+
+def test_grouped_merge_keeps_nan_rows_to_their_sequence():
+    """Above 4,096 rows the rows of an invalid sequence (NaN) share the
+    up-projection MFMAs of their 16-token group with valid rows: only its own
+    rows turn NaN, and the one launch still gives the bits of the two."""
+    wl = FUSED_WIDE["paged_q8_5120_rows"]
+    case = Case(wl, seed=11)
+    pt = case.inp.page_table.copy()
+    pt[5, 0] = case.inp.num_pages + 3  # sequence 5: tokens 40..47, grouped with 32..39
+    case.pt = upload(pt, torch.int32)
+    s = case.step
+    s.absorb(case.q_nope, case.q_rope, case.w_uk)
+    s.decode(case.pool, case.pt, case.seq_lens)
+    s.combine_up_project(case.w_uv)
+    torch.cuda.synchronize()
+    one = {k: to64(getattr(s, k)) for k in ("out", "o_lat", "lse")}
+    for k in one:
+        getattr(s, k).fill_(0.0)
+    s.combine()
+    s.up_project(case.w_uv)
+    torch.cuda.synchronize()
+    for k, v in one.items():
+        assert np.array_equal(v, to64(getattr(s, k)), equal_nan=True), k
+        assert np.all(np.isnan(v[5])), k
+        assert np.all(np.isfinite(np.delete(v, 5, axis=0))), k
