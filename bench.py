@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as five library calls instead of three")
+    ap.add_argument("--no-stream-read", action="store_true",
+                    help="skip the plain streaming-read reference (achievable HBM read rate)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -103,17 +105,30 @@ def visible_pairs(wl, inp):
     return sum(Q * (int(L) - Q) + Q * (Q + 1) // 2 for L in inp.seq_lens)
 
 
+def cpu_threads():
+    """(threads the oracle's BLAS calls run on, host CPU counts): the oracle
+    is NumPy, whose matrix products use the BLAS thread pool and whose other
+    operations run on one thread."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas = 1
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = os.cpu_count() or 1
+    return int(min(blas, aff)), {"host_cpus": os.cpu_count(), "affinity_cpus": aff,
+                                 "blas_threads": int(blas)}
+
+
 def cpu_baseline_prefill(wl, inp, flops_step, bytes_step, n_queries=8):
     """Prefill chunk: the oracle on sampled queries of the chunk (each one a
     one-token decode over the tokens it sees, head 0 only), scaled by the
     share of the step's algorithmic work they represent."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    threads, host = cpu_threads()
     L, Q = int(inp.seq_lens[0]), wl.q_len
     P = L - Q
     js = [int(x) for x in np.linspace(0, Q - 1, n_queries)]
@@ -127,7 +142,7 @@ def cpu_baseline_prefill(wl, inp, flops_step, bytes_step, n_queries=8):
     flops = sum(P + j + 1 for j in js) * (2 * wl.dim + 2 * wl.kv_rank)
     share = flops / flops_step
     return {"value": round(bytes_step * share / dt / 1e9, 6), "unit": "GB/s",
-            "cores": int(threads), "kind": "oracle",
+            "cores": int(threads), **host, "kind": "oracle",
             "sample": f"{len(js)} of {Q} queries of sequence 0 (each a one-token decode over the "
                       f"tokens it sees), head 0 of {wl.heads}, {dt:.1f} s; fp64 unabsorbed NumPy "
                       f"oracle; scaled by the sample's share {share:.2e} of the step's "
@@ -146,11 +161,7 @@ def cpu_baseline(wl, inp, budget_flops=2.4e12):
     in proportion to the heads sampled.
     """
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    threads, host = cpu_threads()
     per_tok_head = 2 * wl.kv_rank * (wl.nope_dim + wl.v_dim) + 4 * (wl.nope_dim + wl.rope_dim)
     heads = wl.heads
     seq_cost = lambda b, h: int(inp.seq_lens[b]) * h * wl.q_len * per_tok_head  # noqa: E731
@@ -180,7 +191,7 @@ def cpu_baseline(wl, inp, budget_flops=2.4e12):
     else:
         nbytes = tokens * wl.cache_row_bytes * heads / wl.heads
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            **host, "kind": "oracle",
             "sample": f"{len(seqs)} of {wl.batch} sequences ({tokens} cached tokens), "
                       f"{heads} of {wl.heads} heads, {dt:.1f} s; fp64 unabsorbed NumPy oracle"
                       f"{' (rows coded to 8 bits first)' if wl.cache == 'q8' else ''}"
@@ -206,6 +217,33 @@ def sparse_selection(inp, seqs):
     return out
 
 
+def stream_read_rate(torch, mla, stream, nbytes=4 << 30, reps=10):
+    """GB/s of a plain coalesced read of a 4 GiB buffer (16-byte non-temporal
+    loads, mla_stream_read): what a stream with no arithmetic reaches on this
+    device, for context beside the decode kernel's fraction of the 8 TB/s
+    peak. Best over a few grid sizes; HIP events on the launch stream."""
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(1)
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        mla.stream_read(buf, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            mla.stream_read(buf, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbs = nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, blocks)
+    del buf
+    return {"gbs": round(best[0], 1), "pct_of_peak": round(100 * best[0] / HBM_PEAK_GBS, 2),
+            "bytes": nbytes, "blocks": best[1], "threads_per_block": 256,
+            "kernel": "stream_read_kernel (16-byte non-temporal loads)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -218,7 +256,7 @@ def main():
     import workload
     import mla_latent_kv_03_amd as mla
     from mla_latent_kv_03_amd.pipeline import (DecodeStep, fill_cache, fill_cache_q8,
-                                               fill_index_cache, token_rope_positions, upload)
+                                               fill_index_cache, upload)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -251,14 +289,8 @@ def main():
                            device="cuda")
     si = np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(inp.seq_lens)])
     pos = np.concatenate([np.arange(int(L), dtype=np.int32) for L in inp.seq_lens])
-    rope_pos = None
-    if inp.parents is not None:  # a drafted tree: its keys sit at prefix + depth
-        rope_pos = upload(np.asarray(token_rope_positions(inp.seq_lens, wl.q_len, inp.parents),
-                                     np.int32), torch.int32)
     (fill_cache_q8 if q8 else fill_cache)(cfg, pool0, pt, upload(inp.c, dt), upload(inp.k_rope, dt),
-                                          upload(si, torch.int32), upload(pos, torch.int32),
-                                          rope_pos=rope_pos)
-    pools = [pool0] + [pool0.clone() for _ in range(n_layers - 1)]
+                                          upload(si, torch.int32), upload(pos, torch.int32))
     q_nope, q_rope = upload(inp.q_nope, dt), upload(inp.q_rope, dt)
     w_uk, w_uv = upload(inp.w_uk, dt), upload(inp.w_uv, dt)
     rows = np.concatenate([inp.offsets[b] + np.arange(int(L) - Q, int(L))
@@ -275,6 +307,10 @@ def main():
         k_idx_new = upload(inp.k_idx[rows], dt)
     st = DecodeStep(cfg, B, Q, wl.num_splits, inp.seq_lens, split_chunk=wl.split_chunk,
                     tree_parents=inp.parents, cache_q8=q8, index_topk=wl.index_topk)
+    # the drafted rows at their positions (a tree's keys sit at prefix + depth;
+    # the fill rotated every key at its slot), then one copy per layer
+    st.append(c_new, k_new, pt, pool0)
+    pools = [pool0] + [pool0.clone() for _ in range(n_layers - 1)]
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
 
@@ -482,6 +518,8 @@ def main():
     props = torch.cuda.get_device_properties(0)
     out["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
                      "gcn_arch": getattr(props, "gcnArchName", "")}
+    if not args.no_stream_read:
+        out["hbm_stream_read"] = stream_read_rate(torch, mla, stream)
     if args.calibrate_copy:
         # a plain copy of known size, for scaling the HBM byte counters
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")

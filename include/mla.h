@@ -29,7 +29,10 @@
  *     library never allocates, frees or keeps a pointer after returning.
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and returns once the work is enqueued. The
- *     library keeps no state and may be called from several threads.
+ *     library holds no per-call state; the one thing it remembers is which
+ *     kernels have had their LDS limit raised on which device (set under a
+ *     lock on first use), so calls may come from several threads. Calls that
+ *     write the same buffers must not overlap.
  *   - Layouts are dense, row-major, in the order written in brackets; element
  *     type "T" is cfg->dtype (fp32 or bf16) for queries, weights, cache and
  *     outputs; partials are always fp32.
@@ -167,6 +170,28 @@ mla_status_t mla_cache_append_at(const mla_config_t* cfg, int32_t n_tok, const v
                                  const int32_t* rope_pos, const int32_t* page_table,
                                  int32_t batch, int32_t max_pages, void* cache, int64_t num_pages,
                                  int32_t flags, void* stream);
+
+/* Positions of the drafted tokens of a verify step, derived on the device
+ * from the lengths and the tree ("The Architecture of Memory", "Tree
+ * Attention Verification": a drafted token sits in the cache after its
+ * siblings but one position past its parent). For row n = b * q_len + i:
+ *   seq_idx[n] = b,  slot[n] = L_b - q_len + i,  pos[n] = L_b - q_len + depth(i)
+ * where depth(i) is 0 when tree_parent[b][i] = -1, else one more than the
+ * parent's depth; tree_parent NULL means the chain (pos = slot). A sequence
+ * whose L_b lies outside [q_len, max_seq_len] or whose tree breaks
+ * tree_parent[b][i] in [-1, i) gets slot = pos = -1 for all its rows, so the
+ * append calls skip them and mla_decode_paged_tree returns NaN for it.
+ * seq_lens [batch], tree_parent [batch][q_len] (q_len <= 64) or NULL,
+ * seq_idx, slot, pos [batch * q_len] int32 (out), all device pointers.
+ * A tree step passes pos as the query positions (mla_absorb_q / the pos_q of
+ * mla_absorb_append_at), slot and pos as the slot and RoPE position of each
+ * drafted row (mla_cache_append_at, mla_absorb_append_at,
+ * mla_cache_append_q8), and the same tree_parent to the decode: the RoPE
+ * rotations then agree with the tree the decode masks by, which the decode
+ * itself cannot check (it sees only rotated values). */
+mla_status_t mla_draft_positions(int32_t batch, int32_t q_len, int32_t max_seq_len,
+                                 const int32_t* seq_lens, const int32_t* tree_parent,
+                                 int32_t* seq_idx, int32_t* slot, int32_t* pos, void* stream);
 
 /* a1 + a2 in one launch, for callers that run both every step: the same
  * arguments, work and results (bit for bit) as
@@ -432,6 +457,15 @@ mla_status_t mla_combine_up_project(const mla_config_t* cfg, int32_t batch, int3
                                     int32_t num_splits, const float* o_part,
                                     const float* lse_part, void* o_lat, float* lse,
                                     const void* w_uv, void* out, void* stream);
+
+/* Measurement aid, not part of the decode: reads `bytes` of device memory
+ * (a multiple of 16, buf 16-byte aligned) with 16-byte non-temporal loads
+ * spread over `blocks` blocks of 256 threads (1 .. 65,536) and writes one
+ * checksum word per block to sink [blocks] uint32, so that no load can be
+ * dropped. Its rate is the HBM read rate a plain coalesced stream reaches,
+ * the context for the decode kernels' fraction of the 8 TB/s peak. */
+mla_status_t mla_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,8 +15,9 @@ fallback. If the library is missing, every call raises.
 
 absorb_append and combine_up_project run the first two and the last two of
 these calls in one launch each, with the same results. A tree of drafted
-tokens is verified with cache_append_at / absorb_append_at (slot and RoPE
-position differ) and decode_paged_tree. An 8-bit latent cache (uint8 rows
+tokens is verified with draft_positions (each drafted row's slot and RoPE
+position, derived on the device from the tree), cache_append_at /
+absorb_append_at and decode_paged_tree. An 8-bit latent cache (uint8 rows
 of codes plus per-part min and step) is written by cache_append_q8 and read
 by decode_paged_q8. A sparse read (attention over the top-scored tokens
 only) runs index_append, index_scores, topk_select and decode_sparse.
@@ -60,4 +61,6 @@ from ._binding import (  # noqa: F401
     sparse_chunk,
     decode_sparse_kernel_kind,
     decode_sparse,
+    draft_positions,
+    stream_read,
 )

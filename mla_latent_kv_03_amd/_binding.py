@@ -134,6 +134,8 @@ def lib() -> ctypes.CDLL:
         "mla_decode_sparse_kernel_name": (ctypes.c_char_p, [P, I32, I32]),
         "mla_decode_sparse": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32, VP,
                                              VP, VP, FP, FP, VP]),
+        "mla_draft_positions": (ctypes.c_int, [I32, I32, I32, VP, VP, VP, VP, VP, VP]),
+        "mla_stream_read": (ctypes.c_int, [VP, ctypes.c_size_t, VP, I32, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -306,6 +308,35 @@ def absorb_append_at(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_r
     rp = _rope_pos_arg(rope_pos, b[0])
     _ck(lib().mla_absorb_append_at(cfg.cptr(), *a, *b[:5], rp, *b[5:],
                                    _stream(stream)), "mla_absorb_append_at")
+
+
+def draft_positions(seq_lens, q_len: int, max_seq_len: int, tree_parent, seq_idx, slot, pos,
+                    stream=None):
+    """Drafted-token rows of a verify step, on the device: seq_idx, slot and
+    pos [B*Q] int32 (out) from seq_lens [B] and tree_parent [B][Q] (None: a
+    chain); -1 slots and positions for an invalid sequence."""
+    t = _torch()
+    B, Q = int(seq_lens.numel()), int(q_len)
+    tp = None if tree_parent is None else _need(tree_parent, "tree_parent", t.int32, B * Q)
+    _ck(lib().mla_draft_positions(B, Q, int(max_seq_len), _need(seq_lens, "seq_lens", t.int32, B),
+                                  tp, _need(seq_idx, "seq_idx", t.int32, B * Q),
+                                  _need(slot, "slot", t.int32, B * Q),
+                                  _need(pos, "pos", t.int32, B * Q), _stream(stream)),
+        "mla_draft_positions")
+
+
+def stream_read(buf, sink, stream=None):
+    """Read every byte of the device tensor ``buf`` once (16-byte loads);
+    sink: a uint32-sized device tensor of one word per block (its numel
+    blocks)."""
+    t = _torch()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf: must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    blocks = int(sink.numel())
+    _ck(lib().mla_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                              _need(sink, "sink", t.int32, blocks), blocks, _stream(stream)),
+        "mla_stream_read")
 
 
 def cache_q8_bytes_per_token(cfg: Config) -> int:

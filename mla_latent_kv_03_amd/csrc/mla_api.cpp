@@ -267,6 +267,32 @@ mla_status_t mla_cache_append_at(const mla_config_t* cfg, int32_t n_tok, const v
                                              num_pages, flags == MLA_APPEND_ROTATE, stream));
 }
 
+mla_status_t mla_draft_positions(int32_t batch, int32_t q_len, int32_t max_seq_len,
+                                 const int32_t* seq_lens, const int32_t* tree_parent,
+                                 int32_t* seq_idx, int32_t* slot, int32_t* pos, void* stream) {
+  MLA_REQUIRE(batch >= 0 && q_len >= 1, MLA_ERR_SHAPE);
+  if (tree_parent) MLA_REQUIRE(q_len <= kMaxTreeDrafts, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)batch * q_len <= INT32_MAX, MLA_ERR_SHAPE);
+  MLA_REQUIRE(max_seq_len >= q_len, MLA_ERR_CAPACITY);
+  if (batch == 0) return MLA_OK;
+  MLA_CHECK_PTR(seq_lens);
+  if (tree_parent) MLA_CHECK_PTR(tree_parent);
+  MLA_CHECK_PTR(seq_idx);
+  MLA_CHECK_PTR(slot);
+  MLA_CHECK_PTR(pos);
+  return hip_status(mla::launch_draft_positions(batch, q_len, max_seq_len, seq_lens, tree_parent,
+                                                seq_idx, slot, pos, stream));
+}
+
+mla_status_t mla_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,
+                             void* stream) {
+  MLA_REQUIRE(bytes % 16 == 0 && blocks >= 1 && blocks <= 65536, MLA_ERR_SHAPE);
+  if (bytes == 0) return MLA_OK;
+  MLA_CHECK_PTR(buf);
+  MLA_CHECK_PTR(sink);
+  return hip_status(mla::launch_stream_read(buf, bytes, sink, blocks, stream));
+}
+
 mla_status_t mla_absorb_append(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
                                const void* q_rope, const int32_t* pos_q, const void* w_uk,
                                void* q_full, int32_t n_app, const void* c_kv, const void* k_rope,

@@ -428,13 +428,9 @@ int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, i
                          const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                          const int32_t* tree_parent, float* o_part, float* lse_part,
                          void* stream) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_rows16_kernel<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    if (e != hipSuccess) return (int)e;
-    attr = true;
-  }
+  if (int e = set_max_lds(reinterpret_cast<const void*>(decode_rows16_kernel<false>),
+                          (int)kLdsBytes))
+    return e;
   const int units = batch * num_splits;
   const int groups = q_len * s.H / kRows;
   const int blocks = grid_blocks(units, groups);
@@ -452,14 +448,9 @@ int launch_decode_sparse_rows16(const Shape& s, int batch, int q_len, int topk, 
                                 int max_pages, const int32_t* seq_lens, const int32_t* sel_idx,
                                 const int32_t* sel_cnt, float* o_part, float* lse_part,
                                 void* stream) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_rows16_kernel<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kGatherLdsBytes);
-    if (e != hipSuccess) return (int)e;
-    attr = true;
-  }
+  if (int e = set_max_lds(reinterpret_cast<const void*>(decode_rows16_kernel<true>),
+                          (int)kGatherLdsBytes))
+    return e;
   const int units = batch * num_splits;
   const int groups = q_len * s.H / kRows;
   const int blocks = grid_blocks(units, groups);

@@ -391,13 +391,7 @@ int launch_decode_ws(const Shape& s, int batch, int q_len, int num_splits, int m
                      const void* q_full, const void* cache, int64_t num_pages,
                      const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                      const int32_t* tree_parent, float* o_part, float* lse_part, void* stream) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_ws_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWLds);
-    if (e != hipSuccess) return (int)e;
-    attr = true;
-  }
+  if (int e = set_max_lds(reinterpret_cast<const void*>(decode_ws_kernel), (int)kWLds)) return e;
   const int units = batch * num_splits;
   const int groups = q_len * s.H / kWRows;
   const int blocks = grid_blocks(units, groups);

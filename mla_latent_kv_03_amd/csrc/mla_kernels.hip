@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "mla_common.h"
 #include "mla_append.h"
 #include "mla_combine.h"
@@ -19,6 +23,89 @@ namespace mla {
   } while (0)
 
 static inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int set_max_lds(const void* kernel, int bytes) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return 0;
+  HIPCHK(hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+  done.insert({kernel, dev});
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Drafted-token positions ("The Architecture of Memory", "Tree Attention
+// Verification"): drafted token i of sequence b is cached at slot
+// L_b - Q + i and positioned at L_b - Q + depth(i), its depth being 0 under
+// the prefix and one more than its parent's. One 64-lane block per sequence.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void draft_positions_kernel(int Q, int max_seq_len,
+                                                             const int32_t* __restrict__ seq_lens,
+                                                             const int32_t* __restrict__ tree,
+                                                             int32_t* __restrict__ seq_idx,
+                                                             int32_t* __restrict__ slot,
+                                                             int32_t* __restrict__ pos) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int L = seq_lens[b];
+  const int32_t* par = tree ? tree + (size_t)b * Q : nullptr;
+  bool ok = L >= Q && L <= max_seq_len;
+  if (par) ok = __all(lane >= Q || tree_entry_ok(par, lane)) && ok;  // Q <= 64 with a tree
+  for (int i = lane; i < Q; i += 64) {
+    int d = i;
+    if (par && ok) {  // a valid tree: every walk ends within i steps
+      d = 0;
+      for (int k = par[i]; k >= 0; k = par[k]) ++d;
+    }
+    const size_t n = (size_t)b * Q + i;
+    seq_idx[n] = b;
+    slot[n] = ok ? L - Q + i : -1;
+    pos[n] = ok ? L - Q + d : -1;
+  }
+}
+
+int launch_draft_positions(int batch, int q_len, int max_seq_len, const int32_t* seq_lens,
+                           const int32_t* tree_parent, int32_t* seq_idx, int32_t* slot,
+                           int32_t* pos, void* stream) {
+  hipLaunchKernelGGL(draft_positions_kernel, dim3(batch), dim3(64), 0, as_stream(stream), q_len,
+                     max_seq_len, seq_lens, tree_parent, seq_idx, slot, pos);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Streaming read for context: grid-stride 16-byte non-temporal loads, XOR of
+// everything a block read into one word (so no load can be dropped).
+// ---------------------------------------------------------------------------
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_nt* __restrict__ src,
+                                                          size_t n16, uint32_t* __restrict__ sink) {
+  u32x4_nt x = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_nt a = __builtin_nontemporal_load(src + i);
+    const u32x4_nt b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4_nt c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4_nt d = __builtin_nontemporal_load(src + i + 3 * stride);
+    x ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) x ^= __builtin_nontemporal_load(src + i);
+  uint32_t w = x.x ^ x.y ^ x.z ^ x.w;
+  for (int off = 32; off > 0; off >>= 1) w ^= __shfl_xor(w, off, 64);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, void* stream) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, as_stream(stream),
+                     reinterpret_cast<const u32x4_nt*>(buf), bytes / 16, sink);
+  return (int)hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // a1: query absorption + query RoPE
@@ -327,12 +414,7 @@ static int decode_generic_impl(const Shape& s, int batch, int q_len, int num_spl
                                const int32_t* seq_lens, const int32_t* tree_parent, float* o_part,
                                float* lse_part, void* stream) {
   const int D = s.D();
-  static bool attr_set = false;
-  if (!attr_set) {
-    HIPCHK(hipFuncSetAttribute((const void*)decode_generic_kernel<T, false>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024));
-    attr_set = true;
-  }
+  if (int e = set_max_lds((const void*)decode_generic_kernel<T, false>, 160 * 1024)) return e;
   const int R = q_len * s.H;
   dim3 grid(num_splits, batch, (R + kGenRows - 1) / kGenRows);
   hipLaunchKernelGGL((decode_generic_kernel<T, false>), grid, dim3(256), generic_lds_bytes(D),
@@ -351,12 +433,7 @@ static int decode_sparse_generic_impl(const Shape& s, int batch, int q_len, int 
                                       const int32_t* seq_lens, const int32_t* sel_idx,
                                       const int32_t* sel_cnt, float* o_part, float* lse_part,
                                       void* stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    HIPCHK(hipFuncSetAttribute((const void*)decode_generic_kernel<T, true>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024));
-    attr_set = true;
-  }
+  if (int e = set_max_lds((const void*)decode_generic_kernel<T, true>, 160 * 1024)) return e;
   dim3 grid(num_splits, batch, q_len * ((s.H + kGenRows - 1) / kGenRows));
   hipLaunchKernelGGL((decode_generic_kernel<T, true>), grid, dim3(256), generic_lds_bytes(s.D()),
                      as_stream(stream), q_len, s.H, s.dc, s.dr, s.page, num_splits, chunk,

@@ -25,6 +25,23 @@ inline int append_vectorizable(const Shape& s, const void* c_kv, const void* cac
 }
 
 // Each returns 0 on success or the hipError_t of the failed launch.
+
+// Raise a kernel's dynamic LDS limit to `bytes` once per kernel and device
+// (the first launch on each device sets it; thread-safe). 0 or a hipError_t.
+int set_max_lds(const void* kernel, int bytes);
+
+// Drafted-token positions of one verify step: for row n = b * q_len + i,
+// seq_idx[n] = b, slot[n] = L_b - q_len + i and pos[n] = L_b - q_len +
+// depth_b(i) (the slot for a chain, tree_parent NULL); -1 for both when L_b
+// is outside [q_len, max_seq_len] or b's tree breaks parent[i] in [-1, i).
+int launch_draft_positions(int batch, int q_len, int max_seq_len, const int32_t* seq_lens,
+                           const int32_t* tree_parent, int32_t* seq_idx, int32_t* slot,
+                           int32_t* pos, void* stream);
+
+// A plain streaming read of `bytes` (a multiple of 16) with 16-byte
+// non-temporal loads, one checksum word per block into sink[0 .. blocks):
+// the achievable HBM read rate, for context beside the decode kernels.
+int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, void* stream);
 int launch_absorb_q(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
                     const int32_t* pos, const void* w_uk, void* q_full, void* stream);
 

@@ -218,12 +218,22 @@ constexpr int kQAReads = kKSteps / 2;                // 9 reads of 16 B per subt
 //          (latent, RoPE), QK^T = 18 v_mfma_f32_16x16x32_f16 per subtile
 //          (A = 8 codes of token n per lane, B = the query rows in fp16)
 //   P.C:   sum_t p_t (min_t + step_t c_t)
-//            = 2^24 sum_t P_t (c_t 2^-24) + sum_t p_t min_t, P_t = fp16(p_t step_t)
+//            = 2^(24 - g) sum_t P_t (c_t 2^-24) + sum_t p_t min_t,
+//          P_t = fp16(p_t step_t 2^g)
 //          32 v_mfma_f32_16x16x16_f16 per subtile: A = P of row n over the 4
 //          tokens whose scores the lane already holds, B = one column of those
 //          4 tokens' codes (two v_perm), columns 64 g + 4 n + r
-// The query rows are converted to fp16 once per block (exact for bf16 values
-// within fp16 range).
+// The query rows are converted to fp16 once per block, each row part (latent,
+// RoPE) scaled by the power of two 2^e that brings its largest magnitude into
+// [2^14, 2^15): bf16 values then convert exactly unless they lie more than
+// 2^28 below that largest one, where their part of a dot product is below
+// what the fp32 accumulation resolves; the factor 2^-e goes into the row's
+// score terms. P_t = p_t step_t 2^g carries a per-row power of two as well,
+// chosen so that the largest P of the row since the last change lies in
+// [2^-2, 2^12]: every P fits fp16, and one that falls into fp16's subnormal
+// band is at least 2^16 below that largest term. Both factors are exact, so
+// the rows' own scales (steps from 2^-100 to 2^100, queries of any finite
+// bf16 magnitude) leave the rounding of the contractions unchanged.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
                       float scale_log2, int units, int groups, const bf16_t* __restrict__ q_full,
@@ -236,6 +246,8 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   __shared__ float st_m[kWaves][16], st_l[kWaves][16], st_o[kWaves][16];
   __shared__ int pwin[kWaves][64];     // each wave's copy of the page window
   __shared__ float sqp[kWaves][16][2];  // each wave's part of the query row sums
+  __shared__ float sqa[kWaves][16][2];  // ... and of their largest magnitudes
+  __shared__ int st_g[kWaves][16];      // each wave's exponent of its P factor
   int unit, grp;
   if (!map_block(units, groups, &unit, &grp)) return;
   const int R = Q * H;
@@ -313,6 +325,9 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   float off = 0.0f;  // this lane's part of sum_t p_t min_t (row n)
   float sq_lat = 0.0f, sq_rope = 0.0f;             // row sums of the query parts
   const float c24 = scale_log2 * 16777216.0f;
+  float c24l = c24, c24r = c24;  // with the query parts' 2^-e
+  int ge = 0;                    // P_t = p_t step_t 2^ge (row n)
+  float pmax = 0.0f;             // largest P_t of row n since ge last changed
   f32x4_t acc[kFB][4];
 #pragma unroll
   for (int g = 0; g < kFB; ++g)
@@ -356,19 +371,50 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
     // the B operand of step ks for lane (row n, kg), columns q8_col(ks, kg) .. + 7,
     // in fp16 at qop + 1 KB * ks + 16 * lane: wave w converts the steps
     // ks = w mod 4 and its part of the row sums, which meet in LDS
+    auto q_stage = [&](int ks) {
+      const int gb = n * kD * 2 + 2 * q8_col(ks, kg);
+      const int li = gb >> 10;
+      const char* p = lbase + (li % kWaves) * kQWaveBytes + (kQRing - 1) * kQSubBytes +
+                      (li / kWaves) * 1024 + (gb & 1023);
+      return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+    };
+    {
+      float al = 0.0f, ar = 0.0f;
+      for (int ks = wave; ks < kKSteps; ks += kWaves) {  // wave-uniform bounds
+        const bf16x8_t qv = q_stage(ks);
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf((float)qv[j]));
+        if (ks < kDC / 32)
+          al = fmaxf(al, a);
+        else
+          ar = fmaxf(ar, a);
+      }
+      al = row_max4(al);
+      ar = row_max4(ar);
+      if (kg == 0) {
+        sqa[wave][n][0] = al;
+        sqa[wave][n][1] = ar;
+      }
+    }
+    __syncthreads();
+    // 2^e with (largest magnitude) 2^e in [2^14, 2^15), e within [-100, 100]
+    auto q_exp = [](float a) {
+      if (!(a > 0.0f) || !(a < INFINITY)) return 0;
+      return min(100, max(-100, 15 - __builtin_amdgcn_frexp_expf(a)));
+    };
+    const int el = q_exp(fmaxf(fmaxf(sqa[0][n][0], sqa[1][n][0]), fmaxf(sqa[2][n][0], sqa[3][n][0])));
+    const int er = q_exp(fmaxf(fmaxf(sqa[0][n][1], sqa[1][n][1]), fmaxf(sqa[2][n][1], sqa[3][n][1])));
     {
       float sl = 0.0f, sr = 0.0f;
       for (int ks = wave; ks < kKSteps; ks += kWaves) {  // wave-uniform bounds
-        const int gb = n * kD * 2 + 2 * q8_col(ks, kg);
-        const int li = gb >> 10;
-        const char* p = lbase + (li % kWaves) * kQWaveBytes + (kQRing - 1) * kQSubBytes +
-                        (li / kWaves) * 1024 + (gb & 1023);
-        const bf16x8_t qv = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+        const bf16x8_t qv = q_stage(ks);
+        const int e = ks < kDC / 32 ? el : er;
         f16x8_t h;
         float part = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          h[j] = (_Float16)(float)qv[j];
+          h[j] = (_Float16)ldexpf((float)qv[j], e);
           part += (float)h[j];
         }
         *reinterpret_cast<f16x8_t*>(qop + ks * 1024 + 16 * lane) = h;
@@ -385,8 +431,10 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
       }
     }
     __syncthreads();  // the operands are written and the staging slots are free
-    sq_lat = (sqp[0][n][0] + sqp[1][n][0] + sqp[2][n][0] + sqp[3][n][0]) * scale_log2;
-    sq_rope = (sqp[0][n][1] + sqp[1][n][1] + sqp[2][n][1] + sqp[3][n][1]) * scale_log2;
+    sq_lat = ldexpf((sqp[0][n][0] + sqp[1][n][0] + sqp[2][n][0] + sqp[3][n][0]) * scale_log2, -el);
+    sq_rope = ldexpf((sqp[0][n][1] + sqp[1][n][1] + sqp[2][n][1] + sqp[3][n][1]) * scale_log2, -er);
+    c24l = ldexpf(c24, -el);
+    c24r = ldexpf(c24, -er);
     if (nk > kQRing - 1) issue_next();
 
     // QK: A operand of lane (token n, kg) at bytes n * 592 + q8_col(ks, kg);
@@ -439,8 +487,8 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
       float sv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sv[r] = fmaf(mt[r].y * c24, al[r],
-                     fmaf(mt[r].w * c24, cr[r], fmaf(mt[r].x, sq_lat, mt[r].z * sq_rope)));
+        sv[r] = fmaf(mt[r].y * c24l, al[r],
+                     fmaf(mt[r].w * c24r, cr[r], fmaf(mt[r].x, sq_lat, mt[r].z * sq_rope)));
       }
       if (!__all(ts + kQT - 1 <= lim)) {  // some token of the subtile is masked for some row
         const uint32_t vl =
@@ -457,6 +505,7 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
         const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
         off *= alpha;
+        pmax *= alpha;
         if (__any(raise && m_run != -INFINITY)) {
           float ar[4];
 #pragma unroll
@@ -471,14 +520,40 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
         m_run = m_new;
       }
       const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-      f16x4_t pa;
+      float x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = __builtin_amdgcn_exp2f(sv[r] - m_use);
         l_run += p;
         off = fmaf(p, mt[r].x, off);
-        pa[r] = (_Float16)(p * mt[r].y);
+        x[r] = p * ldexpf(mt[r].y, ge);
       }
+      // keep the row's largest P since the last change of ge in [2^-2, 2^12]
+      // (a change sets it to [1, 2) and rescales the accumulators exactly)
+      const float xm = fmaxf(pmax, row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))));
+      const bool refit = xm > 4096.0f || (xm > 0.0f && xm < 0.25f);
+      if (__any(refit)) {
+        const int k = refit ? min(100 - ge, max(-100 - ge, 1 - __builtin_amdgcn_frexp_expf(xm)))
+                            : 0;
+        ge += k;
+        pmax = ldexpf(xm, k);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = ldexpf(x[r], k);
+        int kr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kr[r] = __shfl(k, 4 * kg + r, 64);
+#pragma unroll
+        for (int g = 0; g < kFB; ++g)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[g][c][r] = ldexpf(acc[g][c][r], kr[r]);
+      } else {
+        pmax = xm;
+      }
+      f16x4_t pa;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pa[r] = (_Float16)x[r];
 
       // the slot is read: subtile k + kQRing may land in it
       if (k + kQRing < nk) {
@@ -510,6 +585,7 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
     st_m[wave][n] = m_run;
     st_l[wave][n] = l_row;
     st_o[wave][n] = off_row;
+    st_g[wave][n] = ge;
   }
   const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
   // every loop has ended: the rings and the query operands are free. Each
@@ -524,8 +600,8 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   }
   __syncthreads();
   const float nanv = __int_as_float(0x7fc00000);
-  // per output row 4 kg + r: each wave's factor 2^(m_w - m_all), 1 / l and
-  // sum_t p_t min_t, all relative to m_all
+  // per output row 4 kg + r: each wave's factor 2^(m_w - m_all) for l and
+  // sum_t p_t min_t, the same with 2^(24 - ge_w) for its accumulators, 1 / l
   float fw[kWaves][4], inv[4], base[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -538,7 +614,7 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
     for (int w = 0; w < kWaves; ++w) {
       const float mw = st_m[w][rr];
       const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mr);
-      fw[w][r] = f;
+      fw[w][r] = ldexpf(f, 24 - st_g[w][rr]);
       lr = fmaf(st_l[w][rr], f, lr);
       orr = fmaf(st_o[w][rr], f, orr);
     }
@@ -567,10 +643,8 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
       for (int r = 0; r < 4; ++r) {
         const int orow = row0 + 4 * kg + r;
         float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + 64 * g + 4 * n;
-        float4 v = make_float4(fmaf(16777216.0f, sum[0][r], base[r]) * inv[r],
-                               fmaf(16777216.0f, sum[1][r], base[r]) * inv[r],
-                               fmaf(16777216.0f, sum[2][r], base[r]) * inv[r],
-                               fmaf(16777216.0f, sum[3][r], base[r]) * inv[r]);
+        float4 v = make_float4((sum[0][r] + base[r]) * inv[r], (sum[1][r] + base[r]) * inv[r],
+                               (sum[2][r] + base[r]) * inv[r], (sum[3][r] + base[r]) * inv[r]);
         if (any_bad) v = make_float4(nanv, nanv, nanv, nanv);
         *reinterpret_cast<float4*>(dst) = v;
       }
@@ -600,13 +674,7 @@ int launch_decode_q8(const Shape& s, int batch, int q_len, int num_splits, int m
                      const void* q_full, const void* cache, int64_t num_pages,
                      const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                      const int32_t* tree_parent, float* o_part, float* lse_part, void* stream) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_q8_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kQLds);
-    if (e != hipSuccess) return (int)e;
-    attr = true;
-  }
+  if (int e = set_max_lds(reinterpret_cast<const void*>(decode_q8_kernel), (int)kQLds)) return e;
   const int units = batch * num_splits;
   const int groups = q_len * s.H / 16;
   const int blocks = grid_blocks(units, groups);

@@ -679,14 +679,9 @@ int launch_index_scores(const Shape& s, int Hi, int dI, int batch, int q_len, in
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid((max_seq_len + kIdxTok - 1) / kIdxTok, batch, q_len);
   if (index_scores_mfma_ok(s, Hi, dI)) {
-    static bool attr = false;
-    if (!attr) {
-      hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(index_scores_mfma_kernel<false>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kILds);
-      if (e != hipSuccess) return (int)e;
-      attr = true;
-    }
+    if (int e = set_max_lds(reinterpret_cast<const void*>(index_scores_mfma_kernel<false>),
+                            (int)kILds))
+      return e;
     hipLaunchKernelGGL((index_scores_mfma_kernel<false>), grid, dim3(256), kILds, st, q_len,
                        s.page, max_seq_len, (const bf16_t*)q_idx, w_idx, (const bf16_t*)icache,
                        num_pages, page_table, max_pages, seq_lens, scores, ld, nullptr);
@@ -694,18 +689,11 @@ int launch_index_scores(const Shape& s, int Hi, int dI, int batch, int q_len, in
   }
   const size_t lds_bytes = index_scores_generic_lds(Hi, dI);
   if (lds_bytes > 64 * 1024) {
-    static bool attr[2] = {false, false};
-    if (!attr[s.dtype]) {
-      hipError_t e = s.dtype == 0
-                         ? hipFuncSetAttribute(
-                               reinterpret_cast<const void*>(index_scores_generic_kernel<float>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)
-                         : hipFuncSetAttribute(
-                               reinterpret_cast<const void*>(index_scores_generic_kernel<bf16_t>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return (int)e;
-      attr[s.dtype] = true;
-    }
+    if (int e = set_max_lds(s.dtype == 0
+                                ? reinterpret_cast<const void*>(index_scores_generic_kernel<float>)
+                                : reinterpret_cast<const void*>(index_scores_generic_kernel<bf16_t>),
+                            160 * 1024))
+      return e;
   }
   const dim3 ggrid((max_seq_len + 255) / 256, batch, q_len);
   if (s.dtype == 0)
@@ -758,13 +746,9 @@ int launch_index_scores_topk(const Shape& s, int Hi, int dI, int batch, int q_le
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint32_t* ws = reinterpret_cast<uint32_t*>(workspace);
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(index_scores_mfma_kernel<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kILds);
-    if (e != hipSuccess) return (int)e;
-    attr = true;
-  }
+  if (int e = set_max_lds(reinterpret_cast<const void*>(index_scores_mfma_kernel<true>),
+                          (int)kILds))
+    return e;
   const dim3 grid((max_seq_len + kIdxTok - 1) / kIdxTok, batch, q_len);
   hipLaunchKernelGGL((index_scores_mfma_kernel<true>), grid, dim3(256), kILds, st, q_len, s.page,
                      max_seq_len, (const bf16_t*)q_idx, w_idx, (const bf16_t*)icache, num_pages,

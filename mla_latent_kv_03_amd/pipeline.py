@@ -26,44 +26,6 @@ def upload(x, dtype, device="cuda"):
     return t.from_numpy(x).to(device=device).to(dtype).contiguous()
 
 
-def tree_depths(parents):
-    """Depth of each drafted token of a tree (0 when its parent is -1, else
-    one more than its parent's); parents must precede their children."""
-    d = []
-    for j, p in enumerate(int(x) for x in parents):
-        if not -1 <= p < j:
-            raise ValueError(f"tree: drafted token {j} has parent {p}")
-        d.append(0 if p < 0 else d[p] + 1)
-    return d
-
-
-def draft_positions(seq_lens, q_len: int, tree_parents=None):
-    """(slot, position) of the q_len drafted tokens of every sequence, flat
-    [B*Q] lists: token j of sequence b is cached at slot L_b - Q + j; its
-    position (query RoPE and cached RoPE key) is that slot for a chain, and
-    L_b - Q + depth(j) for a tree ("Tree Attention Verification")."""
-    slot, pos = [], []
-    for b, L in enumerate(int(x) for x in seq_lens):
-        dep = (list(range(q_len)) if tree_parents is None
-               else tree_depths(tree_parents[b]))
-        for j in range(q_len):
-            slot.append(L - q_len + j)
-            pos.append(L - q_len + dep[j])
-    return slot, pos
-
-
-def token_rope_positions(seq_lens, q_len: int, tree_parents=None):
-    """Position of every cached token of the batch (sequence-major, the order
-    of a setup fill): t for prefix tokens, the draft_positions of the last
-    q_len."""
-    out = []
-    _, dpos = draft_positions(seq_lens, q_len, tree_parents)
-    for b, L in enumerate(int(x) for x in seq_lens):
-        out.extend(range(L - q_len))
-        out.extend(dpos[b * q_len:(b + 1) * q_len])
-    return out
-
-
 class DecodeStep:
     """Device state of one decode step for ``batch`` sequences of ``q_len`` tokens.
 
@@ -83,16 +45,16 @@ class DecodeStep:
         dt = dtype_of(cfg)
         lens = [int(x) for x in seq_lens_host]
         self.max_seq_len = max(lens)
-        # drafted token j of sequence b: cached at slot L_b - Q + j, positioned
-        # there for a chain and at L_b - Q + depth(j) for a tree
-        slot, pos = draft_positions(lens, q_len, tree_parents)
-        self.qpos = t.tensor(pos, dtype=t.int32, device=device)
-        self.slot = t.tensor(slot, dtype=t.int32, device=device)
         self.tree = (None if tree_parents is None else
                      t.tensor([[int(p) for p in row] for row in tree_parents], dtype=t.int32,
                               device=device))
-        self.seq_idx = t.tensor([b for b in range(batch) for _ in range(q_len)], dtype=t.int32,
-                                device=device)
+        # drafted token j of sequence b: cached at slot L_b - Q + j, positioned
+        # there for a chain and at L_b - Q + depth(j) for a tree (derived by the
+        # library from the same tree the decode masks by)
+        self.seq_idx = t.empty(batch * q_len, dtype=t.int32, device=device)
+        self.slot = t.empty(batch * q_len, dtype=t.int32, device=device)
+        self.qpos = t.empty(batch * q_len, dtype=t.int32, device=device)
+        self.set_lengths(t.tensor(lens, dtype=t.int32, device=device))
         self.q_full = t.empty((batch, q_len, H, D), dtype=dt, device=device)
         self.o_part = t.empty((batch, q_len, H, num_splits, dc), dtype=t.float32, device=device)
         self.lse_part = t.empty((batch, q_len, H, num_splits), dtype=t.float32, device=device)
@@ -108,6 +70,13 @@ class DecodeStep:
             # zero once: every selection leaves it zero
             self.topk_ws = t.zeros(B.topk_workspace_bytes(batch, q_len), dtype=t.uint8,
                                    device=device)
+
+    def set_lengths(self, seq_lens, stream=None):
+        """Derive the drafted rows' slots and positions from new lengths
+        (a device tensor [B] int32, each at most the max_seq_len given at
+        construction)."""
+        B.draft_positions(seq_lens, self.q_len, self.max_seq_len, self.tree, self.seq_idx,
+                          self.slot, self.qpos, stream)
 
     def absorb(self, q_nope, q_rope, w_uk, stream=None):
         B.absorb_q(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, stream)
@@ -237,7 +206,7 @@ def fill_cache_q8(cfg: B.Config, cache_q8, page_table, c_all, k_all, seq_idx, po
 def fill_cache(cfg: B.Config, cache, page_table, c_all, k_all, seq_idx, pos, stream=None,
                rows_per_call: int = 1 << 20, rope_pos=None):
     """Write every cached row (setup): rows n go to (seq_idx[n], pos[n]), keys
-    rotated by pos[n] (rope_pos[n] when given: see token_rope_positions)."""
+    rotated by pos[n] (rope_pos[n] when given)."""
     n = int(pos.numel())
     for a in range(0, n, rows_per_call):
         e = min(n, a + rows_per_call)

@@ -13,7 +13,7 @@ import oracle
 import workload
 import mla_latent_kv_03_amd as mla
 from mla_latent_kv_03_amd.pipeline import (DecodeStep, dtype_of, fill_cache, fill_cache_q8,
-                                           fill_index_cache, token_rope_positions, upload)
+                                           fill_index_cache, upload)
 
 NAN_BF16 = 0x7FC1      # quiet NaN with a payload: poison for unused cache slots
 NAN_F32 = 0x7FC00001
@@ -72,13 +72,9 @@ class Case:
         self.pt = upload(inp.page_table, torch.int32)
         self.seq_lens = upload(inp.seq_lens, torch.int32)
         si, pos = tok_index(inp)
-        rope_pos = None
-        if inp.parents is not None:  # drafted tree: keys rotated at prefix + depth
-            rope_pos = upload(np.asarray(token_rope_positions(inp.seq_lens, Q, inp.parents),
-                                         np.int32), torch.int32)
         fill = fill_cache_q8 if self.q8 else fill_cache
         fill(cfg, self.pool, self.pt, upload(inp.c, dt), upload(inp.k_rope, dt),
-             upload(si, torch.int32), upload(pos, torch.int32), rope_pos=rope_pos)
+             upload(si, torch.int32), upload(pos, torch.int32))
         self.q_nope = upload(np.ascontiguousarray(inp.q_nope), dt)
         self.q_rope = upload(np.ascontiguousarray(inp.q_rope), dt)
         self.w_uk = upload(inp.w_uk, dt)
@@ -101,6 +97,10 @@ class Case:
         self.step = DecodeStep(cfg, B, Q, self.S, inp.seq_lens, split_chunk=self.chunk,
                                tree_parents=inp.parents, cache_q8=self.q8,
                                index_topk=wl.index_topk)
+        if inp.parents is not None:
+            # the fill rotated every key at its slot; a drafted tree's rows are
+            # rotated at prefix + depth: the step's own append rewrites them
+            self.step.append(self.c_new, self.k_new, self.pt, self.pool)
         torch.cuda.synchronize()
 
     def run(self, max_seq_len=None, fused=True):

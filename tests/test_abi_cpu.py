@@ -218,25 +218,24 @@ def test_append_at_errors(L):
                                   None) == 1
 
 
-def test_pipeline_tree_positions_agree_with_oracle():
-    import oracle
-    import workload
-    from mla_latent_kv_03_amd.pipeline import draft_positions, token_rope_positions
-    wl = workload.WORKLOADS["tiny_f32"].replace(batch=4, q_len=7, seq_len=None, len_range=(7, 90),
-                                                tree="random")
-    inp = workload.make(wl, 6, with_latents=False)
-    slot, pos = draft_positions(inp.seq_lens, 7, inp.parents)
-    allpos = token_rope_positions(inp.seq_lens, 7, inp.parents)
-    off = 0
-    for b, L in enumerate(inp.seq_lens):
-        kp, qp = oracle.tree_positions(int(L), inp.parents[b])
-        assert pos[7 * b:7 * b + 7] == qp.tolist()
-        assert slot[7 * b:7 * b + 7] == list(range(int(L) - 7, int(L)))
-        assert allpos[off:off + int(L)] == kp.tolist()
-        off += int(L)
-    # a chain: positions are the slots
-    slot, pos = draft_positions(inp.seq_lens, 7)
-    assert slot == pos
+def test_draft_positions_errors(L):
+    # batch, q_len, max_seq_len, seq_lens, tree_parent, seq_idx, slot, pos, stream
+    def call(batch=2, q_len=4, max_len=64, lens=A16, tree=A16, si=A16, sl=A16, pos=A16):
+        return L.mla_draft_positions(batch, q_len, max_len, lens, tree, si, sl, pos, None)
+    assert call(q_len=0) == 2 and call(batch=-1) == 2
+    assert call(q_len=65) == 2                                 # one 64-bit branch mask per query
+    assert call(q_len=65, tree=None, max_len=64) == 5          # q_len above max_seq_len
+    assert call(lens=None) == 1 and call(pos=None) == 1 and call(si=MIS) == 4
+    assert call(tree=MIS) == 4
+    assert call(batch=0, lens=None) == 0                       # nothing to do
+
+
+def test_stream_read_errors(L):
+    assert L.mla_stream_read(A16, 24, A16, 4, None) == 2       # not a multiple of 16
+    assert L.mla_stream_read(A16, 32, A16, 0, None) == 2
+    assert L.mla_stream_read(None, 32, A16, 4, None) == 1
+    assert L.mla_stream_read(MIS, 32, A16, 4, None) == 4
+    assert L.mla_stream_read(None, 0, None, 4, None) == 0      # nothing to read
 
 
 def test_q8_entry_errors(L):

@@ -233,6 +233,26 @@ def test_up_project(dtype):
     assert_close(to64(out), ref, 1e-6 if dtype == "f32" else 2.0 ** -8, "out")
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "v2lite_small", "v2_h128_small"])
+def test_up_project_against_oracle(name):
+    # the oracle's latent output o_lat = sum_t p_t c_t (no absorption), rounded
+    # to the workload dtype, up-projected on the GPU, against the oracle's own
+    # unabsorbed output o = sum_t p_t W_UV c_t
+    wl = SMALL[name]
+    inp = workload.make(wl, 9)
+    ref = oracle.mla_decode_ref(inp)
+    B, Q, H = wl.batch, wl.q_len, wl.heads
+    ol = ref["o_lat"].astype(np.float32).reshape(B * Q, H, wl.kv_rank)
+    if wl.dtype == "bf16":
+        ol = workload.round_bf16(ol)
+    cfg = mla.Config.from_workload(wl)
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    out = torch.empty((B * Q, H, wl.v_dim), dtype=dt, device="cuda")
+    mla.up_project_v(cfg, upload(ol, dt), upload(inp.w_uv, dt), out)
+    torch.cuda.synchronize()
+    assert_close(to64(out), ref["o"].reshape(B * Q, H, wl.v_dim), tau(wl), "out")
+
+
 # ---------------------------------------------------------------- whole step
 @pytest.mark.parametrize("name", list(SMALL))
 def test_end_to_end_small(name):

@@ -146,3 +146,71 @@ def test_q8_invalid_sequence_gives_nan_only_there():
     got = case.results()
     assert np.all(np.isnan(got["lse"][1])) and np.all(np.isnan(got["o"][1]))
     check_against_oracle(case, got, case.oracle(seqs=[0, 2]), seqs=[0, 2])
+
+
+# ---------------------------------------------------------------- row scales
+# The decode feeds fp16 MFMA operands: the query parts and P = p * step. Each
+# is scaled by a power of two per row inside the kernel, so the rows' own
+# scales must not matter. Latents scaled by alpha with the content query
+# scaled by 1/alpha (and the RoPE parts by beta, 1/beta) keep the scores and
+# the softmax of the unit-scale workload while the steps and the query values
+# move across 2^-16 .. 2^16 (powers of two: every value stays bf16-exact).
+SCALED = small("v2lite_32k_q8", batch=2, seq_len=700, num_splits=3)
+
+
+def _scaled_case(alpha, beta, seed=6):
+    inp = workload.make(SCALED, seed)
+    inp.c *= np.float32(alpha)
+    inp.q_nope *= np.float32(1.0 / alpha)
+    inp.k_rope *= np.float32(beta)
+    inp.q_rope *= np.float32(1.0 / beta)
+    return Case(SCALED, inputs=inp)
+
+
+@pytest.mark.parametrize("alpha,beta", [(2.0 ** -14, 2.0 ** -14), (2.0 ** 14, 2.0 ** 14),
+                                        (2.0 ** -16, 2.0 ** 16), (2.0 ** 7, 2.0 ** -7)],
+                         ids=["2^-14", "2^14", "lat2^-16_rope2^16", "lat2^7_rope2^-7"])
+def test_q8_decode_scaled_rows(alpha, beta):
+    case = _scaled_case(alpha, beta)
+    case.run()
+    check_against_oracle(case, case.results(), case.oracle())
+
+
+def test_q8_decode_per_token_scales():
+    # every cached row scaled by its own 2^u, u in [-14, 14] (latent and RoPE
+    # parts separately): the steps of one sequence span 2^28, and the row a
+    # query weights most is rarely the one with the largest step
+    inp = workload.make(SCALED, 7)
+    rng = np.random.default_rng(11)
+    T = inp.c.shape[0]
+    inp.c *= np.exp2(rng.integers(-14, 15, (T, 1))).astype(np.float32)
+    inp.k_rope *= np.exp2(rng.integers(-14, 15, (T, 1))).astype(np.float32)
+    inp.q_nope *= np.float32(2.0 ** -12)
+    inp.q_rope *= np.float32(2.0 ** -12)
+    case = Case(SCALED, inputs=inp)
+    case.run()
+    check_against_oracle(case, case.results(), case.oracle())
+
+
+def test_q8_decode_constant_and_narrow_parts():
+    # a tenth of the rows with a constant latent part (step 0), a tenth with a
+    # zero RoPE key (a constant rotated part), a tenth with a latent part
+    # 3 + 2^-6 N(0, 1) (a few levels of a narrow range far from zero)
+    inp = workload.make(SCALED, 8)
+    rng = np.random.default_rng(12)
+    T = inp.c.shape[0]
+    kind = rng.integers(0, 10, T)
+    const = kind == 0
+    inp.c[const] = workload.round_bf16(rng.standard_normal((int(const.sum()), 1))
+                                       .astype(np.float32)) * np.ones((1, SCALED.kv_rank),
+                                                                      np.float32)
+    inp.k_rope[kind == 1] = 0.0
+    narrow = kind == 2
+    inp.c[narrow] = workload.round_bf16(
+        (3.0 + rng.standard_normal((int(narrow.sum()), SCALED.kv_rank)) / 64.0).astype(np.float32))
+    # the newest row of each sequence (the one every step re-appends) constant
+    for b in range(SCALED.batch):
+        inp.c[int(inp.offsets[b + 1]) - 1] = np.float32(-0.75)
+    case = Case(SCALED, inputs=inp)
+    case.run()
+    check_against_oracle(case, case.results(), case.oracle())

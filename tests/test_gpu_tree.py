@@ -159,3 +159,63 @@ def test_append_at_slot_and_rope_position():
     mask[[oracle.cache_slot(inp.page_table, int(s), int(p), wl.page_size)
           for s, p in zip(seq, pos)]] = False
     assert np.all(np.isnan(flat_g[mask]))
+
+
+# ---------------------------------------------------------------- positions from the tree
+def test_draft_positions_match_oracle():
+    Q = 7
+    wl = small("tiny_f32", batch=7, q_len=Q, seq_len=None, len_range=(Q, 90), tree="random")
+    inp = workload.make(wl, 6, with_latents=False)
+    lens = inp.seq_lens.copy()
+    par = inp.parents.copy()
+    lens[4] = Q - 2        # shorter than the drafts: invalid
+    par[5, 2] = 2          # a drafted token that continues itself: invalid tree
+    lens[6] = 91           # beyond max_seq_len: invalid
+    B = wl.batch
+    out = [torch.full((B * Q,), 99, dtype=torch.int32, device="cuda") for _ in range(3)]
+    d_lens = upload(lens, torch.int32)
+    mla.draft_positions(d_lens, Q, 90, upload(par, torch.int32), *out)
+    torch.cuda.synchronize()
+    si, slot, pos = (x.cpu().numpy().reshape(B, Q) for x in out)
+    assert np.array_equal(si, np.repeat(np.arange(B), Q).reshape(B, Q))
+    for b in range(B):
+        L = int(lens[b])
+        if b in (4, 5, 6):
+            assert np.all(slot[b] == -1) and np.all(pos[b] == -1), b
+            continue
+        kp, qp = oracle.tree_positions(L, par[b])
+        assert np.array_equal(pos[b], qp) and np.array_equal(kp[L - Q:], qp)
+        assert np.array_equal(slot[b], L - Q + np.arange(Q))
+    # the chain: positions are the slots
+    mla.draft_positions(d_lens, Q, 90, None, *out)
+    torch.cuda.synchronize()
+    si, slot, pos = (x.cpu().numpy().reshape(B, Q) for x in out)
+    for b in range(B):
+        want = (np.full(Q, -1) if b in (4, 6) else int(lens[b]) - Q + np.arange(Q))
+        assert np.array_equal(slot[b], want) and np.array_equal(pos[b], want), b
+
+
+def test_inconsistent_tree_reaches_neither_cache_nor_outputs():
+    # the step's positions come from the tree it verifies: a malformed tree
+    # gets no slots, so its drafted rows are never written, and the decode
+    # turns that sequence to NaN; the other sequences are untouched
+    Q = 6
+    wl = small("v2lite_paged_varlen", batch=3, q_len=Q, len_range=(50, 400), num_splits=2,
+               tree="random")
+    inp = workload.make(wl, 10)
+    inp.parents[1, 3] = 4                     # a parent after its child
+    case = Case(wl, inputs=inp)
+    k_new = case.k_new.clone()
+    c_new = case.c_new.clone()
+    c_new[Q:2 * Q] = 7.0                      # sequence 1's drafted rows: a sentinel
+    case.c_new = c_new
+    case.run()
+    flat = case.pool.float().cpu().numpy().reshape(-1, wl.dim)
+    L1 = int(inp.seq_lens[1])
+    for i in range(Q):
+        slot = oracle.cache_slot(inp.page_table, 1, L1 - Q + i, wl.page_size)
+        assert not np.any(flat[slot, :wl.kv_rank] == 7.0)
+    got = case.results()
+    assert np.all(np.isnan(got["lse"][1])) and np.all(np.isnan(got["o"][1]))
+    check_against_oracle(case, got, case.oracle(seqs=[0, 2]), seqs=[0, 2])
+    assert torch.equal(k_new, case.k_new)

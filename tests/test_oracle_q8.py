@@ -189,3 +189,113 @@ def test_planted_q8_mistakes_are_caught(monkeypatch, target, mutant):
     monkeypatch.setattr(mla_ref, target, mutant)
     monkeypatch.setattr(oracle, target, mutant)
     assert not _battery(), f"planted mistake in {target} went unnoticed"
+
+
+# ---------------------------------------------------------------- drafted trees
+# A drafted token of a tree is cached after its siblings but positioned one past
+# its parent ("The Architecture of Memory", "Tree Attention Verification"), and
+# verification must give what decoding its branch token by token would
+# ("Speculative Decoding: Amortizing the Memory Fetch"). For the 8-bit cache
+# that fixes where a drafted RoPE key is rotated before it is coded: at prefix
+# + depth, where the chain of its branch would put it.
+def _q8_tree_inputs(seed, L=45, Q=6, parents=None):
+    wl = workload.WORKLOADS["tiny_f32"].replace(q_len=Q, seq_len=L, tree="random")
+    inp = workload.make(wl, seed)
+    if parents is not None:
+        inp.parents = np.asarray([parents], np.int32)
+    return inp
+
+
+def _branch(parents, j):
+    path = []
+    while j != -1:
+        path.append(j)
+        j = int(parents[j])
+    return path[::-1]
+
+
+def _branch_as_chain(inp, j):
+    """The same sequence cut to its prefix plus query j's branch, decoded as a
+    single-query chain."""
+    import types
+    wl = inp.wl
+    c, kr = inp.seq(0)
+    L, Q = c.shape[0], wl.q_len
+    rows = list(range(L - Q)) + [L - Q + i for i in _branch(inp.parents[0], j)]
+    cw = wl.replace(q_len=1, seq_len=len(rows), tree=None)
+    return types.SimpleNamespace(
+        wl=cw, seq=lambda b: (c[rows], kr[rows]), parents=None, w_uk=inp.w_uk, w_uv=inp.w_uv,
+        q_nope=inp.q_nope[:, j:j + 1], q_rope=inp.q_rope[:, j:j + 1])
+
+
+def _q8_branches_ok(inp, tol=1e-12):
+    ref = oracle.mla_decode_ref_q8(inp)
+    ok = True
+    for j in range(inp.wl.q_len):
+        ch = oracle.mla_decode_ref_q8(_branch_as_chain(inp, j))
+        for key in ("o", "o_lat"):
+            a, b = ref[key][0, j], ch[key][0, 0]
+            ok &= bool(np.max(np.abs(a - b)) <= tol * np.max(np.abs(b)))
+        ok &= bool(abs(ref["lse"][0, j] - ch["lse"][0, 0]).max() <= tol * abs(ch["lse"]).max())
+    return ok
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_q8_every_branch_equals_its_chain(seed):
+    inp = _q8_tree_inputs(40 + seed)
+    par = inp.parents[0]
+    # the random tree must hold a token positioned before its slot, or the
+    # pin would not tell slots from positions
+    assert np.any(oracle.tree_depths(par) < np.arange(len(par)))
+    assert _q8_branches_ok(inp)
+
+
+def test_q8_tree_codes_keys_rotated_at_prefix_plus_depth():
+    # the coded RoPE part of drafted token i is that of its raw key rotated at
+    # L - Q + depth(i): equal to the chain-coded row of that position
+    par = [-1, 0, 0, 1, -1, 4]
+    inp = _q8_tree_inputs(5, parents=par)
+    L, Q = 45, 6
+    rows = oracle.mla_decode_ref_q8(inp)["rows"][0]
+    c, kr = inp.seq(0)
+    d = oracle.tree_depths(par)
+    for i in range(Q):
+        k = oracle.rotated_keys_f32(kr[L - Q + i:L - Q + i + 1], [L - Q + d[i]])
+        r1, _, _ = oracle.quantize_cache_rows(c[L - Q + i:L - Q + i + 1], k)
+        assert np.array_equal(rows["codes"][L - Q + i], r1["codes"][0])
+        assert rows["rope_min"][L - Q + i] == r1["rope_min"][0]
+        assert rows["rope_step"][L - Q + i] == r1["rope_step"][0]
+
+
+def _q8_tree_battery():
+    ok = True
+    for seed in (60, 61):
+        ok &= _q8_branches_ok(_q8_tree_inputs(seed))
+    return bool(ok)
+
+
+def _mut_keys_at_slots(seq_len, parents):
+    # drafted keys rotated at their cache slot instead of prefix + depth
+    _, qp = mla_ref._orig_positions(seq_len, parents)
+    return np.arange(seq_len), qp
+
+
+def _mut_queries_at_slots(seq_len, parents):
+    kp, _ = mla_ref._orig_positions(seq_len, parents)
+    return kp, seq_len - len(parents) + np.arange(len(parents))
+
+
+def _mut_depth_plus_one(seq_len, parents):
+    kp, qp = mla_ref._orig_positions(seq_len, parents)
+    kp = kp.copy()
+    kp[seq_len - len(parents):] += 1
+    return kp, qp
+
+
+@pytest.mark.parametrize("mutant", [_mut_keys_at_slots, _mut_queries_at_slots,
+                                    _mut_depth_plus_one])
+def test_planted_q8_tree_mistakes_are_caught(monkeypatch, mutant):
+    assert _q8_tree_battery(), "clean oracle must pass the battery"
+    monkeypatch.setattr(mla_ref, "_orig_positions", mla_ref.tree_positions, raising=False)
+    monkeypatch.setattr(mla_ref, "tree_positions", mutant)
+    assert not _q8_tree_battery(), "planted tree-position mistake went unnoticed"
