@@ -168,8 +168,10 @@ def _scaled_case(alpha, beta, seed=6):
 
 
 @pytest.mark.parametrize("alpha,beta", [(2.0 ** -14, 2.0 ** -14), (2.0 ** 14, 2.0 ** 14),
-                                        (2.0 ** -16, 2.0 ** 16), (2.0 ** 7, 2.0 ** -7)],
-                         ids=["2^-14", "2^14", "lat2^-16_rope2^16", "lat2^7_rope2^-7"])
+                                        (2.0 ** -16, 2.0 ** 16), (2.0 ** 7, 2.0 ** -7),
+                                        (2.0 ** 22, 2.0 ** -20)],
+                         ids=["2^-14", "2^14", "lat2^-16_rope2^16", "lat2^7_rope2^-7",
+                              "lat2^22_rope2^-20"])
 def test_q8_decode_scaled_rows(alpha, beta):
     case = _scaled_case(alpha, beta)
     case.run()
