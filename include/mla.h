@@ -399,6 +399,26 @@ mla_status_t mla_index_scores_topk(const mla_config_t* cfg, int32_t index_heads,
                                    int32_t topk, void* workspace, int32_t* indices,
                                    int32_t* counts, void* stream);
 
+/* mla_index_scores_topk for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid it): the
+ * same arguments without `workspace`, the same scores, indices and counts
+ * bit for bit. The workspace lives in a device array inside the library,
+ * one per GPU, held until the process ends, sized for batch * q_len <=
+ * MLA_TOPK_NOALLOC_MAX_QUERIES queries (MLA_ERR_CAPACITY beyond). The first
+ * call on a device clears it with a fill kernel on `stream` (as does the
+ * call after a failed launch); every selection leaves it zero. All calls on
+ * one GPU share that array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. */
+enum { MLA_TOPK_NOALLOC_MAX_QUERIES = 256 };
+mla_status_t mla_index_scores_topk_noalloc(const mla_config_t* cfg, int32_t index_heads,
+                                           int32_t index_dim, int32_t batch, int32_t q_len,
+                                           int32_t max_seq_len, const void* q_idx,
+                                           const float* w_idx, const void* index_cache,
+                                           int64_t num_pages, const int32_t* page_table,
+                                           int32_t max_pages, const int32_t* seq_lens,
+                                           float* scores, int32_t ld_scores, int32_t topk,
+                                           int32_t* indices, int32_t* counts, void* stream);
+
 /* List entries per partition of mla_decode_sparse: ceil(topk / num_splits)
  * rounded up to a multiple of 32; 0 for invalid arguments. */
 int32_t mla_sparse_chunk(int32_t topk, int32_t num_splits);

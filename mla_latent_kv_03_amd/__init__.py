@@ -63,4 +63,6 @@ from ._binding import (  # noqa: F401
     decode_sparse,
     draft_positions,
     stream_read,
+    index_scores_topk_noalloc,
+    TOPK_NOALLOC_MAX_QUERIES,
 )

@@ -135,6 +135,9 @@ def lib() -> ctypes.CDLL:
         "mla_decode_sparse": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32, VP,
                                              VP, VP, FP, FP, VP]),
         "mla_draft_positions": (ctypes.c_int, [I32, I32, I32, VP, VP, VP, VP, VP, VP]),
+        "mla_index_scores_topk_noalloc": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, FP, VP,
+                                                         I64, VP, I32, VP, FP, I32, I32, VP, VP,
+                                                         VP]),
         "mla_stream_read": (ctypes.c_int, [VP, ctypes.c_size_t, VP, I32, VP]),
     }
     for name, (res, args) in sig.items():
@@ -516,6 +519,37 @@ def index_scores_topk(cfg: Config, q_idx, w_idx, index_cache, page_table, seq_le
                                     _need(indices, "indices", t.int32, B * Q * K),
                                     _need(counts, "counts", t.int32, B * Q), _stream(stream)),
         "mla_index_scores_topk")
+
+
+TOPK_NOALLOC_MAX_QUERIES = 256  # MLA_TOPK_NOALLOC_MAX_QUERIES
+
+
+def index_scores_topk_noalloc(cfg: Config, q_idx, w_idx, index_cache, page_table, seq_lens,
+                              scores, max_seq_len: int, indices, counts, stream=None):
+    """index_scores_topk with the workspace held inside the library (no
+    device allocation by the call; batch * q_len <= TOPK_NOALLOC_MAX_QUERIES).
+    Calls that overlap on one GPU race on that workspace."""
+    t = _torch()
+    if q_idx.dim() != 4 or scores.dim() != 3 or indices.dim() != 3:
+        raise ValueError("q_idx: expected [batch][q_len][heads][dim]; scores [batch][q_len][ld]; "
+                         "indices [batch][q_len][topk]")
+    B, Q, Hi, dI = (int(x) for x in q_idx.shape)
+    num_pages, dI2 = _index_cache_dims(cfg, index_cache)
+    if dI2 != dI:
+        raise ValueError("index_cache width does not match q_idx")
+    max_pages = int(page_table.shape[1])
+    ld = int(scores.shape[2])
+    K = int(indices.shape[2])
+    dt = _elem_dtype(cfg)
+    _ck(lib().mla_index_scores_topk_noalloc(
+        cfg.cptr(), Hi, dI, B, Q, int(max_seq_len), _need(q_idx, "q_idx", dt, B * Q * Hi * dI),
+        _need(w_idx, "w_idx", t.float32, B * Q * Hi),
+        _need(index_cache, "index_cache", dt, index_cache.numel()), num_pages,
+        _need(page_table, "page_table", t.int32, B * max_pages), max_pages,
+        _need(seq_lens, "seq_lens", t.int32, B), _need(scores, "scores", t.float32, B * Q * ld),
+        ld, K, _need(indices, "indices", t.int32, B * Q * K),
+        _need(counts, "counts", t.int32, B * Q), _stream(stream)),
+        "mla_index_scores_topk_noalloc")
 
 
 def topk_workspace_bytes(batch: int, q_len: int) -> int:

@@ -561,6 +561,44 @@ mla_status_t mla_index_scores_topk(const mla_config_t* cfg, int32_t index_heads,
       stream));
 }
 
+mla_status_t mla_index_scores_topk_noalloc(const mla_config_t* cfg, int32_t index_heads,
+                                           int32_t index_dim, int32_t batch, int32_t q_len,
+                                           int32_t max_seq_len, const void* q_idx,
+                                           const float* w_idx, const void* index_cache,
+                                           int64_t num_pages, const int32_t* page_table,
+                                           int32_t max_pages, const int32_t* seq_lens,
+                                           float* scores, int32_t ld_scores, int32_t topk,
+                                           int32_t* indices, int32_t* counts, void* stream) {
+  static_assert(MLA_TOPK_NOALLOC_MAX_QUERIES == mla::kTopkNoallocMaxQueries,
+                "the header states the library's limit");
+  mla_status_t st = check_index_shape(cfg, index_heads, index_dim);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(batch >= 0 && q_len >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(q_len <= 65535, MLA_ERR_SHAPE);
+  MLA_REQUIRE(topk >= 1 && topk <= kMaxTopk, MLA_ERR_SHAPE);
+  MLA_REQUIRE((int64_t)batch * q_len <= MLA_TOPK_NOALLOC_MAX_QUERIES, MLA_ERR_CAPACITY);
+  MLA_REQUIRE(max_seq_len >= q_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size >= (int64_t)max_seq_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE(ld_scores >= max_seq_len, MLA_ERR_SHAPE);
+  mla::Shape sh = shape_of(cfg);
+  if (!mla::index_scores_mfma_ok(sh, index_heads, index_dim))
+    MLA_REQUIRE(mla::index_scores_generic_lds(index_heads, index_dim) <= 160 * 1024,
+                MLA_ERR_UNSUPPORTED);
+  if (batch == 0) return MLA_OK;
+  MLA_CHECK_PTR(q_idx);
+  MLA_CHECK_PTR(w_idx);
+  MLA_CHECK_PTR(index_cache);
+  MLA_CHECK_PTR(page_table);
+  MLA_CHECK_PTR(seq_lens);
+  MLA_CHECK_PTR(scores);
+  MLA_CHECK_PTR(indices);
+  MLA_CHECK_PTR(counts);
+  return hip_status(mla::launch_index_scores_topk_noalloc(
+      sh, index_heads, index_dim, batch, q_len, max_seq_len, q_idx, w_idx, index_cache,
+      num_pages, page_table, max_pages, seq_lens, scores, ld_scores, topk, indices, counts,
+      stream));
+}
+
 int32_t mla_sparse_chunk(int32_t topk, int32_t num_splits) {
   if (topk < 1 || topk > kMaxTopk || num_splits < 1 || num_splits > kMaxSplits) return 0;
   return sparse_chunk(topk, num_splits);

@@ -122,6 +122,18 @@ int launch_index_scores_topk(const Shape& s, int Hi, int dI, int batch, int q_le
                              int max_pages, const int32_t* seq_lens, float* scores, int ld,
                              int topk, void* workspace, int32_t* indices, int32_t* counts,
                              void* stream);
+// launch_index_scores_topk with the workspace in the library's own device
+// array (queries batch * q_len <= kTopkNoallocMaxQueries; checked by the
+// caller): allocates nothing. The array is cleared by a fill kernel on the
+// first call on each device (and after a failed launch); every selection
+// leaves the rows it used zero again.
+constexpr int kTopkNoallocMaxQueries = 256;
+int launch_index_scores_topk_noalloc(const Shape& s, int Hi, int dI, int batch, int q_len,
+                                     int max_seq_len, const void* q_idx, const float* w_idx,
+                                     const void* icache, int64_t num_pages,
+                                     const int32_t* page_table, int max_pages,
+                                     const int32_t* seq_lens, float* scores, int ld, int topk,
+                                     int32_t* indices, int32_t* counts, void* stream);
 // decode over the selected tokens: partition s of query (b, j) covers list
 // entries [s * chunk, min(count, (s + 1) * chunk)); kind 1 = the bf16 MFMA
 // kernel (16 rows per block, H % 16 == 0, chunk a multiple of 32 up to

@@ -11,6 +11,9 @@
 // Selection: of the tokens query j sees (t <= L - q_len + j), the topk with
 // the highest scores, equal scores going to the smaller token index, listed
 // in increasing token order.
+#include <map>
+#include <mutex>
+
 #include "mla_common.h"
 #include "mla_decode_common.h"
 #include "mla_launch.h"
@@ -772,5 +775,77 @@ int launch_topk_select(int batch, int q_len, int max_seq_len, int topk, const fl
   return (int)hipGetLastError();
 }
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// The top-k workspace of callers that cannot allocate: a file-scope device
+// array with the rows of up to kTopkNoallocMaxQueries queries (4,198,400
+// bytes; each device holds its own copy for the life of the process). Host
+// code never passes the array's name to a kernel: that name is a host-side
+// stand-in. The device address comes from hipGetSymbolAddress, once per
+// device with that device current, and is kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint32_t scratch[(size_t)kTopkNoallocMaxQueries * kTkWsRow];
+
+namespace {
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+struct ScratchState {
+  uint32_t* ptr = nullptr;  // device address of `scratch` on this device
+  bool clean = false;       // every row zero, as the selection leaves it
+};
+std::mutex g_scratch_mu;
+std::map<int, ScratchState> g_scratch;
+
+}  // namespace
+
+int launch_index_scores_topk_noalloc(const Shape& s, int Hi, int dI, int batch, int q_len,
+                                     int max_seq_len, const void* q_idx, const float* w_idx,
+                                     const void* icache, int64_t num_pages,
+                                     const int32_t* page_table, int max_pages,
+                                     const int32_t* seq_lens, float* scores, int ld, int topk,
+                                     int32_t* indices, int32_t* counts, void* stream) {
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return (int)he;
+  uint32_t* ws = nullptr;
+  bool clear = false;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchState& d = g_scratch[dev];
+    if (!d.ptr) {
+      void* p = nullptr;
+      he = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (he != hipSuccess) return (int)he;
+      d.ptr = reinterpret_cast<uint32_t*>(p);
+    }
+    ws = d.ptr;
+    clear = !d.clean;
+    d.clean = true;
+  }
+  auto mark_dirty = [&]() {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    g_scratch[dev].clean = false;
+  };
+  if (clear) {
+    const size_t n = (size_t)kTopkNoallocMaxQueries * kTkWsRow;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), ws, n);
+    const int e = (int)hipGetLastError();
+    if (e != 0) {
+      mark_dirty();
+      return e;
+    }
+  }
+  const int e = launch_index_scores_topk(s, Hi, dI, batch, q_len, max_seq_len, q_idx, w_idx,
+                                         icache, num_pages, page_table, max_pages, seq_lens,
+                                         scores, ld, topk, ws, indices, counts, stream);
+  if (e != 0) mark_dirty();
+  return e;
+}
 
 }  // namespace mla
