@@ -218,14 +218,15 @@ def sparse_selection(inp, seqs):
 
 
 def stream_read_rate(torch, mla, stream, nbytes=4 << 30, reps=10):
-    """GB/s of a plain coalesced read of a 4 GiB buffer (16-byte non-temporal
-    loads, mla_stream_read): what a stream with no arithmetic reaches on this
-    device, for context beside the decode kernel's fraction of the 8 TB/s
-    peak. Best over a few grid sizes; HIP events on the launch stream."""
+    """GB/s of a plain coalesced read of a 4 GiB buffer (each block one
+    contiguous chunk, 16-byte non-temporal loads, mla_stream_read): what a
+    stream with no arithmetic reaches on this device, for context beside the
+    decode kernel's fraction of the 8 TB/s peak. Best over a few grid sizes;
+    HIP events on the launch stream."""
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
     buf.fill_(1)
     best = None
-    for blocks in (1024, 2048, 4096, 8192):
+    for blocks in (512, 1024, 2048, 4096):
         sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
         mla.stream_read(buf, sink)
         torch.cuda.synchronize()
@@ -241,7 +242,8 @@ def stream_read_rate(torch, mla, stream, nbytes=4 << 30, reps=10):
     del buf
     return {"gbs": round(best[0], 1), "pct_of_peak": round(100 * best[0] / HBM_PEAK_GBS, 2),
             "bytes": nbytes, "blocks": best[1], "threads_per_block": 256,
-            "kernel": "stream_read_kernel (16-byte non-temporal loads)"}
+            "kernel": "stream_read_kernel (one contiguous chunk per block, 16-byte non-temporal "
+                      "loads)"}
 
 
 def main():

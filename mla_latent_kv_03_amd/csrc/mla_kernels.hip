@@ -75,24 +75,26 @@ int launch_draft_positions(int batch, int q_len, int max_seq_len, const int32_t*
 }
 
 // ---------------------------------------------------------------------------
-// Streaming read for context: grid-stride 16-byte non-temporal loads, XOR of
-// everything a block read into one word (so no load can be dropped).
+// Streaming read for context: each block reads one contiguous chunk with
+// 16-byte non-temporal loads, four per thread in flight, and XORs everything
+// it read into one word (so no load can be dropped).
 // ---------------------------------------------------------------------------
 typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_nt* __restrict__ src,
                                                           size_t n16, uint32_t* __restrict__ sink) {
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t beg = (size_t)blockIdx.x * per;
+  const size_t end = beg + per < n16 ? beg + per : n16;
   u32x4_nt x = {0u, 0u, 0u, 0u};
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4_nt a = __builtin_nontemporal_load(src + i);
-    const u32x4_nt b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4_nt c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4_nt d = __builtin_nontemporal_load(src + i + 3 * stride);
-    x ^= a ^ b ^ c ^ d;
+  for (size_t i = beg + threadIdx.x; i < end; i += 4 * 256) {
+    u32x4_nt v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = i + 256 * u < end ? __builtin_nontemporal_load(src + i + 256 * u) : u32x4_nt{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x ^= v[u];
   }
-  for (; i < n16; i += stride) x ^= __builtin_nontemporal_load(src + i);
   uint32_t w = x.x ^ x.y ^ x.z ^ x.w;
   for (int off = 32; off > 0; off >>= 1) w ^= __shfl_xor(w, off, 64);
   __shared__ uint32_t red[4];
