@@ -32,6 +32,11 @@ from .mla_ref import (  # noqa: F401
     rotated_keys_f32,
     attend_sequence_rotated,
     mla_decode_ref_q8,
+    Q4_LEVELS,
+    quantize_q4,
+    pack_q4,
+    unpack_q4,
+    mla_decode_ref_q4,
     indexer_scores,
     topk_tokens,
     dsa_selection,

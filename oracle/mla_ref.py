@@ -478,12 +478,52 @@ def dequantize_q8(codes, mn, step):
     return F64(mn) + np.asarray(codes, F64) * F64(step)
 
 
-def quantize_cache_rows(c, k_rope_rotated_f32):
-    """Quantize cached rows [c ; k^R] per token, the latent part and the RoPE
-    part each on its own range. Inputs float32 [T][d_c], [T][d_r] (the RoPE
-    keys already rotated and in float32). Returns dict(codes uint8 [T][D],
-    lat_min, lat_step, rope_min, rope_step float32 [T]) and the dequantized
-    rows float64 (c_hat [T][d_c], k_hat [T][d_r])."""
+# --------------------------------------------------------------------------
+# 4-bit latent cache: the same per-row coding with 16 levels
+# ("KV Cache Optimization: Scaling to Million-Token Contexts", technique 3,
+# whose listing defaults to 4 bits, and its comparison table: INT4, 4x)
+# --------------------------------------------------------------------------
+Q4_LEVELS = 15  # codes 0 .. 15
+
+
+def quantize_q4(x):
+    """Asymmetric 4-bit codes of one row part between its min and max: step =
+    (max - min) / 15, code = the distance from the minimum in steps rounded to
+    the nearest integer (ties to even), in float32; a constant part has step
+    0 and codes 0. Returns (codes uint8 [n] in 0 .. 15, minimum, step)."""
+    x = np.asarray(x, dtype=np.float32)
+    mn, mx = np.float32(x.min()), np.float32(x.max())
+    step = np.float32((mx - mn) / np.float32(Q4_LEVELS))
+    if step == 0:
+        return np.zeros(x.shape, dtype=np.uint8), mn, step
+    codes = np.rint((x - mn) / step)
+    return np.clip(codes, 0, Q4_LEVELS).astype(np.uint8), mn, step
+
+
+def pack_q4(codes):
+    """Two 4-bit codes per byte: column 2i in the low nibble of byte i and
+    column 2i + 1 in its high nibble (the layout of a 4-bit cache row)."""
+    codes = np.asarray(codes, np.uint8)
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_q4(packed):
+    """Inverse of pack_q4: the 4-bit codes of each byte, low nibble first."""
+    packed = np.asarray(packed, np.uint8)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), np.uint8)
+    out[..., 0::2] = packed & 0x0F
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def quantize_cache_rows(c, k_rope_rotated_f32, bits: int = 8):
+    """Quantize cached rows [c ; k^R] per token in ``bits`` (8 or 4) bits, the
+    latent part and the RoPE part each on its own range. Inputs float32
+    [T][d_c], [T][d_r] (the RoPE keys already rotated and in float32). Returns
+    dict(codes uint8 [T][D] (one code per entry, unpacked), lat_min, lat_step,
+    rope_min, rope_step float32 [T]) and the dequantized rows float64
+    (c_hat [T][d_c], k_hat [T][d_r])."""
+    quant = {8: quantize_q8, 4: quantize_q4}[bits]
     c = np.asarray(c, np.float32)
     k = np.asarray(k_rope_rotated_f32, np.float32)
     T, dc = c.shape
@@ -493,10 +533,10 @@ def quantize_cache_rows(c, k_rope_rotated_f32):
     c_hat = np.empty((T, dc), F64)
     k_hat = np.empty((T, dr), F64)
     for t in range(T):
-        q, mn, st = quantize_q8(c[t])
+        q, mn, st = quant(c[t])
         codes[t, :dc], meta["lat_min"][t], meta["lat_step"][t] = q, mn, st
         c_hat[t] = dequantize_q8(q, mn, st)
-        q, mn, st = quantize_q8(k[t])
+        q, mn, st = quant(k[t])
         codes[t, dc:], meta["rope_min"][t], meta["rope_step"][t] = q, mn, st
         k_hat[t] = dequantize_q8(q, mn, st)
     return dict(codes=codes, **meta), c_hat, k_hat
@@ -544,12 +584,13 @@ def attend_sequence_rotated(c, k_rotated, q_nope, q_rope, w_uk, w_uv, scale,
 
 
 def mla_decode_ref_q8(inputs, heads: Optional[Sequence[int]] = None,
-                      seqs: Optional[Sequence[int]] = None):
-    """The oracle over an 8-bit latent cache: every cached row of ``inputs`` is
-    quantized as the cache stores it (quantize_cache_rows, RoPE keys rotated
-    at their positions first) and the decode attends over the dequantized
-    rows. Returns the dict of mla_decode_ref plus "codes" per selected
-    sequence for the append checks."""
+                      seqs: Optional[Sequence[int]] = None, bits: int = 8):
+    """The oracle over an 8-bit (or, with bits=4, 4-bit) latent cache: every
+    cached row of ``inputs`` is quantized as the cache stores it
+    (quantize_cache_rows, RoPE keys rotated at their positions first) and the
+    decode attends over the dequantized rows. Returns the dict of
+    mla_decode_ref plus "rows" (codes and ranges) per selected sequence for
+    the append checks."""
     wl = inputs.wl
     hs = list(range(wl.heads)) if heads is None else list(heads)
     bs = list(range(wl.batch)) if seqs is None else list(seqs)
@@ -565,12 +606,19 @@ def mla_decode_ref_q8(inputs, heads: Optional[Sequence[int]] = None,
         L = c.shape[0]
         par = None if getattr(inputs, "parents", None) is None else inputs.parents[b]
         kpos = np.arange(L) if par is None else tree_positions(L, par)[0]
-        qrows, c_hat, k_hat = quantize_cache_rows(c, rotated_keys_f32(kr, kpos, wl.rope_base))
+        qrows, c_hat, k_hat = quantize_cache_rows(c, rotated_keys_f32(kr, kpos, wl.rope_base),
+                                                  bits)
         rows[b] = qrows
         o[b], o_lat[b], lse[b] = attend_sequence_rotated(
             c_hat, k_hat, inputs.q_nope[b][:, hs], inputs.q_rope[b][:, hs], w_uk, w_uv,
             wl.softmax_scale, wl.rope_base, parents=par)
     return {"o": o, "o_lat": o_lat, "lse": lse, "rows": rows}
+
+
+def mla_decode_ref_q4(inputs, heads: Optional[Sequence[int]] = None,
+                      seqs: Optional[Sequence[int]] = None):
+    """The oracle over a 4-bit latent cache (mla_decode_ref_q8 with 16 levels)."""
+    return mla_decode_ref_q8(inputs, heads=heads, seqs=seqs, bits=4)
 
 
 # --------------------------------------------------------------------------

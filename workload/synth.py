@@ -56,7 +56,8 @@ class Workload:
     # random tree per sequence (parent of token j uniform in [-1, j-1])
     tree: object = None
     # cache format: "native" = rows in the workload dtype; "q8" = 8-bit codes
-    # per row part plus (min, step) pairs, D + 16 bytes per token
+    # per row part plus (min, step) pairs, D + 16 bytes per token; "q4" =
+    # 4-bit codes, two per byte, plus the same pairs, D / 2 + 16 bytes
     cache: str = "native"
     # sparse read: > 0 = each query reads only the index_topk cached tokens an
     # indexer of index_heads heads x index_dim rates highest
@@ -86,7 +87,11 @@ class Workload:
     @property
     def cache_row_bytes(self) -> int:
         """Bytes one cached token occupies (per layer)."""
-        return self.dim + 16 if self.cache == "q8" else self.dim * self.elem_bytes
+        if self.cache == "q8":
+            return self.dim + 16
+        if self.cache == "q4":
+            return self.dim // 2 + 16
+        return self.dim * self.elem_bytes
 
     @property
     def max_seq_len(self) -> int:
@@ -126,6 +131,10 @@ WORKLOADS: Dict[str, Workload] = {
                  nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=32,
                  cache="q8",
                  description="DeepSeek-V2-Lite layer shape, B=8, L=32768, 8-bit latent cache"),
+        Workload("v2lite_32k_q4", batch=8, q_len=1, heads=16, kv_rank=512, rope_dim=64,
+                 nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=32,
+                 cache="q4",
+                 description="DeepSeek-V2-Lite layer shape, B=8, L=32768, 4-bit latent cache"),
         Workload("v2lite_32k_dsa", batch=8, q_len=1, heads=16, kv_rank=512, rope_dim=64,
                  nope_dim=128, v_dim=128, dtype="bf16", seq_len=32768, num_splits=16,
                  index_topk=2048,
