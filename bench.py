@@ -38,7 +38,7 @@ METRIC = "MLA decode latent-cache GB/s (% of HBM peak) + decode tokens/s, V2-Lit
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 LAYERS = {"v2lite_32k": 27, "v2lite_paged_varlen": 27, "v2_h128_8k": 4, "v2_h128_1m_q4": 2,
-          "v2lite_32k_tree8": 27, "v2lite_32k_q8": 27, "v2lite_32k_dsa": 27,
+          "v2lite_32k_tree8": 27, "v2lite_32k_q8": 27, "v2lite_32k_q4": 27, "v2lite_32k_dsa": 27,
           "v2lite_prefill_32k_c4k": 2, "tiny_f32": 4}
 PREFILL_MIN_Q = 64             # q_len from which a step is a prefill chunk
 CSRC = os.path.join(ROOT, "mla_latent_kv_03_amd", "csrc")
@@ -47,7 +47,8 @@ DECODE_KERNELS = {
     "mfma_rows16": ("decode_rows16_kernel", ["mla_decode_common.h", "mla_decode_rows16.hip"]),
     "mfma_ws": ("decode_ws_kernel", ["mla_decode_common.h", "mla_decode_ws.hip"]),
     "generic": ("decode_generic_kernel", ["mla_kernels.hip"]),
-    "mfma_q8": ("decode_q8_kernel", ["mla_decode_common.h", "mla_q8.hip"]),
+    "mfma_q8": ("decode_q8_kernel<8>", ["mla_decode_common.h", "mla_q8.hip"]),
+    "mfma_q4": ("decode_q8_kernel<4>", ["mla_decode_common.h", "mla_q8.hip"]),
     # sparse read: the indexer pass is the step's dominant kernel
     "index_scores_mfma": ("index_scores_mfma_kernel<false>", ["mla_decode_common.h", "mla_sparse.hip"]),
 }
@@ -178,7 +179,10 @@ def cpu_baseline(wl, inp, budget_flops=2.4e12):
         ref = lambda x, heads, seqs: oracle.mla_decode_ref_sparse(  # noqa: E731
             x, sparse_selection(x, seqs), heads=heads, seqs=seqs)
     else:
-        ref = oracle.mla_decode_ref_q8 if wl.cache == "q8" else oracle.mla_decode_ref
+        bits = {"q8": 8, "q4": 4}.get(wl.cache)
+        ref = ((lambda x, heads, seqs: oracle.mla_decode_ref_q8(x, heads=heads, seqs=seqs,
+                                                                bits=bits))
+               if bits else oracle.mla_decode_ref)
     t = time.perf_counter()
     ref(inp, heads=list(range(heads)), seqs=seqs)
     dt = time.perf_counter() - t
@@ -195,6 +199,7 @@ def cpu_baseline(wl, inp, budget_flops=2.4e12):
             "sample": f"{len(seqs)} of {wl.batch} sequences ({tokens} cached tokens), "
                       f"{heads} of {wl.heads} heads, {dt:.1f} s; fp64 unabsorbed NumPy oracle"
                       f"{' (rows coded to 8 bits first)' if wl.cache == 'q8' else ''}"
+                      f"{' (rows coded to 4 bits first)' if wl.cache == 'q4' else ''}"
                       f"{' (indexer scores and top-k selection first)' if sparse else ''}; "
                       f"bytes counted x {heads}/{wl.heads}",
             "seconds": round(dt, 2),
@@ -282,17 +287,22 @@ def main():
     # ---- device state: one cache pool per layer (same bytes, distinct addresses)
     pt = upload(inp.page_table, torch.int32)
     seq_lens = upload(inp.seq_lens, torch.int32)
-    q8 = wl.cache == "q8"
-    if q8:  # 8-bit rows: codes plus (min, step) pairs
-        pool0 = torch.full((inp.num_pages, wl.page_size, wl.dim + 16), 255, dtype=torch.uint8,
-                           device="cuda")
+    bits = {"q8": 8, "q4": 4}.get(wl.cache, 0)
+    q8 = bits != 0
+    if q8:  # 8- or 4-bit rows: codes plus (min, step) pairs
+        pool0 = torch.full((inp.num_pages, wl.page_size, wl.cache_row_bytes), 255,
+                           dtype=torch.uint8, device="cuda")
     else:
         pool0 = torch.full((inp.num_pages, wl.page_size, wl.dim), float("nan"), dtype=dt,
                            device="cuda")
     si = np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(inp.seq_lens)])
     pos = np.concatenate([np.arange(int(L), dtype=np.int32) for L in inp.seq_lens])
-    (fill_cache_q8 if q8 else fill_cache)(cfg, pool0, pt, upload(inp.c, dt), upload(inp.k_rope, dt),
-                                          upload(si, torch.int32), upload(pos, torch.int32))
+    if q8:
+        fill_cache_q8(cfg, pool0, pt, upload(inp.c, dt), upload(inp.k_rope, dt),
+                      upload(si, torch.int32), upload(pos, torch.int32), bits=bits)
+    else:
+        fill_cache(cfg, pool0, pt, upload(inp.c, dt), upload(inp.k_rope, dt),
+                   upload(si, torch.int32), upload(pos, torch.int32))
     q_nope, q_rope = upload(inp.q_nope, dt), upload(inp.q_rope, dt)
     w_uk, w_uv = upload(inp.w_uk, dt), upload(inp.w_uv, dt)
     rows = np.concatenate([inp.offsets[b] + np.arange(int(L) - Q, int(L))
@@ -308,7 +318,7 @@ def main():
         q_idx, w_idx = upload(inp.q_idx, dt), upload(inp.w_idx, torch.float32)
         k_idx_new = upload(inp.k_idx[rows], dt)
     st = DecodeStep(cfg, B, Q, wl.num_splits, inp.seq_lens, split_chunk=wl.split_chunk,
-                    tree_parents=inp.parents, cache_q8=q8, index_topk=wl.index_topk)
+                    tree_parents=inp.parents, cache_bits=bits, index_topk=wl.index_topk)
     # the drafted rows at their positions (a tree's keys sit at prefix + depth;
     # the fill rotated every key at its slot), then one copy per layer
     st.append(c_new, k_new, pt, pool0)
@@ -446,7 +456,7 @@ def main():
         kernel_bytes = step_bytes = total_tokens * wl.cache_row_bytes  # read once per step
         # every (query row, visible token) pair: 2 * D for the score, 2 * d_c for P.V
         flops = visible_pairs(wl, inp) * H * (2 * wl.dim + 2 * wl.kv_rank)
-        kernel = "mfma_q8" if q8 else mla.decode_kernel_kind(cfg, Q)
+        kernel = {8: "mfma_q8", 4: "mfma_q4"}[bits] if q8 else mla.decode_kernel_kind(cfg, Q)
     cache_bytes = kernel_bytes
     gbs_step = step_bytes / (ms_step * 1e-3) / 1e9
     gbs_decode = cache_bytes / (decode_ms * 1e-3) / 1e9

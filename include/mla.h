@@ -323,6 +323,31 @@ mla_status_t mla_decode_paged_q8(const mla_config_t* cfg, int32_t batch, int32_t
                                  const int32_t* seq_lens, const int32_t* tree_parent,
                                  float* o_part, float* lse_part, void* stream);
 
+/* 4-bit latent cache ("KV Cache Optimization: Scaling to Million-Token
+ * Contexts", technique 3, whose listing defaults to 4 bits, and its comparison
+ * table: INT4 at 4x less memory): the 8-bit cache's per-row coding with 16
+ * levels, step = (max - min) / 15, code = rint((x - min) / step) in float32,
+ * two codes per byte (column 2i in the low nibble of byte i, 2i + 1 in the
+ * high nibble), then the same four fp32 (latent min, latent step, RoPE min,
+ * RoPE step): cache_q4 [num_pages][page_size][(D / 2) + 16] bytes, 304 per
+ * token for d_c = 512, d_r = 64 (1,152 in bf16, 3.79x less).
+ * mla_cache_q4_bytes_per_token: D / 2 + 16, or 0 for an invalid config or
+ * unless d_c and d_r are multiples of 8 and D of 32. The append and decode
+ * take the arguments, checks and errors of mla_cache_append_q8 and
+ * mla_decode_paged_q8 (the same kernel limits). */
+size_t mla_cache_q4_bytes_per_token(const mla_config_t* cfg);
+mla_status_t mla_cache_append_q4(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                                 const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                 const int32_t* rope_pos, const int32_t* page_table,
+                                 int32_t batch, int32_t max_pages, void* cache_q4,
+                                 int64_t num_pages, int32_t flags, void* stream);
+mla_status_t mla_decode_paged_q4(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                 int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
+                                 const void* q_full, const void* cache_q4, int64_t num_pages,
+                                 const int32_t* page_table, int32_t max_pages,
+                                 const int32_t* seq_lens, const int32_t* tree_parent,
+                                 float* o_part, float* lse_part, void* stream);
+
 /* Sparse read (f3; "DeepSeek's Config Says 16 KV Heads, Its Cache Holds a
  * Ninth of That", section 6 "Sparse attention"): a small scorer (the pages:
  * 64 heads of 128 dimensions) rates every cached token for each query, and

@@ -19,7 +19,8 @@ tokens is verified with draft_positions (each drafted row's slot and RoPE
 position, derived on the device from the tree), cache_append_at /
 absorb_append_at and decode_paged_tree. An 8-bit latent cache (uint8 rows
 of codes plus per-part min and step) is written by cache_append_q8 and read
-by decode_paged_q8. A sparse read (attention over the top-scored tokens
+by decode_paged_q8; a 4-bit one (two codes per byte) by cache_append_q4 and
+decode_paged_q4. A sparse read (attention over the top-scored tokens
 only) runs index_append, index_scores, topk_select and decode_sparse.
 """
 from ._binding import (  # noqa: F401
@@ -53,6 +54,9 @@ from ._binding import (  # noqa: F401
     cache_q8_bytes_per_token,
     cache_append_q8,
     decode_paged_q8,
+    cache_q4_bytes_per_token,
+    cache_append_q4,
+    decode_paged_q4,
     index_append,
     index_scores,
     index_scores_topk,

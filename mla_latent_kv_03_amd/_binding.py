@@ -119,6 +119,11 @@ def lib() -> ctypes.CDLL:
         "mla_decode_paged_tree": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32,
                                                  VP, VP, FP, FP, VP]),
         "mla_cache_q8_bytes_per_token": (ctypes.c_size_t, [P]),
+        "mla_cache_q4_bytes_per_token": (ctypes.c_size_t, [P]),
+        "mla_cache_append_q4": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, VP, I32, I32, VP, I64,
+                                               I32, VP]),
+        "mla_decode_paged_q4": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32,
+                                               VP, VP, FP, FP, VP]),
         "mla_cache_append_q8": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, VP, I32, I32, VP, I64,
                                                I32, VP]),
         "mla_decode_paged_q8": (ctypes.c_int, [P, I32, I32, I32, I32, I32, VP, VP, I64, VP, I32,
@@ -244,14 +249,19 @@ def _absorb_args(cfg: Config, q_nope, q_rope, pos, w_uk, q_full):
             _need(q_full, "q_full", dt, n * H * cfg.dim))
 
 
-def _append_args(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache, mode, q8=False):
+def _coded_row(cfg: Config, bits: int) -> int:
+    """Bytes per cached row: the workload dtype (bits 0), 8-bit or 4-bit codes."""
+    return {0: cfg.dim, 8: cfg.dim + 16, 4: cfg.dim // 2 + 16}[bits]
+
+
+def _append_args(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache, mode, bits=0):
     t = _torch()
     n = int(pos.numel())
     dt = _elem_dtype(cfg)
     if page_table.dim() != 2:
         raise ValueError("page_table: expected [batch][max_pages]")
     batch, max_pages = page_table.shape
-    row = cfg.dim + 16 if q8 else cfg.dim
+    row = _coded_row(cfg, bits)
     if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != row:
         raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{row}]")
     num_pages = int(cache.shape[0])
@@ -261,7 +271,7 @@ def _append_args(cfg: Config, c_kv, k_rope, seq_idx, pos, page_table, cache, mod
             _need(pos, "pos", t.int32, n),
             _need(page_table, "page_table", t.int32, batch * max_pages),
             int(batch), int(max_pages),
-            _need(cache, "cache", t.uint8 if q8 else dt, cache.numel()), num_pages, int(mode))
+            _need(cache, "cache", t.uint8 if bits else dt, cache.numel()), num_pages, int(mode))
 
 
 def absorb_q(cfg: Config, q_nope, q_rope, pos, w_uk, q_full, stream=None):
@@ -351,10 +361,25 @@ def cache_append_q8(cfg: Config, c_kv, k_rope, seq_idx, pos, rope_pos, page_tabl
                     mode: int = APPEND_ROTATE, stream=None):
     """a2 into an 8-bit cache: cache_q8 uint8 [num_pages][page][D + 16]; each row
     coded per part between its own min and max; rope_pos as cache_append_at."""
-    a = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache_q8, mode, q8=True)
+    a = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache_q8, mode, bits=8)
     rp = _rope_pos_arg(rope_pos, a[0])
     _ck(lib().mla_cache_append_q8(cfg.cptr(), *a[:5], rp, *a[5:], _stream(stream)),
         "mla_cache_append_q8")
+
+
+def cache_q4_bytes_per_token(cfg: Config) -> int:
+    """Bytes of one 4-bit cache row: (d_c + d_r) / 2 code bytes + 16 of (min, step)."""
+    return lib().mla_cache_q4_bytes_per_token(cfg.cptr())
+
+
+def cache_append_q4(cfg: Config, c_kv, k_rope, seq_idx, pos, rope_pos, page_table, cache_q4,
+                    mode: int = APPEND_ROTATE, stream=None):
+    """a2 into a 4-bit cache: cache_q4 uint8 [num_pages][page][D / 2 + 16]; two
+    codes per byte (low nibble first); otherwise as cache_append_q8."""
+    a = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache_q4, mode, bits=4)
+    rp = _rope_pos_arg(rope_pos, a[0])
+    _ck(lib().mla_cache_append_q4(cfg.cptr(), *a[:5], rp, *a[5:], _stream(stream)),
+        "mla_cache_append_q4")
 
 
 def chunk_plan(cfg: Config, total_tokens: int, max_seq_len: int, num_cus: int = 256):
@@ -379,7 +404,15 @@ def decode_paged_q8(cfg: Config, q_full, cache_q8, page_table, seq_lens, o_part,
     """a4 over an 8-bit cache (cache_q8 uint8 [num_pages][page][D + 16]); other
     arguments as decode_paged / decode_paged_tree."""
     _decode(cfg, q_full, cache_q8, page_table, seq_lens, tree_parent, o_part, lse_part,
-            max_seq_len, stream, chunk_tokens, q8=True)
+            max_seq_len, stream, chunk_tokens, bits=8)
+
+
+def decode_paged_q4(cfg: Config, q_full, cache_q4, page_table, seq_lens, o_part, lse_part,
+                    max_seq_len: int, stream=None, chunk_tokens: int = 0, tree_parent=None):
+    """a4 over a 4-bit cache (cache_q4 uint8 [num_pages][page][D / 2 + 16]); other
+    arguments as decode_paged_q8."""
+    _decode(cfg, q_full, cache_q4, page_table, seq_lens, tree_parent, o_part, lse_part,
+            max_seq_len, stream, chunk_tokens, bits=4)
 
 
 def decode_paged_tree(cfg: Config, q_full, cache, page_table, seq_lens, tree_parent, o_part,
@@ -392,7 +425,7 @@ def decode_paged_tree(cfg: Config, q_full, cache, page_table, seq_lens, tree_par
 
 
 def _decode(cfg, q_full, cache, page_table, seq_lens, tree_parent, o_part, lse_part, max_seq_len,
-            stream, chunk_tokens, q8=False):
+            stream, chunk_tokens, bits=0):
     t = _torch()
     if q_full.dim() != 4:
         raise ValueError("q_full: expected [batch][q_len][H][D]")
@@ -404,22 +437,22 @@ def _decode(cfg, q_full, cache, page_table, seq_lens, tree_parent, o_part, lse_p
     if page_table.dim() != 2 or page_table.shape[0] != B:
         raise ValueError("page_table: expected [batch][max_pages]")
     max_pages = int(page_table.shape[1])
-    row = cfg.dim + 16 if q8 else cfg.dim
+    row = _coded_row(cfg, bits)
     if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != row:
         raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{row}]")
     num_pages = int(cache.shape[0])
     args = (_need(q_full, "q_full", dt, B * Q * H * cfg.dim),
-            _need(cache, "cache", t.uint8 if q8 else dt, cache.numel()))
+            _need(cache, "cache", t.uint8 if bits else dt, cache.numel()))
     pt = _need(page_table, "page_table", t.int32, B * max_pages)
     sl = _need(seq_lens, "seq_lens", t.int32, B)
     op = _need(o_part, "o_part", t.float32, B * Q * H * S * cfg.kv_rank)
     lp = _need(lse_part, "lse_part", t.float32, B * Q * H * S)
-    if q8:
+    if bits:
         tp = None if tree_parent is None else _need(tree_parent, "tree_parent", t.int32, B * Q)
-        _ck(lib().mla_decode_paged_q8(cfg.cptr(), B, Q, int(chunk_tokens), S,
-                                      int(max_seq_len), args[0], args[1], num_pages, pt,
-                                      max_pages, sl, tp, op, lp, _stream(stream)),
-            "mla_decode_paged_q8")
+        name = "mla_decode_paged_q8" if bits == 8 else "mla_decode_paged_q4"
+        _ck(getattr(lib(), name)(cfg.cptr(), B, Q, int(chunk_tokens), S, int(max_seq_len),
+                                 args[0], args[1], num_pages, pt, max_pages, sl, tp, op, lp,
+                                 _stream(stream)), name)
         return
     if tree_parent is not None:
         tp = _need(tree_parent, "tree_parent", t.int32, B * Q)

@@ -376,33 +376,44 @@ mla_status_t mla_decode_paged_tree(const mla_config_t* cfg, int32_t batch, int32
                      stream);
 }
 
-size_t mla_cache_q8_bytes_per_token(const mla_config_t* cfg) {
-  if (check_config(cfg) != MLA_OK || (cfg->kv_rank + cfg->rope_dim) % 16) return 0;
-  return (size_t)(cfg->kv_rank + cfg->rope_dim) + 16;
+namespace {
+
+// bits = 8 or 4: bytes of one coded row, 0 when the config cannot be coded
+size_t coded_row_bytes(const mla_config_t* cfg, int bits) {
+  if (check_config(cfg) != MLA_OK) return 0;
+  const int D = cfg->kv_rank + cfg->rope_dim;
+  if (bits == 8) return D % 16 ? 0 : (size_t)D + 16;
+  if (cfg->kv_rank % 8 || cfg->rope_dim % 8 || D % 32) return 0;
+  return (size_t)D / 2 + 16;
 }
 
-mla_status_t mla_cache_append_q8(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
-                                 const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
-                                 const int32_t* rope_pos, const int32_t* page_table,
-                                 int32_t batch, int32_t max_pages, void* cache_q8,
-                                 int64_t num_pages, int32_t flags, void* stream) {
+mla_status_t append_coded(int bits, const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                          const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                          const int32_t* rope_pos, const int32_t* page_table, int32_t batch,
+                          int32_t max_pages, void* cache, int64_t num_pages, int32_t flags,
+                          void* stream) {
   mla_status_t st = check_append(cfg, n_tok, c_kv, k_rope, seq_idx, pos, page_table, batch,
-                                 max_pages, cache_q8, num_pages, flags);
+                                 max_pages, cache, num_pages, flags);
   if (st != MLA_OK) return st;
-  MLA_REQUIRE((cfg->kv_rank + cfg->rope_dim) % 16 == 0, MLA_ERR_UNSUPPORTED);
+  MLA_REQUIRE(coded_row_bytes(cfg, bits) != 0, MLA_ERR_UNSUPPORTED);
   if (n_tok == 0) return MLA_OK;
   if (rope_pos) MLA_CHECK_PTR(rope_pos);
-  return hip_status(mla::launch_cache_append_q8(shape_of(cfg), n_tok, c_kv, k_rope, seq_idx, pos,
-                                                rope_pos, page_table, batch, max_pages, cache_q8,
-                                                num_pages, flags == MLA_APPEND_ROTATE, stream));
+  const int rot = flags == MLA_APPEND_ROTATE;
+  return hip_status(
+      bits == 8 ? mla::launch_cache_append_q8(shape_of(cfg), n_tok, c_kv, k_rope, seq_idx, pos,
+                                              rope_pos, page_table, batch, max_pages, cache,
+                                              num_pages, rot, stream)
+                : mla::launch_cache_append_q4(shape_of(cfg), n_tok, c_kv, k_rope, seq_idx, pos,
+                                              rope_pos, page_table, batch, max_pages, cache,
+                                              num_pages, rot, stream));
 }
 
-mla_status_t mla_decode_paged_q8(const mla_config_t* cfg, int32_t batch, int32_t q_len,
-                                 int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
-                                 const void* q_full, const void* cache_q8, int64_t num_pages,
-                                 const int32_t* page_table, int32_t max_pages,
-                                 const int32_t* seq_lens, const int32_t* tree_parent,
-                                 float* o_part, float* lse_part, void* stream) {
+mla_status_t decode_coded(int bits, const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                          int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
+                          const void* q_full, const void* cache, int64_t num_pages,
+                          const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                          const int32_t* tree_parent, float* o_part, float* lse_part,
+                          void* stream) {
   mla_status_t st = check_config(cfg);
   if (st != MLA_OK) return st;
   MLA_REQUIRE(batch >= 0 && q_len >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
@@ -420,16 +431,66 @@ mla_status_t mla_decode_paged_q8(const mla_config_t* cfg, int32_t batch, int32_t
   MLA_REQUIRE(mla::decode_q8_ok(sh, q_len), MLA_ERR_UNSUPPORTED);
   if (batch == 0) return MLA_OK;
   MLA_CHECK_PTR(q_full);
-  MLA_CHECK_PTR(cache_q8);
+  MLA_CHECK_PTR(cache);
   MLA_CHECK_PTR(page_table);
   MLA_CHECK_PTR(seq_lens);
   MLA_CHECK_PTR(o_part);
   MLA_CHECK_PTR(lse_part);
   if (tree_parent) MLA_CHECK_PTR(tree_parent);
   sh.split_fixed = chunk_tokens;
-  return hip_status(mla::launch_decode_q8(sh, batch, q_len, num_splits, max_seq_len, q_full,
-                                          cache_q8, num_pages, page_table, max_pages, seq_lens,
-                                          tree_parent, o_part, lse_part, stream));
+  return hip_status(
+      bits == 8 ? mla::launch_decode_q8(sh, batch, q_len, num_splits, max_seq_len, q_full, cache,
+                                        num_pages, page_table, max_pages, seq_lens, tree_parent,
+                                        o_part, lse_part, stream)
+                : mla::launch_decode_q4(sh, batch, q_len, num_splits, max_seq_len, q_full, cache,
+                                        num_pages, page_table, max_pages, seq_lens, tree_parent,
+                                        o_part, lse_part, stream));
+}
+
+}  // namespace
+
+size_t mla_cache_q8_bytes_per_token(const mla_config_t* cfg) { return coded_row_bytes(cfg, 8); }
+
+size_t mla_cache_q4_bytes_per_token(const mla_config_t* cfg) { return coded_row_bytes(cfg, 4); }
+
+mla_status_t mla_cache_append_q8(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                                 const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                 const int32_t* rope_pos, const int32_t* page_table,
+                                 int32_t batch, int32_t max_pages, void* cache_q8,
+                                 int64_t num_pages, int32_t flags, void* stream) {
+  return append_coded(8, cfg, n_tok, c_kv, k_rope, seq_idx, pos, rope_pos, page_table, batch,
+                      max_pages, cache_q8, num_pages, flags, stream);
+}
+
+mla_status_t mla_cache_append_q4(const mla_config_t* cfg, int32_t n_tok, const void* c_kv,
+                                 const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                 const int32_t* rope_pos, const int32_t* page_table,
+                                 int32_t batch, int32_t max_pages, void* cache_q4,
+                                 int64_t num_pages, int32_t flags, void* stream) {
+  return append_coded(4, cfg, n_tok, c_kv, k_rope, seq_idx, pos, rope_pos, page_table, batch,
+                      max_pages, cache_q4, num_pages, flags, stream);
+}
+
+mla_status_t mla_decode_paged_q8(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                 int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
+                                 const void* q_full, const void* cache_q8, int64_t num_pages,
+                                 const int32_t* page_table, int32_t max_pages,
+                                 const int32_t* seq_lens, const int32_t* tree_parent,
+                                 float* o_part, float* lse_part, void* stream) {
+  return decode_coded(8, cfg, batch, q_len, chunk_tokens, num_splits, max_seq_len, q_full,
+                      cache_q8, num_pages, page_table, max_pages, seq_lens, tree_parent, o_part,
+                      lse_part, stream);
+}
+
+mla_status_t mla_decode_paged_q4(const mla_config_t* cfg, int32_t batch, int32_t q_len,
+                                 int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
+                                 const void* q_full, const void* cache_q4, int64_t num_pages,
+                                 const int32_t* page_table, int32_t max_pages,
+                                 const int32_t* seq_lens, const int32_t* tree_parent,
+                                 float* o_part, float* lse_part, void* stream) {
+  return decode_coded(4, cfg, batch, q_len, chunk_tokens, num_splits, max_seq_len, q_full,
+                      cache_q4, num_pages, page_table, max_pages, seq_lens, tree_parent, o_part,
+                      lse_part, stream);
 }
 
 namespace {

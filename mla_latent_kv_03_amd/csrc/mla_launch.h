@@ -93,6 +93,17 @@ int launch_decode_q8(const Shape& s, int batch, int q_len, int num_splits, int m
                      const void* q_full, const void* cache, int64_t num_pages,
                      const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                      const int32_t* tree_parent, float* o_part, float* lse_part, void* stream);
+// 4-bit latent cache: the same rows with two codes per byte (column 2i in the
+// low nibble of byte i), (d_c + d_r) / 2 + 16 bytes; the decode has the
+// 8-bit decode's limits (decode_q8_ok).
+int launch_cache_append_q4(const Shape& s, int n_tok, const void* c_kv, const void* k_rope,
+                           const int32_t* seq_idx, const int32_t* pos, const int32_t* rope_pos,
+                           const int32_t* page_table, int batch, int max_pages, void* cache,
+                           int64_t num_pages, int rotate, void* stream);
+int launch_decode_q4(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
+                     const void* q_full, const void* cache, int64_t num_pages,
+                     const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                     const int32_t* tree_parent, float* o_part, float* lse_part, void* stream);
 
 // Which decode kernel a shape takes (for tests and tools): 0 = generic VALU
 // kernel, 1 = bf16 MFMA kernel with 16 query rows per block, 2 = bf16 MFMA

@@ -54,16 +54,16 @@ __device__ __forceinline__ float block_reduce_min(float v, float* red) {
   return -block_reduce_max(-v, red);
 }
 
-// code of x on [mn, mn + 255 step]: rint((x - mn) / step) in float32
-__device__ __forceinline__ uint32_t q8_code(float x, float mn, float step) {
+// code of x on [mn, mn + levels * step]: rint((x - mn) / step) in float32
+__device__ __forceinline__ uint32_t q_code(float x, float mn, float step, float levels) {
   if (step == 0.0f) return 0u;
   const float c = rintf((x - mn) / step);
-  return (uint32_t)fminf(fmaxf(c, 0.0f), 255.0f);
+  return (uint32_t)fminf(fmaxf(c, 0.0f), levels);
 }
 
 }  // namespace
 
-template <typename T>
+template <typename T, int kBits>
 __global__ __launch_bounds__(128) void append_q8_kernel(
     int dc, int dr, int page, const T* __restrict__ c_kv, const T* __restrict__ k_rope,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
@@ -78,7 +78,9 @@ __global__ __launch_bounds__(128) void append_q8_kernel(
   const int pg = page_table[(size_t)b * max_pages + p / page];
   if (pg < 0 || (int64_t)pg >= num_pages) return;
   const int D = dc + dr;
-  uint8_t* row = cache + ((size_t)pg * page + p % page) * (size_t)(D + kQ8Meta);
+  constexpr float kLevels = (float)((1 << kBits) - 1);  // 255 or 15
+  constexpr int kPer = 32 / kBits;                       // codes per 32-bit word: 4 or 8
+  uint8_t* row = cache + ((size_t)pg * page + p % page) * (size_t)(D * kBits / 8 + kQ8Meta);
   const T* src = c_kv + (size_t)n * dc;
   const T* ks = k_rope + (size_t)n * dr;
   const int rp = rope_pos ? rope_pos[n] : p;
@@ -104,12 +106,13 @@ __global__ __launch_bounds__(128) void append_q8_kernel(
   }
   const float lmn = block_reduce_min(lo, red);
   const float lmx = block_reduce_max(hi, red);
-  const float lstep = (lmx - lmn) / 255.0f;
-  for (int i = 4 * tid; i < dc; i += 4 * blockDim.x) {
+  const float lstep = (lmx - lmn) / kLevels;
+  for (int i = kPer * tid; i < dc; i += kPer * blockDim.x) {
     uint32_t w = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w |= q8_code(Elt<T>::ld(src + i + j), lmn, lstep) << (8 * j);
-    *reinterpret_cast<uint32_t*>(row + i) = w;
+    for (int j = 0; j < kPer; ++j)
+      w |= q_code(Elt<T>::ld(src + i + j), lmn, lstep, kLevels) << (kBits * j);
+    *reinterpret_cast<uint32_t*>(row + i * kBits / 8) = w;
   }
   // RoPE part (kr is complete: the reductions above passed block barriers)
   lo = INFINITY;
@@ -120,34 +123,52 @@ __global__ __launch_bounds__(128) void append_q8_kernel(
   }
   const float rmn = block_reduce_min(lo, red);
   const float rmx = block_reduce_max(hi, red);
-  const float rstep = (rmx - rmn) / 255.0f;
-  for (int i = 4 * tid; i < dr; i += 4 * blockDim.x) {
+  const float rstep = (rmx - rmn) / kLevels;
+  for (int i = kPer * tid; i < dr; i += kPer * blockDim.x) {
     uint32_t w = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w |= q8_code(kr[i + j], rmn, rstep) << (8 * j);
-    *reinterpret_cast<uint32_t*>(row + dc + i) = w;
+    for (int j = 0; j < kPer; ++j) w |= q_code(kr[i + j], rmn, rstep, kLevels) << (kBits * j);
+    *reinterpret_cast<uint32_t*>(row + (dc + i) * kBits / 8) = w;
   }
   if (tid == 0)
-    *reinterpret_cast<float4*>(row + D) = make_float4(lmn, lstep, rmn, rstep);
+    *reinterpret_cast<float4*>(row + D * kBits / 8) = make_float4(lmn, lstep, rmn, rstep);
+}
+
+template <int kBits>
+static int launch_cache_append_qn(const Shape& s, int n_tok, const void* c_kv,
+                                  const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                  const int32_t* rope_pos, const int32_t* page_table, int batch,
+                                  int max_pages, void* cache, int64_t num_pages, int rotate,
+                                  void* stream) {
+  if (s.dtype == 0)
+    hipLaunchKernelGGL((append_q8_kernel<float, kBits>), dim3(n_tok), dim3(128), 0,
+                       reinterpret_cast<hipStream_t>(stream), s.dc, s.dr, s.page,
+                       (const float*)c_kv, (const float*)k_rope, seq_idx, pos, rope_pos,
+                       page_table, batch, max_pages, (uint8_t*)cache, num_pages, rotate,
+                       s.log2_base);
+  else
+    hipLaunchKernelGGL((append_q8_kernel<bf16_t, kBits>), dim3(n_tok), dim3(128), 0,
+                       reinterpret_cast<hipStream_t>(stream), s.dc, s.dr, s.page,
+                       (const bf16_t*)c_kv, (const bf16_t*)k_rope, seq_idx, pos, rope_pos,
+                       page_table, batch, max_pages, (uint8_t*)cache, num_pages, rotate,
+                       s.log2_base);
+  return (int)hipGetLastError();
 }
 
 int launch_cache_append_q8(const Shape& s, int n_tok, const void* c_kv, const void* k_rope,
                            const int32_t* seq_idx, const int32_t* pos, const int32_t* rope_pos,
                            const int32_t* page_table, int batch, int max_pages, void* cache,
                            int64_t num_pages, int rotate, void* stream) {
-  if (s.dtype == 0)
-    hipLaunchKernelGGL(append_q8_kernel<float>, dim3(n_tok), dim3(128), 0,
-                       reinterpret_cast<hipStream_t>(stream), s.dc, s.dr, s.page,
-                       (const float*)c_kv, (const float*)k_rope, seq_idx, pos, rope_pos,
-                       page_table, batch, max_pages, (uint8_t*)cache, num_pages, rotate,
-                       s.log2_base);
-  else
-    hipLaunchKernelGGL(append_q8_kernel<bf16_t>, dim3(n_tok), dim3(128), 0,
-                       reinterpret_cast<hipStream_t>(stream), s.dc, s.dr, s.page,
-                       (const bf16_t*)c_kv, (const bf16_t*)k_rope, seq_idx, pos, rope_pos,
-                       page_table, batch, max_pages, (uint8_t*)cache, num_pages, rotate,
-                       s.log2_base);
-  return (int)hipGetLastError();
+  return launch_cache_append_qn<8>(s, n_tok, c_kv, k_rope, seq_idx, pos, rope_pos, page_table,
+                                   batch, max_pages, cache, num_pages, rotate, stream);
+}
+
+int launch_cache_append_q4(const Shape& s, int n_tok, const void* c_kv, const void* k_rope,
+                           const int32_t* seq_idx, const int32_t* pos, const int32_t* rope_pos,
+                           const int32_t* page_table, int batch, int max_pages, void* cache,
+                           int64_t num_pages, int rotate, void* stream) {
+  return launch_cache_append_qn<4>(s, n_tok, c_kv, k_rope, seq_idx, pos, rope_pos, page_table,
+                                   batch, max_pages, cache, num_pages, rotate, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -156,24 +177,32 @@ int launch_cache_append_q8(const Shape& s, int n_tok, const void* c_kv, const vo
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int kQRow = kD + kQ8Meta;                  // 592 bytes per cached row
 constexpr int kQT = 16;                              // tokens per wave subtile
-constexpr int kQSubBytes = kQT * kQRow;              // 9,472
-constexpr int kQRing = 3;                            // ring slots per wave
-constexpr int kQWaveBytes = kQRing * kQSubBytes;     // 28,416
 constexpr int kQQBytes = kKSteps * 64 * 16;          // 18,432: the query B operands in fp16
-constexpr size_t kQLds = (size_t)kWaves * kQWaveBytes + kQQBytes;  // 132,096
-constexpr int kQWide = kQSubBytes / 1024;            // 9 loads of 16 B per lane ...
-constexpr int kQSubLoads = kQWide + 1;               // ... and one of 4 B per lane
 constexpr int kQQueryLoads = 16 * kD * 2 / 1024;     // 18: the 16 query rows in bf16
 constexpr int kQAcc = 16 * kDC * 4;                  // 32,768: one wave's accumulators
 
-static_assert(kQSubBytes - kQWide * 1024 == 256, "a subtile is 9 wide loads and one narrow");
-static_assert(kQRow % 16 == 0, "a 16-byte chunk never straddles two rows");
-static_assert((kQQueryLoads + kWaves - 1) / kWaves * 1024 <= kQSubBytes,
-              "a wave's share of the query rows fits one ring slot");
-static_assert((size_t)kWaves * kQAcc <= kQLds, "the four waves' accumulators fit the LDS");
-static_assert(kQLds + 4096 <= 160 * 1024, "LDS of one CU, with the static arrays");
+// Row and ring geometry of a cache with kBits-bit codes (8: one code per byte;
+// 4: two per byte, column 2i in the low nibble of byte i)
+template <int kBits>
+struct QFmt {
+  static constexpr int kCode = kD * kBits / 8;       // code bytes: 576 / 288
+  static constexpr int kRow = kCode + kQ8Meta;       // bytes per cached row: 592 / 304
+  static constexpr int kSub = kQT * kRow;            // one subtile: 9,472 / 4,864
+  static constexpr int kWide = kSub / 1024;          // loads of 16 B per lane: 9 / 4 ...
+  static constexpr int kTail = (kSub - kWide * 1024) / 256;  // ... of 4 B per lane: 1 / 3
+  static constexpr int kSubLoads = kWide + kTail;
+  static constexpr int kRing = kBits == 8 ? 3 : 6;   // ring slots per wave
+  static constexpr int kStage = (((kQQueryLoads + kWaves - 1) / kWaves) * 1024 + kSub - 1) / kSub;
+  static constexpr int kWaveBytes = kRing * kSub;
+  static constexpr size_t kRingLds = (size_t)kWaves * kWaveBytes + kQQBytes;
+  static constexpr size_t kLds = kRingLds > (size_t)kWaves * kQAcc ? kRingLds
+                                                                   : (size_t)kWaves * kQAcc;
+  static_assert(kSub - kWide * 1024 == 256 * kTail, "a subtile is whole loads");
+  static_assert(kRow % 16 == 0, "a 16-byte chunk never straddles two rows");
+  static_assert(kStage < kRing, "the query rows are staged in the ring's last slots");
+  static_assert(kLds + 4096 <= 160 * 1024, "LDS of one CU, with the static arrays");
+};
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
@@ -188,6 +217,17 @@ __device__ __forceinline__ f16x8_t codes8_sub(u32x2_t c) {
                                               __builtin_amdgcn_perm(0u, c.y, 0x0c030c02u)});
 }
 
+// The same for eight 4-bit codes of a dword (codes 2i and 2i + 1 in the low
+// and high nibble of byte i): the nibbles are split into two dwords of bytes,
+// then one v_perm per two codes as above.
+__device__ __forceinline__ f16x8_t codes4_sub(uint32_t c) {
+  const uint32_t lo = c & 0x0f0f0f0fu, hi = (c >> 4) & 0x0f0f0f0fu;
+  return __builtin_bit_cast(f16x8_t, u32x4_t{__builtin_amdgcn_perm(hi, lo, 0x0c040c00u),
+                                              __builtin_amdgcn_perm(hi, lo, 0x0c050c01u),
+                                              __builtin_amdgcn_perm(hi, lo, 0x0c060c02u),
+                                              __builtin_amdgcn_perm(hi, lo, 0x0c070c03u)});
+}
+
 // The MFMA's k index 8 kg + i of step ks stands for code column
 // q8_col(ks, kg) + i: in the latent part a lane's four steps 4 G .. 4 G + 3
 // cover 32 contiguous codes (two 16-byte LDS reads), in the RoPE part its two
@@ -197,7 +237,6 @@ __device__ __forceinline__ int q8_col(int ks, int kg) {
   return ks < kDC / 32 ? 128 * (ks >> 2) + 32 * kg + 8 * (ks & 3)
                        : kDC + 16 * kg + 8 * (ks - kDC / 32);
 }
-constexpr int kQAReads = kKSteps / 2;                // 9 reads of 16 B per subtile
 
 }  // namespace
 
@@ -234,6 +273,7 @@ constexpr int kQAReads = kKSteps / 2;                // 9 reads of 16 B per subt
 // band is at least 2^16 below that largest term. Both factors are exact, so
 // the rows' own scales (steps from 2^-100 to 2^100, queries of any finite
 // bf16 magnitude) leave the rounding of the contractions unchanged.
+template <int kBits>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
                       float scale_log2, int units, int groups, const bf16_t* __restrict__ q_full,
@@ -242,6 +282,7 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
                       const int32_t* __restrict__ seq_lens,
                       const int32_t* __restrict__ tree_parent, float* __restrict__ o_part,
                       float* __restrict__ lse_part) {
+  using F = QFmt<kBits>;
   extern __shared__ u32x4_t lds[];
   __shared__ float st_m[kWaves][16], st_l[kWaves][16], st_o[kWaves][16];
   __shared__ int pwin[kWaves][64];     // each wave's copy of the page window
@@ -269,8 +310,8 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   bool bad = bad_len;
 
   char* const lbase = reinterpret_cast<char*>(lds);
-  char* const wbase = lbase + wave * kQWaveBytes;
-  char* const qop = lbase + kWaves * kQWaveBytes;  // the query B operands
+  char* const wbase = lbase + wave * F::kWaveBytes;
+  char* const qop = lbase + kWaves * F::kWaveBytes;  // the query B operands
 
   // The page-table window (lane i: unit page i of the partition) is copied
   // into LDS ahead of the query rows, so that waiting for it leaves the
@@ -287,38 +328,46 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   // which crosses at most one page boundary.
   int i_up = 0, i_off = kQT * wave, i_slot = 0;
   const int pg_lim = (int)min(num_pages, (int64_t)0x7fffffff);
-  const size_t page_bytes = (size_t)page * kQRow;
+  const size_t page_bytes = (size_t)page * F::kRow;
   auto issue_next = [&]() {
     int pg = pw.get(i_up, lane);
     if (pg < 0 || pg >= pg_lim) {
       bad = true;
       pg = 0;
     }
-    const uint8_t* src = cache + (size_t)pg * page_bytes + (size_t)i_off * kQRow;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(wbase + i_slot * kQSubBytes));
+    const uint8_t* src = cache + (size_t)pg * page_bytes + (size_t)i_off * F::kRow;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(wbase + i_slot * F::kSub));
 #pragma unroll
-    for (int i = 0; i < kQWide; ++i)
+    for (int i = 0; i < F::kWide; ++i)
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                    :
                    : "s"(dst + i * 1024), "v"((uint32_t)(i * 1024 + 16 * lane)), "s"(src)
                    : "memory");
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 nt"
-                 :
-                 : "s"(dst + kQWide * 1024), "v"((uint32_t)(kQWide * 1024 + 4 * lane)), "s"(src)
-                 : "memory");
+#pragma unroll
+    for (int i = 0; i < F::kTail; ++i)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 nt"
+                   :
+                   : "s"(dst + F::kWide * 1024 + i * 256),
+                     "v"((uint32_t)(F::kWide * 1024 + i * 256 + 4 * lane)), "s"(src)
+                   : "memory");
     i_off += kWaves * kQT;
     if (i_off >= page) {
       i_off -= page;
       ++i_up;
     }
-    i_slot = i_slot == kQRing - 1 ? 0 : i_slot + 1;
+    i_slot = i_slot == F::kRing - 1 ? 0 : i_slot + 1;
   };
   // wait until at most `in_flight` later subtiles of this wave are in flight
   auto wait_subs = [&](int in_flight) {
-    static_assert(kQRing == 3, "waits for up to two later subtiles");
-    if (in_flight >= 2) wait_vmcnt<2 * kQSubLoads>();
-    else if (in_flight == 1) wait_vmcnt<kQSubLoads>();
-    else wait_vmcnt<0>();
+    static_assert(F::kRing <= 6 && 5 * F::kSubLoads <= 63, "the waits below cover the ring");
+    switch (min(in_flight, F::kRing - 1)) {
+      case 5: wait_vmcnt<5 * F::kSubLoads>(); break;
+      case 4: wait_vmcnt<4 * F::kSubLoads>(); break;
+      case 3: wait_vmcnt<3 * F::kSubLoads>(); break;
+      case 2: wait_vmcnt<2 * F::kSubLoads>(); break;
+      case 1: wait_vmcnt<F::kSubLoads>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
   };
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -339,7 +388,8 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
 
   if (nsub > 0) {
     // ---- prologue: the page window; query load i (1 KB of the 16 bf16 rows)
-    // to the last slot of wave i % 4 at 1 KB * (i / 4); subtiles 0 .. kQRing - 2
+    // to the last kStage slots of wave i % 4 at 1 KB * (i / 4); subtiles
+    // 0 .. kRing - kStage - 1
     {
       const int* src = pw.row + min(lane, pw.upages - 1);  // pw.upages >= 1 here
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(&pwin[wave][0]));
@@ -348,8 +398,8 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
                    : "s"(dst), "v"(src)
                    : "memory");
       const bf16_t* qsrc = q_full + ((size_t)b * R + row0) * kD;
-      const uint32_t qdst =
-          __builtin_amdgcn_readfirstlane(lds_addr(wbase + (kQRing - 1) * kQSubBytes));
+      const uint32_t qdst = __builtin_amdgcn_readfirstlane(
+          lds_addr(wbase + (F::kRing - F::kStage) * F::kSub));
       for (int i = wave; i < kQQueryLoads; i += kWaves)  // wave-uniform bounds
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                      :
@@ -364,7 +414,7 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
         wait_vmcnt<kQQueryLoads / kWaves>();
       pw.reg = pwin[wave][lane];
     }
-    const int npre = min(nk, kQRing - 1);
+    const int npre = min(nk, F::kRing - F::kStage);
     for (int k = 0; k < npre; ++k) issue_next();
     wait_subs(npre);  // own query loads (issued before the subtiles)
     __syncthreads();
@@ -374,8 +424,8 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
     auto q_stage = [&](int ks) {
       const int gb = n * kD * 2 + 2 * q8_col(ks, kg);
       const int li = gb >> 10;
-      const char* p = lbase + (li % kWaves) * kQWaveBytes + (kQRing - 1) * kQSubBytes +
-                      (li / kWaves) * 1024 + (gb & 1023);
+      const char* p = lbase + (li % kWaves) * F::kWaveBytes +
+                      (F::kRing - F::kStage) * F::kSub + (li / kWaves) * 1024 + (gb & 1023);
       return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
     };
     {
@@ -435,39 +485,58 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
     sq_rope = ldexpf((sqp[0][n][1] + sqp[1][n][1] + sqp[2][n][1] + sqp[3][n][1]) * scale_log2, -er);
     c24l = ldexpf(c24, -el);
     c24r = ldexpf(c24, -er);
-    if (nk > kQRing - 1) issue_next();
+    for (int k = npre; k < min(nk, F::kRing); ++k) issue_next();  // the staging slots
 
-    // QK: A operand of lane (token n, kg) at bytes n * 592 + q8_col(ks, kg);
-    // PV: B operand of lane (column 64 g + 4 n + r, kg) from tokens 4 kg + j
-    const int arow = n * kQRow;
-    const int brow = 4 * kg * kQRow + 4 * n;
+    // QK: A operand of lane (token n, kg), code columns q8_col(ks, kg) .. + 7
+    // of row n; PV: B operand of lane (n, kg) from tokens 4 kg + j (8 bits:
+    // columns 64 g + 4 n + r; 4 bits: columns 128 (g >> 1) + 8 n + 4 (g & 1) + r)
+    const int arow = n * F::kRow;
+    const int brow = 4 * kg * F::kRow + 4 * n;
     const char* const qb = qop + 16 * lane;
     int c_slot = 0;  // slot of subtile k
     for (int k = 0; k < nk; ++k) {
-      wait_subs(min(nk - 1 - k, kQRing - 1));
+      wait_subs(min(nk - 1 - k, F::kRing - 1));
       const int ts = t0 + kQT * (kWaves * k + wave);
-      char* tile = wbase + c_slot * kQSubBytes;
-      c_slot = c_slot == kQRing - 1 ? 0 : c_slot + 1;
+      char* tile = wbase + c_slot * F::kSub;
+      c_slot = c_slot == F::kRing - 1 ? 0 : c_slot + 1;
       if (ts + kQT > t1) {  // rows past the partition end (another token, or poison) -> 0
-        for (int c = (t1 - ts) * (kQRow / 16) + lane; c < kQSubBytes / 16; c += 64)
+        for (int c = (t1 - ts) * (F::kRow / 16) + lane; c < F::kSub / 16; c += 64)
           reinterpret_cast<u32x4_t*>(tile)[c] = u32x4_t{0u, 0u, 0u, 0u};
       }
-      // the QK operands and the row metadata first
-      u32x4_t cv[kQAReads];
+      // the QK operands and the row metadata first: 8 bits, nine 16-byte
+      // reads of two k-steps each; 4 bits, four 16-byte reads of four latent
+      // k-steps each and one 8-byte read of the two RoPE k-steps
+      constexpr int kAR = kBits == 8 ? kKSteps / 2 : 5;
+      u32x4_t cv[kAR];
+      if constexpr (kBits == 8) {
 #pragma unroll
-      for (int i = 0; i < kQAReads; ++i)
-        cv[i] = *reinterpret_cast<const u32x4_t*>(tile + arow + q8_col(2 * i, kg));
+        for (int i = 0; i < kAR; ++i)
+          cv[i] = *reinterpret_cast<const u32x4_t*>(tile + arow + q8_col(2 * i, kg));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          cv[i] = *reinterpret_cast<const u32x4_t*>(tile + arow + 64 * i + 16 * kg);
+        const u32x2_t r2 = *reinterpret_cast<const u32x2_t*>(tile + arow + kDC / 2 + 8 * kg);
+        cv[4] = u32x4_t{r2.x, r2.y, 0u, 0u};
+      }
       float4 mt[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        mt[r] = *reinterpret_cast<const float4*>(tile + (4 * kg + r) * kQRow + kD);
+        mt[r] = *reinterpret_cast<const float4*>(tile + (4 * kg + r) * F::kRow + F::kCode);
 
       f32x4_t cl[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
       f32x4_t cr = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        const u32x4_t& w = cv[ks >> 1];
-        const f16x8_t a = codes8_sub((ks & 1) ? u32x2_t{w.z, w.w} : u32x2_t{w.x, w.y});
+        f16x8_t a;
+        if constexpr (kBits == 8) {
+          const u32x4_t& w = cv[ks >> 1];
+          a = codes8_sub((ks & 1) ? u32x2_t{w.z, w.w} : u32x2_t{w.x, w.y});
+        } else {
+          const u32x4_t& w = cv[ks < kDC / 32 ? ks >> 2 : 4];
+          const int d = ks < kDC / 32 ? ks & 3 : ks - kDC / 32;
+          a = codes4_sub(d == 0 ? w.x : d == 1 ? w.y : d == 2 ? w.z : w.w);
+        }
         const f16x8_t qk = *reinterpret_cast<const f16x8_t*>(qb + ks * 1024);
         if (ks < kDC / 32)
           cl[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qk, cl[ks & 1], 0, 0, 0);
@@ -475,12 +544,15 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
           cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qk, cr, 0, 0, 0);
       }
       // the PV operands: their reads overlap the score and softmax arithmetic
-      uint32_t u[kFB][4];
+      // (8 bits: four codes of a token per dword, one dword per column block
+      // g; 4 bits: eight codes per dword, one dword per pair of blocks)
+      constexpr int kPB = kBits == 8 ? kFB : kFB / 2;
+      uint32_t u[kPB][4];
 #pragma unroll
-      for (int g = 0; g < kFB; ++g)
+      for (int g = 0; g < kPB; ++g)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          u[g][j] = *reinterpret_cast<const uint32_t*>(tile + brow + j * kQRow + 64 * g);
+          u[g][j] = *reinterpret_cast<const uint32_t*>(tile + brow + j * F::kRow + 64 * g);
 
       // ---- scores of row n, tokens 4 kg + r (log2 units)
       const f32x4_t al = cl[0] + cl[1];
@@ -555,23 +627,48 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
 #pragma unroll
       for (int r = 0; r < 4; ++r) pa[r] = (_Float16)x[r];
 
-      // the slot is read: subtile k + kQRing may land in it
-      if (k + kQRing < nk) {
+      // the slot is read: subtile k + kRing may land in it
+      if (k + F::kRing < nk) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         issue_next();
       }
 
       // ---- PV: all 512 latent columns of the 16 rows, K = this subtile's 16 tokens
+      if constexpr (kBits == 8) {
 #pragma unroll
-      for (int g = 0; g < kFB; ++g) {
+        for (int g = 0; g < kFB; ++g) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // column 64 g + 4 n + r of tokens 4 kg .. 4 kg + 3, as subnormals
-          const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + r) << 16) | (uint32_t)r;
-          const u32x2_t bw = {__builtin_amdgcn_perm(u[g][1], u[g][0], sel),
-                              __builtin_amdgcn_perm(u[g][3], u[g][2], sel)};
-          acc[g][r] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              pa, __builtin_bit_cast(f16x4_t, bw), acc[g][r], 0, 0, 0);
+          for (int r = 0; r < 4; ++r) {
+            // column 64 g + 4 n + r of tokens 4 kg .. 4 kg + 3, as subnormals
+            const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + r) << 16) | (uint32_t)r;
+            const u32x2_t bw = {__builtin_amdgcn_perm(u[g][1], u[g][0], sel),
+                                __builtin_amdgcn_perm(u[g][3], u[g][2], sel)};
+            acc[g][r] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                pa, __builtin_bit_cast(f16x4_t, bw), acc[g][r], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int gp = 0; gp < kFB / 2; ++gp) {
+          // the dword of token 4 kg + j holds columns 128 gp + 8 n .. + 7:
+          // low nibbles (even columns) and high nibbles (odd) as bytes
+          uint32_t lo[4], hi[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            lo[j] = u[gp][j] & 0x0f0f0f0fu;
+            hi[j] = (u[gp][j] >> 4) & 0x0f0f0f0fu;
+          }
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            // column 128 gp + 8 n + c: byte c / 2 of the low or high nibbles
+            const uint32_t i = (uint32_t)(c >> 1);
+            const uint32_t sel = 0x0c000c00u | ((4u + i) << 16) | i;
+            const uint32_t* src = (c & 1) ? hi : lo;
+            const u32x2_t bw = {__builtin_amdgcn_perm(src[1], src[0], sel),
+                                __builtin_amdgcn_perm(src[3], src[2], sel)};
+            acc[2 * gp + (c >> 2)][c & 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                pa, __builtin_bit_cast(f16x4_t, bw), acc[2 * gp + (c >> 2)][c & 3], 0, 0, 0);
+          }
         }
       }
     }
@@ -642,7 +739,8 @@ void decode_q8_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int orow = row0 + 4 * kg + r;
-        float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + 64 * g + 4 * n;
+        const int col = kBits == 8 ? 64 * g + 4 * n : 128 * (g >> 1) + 8 * n + 4 * (g & 1);
+        float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + col;
         float4 v = make_float4((sum[0][r] + base[r]) * inv[r], (sum[1][r] + base[r]) * inv[r],
                                (sum[2][r] + base[r]) * inv[r], (sum[3][r] + base[r]) * inv[r]);
         if (any_bad) v = make_float4(nanv, nanv, nanv, nanv);
@@ -670,20 +768,42 @@ bool decode_q8_ok(const Shape& s, int q_len) {
          (q_len * s.H) % 16 == 0;
 }
 
-int launch_decode_q8(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
-                     const void* q_full, const void* cache, int64_t num_pages,
-                     const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                     const int32_t* tree_parent, float* o_part, float* lse_part, void* stream) {
-  if (int e = set_max_lds(reinterpret_cast<const void*>(decode_q8_kernel), (int)kQLds)) return e;
+template <int kBits>
+static int launch_decode_qn(const Shape& s, int batch, int q_len, int num_splits,
+                            int max_seq_len, const void* q_full, const void* cache,
+                            int64_t num_pages, const int32_t* page_table, int max_pages,
+                            const int32_t* seq_lens, const int32_t* tree_parent, float* o_part,
+                            float* lse_part, void* stream) {
+  constexpr size_t kLds = QFmt<kBits>::kLds;
+  if (int e = set_max_lds(reinterpret_cast<const void*>(decode_q8_kernel<kBits>), (int)kLds))
+    return e;
   const int units = batch * num_splits;
   const int groups = q_len * s.H / 16;
   const int blocks = grid_blocks(units, groups);
-  hipLaunchKernelGGL(decode_q8_kernel, dim3(blocks), dim3(256), kQLds,
+  hipLaunchKernelGGL(decode_q8_kernel<kBits>, dim3(blocks), dim3(256), kLds,
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page,
                      s.split_fixed, max_seq_len, s.scale * 1.4426950408889634f, units, groups,
                      (const bf16_t*)q_full, (const uint8_t*)cache, num_pages, page_table,
                      max_pages, seq_lens, tree_parent, o_part, lse_part);
   return (int)hipGetLastError();
+}
+
+int launch_decode_q8(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
+                     const void* q_full, const void* cache, int64_t num_pages,
+                     const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                     const int32_t* tree_parent, float* o_part, float* lse_part, void* stream) {
+  return launch_decode_qn<8>(s, batch, q_len, num_splits, max_seq_len, q_full, cache, num_pages,
+                             page_table, max_pages, seq_lens, tree_parent, o_part, lse_part,
+                             stream);
+}
+
+int launch_decode_q4(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,
+                     const void* q_full, const void* cache, int64_t num_pages,
+                     const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                     const int32_t* tree_parent, float* o_part, float* lse_part, void* stream) {
+  return launch_decode_qn<4>(s, batch, q_len, num_splits, max_seq_len, q_full, cache, num_pages,
+                             page_table, max_pages, seq_lens, tree_parent, o_part, lse_part,
+                             stream);
 }
 
 }  // namespace mla

@@ -36,11 +36,13 @@ class DecodeStep:
 
     def __init__(self, cfg: B.Config, batch: int, q_len: int, num_splits: int,
                  seq_lens_host, device="cuda", split_chunk: int = 0, tree_parents=None,
-                 cache_q8: bool = False, index_topk: int = 0):
+                 cache_q8: bool = False, index_topk: int = 0, cache_bits: int = 0):
         t = _torch()
         self.cfg, self.batch, self.q_len, self.num_splits = cfg, batch, q_len, num_splits
         self.split_chunk = split_chunk  # > 0: fixed-size partitions
-        self.cache_q8 = cache_q8        # the cache holds 8-bit rows
+        # bits of the cache's codes: 0 (rows in the workload dtype), 8 or 4
+        self.cache_bits = cache_bits or (8 if cache_q8 else 0)
+        self.cache_q8 = self.cache_bits != 0  # (either coded format)
         H, D, dc, dv = cfg.num_heads, cfg.dim, cfg.kv_rank, cfg.v_dim
         dt = dtype_of(cfg)
         lens = [int(x) for x in seq_lens_host]
@@ -83,9 +85,10 @@ class DecodeStep:
 
     def append(self, c_new, k_new, page_table, cache, stream=None):
         if self.cache_q8:
-            B.cache_append_q8(self.cfg, c_new, k_new, self.seq_idx, self.slot,
-                              None if self.tree is None else self.qpos, page_table, cache,
-                              B.APPEND_ROTATE, stream)
+            app = B.cache_append_q8 if self.cache_bits == 8 else B.cache_append_q4
+            app(self.cfg, c_new, k_new, self.seq_idx, self.slot,
+                None if self.tree is None else self.qpos, page_table, cache, B.APPEND_ROTATE,
+                stream)
         elif self.tree is None:
             B.cache_append(self.cfg, c_new, k_new, self.seq_idx, self.slot, page_table, cache,
                            B.APPEND_ROTATE, stream)
@@ -117,9 +120,10 @@ class DecodeStep:
                             self.counts, self.o_part, self.lse_part,
                             max_seq_len or self.max_seq_len, stream)
         elif self.cache_q8:
-            B.decode_paged_q8(self.cfg, self.q_full, cache, page_table, seq_lens, self.o_part,
-                              self.lse_part, max_seq_len or self.max_seq_len, stream,
-                              chunk_tokens=self.split_chunk, tree_parent=self.tree)
+            dec = B.decode_paged_q8 if self.cache_bits == 8 else B.decode_paged_q4
+            dec(self.cfg, self.q_full, cache, page_table, seq_lens, self.o_part, self.lse_part,
+                max_seq_len or self.max_seq_len, stream, chunk_tokens=self.split_chunk,
+                tree_parent=self.tree)
         elif self.tree is None:
             B.decode_paged(self.cfg, self.q_full, cache, page_table, seq_lens, self.o_part,
                            self.lse_part, max_seq_len or self.max_seq_len, stream,
@@ -193,14 +197,16 @@ def fill_index_cache(cfg: B.Config, index_cache, page_table, k_all, seq_idx, pos
 
 
 def fill_cache_q8(cfg: B.Config, cache_q8, page_table, c_all, k_all, seq_idx, pos, stream=None,
-                  rows_per_call: int = 1 << 20, rope_pos=None):
-    """fill_cache for an 8-bit cache (cache_q8 uint8 [num_pages][page][D + 16])."""
+                  rows_per_call: int = 1 << 20, rope_pos=None, bits: int = 8):
+    """fill_cache for an 8-bit cache (cache_q8 uint8 [num_pages][page][D + 16]),
+    or with bits=4 a 4-bit one ([num_pages][page][D / 2 + 16])."""
+    app = B.cache_append_q8 if bits == 8 else B.cache_append_q4
     n = int(pos.numel())
     for a in range(0, n, rows_per_call):
         e = min(n, a + rows_per_call)
-        B.cache_append_q8(cfg, c_all[a:e], k_all[a:e], seq_idx[a:e], pos[a:e],
-                          None if rope_pos is None else rope_pos[a:e], page_table, cache_q8,
-                          B.APPEND_ROTATE, stream)
+        app(cfg, c_all[a:e], k_all[a:e], seq_idx[a:e], pos[a:e],
+            None if rope_pos is None else rope_pos[a:e], page_table, cache_q8, B.APPEND_ROTATE,
+            stream)
 
 
 def fill_cache(cfg: B.Config, cache, page_table, c_all, k_all, seq_idx, pos, stream=None,

@@ -63,18 +63,22 @@ class Case:
         dt = dtype_of(cfg)
         self.dt = dt
         B, Q, H = wl.batch, wl.q_len, wl.heads
-        self.q8 = wl.cache == "q8"
-        if self.q8:  # poison: every byte 0xFF (codes 255, NaN minima and steps)
-            self.pool = torch.full((inp.num_pages, cfg.page_size, cfg.dim + 16), 255,
+        self.bits = {"q8": 8, "q4": 4}.get(wl.cache, 0)
+        self.q8 = self.bits != 0  # a coded cache (8 or 4 bits)
+        if self.q8:  # poison: every byte 0xFF (codes 255 / 15, NaN minima and steps)
+            self.pool = torch.full((inp.num_pages, cfg.page_size, wl.cache_row_bytes), 255,
                                    dtype=torch.uint8, device="cuda")
         else:
             self.pool = poisoned_pool(cfg, inp.num_pages)
         self.pt = upload(inp.page_table, torch.int32)
         self.seq_lens = upload(inp.seq_lens, torch.int32)
         si, pos = tok_index(inp)
-        fill = fill_cache_q8 if self.q8 else fill_cache
-        fill(cfg, self.pool, self.pt, upload(inp.c, dt), upload(inp.k_rope, dt),
-             upload(si, torch.int32), upload(pos, torch.int32))
+        if self.q8:
+            fill_cache_q8(cfg, self.pool, self.pt, upload(inp.c, dt), upload(inp.k_rope, dt),
+                          upload(si, torch.int32), upload(pos, torch.int32), bits=self.bits)
+        else:
+            fill_cache(cfg, self.pool, self.pt, upload(inp.c, dt), upload(inp.k_rope, dt),
+                       upload(si, torch.int32), upload(pos, torch.int32))
         self.q_nope = upload(np.ascontiguousarray(inp.q_nope), dt)
         self.q_rope = upload(np.ascontiguousarray(inp.q_rope), dt)
         self.w_uk = upload(inp.w_uk, dt)
@@ -95,7 +99,7 @@ class Case:
             self.k_idx_new = upload(inp.k_idx[rows], dt)
             self.sparse = (self.q_idx, self.w_idx, self.k_idx_new, self.index_pool)
         self.step = DecodeStep(cfg, B, Q, self.S, inp.seq_lens, split_chunk=self.chunk,
-                               tree_parents=inp.parents, cache_q8=self.q8,
+                               tree_parents=inp.parents, cache_bits=self.bits,
                                index_topk=wl.index_topk)
         if inp.parents is not None:
             # the fill rotated every key at its slot; a drafted tree's rows are
@@ -117,8 +121,8 @@ class Case:
     def oracle(self, heads=None, seqs=None, selection=None):
         if self.wl.index_topk > 0:  # attention over the oracle's own selection
             return oracle.mla_decode_ref_sparse(self.inp, selection, heads=heads, seqs=seqs)
-        if self.q8:  # the attention over the rows the 8-bit cache encodes
-            return oracle.mla_decode_ref_q8(self.inp, heads=heads, seqs=seqs)
+        if self.q8:  # the attention over the rows the coded cache encodes
+            return oracle.mla_decode_ref_q8(self.inp, heads=heads, seqs=seqs, bits=self.bits)
         return oracle.mla_decode_ref(self.inp, heads=heads, seqs=seqs)
 
 

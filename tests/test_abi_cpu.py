@@ -258,6 +258,25 @@ def test_q8_entry_errors(L):
     assert L.mla_cache_append_q8(_c(odd), 8, *args, None, A16, 2, 4, A16, 16, 1, None) == 6
 
 
+def test_q4_entry_errors(L):
+    assert L.mla_cache_q4_bytes_per_token(_c(V2)) == 304             # 576 / 2 + 16
+    assert L.mla_cache_q4_bytes_per_token(_c(TINY)) == 0             # D = 80: not a multiple of 32
+    ok = mla.Config(num_heads=4, kv_rank=112, rope_dim=16, nope_dim=32, v_dim=32, dtype=mla.F32)
+    assert L.mla_cache_q4_bytes_per_token(_c(ok)) == 80               # 128 / 2 + 16
+    odd = mla.Config(num_heads=4, kv_rank=64, rope_dim=8, nope_dim=32, v_dim=32, dtype=mla.F32)
+    assert L.mla_cache_q4_bytes_per_token(_c(odd)) == 0              # D = 72: not a multiple of 32
+    def dec(cfg=V2, q_len=1, batch=2, S=4, tree=None, o=A16):
+        return L.mla_decode_paged_q4(_c(cfg), batch, q_len, 0, S, 256, A16, A16, 8, A16, 4,
+                                     A16, tree, o, A16, None)
+    assert dec(o=None) == 1 and dec(tree=MIS) == 4 and dec(q_len=65, tree=A16) == 2
+    assert dec(cfg=mla.Config(num_heads=8)) == 6 and dec(cfg=TINY) == 6
+    assert dec(batch=0) == 0
+    args = [A16, A16, A16, A16]
+    assert L.mla_cache_append_q4(_c(V2), 8, *args, MIS, A16, 2, 4, A16, 16, 1, None) == 4
+    assert L.mla_cache_append_q4(_c(V2), 8, *args, None, A16, 2, 4, None, 16, 1, None) == 1
+    assert L.mla_cache_append_q4(_c(odd), 8, *args, None, A16, 2, 4, A16, 16, 1, None) == 6
+
+
 def test_sparse_entry_errors(L):
     c = _c(V2)
     # indexer key append: width rule, pointers, alignment, empty call
