@@ -51,6 +51,9 @@ DECODE_KERNELS = {
     "mfma_q4": ("decode_q8_kernel<4>", ["mla_decode_common.h", "mla_q8.hip"]),
     # sparse read: the indexer pass is the step's dominant kernel
     "index_scores_mfma": ("index_scores_mfma_kernel<false>", ["mla_decode_common.h", "mla_sparse.hip"]),
+    # prefill chunk in the unabsorbed form: one library call, three launches
+    "prefill_unabsorbed": ("prefill_expand_kernel + prefill_query_kernel + prefill_attn_kernel",
+                           ["mla_decode_common.h", "mla_prefill.hip"]),
 }
 
 
@@ -66,6 +69,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--graph", action="store_true", help="replay each layer's step as a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-form", choices=["auto", "absorbed", "unabsorbed"], default="auto",
+                    help="prefill chunks (q_len >= 64): the form the step takes (auto: the "
+                         "library's choice, mla_prefill_form)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as five library calls instead of three")
     ap.add_argument("--no-stream-read", action="store_true",
@@ -328,7 +334,33 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def one_step(layer):
+    # prefill chunk: the absorbed form (the decode calls with q_len = C) or the
+    # unabsorbed one (append the chunk, then mla_prefill_unabsorbed per sequence)
+    prefill = Q >= PREFILL_MIN_Q
+    form = None
+    if prefill:
+        form = (mla.prefill_form(cfg, Q, int(inp.seq_lens.max())) if args.prefill_form == "auto"
+                else args.prefill_form)
+        un_ok = mla.prefill_form(cfg, 4096, 4096) == "unabsorbed"  # the form is supported
+        if un_ok:
+            ws_u = [torch.empty(mla.prefill_workspace_bytes(cfg, int(L), Q), dtype=torch.uint8,
+                                device="cuda") for L in inp.seq_lens]
+            out_u = torch.empty((B, Q, H, wl.v_dim), dtype=dt, device="cuda")
+            lse_u = torch.empty((B, Q, H), dtype=torch.float32, device="cuda")
+            qn_b = [q_nope[b].contiguous() for b in range(B)]
+            qr_b = [q_rope[b].contiguous() for b in range(B)]
+
+        def unabsorbed_call(pool):
+            for b in range(B):
+                mla.prefill_unabsorbed(cfg, qn_b[b], qr_b[b], w_uk, w_uv, pool, pt[b],
+                                       int(inp.seq_lens[b]), ws_u[b], out_u[b], lse_u[b])
+
+    def unabsorbed_step(layer):
+        pool = pools[layer % n_layers]
+        st.append(c_new, k_new, pt, pool)
+        unabsorbed_call(pool)
+
+    def absorbed_step(layer):
         pool = pools[layer % n_layers]
         if args.unfused:
             st.absorb(q_nope, q_rope, w_uk)
@@ -349,6 +381,8 @@ def main():
             st.up_project(w_uv)
         else:
             st.combine_up_project(w_uv)
+
+    one_step = unabsorbed_step if form == "unabsorbed" else absorbed_step
 
     graphs = None
     if args.graph:
@@ -382,6 +416,31 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- prefill: the step in both forms (the other one after the timed
+    # region), and the unabsorbed call alone back to back
+    forms = None
+    if prefill and un_ok:
+        def time_steps(fn, k):
+            torch.cuda.synchronize()
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(k):
+                fn(i)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b_) / k
+        kf = max(3, min(args.steps, 20))
+        other = absorbed_step if form == "unabsorbed" else unabsorbed_step
+        other(0)
+        ms_other = time_steps(other, kf)
+        for i in range(n_layers):  # every layer cache holds the chunk
+            st.append(c_new, k_new, pt, pools[i])
+        un_call_ms = time_steps(lambda i: unabsorbed_call(pools[i % n_layers]), kf)
+        forms = {"picked": form,
+                 "absorbed_step_us": round(1e3 * (ms_step if form != "unabsorbed" else ms_other), 1),
+                 "unabsorbed_step_us": round(1e3 * (ms_step if form == "unabsorbed" else ms_other), 1),
+                 "unabsorbed_call_us": round(1e3 * un_call_ms, 1)}
 
     # ---- average duration of the decode kernel: kd launches back to back on
     # the launch stream (rotating the layer caches as the step does), between
@@ -440,6 +499,8 @@ def main():
     decode_call_avg = sum(d_ms) / len(d_ms)
     decode_med = d_ms[len(d_ms) // 2]
     dc_med = dc_ms[len(dc_ms) // 2]
+    if form == "unabsorbed":  # the picked form's call (no split partials to merge)
+        decode_call_avg = decode_med = dc_med = un_call_ms
 
     # ---- algorithmic work
     total_tokens = int(inp.seq_lens.astype(np.int64).sum())
@@ -457,8 +518,17 @@ def main():
         # every (query row, visible token) pair: 2 * D for the score, 2 * d_c for P.V
         flops = visible_pairs(wl, inp) * H * (2 * wl.dim + 2 * wl.kv_rank)
         kernel = {8: "mfma_q8", 4: "mfma_q4"}[bits] if q8 else mla.decode_kernel_kind(cfg, Q)
+    if form == "unabsorbed":
+        # the picked form's work: the expansion of every cached token (2 x 512
+        # x 256 flops per token and head) and the per-head attention (2 x 192
+        # + 2 x 128 per visible pair), timed as one library call (3 launches)
+        flops = (visible_pairs(wl, inp) * H * (2 * (wl.nope_dim + wl.rope_dim) + 2 * wl.v_dim)
+                 + total_tokens * H * 2 * wl.kv_rank * (wl.nope_dim + wl.v_dim))
+        kernel = "prefill_unabsorbed"
     cache_bytes = kernel_bytes
     gbs_step = step_bytes / (ms_step * 1e-3) / 1e9
+    if form == "unabsorbed":
+        decode_ms = un_call_ms
     gbs_decode = cache_bytes / (decode_ms * 1e-3) / 1e9
     tflops_decode = flops / (decode_ms * 1e-3) / 1e12
     ai = flops / cache_bytes
@@ -525,6 +595,7 @@ def main():
     if Q >= PREFILL_MIN_Q:
         out["prefill_tokens_per_s"] = round(B * Q / (ms_step * 1e-3), 1)
         out["prefill_step_tflops"] = round(flops / (ms_step * 1e-3) / 1e12, 2)
+        out["prefill_forms"] = forms
     elif wl.name.startswith("v2lite"):
         out["v2lite_attention_tokens_per_s_27_layers"] = round(B / (27 * ms_step * 1e-3), 1)
     props = torch.cuda.get_device_properties(0)

@@ -503,6 +503,44 @@ mla_status_t mla_combine_up_project(const mla_config_t* cfg, int32_t batch, int3
                                     const float* lse_part, void* o_lat, float* lse,
                                     const void* w_uv, void* out, void* stream);
 
+/* Chunked prefill in the unabsorbed form ("Beyond the Attention Bottleneck",
+ * "Chunked Prefilling": the prompt enters the cache chunk by chunk, each
+ * chunk's queries attending to the cache as it then stands; "Down-Projection
+ * and Up-Projection Mechanics" for the per-head keys K^C = W_UK c and values
+ * V = W_UV c). One sequence: its q_len newest cached tokens (already
+ * appended, e.g. by mla_cache_append with MLA_APPEND_ROTATE) are the chunk,
+ * query i sits at position p = seq_len - q_len + i and sees tokens t <= p.
+ * Every cached latent is expanded into per-head keys and values (in the
+ * workspace), then each head runs dense causal attention over 192-wide keys
+ * [K^C ; RoPE key] and 128-wide values:
+ *   out[i][h] = sum_t softmax_t(scale * q[i][h] . k[t][h]) V[t][h]   (d_v wide)
+ *   lse[i][h] = natural log of the softmax denominator (as mla_splitkv_combine)
+ * with q[i][h] = [q_nope[i][h] ; RoPE(q_rope[i][h], p)]. This is the same
+ * attention as the absorbed form (the decode with q_len = C, then the merge
+ * and the up-projection) without its latent output o_lat; it costs 640
+ * instead of 2,176 flops per (query row, token) plus the expansion.
+ * q_nope [q_len][H][d_n] bf16, q_rope [q_len][H][d_r] bf16 (unrotated), w_uk
+ * [H][d_n][d_c], w_uv [H][d_v][d_c] bf16, cache as for mla_decode_paged,
+ * page_row [max_pages] int32: this sequence's row of the page table (4-byte
+ * alignment suffices for it),
+ * workspace: mla_prefill_workspace_bytes(cfg, seq_len, q_len) bytes of device
+ * memory (contents need not be initialised), out [q_len][H][d_v] bf16, lse
+ * [q_len][H] f32. MLA_ERR_UNSUPPORTED unless bf16 with d_c = 512, d_r = 64,
+ * d_n = d_v = 128. Tokens with an invalid page read as zero rows. */
+size_t mla_prefill_workspace_bytes(const mla_config_t* cfg, int32_t seq_len, int32_t q_len);
+mla_status_t mla_prefill_unabsorbed(const mla_config_t* cfg, int32_t q_len, int32_t seq_len,
+                                    const void* q_nope, const void* q_rope, const void* w_uk,
+                                    const void* w_uv, const void* cache, int64_t num_pages,
+                                    const int32_t* page_row, int32_t max_pages,
+                                    void* workspace, void* out, float* lse, void* stream);
+
+/* Which form a prefill chunk of q_len tokens over seq_len cached tokens
+ * should take: "unabsorbed" (mla_prefill_unabsorbed) when that form is
+ * supported and q_len >= 1,024, where its lower flop count outweighs expanding
+ * every cached token; else "absorbed" (the decode calls with q_len tokens).
+ * "invalid" for invalid arguments. Static string. */
+const char* mla_prefill_form(const mla_config_t* cfg, int32_t q_len, int32_t seq_len);
+
 /* Measurement aid, not part of the decode: reads `bytes` of device memory
  * (a multiple of 16, buf 16-byte aligned) with 16-byte non-temporal loads
  * spread over `blocks` blocks of 256 threads (1 .. 65,536) and writes one

@@ -69,4 +69,7 @@ from ._binding import (  # noqa: F401
     stream_read,
     index_scores_topk_noalloc,
     TOPK_NOALLOC_MAX_QUERIES,
+    prefill_workspace_bytes,
+    prefill_form,
+    prefill_unabsorbed,
 )

@@ -144,6 +144,10 @@ def lib() -> ctypes.CDLL:
                                                          I64, VP, I32, VP, FP, I32, I32, VP, VP,
                                                          VP]),
         "mla_stream_read": (ctypes.c_int, [VP, ctypes.c_size_t, VP, I32, VP]),
+        "mla_prefill_workspace_bytes": (ctypes.c_size_t, [P, I32, I32]),
+        "mla_prefill_unabsorbed": (ctypes.c_int, [P, I32, I32, VP, VP, VP, VP, VP, I64, VP, I32,
+                                                  VP, VP, FP, VP]),
+        "mla_prefill_form": (ctypes.c_char_p, [P, I32, I32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -350,6 +354,40 @@ def stream_read(buf, sink, stream=None):
     _ck(lib().mla_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
                               _need(sink, "sink", t.int32, blocks), blocks, _stream(stream)),
         "mla_stream_read")
+
+
+def prefill_workspace_bytes(cfg: Config, seq_len: int, q_len: int) -> int:
+    """Bytes of the workspace of prefill_unabsorbed."""
+    return int(lib().mla_prefill_workspace_bytes(cfg.cptr(), int(seq_len), int(q_len)))
+
+
+def prefill_form(cfg: Config, q_len: int, seq_len: int) -> str:
+    """"unabsorbed" or "absorbed": the form a prefill chunk should take."""
+    return lib().mla_prefill_form(cfg.cptr(), int(q_len), int(seq_len)).decode()
+
+
+def prefill_unabsorbed(cfg: Config, q_nope, q_rope, w_uk, w_uv, cache, page_row, seq_len: int,
+                       workspace, out, lse, stream=None):
+    """The unabsorbed prefill of one sequence's newest q_len cached tokens:
+    q_nope [q_len][H][d_n], q_rope [q_len][H][d_r] (unrotated), page_row
+    [max_pages] int32 (the sequence's page-table row), workspace uint8 of
+    prefill_workspace_bytes; out [q_len][H][d_v], lse [q_len][H] f32."""
+    t = _torch()
+    C = int(q_nope.shape[0])
+    H, dt = cfg.num_heads, _elem_dtype(cfg)
+    if cache.dim() != 3 or cache.shape[1] != cfg.page_size or cache.shape[2] != cfg.dim:
+        raise ValueError(f"cache: expected [num_pages][{cfg.page_size}][{cfg.dim}]")
+    max_pages = int(page_row.numel())
+    _ck(lib().mla_prefill_unabsorbed(
+        cfg.cptr(), C, int(seq_len), _need(q_nope, "q_nope", dt, C * H * cfg.nope_dim),
+        _need(q_rope, "q_rope", dt, C * H * cfg.rope_dim),
+        _need(w_uk, "w_uk", dt, H * cfg.nope_dim * cfg.kv_rank),
+        _need(w_uv, "w_uv", dt, H * cfg.v_dim * cfg.kv_rank),
+        _need(cache, "cache", dt, cache.numel()), int(cache.shape[0]),
+        _need(page_row, "page_row", t.int32, max_pages), max_pages,
+        _need(workspace, "workspace", t.uint8, prefill_workspace_bytes(cfg, seq_len, C)),
+        _need(out, "out", dt, C * H * cfg.v_dim), _need(lse, "lse", t.float32, C * H),
+        _stream(stream)), "mla_prefill_unabsorbed")
 
 
 def cache_q8_bytes_per_token(cfg: Config) -> int:

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libmla.so")
 ARCH = "gfx950"
 
 SOURCES = ["mla_api.cpp", "mla_kernels.hip", "mla_decode_rows16.hip", "mla_decode_ws.hip",
-           "mla_proj_mfma.hip", "mla_q8.hip", "mla_sparse.hip"]
+           "mla_proj_mfma.hip", "mla_q8.hip", "mla_sparse.hip", "mla_prefill.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -284,6 +284,50 @@ mla_status_t mla_draft_positions(int32_t batch, int32_t q_len, int32_t max_seq_l
                                                 seq_idx, slot, pos, stream));
 }
 
+namespace {
+constexpr int kPrefillUnabsorbedMinQ = 1024;  // from measured chunk times of both forms
+}  // namespace
+
+size_t mla_prefill_workspace_bytes(const mla_config_t* cfg, int32_t seq_len, int32_t q_len) {
+  if (check_config(cfg) != MLA_OK || q_len < 1 || seq_len < q_len) return 0;
+  return mla::prefill_workspace_bytes(shape_of(cfg), seq_len, q_len);
+}
+
+const char* mla_prefill_form(const mla_config_t* cfg, int32_t q_len, int32_t seq_len) {
+  if (check_config(cfg) != MLA_OK || q_len < 1 || seq_len < q_len) return "invalid";
+  return mla::prefill_unabsorbed_ok(shape_of(cfg)) && q_len >= kPrefillUnabsorbedMinQ
+             ? "unabsorbed"
+             : "absorbed";
+}
+
+mla_status_t mla_prefill_unabsorbed(const mla_config_t* cfg, int32_t q_len, int32_t seq_len,
+                                    const void* q_nope, const void* q_rope, const void* w_uk,
+                                    const void* w_uv, const void* cache, int64_t num_pages,
+                                    const int32_t* page_row, int32_t max_pages,
+                                    void* workspace, void* out, float* lse, void* stream) {
+  mla_status_t st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(q_len >= 1 && max_pages >= 1 && num_pages >= 1, MLA_ERR_SHAPE);
+  MLA_REQUIRE(seq_len >= q_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size >= (int64_t)seq_len, MLA_ERR_CAPACITY);
+  MLA_REQUIRE((int64_t)seq_len * cfg->num_heads <= INT32_MAX / 2, MLA_ERR_SHAPE);
+  const mla::Shape sh = shape_of(cfg);
+  MLA_REQUIRE(mla::prefill_unabsorbed_ok(sh), MLA_ERR_UNSUPPORTED);
+  MLA_CHECK_PTR(q_nope);
+  MLA_CHECK_PTR(q_rope);
+  MLA_CHECK_PTR(w_uk);
+  MLA_CHECK_PTR(w_uv);
+  MLA_CHECK_PTR(cache);
+  MLA_REQUIRE(page_row, MLA_ERR_NULL);  // a row of the page table: 4-byte aligned suffices
+  MLA_REQUIRE((reinterpret_cast<uintptr_t>(page_row) & 3u) == 0, MLA_ERR_ALIGN);
+  MLA_CHECK_PTR(workspace);
+  MLA_CHECK_PTR(out);
+  MLA_CHECK_PTR(lse);
+  return hip_status(mla::launch_prefill_unabsorbed(sh, q_len, seq_len, q_nope, q_rope, w_uk, w_uv,
+                                                   cache, num_pages, page_row, max_pages,
+                                                   workspace, out, lse, stream));
+}
+
 mla_status_t mla_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,
                              void* stream) {
   MLA_REQUIRE(bytes % 16 == 0 && blocks >= 1 && blocks <= 65536, MLA_ERR_SHAPE);

@@ -105,6 +105,19 @@ int launch_decode_q4(const Shape& s, int batch, int q_len, int num_splits, int m
                      const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                      const int32_t* tree_parent, float* o_part, float* lse_part, void* stream);
 
+// Chunked prefill in the unabsorbed form: one sequence, q_len query tokens
+// at positions seq_len - q_len + i (their rows already in the cache), bf16
+// with d_c = 512, d_r = 64, d_n = d_v = 128 (prefill_unabsorbed_ok). The
+// workspace holds the expanded keys and values, the RoPE keys and the
+// rotated queries (prefill_workspace_bytes).
+bool prefill_unabsorbed_ok(const Shape& s);
+size_t prefill_workspace_bytes(const Shape& s, int seq_len, int q_len);
+int launch_prefill_unabsorbed(const Shape& s, int q_len, int seq_len, const void* q_nope,
+                              const void* q_rope, const void* w_uk, const void* w_uv,
+                              const void* cache, int64_t num_pages, const int32_t* page_row,
+                              int max_pages, void* workspace, void* out, float* lse,
+                              void* stream);
+
 // Which decode kernel a shape takes (for tests and tools): 0 = generic VALU
 // kernel, 1 = bf16 MFMA kernel with 16 query rows per block, 2 = bf16 MFMA
 // kernel with 64 query rows per block.
