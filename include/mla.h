@@ -18,10 +18,13 @@
  *                       two pairs of the above, each in one launch
  * Verifying a tree of drafted tokens instead of a chain takes
  * mla_absorb_append_at / mla_cache_append_at (a token's cache slot and its
- * RoPE position differ) and mla_decode_paged_tree (the tree mask). An 8-bit
- * cache takes mla_cache_append_q8 / mla_decode_paged_q8; a sparse read
- * (attention over the top-scored tokens only) takes mla_index_append,
- * mla_index_scores, mla_topk_select and mla_decode_sparse.
+ * RoPE position differ) and mla_decode_paged_tree (the tree mask), with the
+ * drafted rows' slots and positions from mla_draft_positions. An 8-bit
+ * cache takes mla_cache_append_q8 (or mla_absorb_append_q8) and
+ * mla_decode_paged_q8, a 4-bit one the _q4 calls; a sparse read (attention
+ * over the top-scored tokens only) takes mla_index_append, mla_index_scores,
+ * mla_topk_select and mla_decode_sparse. A chunked prefill runs the decode
+ * calls with q_len = C, or mla_prefill_unabsorbed.
  *
  * Conventions shared by every call
  *   - Every pointer argument except `cfg` is a DEVICE pointer; `cfg` is a host
@@ -29,10 +32,11 @@
  *     library never allocates, frees or keeps a pointer after returning.
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and returns once the work is enqueued. The
- *     library holds no per-call state; the one thing it remembers is which
- *     kernels have had their LDS limit raised on which device (set under a
- *     lock on first use), so calls may come from several threads. Calls that
- *     write the same buffers must not overlap.
+ *     library holds no per-call state; what it remembers across calls
+ *     (which kernels have had their LDS limit raised on which device, and
+ *     the device address of mla_index_scores_topk_noalloc's array) is set
+ *     under a lock on first use, so calls may come from several threads.
+ *     Calls that write the same buffers must not overlap.
  *   - Layouts are dense, row-major, in the order written in brackets; element
  *     type "T" is cfg->dtype (fp32 or bf16) for queries, weights, cache and
  *     outputs; partials are always fp32.
@@ -341,6 +345,32 @@ mla_status_t mla_cache_append_q4(const mla_config_t* cfg, int32_t n_tok, const v
                                  const int32_t* rope_pos, const int32_t* page_table,
                                  int32_t batch, int32_t max_pages, void* cache_q4,
                                  int64_t num_pages, int32_t flags, void* stream);
+
+/* The query absorption and the coded append in one launch: the same
+ * arguments, work and results (bit for bit) as
+ *   mla_absorb_q(cfg, n_tok, q_nope, q_rope, pos_q, w_uk, q_full, stream);
+ *   mla_cache_append_q8(cfg, n_app, c_kv, k_rope, seq_idx, pos, rope_pos,
+ *                       page_table, batch, max_pages, cache_q8, num_pages,
+ *                       flags, stream);      (mla_absorb_append_q4: ..._q4)
+ * whose outputs are disjoint; the absorbed query of a step and its new rows
+ * of an 8-bit or 4-bit cache ("KV Cache Optimization: Scaling to
+ * Million-Token Contexts", technique 3). One launch when the absorption
+ * runs on bf16 MFMA, the two launches otherwise. Errors as for the two
+ * calls (the absorb arguments are checked first). */
+mla_status_t mla_absorb_append_q8(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                                  const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                                  void* q_full, int32_t n_app, const void* c_kv,
+                                  const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                  const int32_t* rope_pos, const int32_t* page_table,
+                                  int32_t batch, int32_t max_pages, void* cache_q8,
+                                  int64_t num_pages, int32_t flags, void* stream);
+mla_status_t mla_absorb_append_q4(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                                  const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                                  void* q_full, int32_t n_app, const void* c_kv,
+                                  const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                  const int32_t* rope_pos, const int32_t* page_table,
+                                  int32_t batch, int32_t max_pages, void* cache_q4,
+                                  int64_t num_pages, int32_t flags, void* stream);
 mla_status_t mla_decode_paged_q4(const mla_config_t* cfg, int32_t batch, int32_t q_len,
                                  int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
                                  const void* q_full, const void* cache_q4, int64_t num_pages,

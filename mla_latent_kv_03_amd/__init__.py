@@ -20,7 +20,8 @@ position, derived on the device from the tree), cache_append_at /
 absorb_append_at and decode_paged_tree. An 8-bit latent cache (uint8 rows
 of codes plus per-part min and step) is written by cache_append_q8 and read
 by decode_paged_q8; a 4-bit one (two codes per byte) by cache_append_q4 and
-decode_paged_q4. A sparse read (attention over the top-scored tokens
+decode_paged_q4 (absorb_append_coded runs the absorption and either coded
+append in one launch). A sparse read (attention over the top-scored tokens
 only) runs index_append, index_scores, topk_select and decode_sparse.
 """
 from ._binding import (  # noqa: F401
@@ -72,4 +73,5 @@ from ._binding import (  # noqa: F401
     prefill_workspace_bytes,
     prefill_form,
     prefill_unabsorbed,
+    absorb_append_coded,
 )

@@ -148,6 +148,10 @@ def lib() -> ctypes.CDLL:
         "mla_prefill_unabsorbed": (ctypes.c_int, [P, I32, I32, VP, VP, VP, VP, VP, I64, VP, I32,
                                                   VP, VP, FP, VP]),
         "mla_prefill_form": (ctypes.c_char_p, [P, I32, I32]),
+        "mla_absorb_append_q8": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, I32, VP, VP, VP, VP,
+                                                VP, VP, I32, I32, VP, I64, I32, VP]),
+        "mla_absorb_append_q4": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, I32, VP, VP, VP, VP,
+                                                VP, VP, I32, I32, VP, I64, I32, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -403,6 +407,20 @@ def cache_append_q8(cfg: Config, c_kv, k_rope, seq_idx, pos, rope_pos, page_tabl
     rp = _rope_pos_arg(rope_pos, a[0])
     _ck(lib().mla_cache_append_q8(cfg.cptr(), *a[:5], rp, *a[5:], _stream(stream)),
         "mla_cache_append_q8")
+
+
+def absorb_append_coded(cfg: Config, bits: int, q_nope, q_rope, pos_q, w_uk, q_full, c_kv,
+                        k_rope, seq_idx, pos, rope_pos, page_table, cache,
+                        mode: int = APPEND_ROTATE, stream=None):
+    """absorb_q followed by cache_append_q8 (bits 8) or cache_append_q4 (bits 4),
+    in one launch where possible (mla_absorb_append_q8 / _q4)."""
+    if bits not in (8, 4):
+        raise ValueError("bits: 8 or 4")
+    a = _absorb_args(cfg, q_nope, q_rope, pos_q, w_uk, q_full)
+    b = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode, bits=bits)
+    rp = _rope_pos_arg(rope_pos, b[0])
+    name = "mla_absorb_append_q8" if bits == 8 else "mla_absorb_append_q4"
+    _ck(getattr(lib(), name)(cfg.cptr(), *a, *b[:5], rp, *b[5:], _stream(stream)), name)
 
 
 def cache_q4_bytes_per_token(cfg: Config) -> int:

@@ -515,6 +515,55 @@ mla_status_t mla_cache_append_q4(const mla_config_t* cfg, int32_t n_tok, const v
                       max_pages, cache_q4, num_pages, flags, stream);
 }
 
+namespace {
+
+mla_status_t absorb_append_coded(int bits, const mla_config_t* cfg, int32_t n_tok,
+                                 const void* q_nope, const void* q_rope, const int32_t* pos_q,
+                                 const void* w_uk, void* q_full, int32_t n_app, const void* c_kv,
+                                 const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                 const int32_t* rope_pos, const int32_t* page_table,
+                                 int32_t batch, int32_t max_pages, void* cache,
+                                 int64_t num_pages, int32_t flags, void* stream) {
+  mla_status_t st = check_absorb(cfg, n_tok, q_nope, q_rope, pos_q, w_uk, q_full);
+  if (st != MLA_OK) return st;
+  st = check_append(cfg, n_app, c_kv, k_rope, seq_idx, pos, page_table, batch, max_pages, cache,
+                    num_pages, flags);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE(coded_row_bytes(cfg, bits) != 0, MLA_ERR_UNSUPPORTED);
+  if (n_tok == 0 && n_app == 0) return MLA_OK;
+  if (n_app > 0 && rope_pos) MLA_CHECK_PTR(rope_pos);
+  return hip_status(mla::launch_absorb_append_coded(
+      bits, shape_of(cfg), n_tok, q_nope, q_rope, pos_q, w_uk, q_full, n_app, c_kv, k_rope,
+      seq_idx, pos, rope_pos, page_table, batch, max_pages, cache, num_pages,
+      flags == MLA_APPEND_ROTATE, stream));
+}
+
+}  // namespace
+
+mla_status_t mla_absorb_append_q8(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                                  const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                                  void* q_full, int32_t n_app, const void* c_kv,
+                                  const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                  const int32_t* rope_pos, const int32_t* page_table,
+                                  int32_t batch, int32_t max_pages, void* cache_q8,
+                                  int64_t num_pages, int32_t flags, void* stream) {
+  return absorb_append_coded(8, cfg, n_tok, q_nope, q_rope, pos_q, w_uk, q_full, n_app, c_kv,
+                             k_rope, seq_idx, pos, rope_pos, page_table, batch, max_pages,
+                             cache_q8, num_pages, flags, stream);
+}
+
+mla_status_t mla_absorb_append_q4(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                                  const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                                  void* q_full, int32_t n_app, const void* c_kv,
+                                  const void* k_rope, const int32_t* seq_idx, const int32_t* pos,
+                                  const int32_t* rope_pos, const int32_t* page_table,
+                                  int32_t batch, int32_t max_pages, void* cache_q4,
+                                  int64_t num_pages, int32_t flags, void* stream) {
+  return absorb_append_coded(4, cfg, n_tok, q_nope, q_rope, pos_q, w_uk, q_full, n_app, c_kv,
+                             k_rope, seq_idx, pos, rope_pos, page_table, batch, max_pages,
+                             cache_q4, num_pages, flags, stream);
+}
+
 mla_status_t mla_decode_paged_q8(const mla_config_t* cfg, int32_t batch, int32_t q_len,
                                  int32_t chunk_tokens, int32_t num_splits, int32_t max_seq_len,
                                  const void* q_full, const void* cache_q8, int64_t num_pages,

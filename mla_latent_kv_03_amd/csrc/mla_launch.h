@@ -61,6 +61,17 @@ int launch_absorb_append(const Shape& s, int n_tok, const void* q_nope, const vo
                          int batch, int max_pages, void* cache, int64_t num_pages, int rotate,
                          void* stream);
 
+// a1 and the 8-bit (bits = 8) or 4-bit (bits = 4) append in one launch when
+// the absorption takes the bf16 MFMA kernel, else the two launches in order;
+// results identical to launch_absorb_q followed by launch_cache_append_q8/q4.
+int launch_absorb_append_coded(int bits, const Shape& s, int n_tok, const void* q_nope,
+                               const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                               void* q_full, int n_app, const void* c_kv, const void* k_rope,
+                               const int32_t* seq_idx, const int32_t* pos,
+                               const int32_t* rope_pos, const int32_t* page_table, int batch,
+                               int max_pages, void* cache, int64_t num_pages, int rotate,
+                               void* stream);
+
 // tree_parent: [batch][q_len] drafted-token tree (q_len <= 64), or NULL for
 // the chain of drafted tokens
 int launch_decode(const Shape& s, int batch, int q_len, int num_splits, int max_seq_len,

@@ -9,6 +9,7 @@
 #include <math.h>
 
 #include "mla_append.h"
+#include "mla_append_coded.h"
 #include "mla_combine.h"
 #include "mla_common.h"
 #include "mla_launch.h"
@@ -174,7 +175,60 @@ __global__ __launch_bounds__(256) void absorb_append_kernel(
   }
 }
 
+// a1 + the coded append (8 or 4 bits) in one launch: the absorb blocks as
+// in absorb_append_kernel, then one block per appended row running the
+// append kernel's body (append_coded_row) with 256 threads.
+template <int kBits>
+__global__ __launch_bounds__(256) void absorb_append_coded_kernel(
+    int n_tok, int H, int dn, int dc, int dr, double log2_base, const bf16_t* __restrict__ q_nope,
+    const bf16_t* __restrict__ q_rope, const int32_t* __restrict__ pos_q,
+    const bf16_t* __restrict__ w_uk, bf16_t* __restrict__ q_full, int ny, int n_abs, int page,
+    const bf16_t* __restrict__ c_kv, const bf16_t* __restrict__ k_rope,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ rope_pos, const int32_t* __restrict__ page_table, int batch,
+    int max_pages, uint8_t* __restrict__ cache, int64_t num_pages, int rotate) {
+  const int id = blockIdx.x;
+  if (id < n_abs) {
+    absorb_block(id % H, (id / H) % ny, id / (H * ny), n_tok, H, dn, dc, dr, log2_base, q_nope,
+                 q_rope, pos_q, w_uk, q_full);
+  } else {
+    append_coded_row<bf16_t, kBits>(id - n_abs, dc, dr, page, c_kv, k_rope, seq_idx, pos,
+                                    rope_pos, page_table, batch, max_pages, cache, num_pages,
+                                    rotate, log2_base);
+  }
+}
+
 bool absorb_mfma_ok(const Shape& s) { return s.dtype == 1 && s.dn % 64 == 0 && s.dc % 64 == 0; }
+
+int launch_absorb_append_coded(int bits, const Shape& s, int n_tok, const void* q_nope,
+                               const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                               void* q_full, int n_app, const void* c_kv, const void* k_rope,
+                               const int32_t* seq_idx, const int32_t* pos,
+                               const int32_t* rope_pos, const int32_t* page_table, int batch,
+                               int max_pages, void* cache, int64_t num_pages, int rotate,
+                               void* stream) {
+  if (!absorb_mfma_ok(s) || n_tok == 0 || n_app == 0) {
+    int rc = 0;
+    if (n_tok > 0) rc = launch_absorb_q(s, n_tok, q_nope, q_rope, pos_q, w_uk, q_full, stream);
+    if (rc == 0 && n_app > 0)
+      rc = bits == 8 ? launch_cache_append_q8(s, n_app, c_kv, k_rope, seq_idx, pos, rope_pos,
+                                              page_table, batch, max_pages, cache, num_pages,
+                                              rotate, stream)
+                     : launch_cache_append_q4(s, n_app, c_kv, k_rope, seq_idx, pos, rope_pos,
+                                              page_table, batch, max_pages, cache, num_pages,
+                                              rotate, stream);
+    return rc;
+  }
+  const int ny = s.dc / 64 + 1;
+  const int n_abs = s.H * ny * ((n_tok + 15) / 16);
+  auto kern = bits == 8 ? absorb_append_coded_kernel<8> : absorb_append_coded_kernel<4>;
+  hipLaunchKernelGGL(kern, dim3(n_abs + n_app), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     n_tok, s.H, s.dn, s.dc, s.dr, s.log2_base, (const bf16_t*)q_nope,
+                     (const bf16_t*)q_rope, pos_q, (const bf16_t*)w_uk, (bf16_t*)q_full, ny, n_abs,
+                     s.page, (const bf16_t*)c_kv, (const bf16_t*)k_rope, seq_idx, pos, rope_pos,
+                     page_table, batch, max_pages, (uint8_t*)cache, num_pages, rotate);
+  return (int)hipGetLastError();
+}
 
 int launch_absorb_q_mfma(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
                          const int32_t* pos, const void* w_uk, void* q_full, void* stream) {

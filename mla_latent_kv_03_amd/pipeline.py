@@ -140,9 +140,11 @@ class DecodeStep:
         B.up_project_v(self.cfg, self.o_lat, w_uv, self.out, stream)
 
     def absorb_append(self, q_nope, q_rope, w_uk, c_new, k_new, page_table, cache, stream=None):
-        if self.cache_q8:  # no fused call for the 8-bit append: the two calls in order
-            self.absorb(q_nope, q_rope, w_uk, stream)
-            self.append(c_new, k_new, page_table, cache, stream)
+        if self.cache_q8:
+            B.absorb_append_coded(self.cfg, self.cache_bits, q_nope, q_rope, self.qpos, w_uk,
+                                  self.q_full, c_new, k_new, self.seq_idx, self.slot,
+                                  None if self.tree is None else self.qpos, page_table, cache,
+                                  B.APPEND_ROTATE, stream)
         elif self.tree is None:
             B.absorb_append(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, c_new, k_new,
                             self.seq_idx, self.slot, page_table, cache, B.APPEND_ROTATE, stream)

@@ -258,6 +258,23 @@ def test_q8_entry_errors(L):
     assert L.mla_cache_append_q8(_c(odd), 8, *args, None, A16, 2, 4, A16, 16, 1, None) == 6
 
 
+def test_coded_absorb_append_errors(L):
+    a5 = [A16] * 5
+    for name in ("mla_absorb_append_q8", "mla_absorb_append_q4"):
+        f = getattr(L, name)
+        # absorb arguments first, then the append's, then the coded row shape
+        assert f(_c(V2), 4, None, *a5[:4], 4, A16, A16, A16, A16, None, A16, 2, 4, A16, 16, 1,
+                 None) == 1
+        assert f(_c(V2), 4, *a5, 4, A16, A16, A16, A16, None, A16, 2, 4, None, 16, 1, None) == 1
+        assert f(_c(V2), 4, *a5, 4, A16, A16, A16, A16, MIS, A16, 2, 4, A16, 16, 1, None) == 4
+        assert f(_c(V2), 4, *a5, 4, A16, A16, A16, A16, None, A16, 2, 4, A16, 16, 7, None) == 2
+        odd = mla.Config(num_heads=4, kv_rank=64, rope_dim=8, nope_dim=32, v_dim=32,
+                         dtype=mla.F32)
+        assert f(_c(odd), 4, *a5, 4, A16, A16, A16, A16, None, A16, 2, 4, A16, 16, 1,
+                 None) == 6
+        assert f(_c(V2), 0, *[None] * 5, 0, *[None] * 6, 1, 1, None, 1, 1, None) == 0
+
+
 def test_q4_entry_errors(L):
     assert L.mla_cache_q4_bytes_per_token(_c(V2)) == 304             # 576 / 2 + 16
     assert L.mla_cache_q4_bytes_per_token(_c(TINY)) == 0             # D = 80: not a multiple of 32

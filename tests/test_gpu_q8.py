@@ -59,6 +59,31 @@ def test_q8_decode_step_matches_oracle(name):
     check_against_oracle(case, case.results(), case.oracle())
 
 
+@pytest.mark.parametrize("name", ["v2lite_q8", "q4_chain_q8", "tree_q8", "h128_q8"])
+def test_q8_absorb_append_one_launch_bit_exact(name):
+    """mla_absorb_append_q8 gives the bits of mla_absorb_q followed by
+    mla_cache_append_q8: absorbed queries, every byte of the pool, outputs."""
+    case = Case(Q8[name], seed=4)
+    s = case.step
+    case.run(fused=False)
+    ref = {k: v.copy() for k, v in case.results().items()}
+    ref_q = to64(s.q_full)
+    ref_pool = case.pool.cpu().numpy().copy()
+    s.q_full.fill_(float("nan"))
+    # poison the rows the step writes (the drafted rows' slots), so that a
+    # fused call that wrote nothing would show
+    pt, page, Q = case.inp.page_table, case.wl.page_size, case.wl.q_len
+    for b, L in enumerate(case.inp.seq_lens):
+        for t in range(int(L) - Q, int(L)):
+            case.pool[int(pt[b, t // page]), t % page].fill_(255)
+    case.run(fused=True)
+    got = case.results()
+    assert np.array_equal(to64(s.q_full), ref_q)
+    assert np.array_equal(case.pool.cpu().numpy(), ref_pool)
+    for k in ref:
+        assert np.array_equal(got[k], ref[k], equal_nan=True), k
+
+
 @pytest.mark.parametrize("lens,Q", [((1,), 1), ((63, 64, 65), 1), ((4, 128), 4)])
 def test_q8_edge_lengths(lens, Q):
     wl = small("v2lite_paged_varlen", batch=len(lens), q_len=Q, len_range=(1, max(lens)),
