@@ -524,10 +524,11 @@ mla_status_t mla_up_project_v(const mla_config_t* cfg, int32_t n_tok, const void
  *                       o_lat, lse, stream);
  *   mla_up_project_v(cfg, batch * q_len, o_lat, w_uv, out, stream);
  * (o_lat is written as well). One launch for bf16 with d_c = 512, d_v = 128
- * and either batch*q_len*H <= 4096 with num_splits <= 32 (one block pair per
- * row: the decode-step shapes where launch latency dominates) or more rows
- * with num_splits <= 64 (one block per head and 16 tokens, reading W_UV[h]
- * once per block); the two launches otherwise. */
+ * where that is the fastest form: batch*q_len*H <= 160 with num_splits <= 32
+ * (one block pair per row: small decode steps, where launch latency
+ * dominates) or batch*q_len*H >= 2048 with num_splits <= 64 (one block per
+ * head and 16 tokens, reading W_UV[h] once per block); the two launches
+ * otherwise. */
 mla_status_t mla_combine_up_project(const mla_config_t* cfg, int32_t batch, int32_t q_len,
                                     int32_t num_splits, const float* o_part,
                                     const float* lse_part, void* o_lat, float* lse,

@@ -451,8 +451,8 @@ __global__ __launch_bounds__(384) void combine_up_v_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// a5 + a6 in one launch for many rows (more than 4,096 of them; bf16,
-// d_c = 512, d_v = 128, S <= 64): one block of 8 waves per (head h, 16
+// a5 + a6 in one launch for many rows (2,048 or more; bf16, d_c = 512,
+// d_v = 128, S <= 64): one block of 8 waves per (head h, 16
 // tokens), so W_UV[h] is read once per 16 tokens rather than once per row.
 //   merge    wave w merges rows (token n0 + 2 w + i, head h), i = 0, 1, both
 //            256-column halves, with the combine kernel's arithmetic (the
@@ -570,16 +570,22 @@ void combine_up_v_group_kernel(
   }
 }
 
-bool combine_up_v_fused_ok(const Shape& s, int n_tok, int num_splits) {
-  return s.dtype == 1 && s.dc == kFusedDc && s.dv == kFusedDv && n_tok * s.H <= 4096 &&
-         num_splits <= kFusedSplits;
-}
+// Which form merges and projects fastest (GPU time of each, measured by graph
+// replay at 16 heads and 16 or 32 partitions): the per-row kernel reads
+// W_UV[h] for every row (128 KB), so it wins only while the rows are few
+// (128 rows: 4.9 against 5.7 us for the two launches; 256: 8.2 against 6.1);
+// the per-(head, 16 tokens) kernel needs enough token groups to fill the
+// chip (1,024 rows: 16.3 against 10.7 us; 2,048: 18.4 against 18.4; 4,096:
+// 25.3 against 31.0); the two launches are best in between.
+constexpr int kRowFormMaxRows = 160;
+constexpr int kGrpFormMinRows = 2048;
 
 int launch_combine_up_project(const Shape& s, int n_tok, int num_splits, const float* o_part,
                               const float* lse_part, void* o_lat, float* lse, const void* w_uv,
                               void* out, void* stream) {
-  if (s.dtype == 1 && s.dc == kFusedDc && s.dv == kFusedDv && n_tok * s.H > 4096 &&
-      num_splits <= kGrpSplits) {
+  const bool shape_ok = s.dtype == 1 && s.dc == kFusedDc && s.dv == kFusedDv;
+  const int rows = n_tok * s.H;
+  if (shape_ok && rows >= kGrpFormMinRows && num_splits <= kGrpSplits) {
     const int blocks = s.H * ((n_tok + kGrpTok - 1) / kGrpTok);
     auto kern = num_splits <= 2 ? combine_up_v_group_kernel<2> : combine_up_v_group_kernel<4>;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kGrpWaves), 0,
@@ -587,7 +593,7 @@ int launch_combine_up_project(const Shape& s, int n_tok, int num_splits, const f
                        lse_part, (bf16_t*)o_lat, lse, (const bf16_t*)w_uv, (bf16_t*)out);
     return (int)hipGetLastError();
   }
-  if (!combine_up_v_fused_ok(s, n_tok, num_splits)) {
+  if (!(shape_ok && rows <= kRowFormMaxRows && num_splits <= kFusedSplits)) {
     int rc = launch_combine(s, n_tok * s.H, num_splits, o_part, lse_part, o_lat, lse, stream);
     if (rc == 0) rc = launch_up_project_v(s, n_tok, o_lat, w_uv, out, stream);
     return rc;

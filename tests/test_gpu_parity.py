@@ -300,10 +300,13 @@ def test_paged_equals_identity_bit_exact():
     assert np.array_equal(to64(a.step.o_part), to64(b.step.o_part))
 
 
-# above 4,096 query rows the merge + up-projection runs one block per (head,
+# from 2,048 query rows the merge + up-projection runs one block per (head,
 # 16 tokens): ragged last token groups, 128 and 12 heads (both block orders),
 # several query tokens per sequence, 1 to 64 partitions (empty ones included)
 FUSED_WIDE = {
+    "h128_2048_rows_s4": small("v2_h128_8k", batch=16, seq_len=100, num_splits=4),
+    "h16_q8_2560_rows_s3": small("v2lite_paged_varlen", batch=20, q_len=8, len_range=(8, 200),
+                                 num_splits=3),
     "h128_4480_rows_s2": small("v2_h128_8k", batch=35, seq_len=120, num_splits=2),
     "h128_4224_rows_s1": small("v2_h128_8k", batch=33, seq_len=90, num_splits=1),
     "paged_q8_5120_rows": small("v2lite_paged_varlen", batch=40, q_len=8, len_range=(8, 300),
@@ -320,7 +323,7 @@ def test_fused_calls_bit_exact(name):
     """mla_absorb_append and mla_combine_up_project give the bits of the calls they fuse."""
     if name in FUSED_WIDE:
         wl = FUSED_WIDE[name]
-        assert wl.batch * wl.q_len * wl.heads > 4096
+        assert wl.batch * wl.q_len * wl.heads >= 2048
     else:
         wl = SMALL[name] if name in SMALL else small("v2lite_32k", batch=3, heads=12, seq_len=500,
                                                       num_splits=4)
@@ -418,7 +421,7 @@ def test_invalid_sequence_gives_nan_only_there(fault):
 
 
 def test_grouped_merge_keeps_nan_rows_to_their_sequence():
-    """Above 4,096 rows the rows of an invalid sequence (NaN) share the
+    """From 2,048 rows the rows of an invalid sequence (NaN) share the
     up-projection MFMAs of their 16-token group with valid rows: only its own
     rows turn NaN, and the one launch still gives the bits of the two."""
     wl = FUSED_WIDE["paged_q8_5120_rows"]
