@@ -365,11 +365,16 @@ def main():
         if args.unfused:
             st.absorb(q_nope, q_rope, w_uk)
             st.append(c_new, k_new, pt, pool)
+        elif sparse:  # the indexer keys go in the same launch
+            mla.absorb_append_index(cfg, q_nope, q_rope, st.qpos, w_uk, st.q_full, c_new, k_new,
+                                    st.seq_idx, st.slot, pt, pool, k_idx_new,
+                                    ipools[layer % n_layers])
         else:
             st.absorb_append(q_nope, q_rope, w_uk, c_new, k_new, pt, pool)
         if sparse:
             ipool = ipools[layer % n_layers]
-            st.index_append(k_idx_new, pt, ipool)
+            if args.unfused:
+                st.index_append(k_idx_new, pt, ipool)
             if args.unfused:
                 st.index_scores(q_idx, w_idx, ipool, pt, seq_lens)
                 st.select(seq_lens)
@@ -572,7 +577,7 @@ def main():
                    "split_chunk": wl.split_chunk,
                    "layer_caches_rotated": n_layers, "hip_graph": bool(args.graph),
                    "library_calls_per_step": (5 if args.unfused else 3) +
-                                             ((3 if args.unfused else 2) if sparse else 0),
+                                             ((3 if args.unfused else 1) if sparse else 0),
                    "drafted_tree": None if wl.tree is None else list(wl.tree),
                    "cache_format": wl.cache, "cache_bytes_per_token": wl.cache_row_bytes,
                    "decode_kernel": kernel,

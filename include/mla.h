@@ -402,6 +402,27 @@ mla_status_t mla_index_append(const mla_config_t* cfg, int32_t index_dim, int32_
                               const int32_t* page_table, int32_t batch, int32_t max_pages,
                               void* index_cache, int64_t num_pages, void* stream);
 
+/* mla_absorb_append and mla_index_append in one launch, for a sparse-read
+ * step that runs all three every step: the same arguments, work and
+ * results (bit for bit) as
+ *   mla_absorb_append(cfg, n_tok, q_nope, q_rope, pos_q, w_uk, q_full, n_app,
+ *                     c_kv, k_rope, seq_idx, pos, page_table, batch,
+ *                     max_pages, cache, num_pages, flags, stream);
+ *   mla_index_append(cfg, index_dim, n_app, k_idx, seq_idx, pos, page_table,
+ *                    batch, max_pages, index_cache, num_pages, stream);
+ * (the indexer keys k_idx [n_app][index_dim] T go to the same slots as the
+ * latent rows; index_cache [num_pages][page_size][index_dim] T). One launch
+ * when the absorption runs on bf16 MFMA, three launches otherwise. Errors as
+ * for the calls (absorb, append, then indexer arguments). */
+mla_status_t mla_absorb_append_index(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                                     const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                                     void* q_full, int32_t n_app, const void* c_kv,
+                                     const void* k_rope, const int32_t* seq_idx,
+                                     const int32_t* pos, const int32_t* page_table,
+                                     int32_t batch, int32_t max_pages, void* cache,
+                                     int64_t num_pages, int32_t flags, int32_t index_dim,
+                                     const void* k_idx, void* index_cache, void* stream);
+
 /* Index scores of every cached token t < L_b for each query j:
  * scores[b][j][t] (row stride ld_scores >= max_seq_len floats) as above;
  * entries t >= L_b are not written. q_idx [batch][q_len][index_heads]

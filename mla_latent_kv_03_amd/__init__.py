@@ -74,4 +74,5 @@ from ._binding import (  # noqa: F401
     prefill_form,
     prefill_unabsorbed,
     absorb_append_coded,
+    absorb_append_index,
 )

@@ -148,6 +148,9 @@ def lib() -> ctypes.CDLL:
         "mla_prefill_unabsorbed": (ctypes.c_int, [P, I32, I32, VP, VP, VP, VP, VP, I64, VP, I32,
                                                   VP, VP, FP, VP]),
         "mla_prefill_form": (ctypes.c_char_p, [P, I32, I32]),
+        "mla_absorb_append_index": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, I32, VP, VP, VP,
+                                                   VP, VP, I32, I32, VP, I64, I32, I32, VP, VP,
+                                                   VP]),
         "mla_absorb_append_q8": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, I32, VP, VP, VP, VP,
                                                 VP, VP, I32, I32, VP, I64, I32, VP]),
         "mla_absorb_append_q4": (ctypes.c_int, [P, I32, VP, VP, VP, VP, VP, I32, VP, VP, VP, VP,
@@ -303,6 +306,21 @@ def absorb_append(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_rope
     b = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode)
     _ck(lib().mla_absorb_append(cfg.cptr(), *a, *b, _stream(stream)),
         "mla_absorb_append")
+
+
+def absorb_append_index(cfg: Config, q_nope, q_rope, pos_q, w_uk, q_full, c_kv, k_rope, seq_idx,
+                        pos, page_table, cache, k_idx, index_cache, mode: int = APPEND_ROTATE,
+                        stream=None):
+    """absorb_append and index_append (the rows' indexer keys k_idx into
+    index_cache) in one launch where possible."""
+    a = _absorb_args(cfg, q_nope, q_rope, pos_q, w_uk, q_full)
+    b = _append_args(cfg, c_kv, k_rope, seq_idx, pos, page_table, cache, mode)
+    n = b[0]
+    _, dI = _index_cache_dims(cfg, index_cache)
+    dt = _elem_dtype(cfg)
+    _ck(lib().mla_absorb_append_index(cfg.cptr(), *a, *b, dI, _need(k_idx, "k_idx", dt, n * dI),
+                                      _need(index_cache, "index_cache", dt, index_cache.numel()),
+                                      _stream(stream)), "mla_absorb_append_index")
 
 
 def _rope_pos_arg(rope_pos, n: int):

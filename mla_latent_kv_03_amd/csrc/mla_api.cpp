@@ -608,6 +608,33 @@ int32_t sparse_chunk(int32_t topk, int32_t num_splits) {
 }
 }  // namespace
 
+mla_status_t mla_absorb_append_index(const mla_config_t* cfg, int32_t n_tok, const void* q_nope,
+                                     const void* q_rope, const int32_t* pos_q, const void* w_uk,
+                                     void* q_full, int32_t n_app, const void* c_kv,
+                                     const void* k_rope, const int32_t* seq_idx,
+                                     const int32_t* pos, const int32_t* page_table,
+                                     int32_t batch, int32_t max_pages, void* cache,
+                                     int64_t num_pages, int32_t flags, int32_t index_dim,
+                                     const void* k_idx, void* index_cache, void* stream) {
+  mla_status_t st = check_absorb(cfg, n_tok, q_nope, q_rope, pos_q, w_uk, q_full);
+  if (st != MLA_OK) return st;
+  st = check_append(cfg, n_app, c_kv, k_rope, seq_idx, pos, page_table, batch, max_pages, cache,
+                    num_pages, flags);
+  if (st != MLA_OK) return st;
+  st = check_index_shape(cfg, 1, index_dim);
+  if (st != MLA_OK) return st;
+  MLA_REQUIRE((int64_t)max_pages * cfg->page_size <= INT32_MAX, MLA_ERR_CAPACITY);
+  if (n_tok == 0 && n_app == 0) return MLA_OK;
+  if (n_app > 0) {
+    MLA_CHECK_PTR(k_idx);
+    MLA_CHECK_PTR(index_cache);
+  }
+  return hip_status(mla::launch_absorb_append(
+      shape_of(cfg), n_tok, q_nope, q_rope, pos_q, w_uk, q_full, n_app, c_kv, k_rope, seq_idx, pos,
+      nullptr, page_table, batch, max_pages, cache, num_pages, flags == MLA_APPEND_ROTATE, stream,
+      index_dim, k_idx, index_cache));
+}
+
 mla_status_t mla_index_append(const mla_config_t* cfg, int32_t index_dim, int32_t n_tok,
                               const void* k_idx, const int32_t* seq_idx, const int32_t* pos,
                               const int32_t* page_table, int32_t batch, int32_t max_pages,

@@ -72,4 +72,25 @@ __device__ __forceinline__ void append_row(int n, int dc, int dr, int page, cons
   }
 }
 
+// Indexer key append (the sparse read's key cache, "DeepSeek's Config Says
+// 16 KV Heads", section 6): row n of k_new (dI elements) to slot pos[n] of
+// sequence seq_idx[n] through the latent cache's page table, copied as is;
+// invalid rows are skipped. Executed by one whole block (any size).
+template <typename T>
+__device__ __forceinline__ void index_append_row(int n, int dI, int page,
+                                                 const T* __restrict__ k_new,
+                                                 const int32_t* __restrict__ seq_idx,
+                                                 const int32_t* __restrict__ pos,
+                                                 const int32_t* __restrict__ page_table, int batch,
+                                                 int max_pages, T* __restrict__ icache,
+                                                 int64_t num_pages) {
+  const int b = seq_idx[n], p = pos[n];
+  if (b < 0 || b >= batch || p < 0 || (int64_t)p >= (int64_t)max_pages * page) return;
+  const int pg = page_table[(size_t)b * max_pages + p / page];
+  if (pg < 0 || (int64_t)pg >= num_pages) return;
+  T* dst = icache + ((size_t)pg * page + p % page) * dI;
+  const T* src = k_new + (size_t)n * dI;
+  for (int i = threadIdx.x; i < dI; i += blockDim.x) dst[i] = src[i];
+}
+
 }  // namespace mla

@@ -53,13 +53,16 @@ int launch_cache_append(const Shape& s, int n_tok, const void* c_kv, const void*
 
 // a1 and a2 of one decode step in one launch when the absorption takes the
 // bf16 MFMA kernel, else the two launches in order; results identical to
-// launch_absorb_q followed by launch_cache_append.
+// launch_absorb_q followed by launch_cache_append. With dI > 0 the rows'
+// indexer keys k_idx [n_app][dI] go to icache in the same launch (else a
+// third launch, launch_index_append).
 int launch_absorb_append(const Shape& s, int n_tok, const void* q_nope, const void* q_rope,
                          const int32_t* pos_q, const void* w_uk, void* q_full, int n_app,
                          const void* c_kv, const void* k_rope, const int32_t* seq_idx,
                          const int32_t* pos, const int32_t* rope_pos, const int32_t* page_table,
                          int batch, int max_pages, void* cache, int64_t num_pages, int rotate,
-                         void* stream);
+                         void* stream, int dI = 0, const void* k_idx = nullptr,
+                         void* icache = nullptr);
 
 // a1 and the 8-bit (bits = 8) or 4-bit (bits = 4) append in one launch when
 // the absorption takes the bf16 MFMA kernel, else the two launches in order;

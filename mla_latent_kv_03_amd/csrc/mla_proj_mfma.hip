@@ -155,8 +155,9 @@ __global__ __launch_bounds__(256) void absorb_q_mfma_kernel(
 }
 
 // a1 + a2 in one launch: blocks [0, n_abs) are the blocks of
-// absorb_q_mfma_kernel in its own order (x fastest), the next blocks append
-// one row each.
+// absorb_q_mfma_kernel in its own order (x fastest), the next n_app blocks
+// append one row each, and with dI > 0 (a sparse read) the n_app after those
+// append the rows' indexer keys.
 __global__ __launch_bounds__(256) void absorb_append_kernel(
     int n_tok, int H, int dn, int dc, int dr, double log2_base, const bf16_t* __restrict__ q_nope,
     const bf16_t* __restrict__ q_rope, const int32_t* __restrict__ pos_q,
@@ -164,14 +165,18 @@ __global__ __launch_bounds__(256) void absorb_append_kernel(
     const bf16_t* __restrict__ c_kv, const bf16_t* __restrict__ k_rope,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ rope_pos, const int32_t* __restrict__ page_table, int batch,
-    int max_pages, bf16_t* __restrict__ cache, int64_t num_pages, int rotate, int vec) {
+    int max_pages, bf16_t* __restrict__ cache, int64_t num_pages, int rotate, int vec, int n_app,
+    int dI, const bf16_t* __restrict__ k_idx, bf16_t* __restrict__ icache) {
   const int id = blockIdx.x;
   if (id < n_abs) {
     absorb_block(id % H, (id / H) % ny, id / (H * ny), n_tok, H, dn, dc, dr, log2_base, q_nope,
                  q_rope, pos_q, w_uk, q_full);
-  } else {
+  } else if (id < n_abs + n_app) {
     append_row<bf16_t>(id - n_abs, dc, dr, page, c_kv, k_rope, seq_idx, pos, rope_pos, page_table,
                        batch, max_pages, cache, num_pages, rotate, log2_base, vec);
+  } else {
+    index_append_row<bf16_t>(id - n_abs - n_app, dI, page, k_idx, seq_idx, pos, page_table, batch,
+                             max_pages, icache, num_pages);
   }
 }
 
@@ -297,23 +302,28 @@ int launch_absorb_append(const Shape& s, int n_tok, const void* q_nope, const vo
                          const void* c_kv, const void* k_rope, const int32_t* seq_idx,
                          const int32_t* pos, const int32_t* rope_pos, const int32_t* page_table,
                          int batch, int max_pages, void* cache, int64_t num_pages, int rotate,
-                         void* stream) {
+                         void* stream, int dI, const void* k_idx, void* icache) {
   if (!absorb_mfma_ok(s) || n_tok == 0 || n_app == 0) {
     int rc = 0;
     if (n_tok > 0) rc = launch_absorb_q(s, n_tok, q_nope, q_rope, pos_q, w_uk, q_full, stream);
     if (rc == 0 && n_app > 0)
       rc = launch_cache_append(s, n_app, c_kv, k_rope, seq_idx, pos, rope_pos, page_table, batch,
                                max_pages, cache, num_pages, rotate, stream);
+    if (rc == 0 && n_app > 0 && dI > 0)
+      rc = launch_index_append(s, dI, n_app, k_idx, seq_idx, pos, page_table, batch, max_pages,
+                               icache, num_pages, stream);
     return rc;
   }
   const int ny = s.dc / 64 + 1;
   const int n_abs = s.H * ny * ((n_tok + 15) / 16);
-  hipLaunchKernelGGL(absorb_append_kernel, dim3(n_abs + n_app), dim3(256), 0,
+  const int n_idx = dI > 0 ? n_app : 0;
+  hipLaunchKernelGGL(absorb_append_kernel, dim3(n_abs + n_app + n_idx), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), n_tok, s.H, s.dn, s.dc, s.dr,
                      s.log2_base, (const bf16_t*)q_nope, (const bf16_t*)q_rope, pos_q,
                      (const bf16_t*)w_uk, (bf16_t*)q_full, ny, n_abs, s.page, (const bf16_t*)c_kv,
                      (const bf16_t*)k_rope, seq_idx, pos, rope_pos, page_table, batch, max_pages,
-                     (bf16_t*)cache, num_pages, rotate, append_vectorizable(s, c_kv, cache));
+                     (bf16_t*)cache, num_pages, rotate, append_vectorizable(s, c_kv, cache), n_app,
+                     dI, (const bf16_t*)k_idx, (bf16_t*)icache);
   return (int)hipGetLastError();
 }
 

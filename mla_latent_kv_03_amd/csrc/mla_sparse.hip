@@ -15,6 +15,7 @@
 #include <mutex>
 
 #include "mla_common.h"
+#include "mla_append.h"
 #include "mla_decode_common.h"
 #include "mla_launch.h"
 
@@ -65,14 +66,8 @@ __global__ __launch_bounds__(64) void index_append_kernel(int dI, int page,
                                                           int batch, int max_pages,
                                                           T* __restrict__ icache,
                                                           int64_t num_pages) {
-  const int n = blockIdx.x;
-  const int b = seq_idx[n], p = pos[n];
-  if (b < 0 || b >= batch || p < 0 || (int64_t)p >= (int64_t)max_pages * page) return;
-  const int pg = page_table[(size_t)b * max_pages + p / page];
-  if (pg < 0 || (int64_t)pg >= num_pages) return;
-  T* dst = icache + ((size_t)pg * page + p % page) * dI;
-  const T* src = k_new + (size_t)n * dI;
-  for (int i = threadIdx.x; i < dI; i += 64) dst[i] = src[i];
+  index_append_row<T>(blockIdx.x, dI, page, k_new, seq_idx, pos, page_table, batch, max_pages,
+                      icache, num_pages);
 }
 
 // ReLU that keeps a NaN (a NaN dot must not turn into a valid score)

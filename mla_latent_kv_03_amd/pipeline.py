@@ -162,19 +162,29 @@ class DecodeStep:
         """absorb -> append (B*Q new rows) -> decode -> combine -> up-project.
 
         fused: the first two and the last two calls each as one library call
-        (mla_absorb_append, mla_combine_up_project; same results), and for a
-        sparse read the scoring and the selection (mla_index_scores_topk).
+        (mla_absorb_append, mla_combine_up_project; same results); for a
+        sparse read also the indexer-key append with the first two
+        (mla_absorb_append_index) and the scoring with the selection
+        (mla_index_scores_topk).
         sparse: (q_idx, w_idx, k_idx_new, index_cache) for a sparse read: the
         new indexer keys are appended, every cached token scored, the top
         index_topk selected, and the decode reads only those."""
-        if fused:
+        sparse_fused = (fused and self.index_topk > 0 and self.tree is None
+                        and not self.cache_q8)
+        if sparse_fused:  # absorption, latent rows and indexer keys: one call
+            q_idx, w_idx, k_idx_new, index_cache = sparse
+            B.absorb_append_index(self.cfg, q_nope, q_rope, self.qpos, w_uk, self.q_full, c_new,
+                                  k_new, self.seq_idx, self.slot, page_table, cache, k_idx_new,
+                                  index_cache, B.APPEND_ROTATE, stream)
+        elif fused:
             self.absorb_append(q_nope, q_rope, w_uk, c_new, k_new, page_table, cache, stream)
         else:
             self.absorb(q_nope, q_rope, w_uk, stream)
             self.append(c_new, k_new, page_table, cache, stream)
         if self.index_topk > 0:
             q_idx, w_idx, k_idx_new, index_cache = sparse
-            self.index_append(k_idx_new, page_table, index_cache, stream)
+            if not sparse_fused:
+                self.index_append(k_idx_new, page_table, index_cache, stream)
             if fused:
                 self.index_select(q_idx, w_idx, index_cache, page_table, seq_lens, stream)
             else:

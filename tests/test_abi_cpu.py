@@ -258,6 +258,22 @@ def test_q8_entry_errors(L):
     assert L.mla_cache_append_q8(_c(odd), 8, *args, None, A16, 2, 4, A16, 16, 1, None) == 6
 
 
+def test_absorb_append_index_errors(L):
+    a5 = [A16] * 5
+    f = L.mla_absorb_append_index
+    def call(q=A16, k_idx=A16, icache=A16, dI=128, flags=1, n_app=4, cache=A16):
+        return f(_c(V2), 4, q, *a5[1:], n_app, A16, A16, A16, A16, A16, 2, 4, cache, 16, flags, dI,
+                 k_idx, icache, None)
+    assert call(q=None) == 1                   # absorb arguments first
+    assert call(cache=None) == 1               # then the append's
+    assert call(flags=7) == 2
+    assert call(dI=100) == 2                   # then the indexer's: a multiple of 8
+    assert call(dI=0) == 2
+    assert call(k_idx=None) == 1
+    assert call(icache=MIS) == 4
+    assert f(_c(V2), 0, *[None] * 5, 0, *[None] * 5, 1, 1, None, 1, 1, 128, None, None, None) == 0
+
+
 def test_coded_absorb_append_errors(L):
     a5 = [A16] * 5
     for name in ("mla_absorb_append_q8", "mla_absorb_append_q4"):

@@ -338,6 +338,34 @@ def test_sparse_step_matches_oracle(name):
     check_against_oracle(case, case.results(), ref)
 
 
+@pytest.mark.parametrize("name", ["v2lite_step", "v2lite_q2_step", "h128_step"])
+def test_sparse_step_one_launch_append_bit_exact(name):
+    """mla_absorb_append_index gives the bits of mla_absorb_append followed by
+    mla_index_append: absorbed queries, both caches byte for byte, outputs."""
+    wl = STEP[name]
+    case = Case(wl, seed=8)
+    s = case.step
+    case.run(fused=False)
+    ref = {k: v.copy() for k, v in case.results().items()}
+    ref_q = to64(s.q_full)
+    ref_pool = case.pool.view(torch.int16).cpu().numpy().copy()
+    ref_ipool = case.index_pool.view(torch.int16).cpu().numpy().copy()
+    s.q_full.fill_(float("nan"))
+    # poison the rows the step writes, so that a call that wrote nothing shows
+    pt, page, Q = case.inp.page_table, wl.page_size, wl.q_len
+    for b, L in enumerate(case.inp.seq_lens):
+        for t in range(int(L) - Q, int(L)):
+            case.pool[int(pt[b, t // page]), t % page].fill_(float("nan"))
+            case.index_pool[int(pt[b, t // page]), t % page].fill_(float("nan"))
+    case.run(fused=True)
+    got = case.results()
+    assert np.array_equal(to64(s.q_full), ref_q)
+    assert np.array_equal(case.pool.view(torch.int16).cpu().numpy(), ref_pool)
+    assert np.array_equal(case.index_pool.view(torch.int16).cpu().numpy(), ref_ipool)
+    for k in ref:
+        assert np.array_equal(got[k], ref[k], equal_nan=True), k
+
+
 def _valid_selection(inp, K, b, j, got):
     """got is a top-K of query j that some fp32 evaluation within the error
     bound could produce: K (or all visible) distinct visible tokens in
