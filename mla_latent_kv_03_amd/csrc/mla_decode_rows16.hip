@@ -98,7 +98,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   }
   const int jq = row0 / H;  // the query of every row of the block (gather: H % 16 == 0)
   const int32_t* par = (!kGather && tree_parent) ? tree_parent + (size_t)b * Q : nullptr;
-  // a malformed tree makes the sequence invalid (the same verdict in every wave)
+  // a malformed tree makes the sequence invalid (the same decision in every wave)
   const bool bad_tree = par && !__all(lane >= Q || tree_entry_ok(par, lane));
   bool bad_len = (L < Q) || (L > max_seq_len) || bad_tree;
   int cnt = 0;  // gather: length of the query's list

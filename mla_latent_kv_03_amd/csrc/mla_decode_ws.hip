@@ -91,7 +91,7 @@ void decode_ws_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
   auto slot = [&](int k) { return lds + (k & (kWRing - 1)) * kWTChunks; };
 
   const int32_t* par = tree_parent ? tree_parent + (size_t)b * Q : nullptr;
-  // a malformed tree makes the sequence invalid (the same verdict in every wave)
+  // a malformed tree makes the sequence invalid (the same decision in every wave)
   const bool bad_tree = par && !__all(lane >= Q || tree_entry_ok(par, lane));
   const bool bad_len = (L < Q) || (L > max_seq_len) || bad_tree;
   int t0 = 0, t1 = 0;

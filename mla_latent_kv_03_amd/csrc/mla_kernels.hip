@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   const int L = seq_lens[b];
   bool bad = (L < Q) || (L > max_seq_len);
   const int32_t* par = (!kGather && tree_parent) ? tree_parent + (size_t)b * Q : nullptr;
-  if (par) {  // every thread checks every entry: the verdict is block-uniform
+  if (par) {  // every thread checks every entry: the decision is block-uniform
     for (int i = 0; i < Q; ++i) bad |= !tree_entry_ok(par, i);
   }
   int t0 = 0, t1 = 0;  // tokens (gather: list entries) of this partition

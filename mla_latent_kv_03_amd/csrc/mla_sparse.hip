@@ -567,7 +567,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(
     // the bin's last key, cut at hi (in 64 bits: the top bin may end past 2^32)
     hi = (uint32_t)min((uint64_t)hi, (uint64_t)nlo + ((1ull << sh) - 1ull));
     lo = nlo;
-    __syncthreads();  // pick and hist are rewritten next round
+    __syncthreads();  // pick and hist are rewritten in the next pass
   }
   const uint32_t T = lo;
 
