@@ -314,8 +314,17 @@ FUSED_WIDE = {
     "h12_q12_4320_rows_s64": small("v2lite_32k", batch=30, heads=12, q_len=12, seq_len=700,
                                    num_splits=64),
 }
+# the merge + up-projection's form boundaries: 160 rows (one block pair per
+# row), 176 (two launches), 2,032 (two launches), 2,048 (per head and 16
+# tokens)
+FUSED_EDGE = {
+    "b10_160_rows": small("v2lite_paged_varlen", batch=10, len_range=(1, 300), num_splits=7),
+    "b11_176_rows": small("v2lite_paged_varlen", batch=11, len_range=(1, 300), num_splits=7),
+    "b127_2032_rows": small("v2lite_paged_varlen", batch=127, len_range=(1, 200), num_splits=3),
+    "b128_2048_rows": small("v2lite_paged_varlen", batch=128, len_range=(1, 200), num_splits=3),
+}
 FUSED = ["tiny_f32", "v2lite_small", "v2lite_paged_small", "v2_h128_small", "q4_h128_small",
-         "bf16_generic_h8", "bf16_h12"] + list(FUSED_WIDE)
+         "bf16_generic_h8", "bf16_h12"] + list(FUSED_WIDE) + list(FUSED_EDGE)
 
 
 @pytest.mark.parametrize("name", FUSED)
@@ -324,6 +333,8 @@ def test_fused_calls_bit_exact(name):
     if name in FUSED_WIDE:
         wl = FUSED_WIDE[name]
         assert wl.batch * wl.q_len * wl.heads >= 2048
+    elif name in FUSED_EDGE:
+        wl = FUSED_EDGE[name]
     else:
         wl = SMALL[name] if name in SMALL else small("v2lite_32k", batch=3, heads=12, seq_len=500,
                                                       num_splits=4)
