@@ -130,9 +130,14 @@ def test_append_skips_invalid_rows():
 
 
 # ---------------------------------------------------------------- a1 absorb
-@pytest.mark.parametrize("name", ["tiny_f32", "v2lite_small", "v2_h128_small"])
-def test_absorb_q(name):
-    wl = SMALL[name].replace(batch=3, q_len=2)
+# (batch, q_len): a few tokens, and many with a ragged last 16-token group
+@pytest.mark.parametrize("name,bq", [("tiny_f32", (3, 2)), ("v2lite_small", (3, 2)),
+                                     ("v2_h128_small", (3, 2)), ("v2_h128_small", (36, 3)),
+                                     ("v2lite_small", (5, 61))],
+                         ids=["tiny_f32", "v2lite_small", "v2_h128_small", "h128_108_tokens",
+                              "h16_305_tokens"])
+def test_absorb_q(name, bq):
+    wl = SMALL[name].replace(batch=bq[0], q_len=bq[1])
     inp = workload.make(wl, 1, with_latents=False)
     cfg = mla.Config.from_workload(wl)
     dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
