@@ -10,18 +10,22 @@
 // serves all 16 query rows.
 //
 // The partition streams through a ring of four 32-token tiles in LDS, one
-// block barrier per tile. The 4 waves divide each tile's work instead of
-// taking separate tiles, so they stay in step and nothing is merged at the end:
-//   QK   wave w scores 16-token subtile (w & 1) of the tile over half (w >> 1)
-//        of the 576 columns (9 v_mfma_f32_16x16x32_bf16, M = tokens, N = 16
-//        rows) and leaves the partial S^T in LDS;
-//   max  every wave adds the two halves of both subtiles (the same values in
-//        every wave), takes the row max over the 32 tokens with two lane swaps
-//        and forms P = 2^(s - m); the running max is raised only when a score
-//        exceeds it by more than 2^8, so the accumulator rescale almost never
-//        runs (the result is exact either way: the sum uses the same max);
-//   PV   wave w accumulates latent columns [128 w, 128 w + 128) of all 16 rows
-//        (8 v_mfma_f32_16x16x32_bf16, K = 32 tokens): the A operand is P
+// block barrier per tile. The 8 waves divide each tile's work instead of
+// taking separate tiles, so they stay in step and nothing is merged at the
+// end; waves 0-3 score, waves 4-7 run the softmax and P.V, and wave w shares a
+// SIMD with wave w + 4, so one's MFMAs run under the other's vector work:
+//   QK   wave w < 4 copies rows [8 w, 8 w + 8) of every tile into the ring and
+//        scores 16-token subtile (w & 1) of the tile over half (w >> 1) of the
+//        576 columns (9 v_mfma_f32_16x16x32_bf16, M = tokens, N = 16 rows),
+//        leaving the partial S^T in LDS;
+//   max  every softmax wave adds the two halves of both subtiles (the same
+//        values in every wave), takes the row max over the 32 tokens with two
+//        lane swaps and forms P = 2^(s - m); the running max is raised only
+//        when a score exceeds it by more than 2^8, so the accumulator rescale
+//        almost never runs (the result is exact either way: the sum uses the
+//        same max);
+//   PV   wave 4 + c accumulates latent columns [128 c, 128 c + 128) of all 16
+//        rows (8 v_mfma_f32_16x16x32_bf16, K = 32 tokens): the A operand is P
 //        straight from the score layout, the B operand gathers 4 columns of 8
 //        token rows (ds_read_b64) and transposes them in registers.
 // The scores of tile k+1 are computed in the same step as P.V of tile k, so
@@ -36,7 +40,7 @@
 // the partition is a slice of the query's list of selected tokens instead of
 // a token range. The block resolves its slice to physical cache rows once
 // (index list, then page table, into LDS); each tile load then gathers its 8
-// rows per wave with per-lane 64-bit addresses. The 16 rows of a block are
+// rows per scoring wave with per-lane 64-bit addresses. The 16 rows of a block are
 // heads of one query (H % 16 == 0), so they share one list.
 #include "mla_decode_common.h"
 #include "mla_launch.h"
@@ -51,10 +55,10 @@ constexpr int kRows = 16;
 constexpr int kT = 32;                              // tokens per tile
 constexpr int kTChunks = kT * kChunks;              // 2304 chunks = 36,864 B
 constexpr int kRing = 4;                            // tiles in the LDS ring
-constexpr int kPartRows = kT / kWaves;              // 8 rows of each tile per wave
+constexpr int kPartRows = kT / kWaves;              // 8 rows of each tile per scoring wave
 constexpr int kPartChunks = kPartRows * kChunks;    // 576 chunks
-constexpr int kPartLoads = kPartChunks / 64;        // 9 loads per wave per tile
-constexpr int kHalfSteps = kKSteps / 2;             // 9 QK k-steps per wave
+constexpr int kPartLoads = kPartChunks / 64;        // 9 loads per scoring wave per tile
+constexpr int kHalfSteps = kKSteps / 2;             // 9 QK k-steps per scoring wave
 constexpr size_t kRingBytes = (size_t)kRing * kTChunks * 16;   // 147,456 B
 constexpr size_t kScoreBytes = (size_t)2 * kWaves * 64 * 16;   // 8,192 B
 constexpr size_t kLdsBytes = kRingBytes + kScoreBytes;         // 155,648 B
@@ -69,7 +73,7 @@ static_assert(kGatherMaxChunk % kT == 0, "whole tiles");
 }  // namespace
 
 template <bool kGather>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_len,
                           float scale_log2, int units, int groups,
                           const bf16_t* __restrict__ q_full,
@@ -87,7 +91,11 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 15, kg = lane >> 4;
-  const int sub = wave & 1, khalf = wave >> 1;  // QK share: subtile, half of the columns
+  // waves 0-3 score (and copy the tiles), waves 4-7 run the softmax and P.V;
+  // wave w and w + 4 share a SIMD
+  const bool qk_wave = wave < kWaves;
+  const int role = wave & (kWaves - 1);  // QK: the wave's task; PV: its column block
+  const int sub = role & 1, khalf = role >> 1;  // QK share: subtile, half of the columns
   const int s = unit % S;
   int L, b;
   if constexpr (kGather) {
@@ -126,7 +134,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   auto slot = [&](int k) { return lds + (k & (kRing - 1)) * kTChunks; };
 
   RowDma<kPartLoads> dma;
-  dma.init(wave * kPartChunks, lane, wave * kPartRows);
+  dma.init(role * kPartChunks, lane, role * kPartRows);
   PageWindow pw;
   if constexpr (!kGather) {
     // the page window (lane i: unit page i of the partition) is copied into
@@ -136,7 +144,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
     pw.upages = (t1 - t0 + page - 1) / page;
     pw.base = 0;
     pw.reg = 0;
-    if (ntiles > 0) {  // then pw.upages >= 1
+    if (qk_wave && ntiles > 0) {  // then pw.upages >= 1
       const int* win = reinterpret_cast<const int*>(sc) + 64 * wave;
       const int* src = pw.row + min(lane, pw.upages - 1);
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
@@ -162,7 +170,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
     const int32_t* lst = sel_idx + ((size_t)b * Q + jq) * topk;
     const int vis = L - Q + jq;  // the query's own position
     const int nfill = ntiles * kT;
-    for (int i = threadIdx.x; i < nfill; i += 256) {
+    for (int i = threadIdx.x; i < nfill; i += blockDim.x) {
       int row = 0;
       if (i < t1 - t0) {
         const int t = lst[t0 + i];
@@ -176,14 +184,14 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
     }
     __syncthreads();
   }
-  // this wave's rows [8 wave, 8 wave + 8) of tile k (never across a page: 8 | page)
+  // this (QK) wave's rows [8 role, 8 role + 8) of tile k (never across a page: 8 | page)
   auto issue = [&](int k) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(slot(k) + wave * kPartChunks));
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(slot(k) + role * kPartChunks));
     if constexpr (kGather) {
       // load i covers part chunks [64 i, 64 i + 64): rows ra and ra + 1, lane
       // l of load i reading row ra + (l >= split); dma.off[i] holds
       // (that row) * row bytes + the swizzled chunk offset
-      const int lt = k * kT + wave * kPartRows;
+      const int lt = k * kT + role * kPartRows;
       const int4 r03 = *reinterpret_cast<const int4*>(rows + lt);
       const int4 r47 = *reinterpret_cast<const int4*>(rows + lt + 4);
       const int rr[kPartRows] = {r03.x, r03.y, r03.z, r03.w, r47.x, r47.y, r47.z, r47.w};
@@ -202,7 +210,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
                      : "memory");
       }
     } else {
-      const int t = t0 + k * kT + wave * kPartRows;
+      const int t = t0 + k * kT + role * kPartRows;
       int pg = pw.get((t - t0) / page, lane);
       if (pg < 0 || (int64_t)pg >= num_pages) {
         bad = true;
@@ -229,9 +237,11 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
     // ---- prologue: queries (waves 0, 1: 8 rows each, into slot 3, issued
     // above), tiles 0..2
     const int pre = min(ntiles, kRing - 1);  // (the queries are already on their way)
-    issue(0);
-    if (pre > 1) issue(1);
-    if (pre > 2) issue(2);
+    if (qk_wave) {
+      issue(0);
+      if (pre > 1) issue(1);
+      if (pre > 2) issue(2);
+    }
     if (wave < 2) {  // own query rows landed (the tiles behind them may still fly)
       if (pre == 3)
         wait_vmcnt<3 * kPartLoads>();
@@ -243,7 +253,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
     __syncthreads();
     // queries: row n, k-steps [9 khalf, 9 khalf + 9), chunk 4 ks + kg
     bf16x8_t qreg[kHalfSteps];
-    {
+    if (qk_wave) {
       const u32x4_t* qb = slot(kRing - 1);
 #pragma unroll
       for (int j = 0; j < kHalfSteps; ++j) {
@@ -254,14 +264,16 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
       for (int j = 0; j < kHalfSteps; ++j) settle(qreg[j]);
     }
     // own part of tile 0
-    if (pre == 3)
-      wait_vmcnt<2 * kPartLoads>();
-    else if (pre == 2)
-      wait_vmcnt<kPartLoads>();
-    else
-      wait_vmcnt<0>();
-    if (t0 + kT > t1)  // rows past the partition end (may be poison)
-      zero_rows<kPartLoads>(slot(0) + wave * kPartChunks, wave * kPartChunks, lane, t1 - t0);
+    if (qk_wave) {
+      if (pre == 3)
+        wait_vmcnt<2 * kPartLoads>();
+      else if (pre == 2)
+        wait_vmcnt<kPartLoads>();
+      else
+        wait_vmcnt<0>();
+      if (t0 + kT > t1)  // rows past the partition end (may be poison)
+        zero_rows<kPartLoads>(slot(0) + role * kPartChunks, role * kPartChunks, lane, t1 - t0);
+    }
     __syncthreads();
 
     // LDS addressing inside a tile. QK: row 16 sub + n, chunk 4 ks + kg.
@@ -272,7 +284,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = (j < 4) ? 4 * kg + j : 16 + 4 * kg + (j - 4);
-      pv[j] = 16 * (t * kChunks + ((2 * wave * 8 + (n >> 1)) ^ (t & 7))) + 8 * (n & 1);
+      pv[j] = 16 * (t * kChunks + ((2 * role * 8 + (n >> 1)) ^ (t & 7))) + 8 * (n & 1);
     }
 
     // scores of this wave's share of tile k into score buffer k & 1
@@ -289,25 +301,28 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
       for (int j = 0; j < kHalfSteps; ++j)
         c2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[j]),
                                                             qreg[j], c2[j & 1], 0, 0, 0);
-      sc[((k & 1) * kWaves + wave) * 64 + lane] = c2[0] + c2[1];
+      sc[((k & 1) * kWaves + role) * 64 + lane] = c2[0] + c2[1];
     };
-    qk(0);
+    if (qk_wave) qk(0);
 
     for (int k = 0; k < ntiles; ++k) {
-      if (k + 1 < ntiles) {  // own part of tile k+1 (tile k+2 may stay in flight)
+      if (qk_wave && k + 1 < ntiles) {  // own part of tile k+1 (tile k+2 may stay in flight)
         if (k + 2 < ntiles)
           wait_vmcnt<kPartLoads>();
         else
           wait_vmcnt<0>();
         const int ts1 = t0 + (k + 1) * kT;
         if (ts1 + kT > t1)
-          zero_rows<kPartLoads>(slot(k + 1) + wave * kPartChunks, wave * kPartChunks, lane, t1 - ts1);
+          zero_rows<kPartLoads>(slot(k + 1) + role * kPartChunks, role * kPartChunks, lane, t1 - ts1);
       }
       // tile k+1 landed for every wave, the scores of tile k are complete, and
       // slot k-1 (= slot k+3) is no longer read by anyone
       __syncthreads();
-      if (k + 3 < ntiles) issue(k + 3);
-      if (k + 1 < ntiles) qk(k + 1);
+      if (qk_wave) {
+        if (k + 3 < ntiles) issue(k + 3);
+        if (k + 1 < ntiles) qk(k + 1);
+        continue;
+      }
 
       // ---- softmax over the tile's 32 tokens (lane: row n, tokens sigma(kg, j))
       const int ts = t0 + k * kT;
@@ -384,7 +399,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   }
   wait_vmcnt<0>();
 
-  // ---- write rows row0 .. row0+15, columns [128 wave, 128 wave + 128) ------
+  // ---- the softmax waves write rows row0 .. row0+15, columns [128 role, 128 role + 128)
   const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
   const float nanv = __int_as_float(0x7fc00000);
   const float l_row = row_sum4(l_run);
@@ -396,9 +411,9 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
   }
   // an empty partition (no tokens) leaves its o_part rows unwritten
 #pragma unroll
-  for (int r = 0; r < 4 && (t1 > t0 || any_bad); ++r) {
+  for (int r = 0; r < 4 && !qk_wave && (t1 > t0 || any_bad); ++r) {
     const int orow = row0 + 4 * kg + r;
-    float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + 128 * wave + 4 * n;
+    float* dst = o_part + (((size_t)b * R + orow) * S + s) * kDC + 128 * role + 4 * n;
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       float4 v = make_float4(acc[f][0][r] * inv[r], acc[f][1][r] * inv[r], acc[f][2][r] * inv[r],
@@ -407,7 +422,7 @@ void decode_rows16_kernel(int Q, int H, int S, int page, int fixed, int max_seq_
       *reinterpret_cast<float4*>(dst + f * 64) = v;
     }
   }
-  if (wave == 0 && kg == 0) {
+  if (wave == kWaves && kg == 0) {
     const float lse = l_row > 0.0f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
     lse_part[((size_t)b * R + row0 + n) * S + s] = any_bad ? nanv : lse;
   }
@@ -434,7 +449,7 @@ int launch_decode_rows16(const Shape& s, int batch, int q_len, int num_splits, i
   const int units = batch * num_splits;
   const int groups = q_len * s.H / kRows;
   const int blocks = grid_blocks(units, groups);
-  hipLaunchKernelGGL(decode_rows16_kernel<false>, dim3(blocks), dim3(256), kLdsBytes,
+  hipLaunchKernelGGL(decode_rows16_kernel<false>, dim3(blocks), dim3(2 * kWaves * 64), kLdsBytes,
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page,
                      s.split_fixed, max_seq_len, s.scale * 1.4426950408889634f, units, groups,
                      (const bf16_t*)q_full, (const bf16_t*)cache, num_pages, page_table, max_pages,
@@ -454,7 +469,7 @@ int launch_decode_sparse_rows16(const Shape& s, int batch, int q_len, int topk, 
   const int units = batch * num_splits;
   const int groups = q_len * s.H / kRows;
   const int blocks = grid_blocks(units, groups);
-  hipLaunchKernelGGL(decode_rows16_kernel<true>, dim3(blocks), dim3(256), kGatherLdsBytes,
+  hipLaunchKernelGGL(decode_rows16_kernel<true>, dim3(blocks), dim3(2 * kWaves * 64), kGatherLdsBytes,
                      reinterpret_cast<hipStream_t>(stream), q_len, s.H, num_splits, s.page, chunk,
                      max_seq_len, s.scale * 1.4426950408889634f, units, groups,
                      (const bf16_t*)q_full, (const bf16_t*)cache, num_pages, page_table, max_pages,
