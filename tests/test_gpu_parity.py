@@ -39,6 +39,11 @@ SMALL = {
     "f32_ragged": small("tiny_f32", batch=3, seq_len=None, len_range=(1, 300), paged=True,
                         num_splits=3),
     "bf16_generic_h8": small("v2lite_32k", batch=2, heads=8, seq_len=333, num_splits=2),
+    # other head counts the bf16 kernels take: 64 (one 64-row group, the
+    # Kimi K2 width), 48 (three 16-row groups), 32 x 2 queries (a chain)
+    "h64_small": small("v2_h128_8k", batch=2, heads=64, seq_len=777, num_splits=3),
+    "h48_small": small("v2lite_32k", batch=2, heads=48, seq_len=400, num_splits=3),
+    "h32_q2_small": small("v2lite_32k", batch=2, heads=32, q_len=2, seq_len=500, num_splits=2),
     # fixed-size partitions: short sequences leave most partitions empty
     "v2lite_chunked": small("v2lite_paged_varlen", batch=6, len_range=(1, 900), num_splits=8,
                             split_chunk=128),
